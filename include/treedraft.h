@@ -1,0 +1,194 @@
+/*
+ * treedraft.h -- C ABI of the MI355X (gfx950) verify-side path of budget-aware
+ * tree speculative decoding over block-diffusion drafts.
+ *
+ * The method (BASTION: "Bastion: Budget-Aware Speculative Decoding with
+ * Tree-structured Block Diffusion Drafting", technical summary, "Methodik")
+ * turns the drafter's per-position marginals q_k into a prefix-closed draft
+ * tree, sizes the tree with an online budget controller, and has the target
+ * verify the whole tree in one parallel pass.  The five calls below are the
+ * steps of one verify step:
+ *
+ *   td_draft_topk        log-softmax normaliser and top-K of every position
+ *   td_build_tree        best-first tree with the S(N) stop
+ *   td_tree_mask         bit-packed ancestor-or-self masks
+ *   td_tree_verify_attn  tree attention against context KV + tree KV
+ *   td_accept            greedy acceptance walk and bonus token
+ *
+ * Conventions shared by every call
+ *  - Every array pointer is DEVICE memory owned by the caller, unless a
+ *    comment says otherwise.  The library allocates nothing and keeps no
+ *    state besides a thread-local error string and a per-device property
+ *    cache.
+ *  - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t;
+ *    NULL = the default stream).  TD_OK means "validated and enqueued".
+ *    Tree sizes (n_nodes) stay on the device: no call waits for the host.
+ *  - Validation runs first; on any status other than TD_OK nothing was
+ *    enqueued and td_last_error() describes the problem.
+ *  - All arrays are C-contiguous in the layouts stated per call.
+ *  - bf16 is IEEE binary32 truncated to its upper 16 bits (bfloat16).
+ *  - Calls are reentrant; concurrent calls on different streams are safe as
+ *    long as they do not share output or workspace buffers.
+ */
+#ifndef TREEDRAFT_H
+#define TREEDRAFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TD_ABI_VERSION 1
+
+/* Compiled capacities. */
+#define TD_MAX_TOPK 32        /* K */
+#define TD_MAX_BLOCK 32       /* drafter block positions B */
+#define TD_MAX_NODES 255      /* n_max: draft nodes per tree (root excluded) */
+#define TD_MAX_VOCAB 262144   /* token ids must fit in 18 bits */
+#define TD_MAX_BATCH 4096
+
+typedef enum {
+    TD_OK = 0,
+    TD_EINVAL = 1,        /* null pointer, bad size, misaligned buffer, too small workspace */
+    TD_ECAPACITY = 2,     /* a size above the compiled capacities */
+    TD_EUNSUPPORTED = 3,  /* dtype / head_dim combination not built */
+    TD_EHIP = 4           /* the HIP runtime reported an error at launch */
+} td_status;
+
+typedef enum { TD_F32 = 0, TD_BF16 = 1 } td_dtype;
+
+int td_abi_version(void);
+
+/* Text of the last non-OK status returned on the calling thread ("" if none). */
+const char *td_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * td_draft_topk -- stage (a).
+ * The path score of a tree node is the product of the drafter's marginals
+ * q_k along its path (Methodik §1, path scoring).  For every (sequence b,
+ * block position k) this computes, over the FULL vocabulary:
+ *   lse[b][k]        = log sum_v exp(l[b][k][v])                 (float64)
+ *   topk_id[b][k][j] = the j-th largest logit's token id; ties go to the
+ *                      smaller id; j = 0..K-1                     (int32)
+ *   topk_logq[b][k][j] = l[b][k][topk_id] - lse[b][k] = log q_k    (float64)
+ * Inputs:
+ *   logits      [batch][block][*] with row (b,k) starting at element
+ *               (b*block + k) * pos_stride; vocab entries per row are used.
+ *               dtype TD_F32 or TD_BF16.  The base pointer must be aligned
+ *               to the element size (rows aligned to 16 bytes stream fastest).
+ *   1 <= K <= min(TD_MAX_TOPK, vocab); 1 <= block <= TD_MAX_BLOCK.
+ * Workspace: at least td_draft_topk_workspace(batch, block, vocab, K) bytes
+ *   of device memory, 16-byte aligned; contents need no initialisation and
+ *   are garbage afterwards.
+ */
+size_t td_draft_topk_workspace(int32_t batch, int32_t block, int32_t vocab, int32_t K);
+td_status td_draft_topk(const void *logits, td_dtype dtype, int32_t batch, int32_t block,
+                        int32_t vocab, int64_t pos_stride, int32_t K, int32_t *topk_id,
+                        double *topk_logq, double *lse, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * td_build_tree -- stage (b).
+ * Best-first construction of the prefix-closed draft tree (Methodik §2):
+ * starting from the root (the last verified token, depth 0, rho = 1), the
+ * valid candidate with the largest path score rho is added until the budget
+ * is used.  The children of a node at depth d are the top-K tokens of
+ * position d+1, with log rho(child) = log rho(node) + log q_{d+1}(token).
+ * Candidates are ordered by log rho descending, then depth ascending, then
+ * token id ascending, then parent index ascending (a total order).
+ * With use_stop != 0 the online budget controller (Methodik §3) inserts the
+ * next candidate only while the estimated speedup rises:
+ *   A_hat(n) = ahat0 + sum_{i=1..n} rho(i),
+ *   C(n)     = cost_a + cost_b*n + cost_c*max(0, n - cost_knee),
+ *   S(n)     = A_hat(n) * l_ar / C(n),
+ * stopping before node n+1 when S(n+1) <= S(n).  Otherwise exactly
+ * min(n_max, available candidates) nodes are inserted.  log rho, A_hat and S
+ * are accumulated in float64.
+ * Inputs:  topk_id [batch][block][K], topk_logq [batch][block][K] as written
+ *          by td_draft_topk; root_token [batch] or NULL (then -1 is stored).
+ * Outputs (index 0 = root; nodes in insertion order, parent index < child):
+ *   n_nodes     [batch]           number of draft nodes N (root excluded)
+ *   node_token  [batch][n_max+1]  token id (-1 beyond N)
+ *   node_parent [batch][n_max+1]  parent index (-1 for the root and beyond N)
+ *   node_depth  [batch][n_max+1]  depth (-1 beyond N)
+ *   node_logrho [batch][n_max+1]  log rho (0 for the root and beyond N)
+ *   ahat        [batch]           A_hat(N)                     (may be NULL)
+ *   speedup     [batch]           S(N)                         (may be NULL)
+ * 0 <= n_max <= TD_MAX_NODES.
+ */
+td_status td_build_tree(const int32_t *topk_id, const double *topk_logq, int32_t batch,
+                        int32_t block, int32_t K, int32_t n_max, int32_t use_stop, double cost_a,
+                        double cost_b, double cost_c, int32_t cost_knee, double l_ar,
+                        double ahat0, const int32_t *root_token, int32_t *n_nodes,
+                        int32_t *node_token, int32_t *node_parent, int32_t *node_depth,
+                        double *node_logrho, double *ahat, double *speedup, void *stream);
+
+/* ------------------------------------------------------------------------
+ * td_tree_mask -- stage (b').
+ * Bit-packed ancestor-or-self mask of every tree row: bit j of row i is set
+ * iff node j lies on the root path of node i (i included), so that a tree
+ * query sees only its own prefix.  Row i = row(parent(i)) | (1 << i).
+ * Inputs:  node_parent [batch][nq_max], n_nodes [batch] (nq_max = n_max+1).
+ * Output:  mask [batch][nq_max][words], words = (nq_max + 63) / 64; bit j of
+ *          a row is bit (j % 64) of word j / 64.  Rows beyond n_nodes are 0.
+ */
+td_status td_tree_mask(const int32_t *node_parent, const int32_t *n_nodes, int32_t batch,
+                       int32_t nq_max, uint64_t *mask, void *stream);
+
+/* ------------------------------------------------------------------------
+ * td_tree_verify_attn -- stage (c).
+ * The target verifies the whole tree in one parallel pass (Methodik; tree
+ * verification).  For sequence b, query head h and tree row i <= n_nodes[b]:
+ *   out[b][i][h] = sum_j softmax_j(scale * q[b][i][h] . k_j) v_j
+ * over the admitted keys j: all context keys of b, plus the tree keys whose
+ * bit is set in mask row (b, i).  KV head of query head h is h / (hq/hkv).
+ * Rows i > n_nodes[b] are written as zeros.
+ * Inputs:
+ *   q        [batch][nq_max][hq][head_dim]
+ *   k_ctx, v_ctx [total_ctx][hkv][head_dim]; sequence b owns context rows
+ *            ctx_offsets[b] .. ctx_offsets[b+1]-1 (ctx_offsets int64
+ *            [batch+1], device, non-decreasing, ctx_offsets[0] = 0,
+ *            ctx_offsets[batch] = total_ctx).  max_ctx >= every length.
+ *   k_tree, v_tree [batch][nq_max][hkv][head_dim]
+ *   mask     as written by td_tree_mask; n_nodes [batch].
+ *   dtype TD_BF16 or TD_F32 (all of q/k/v/out); head_dim 64 or 128.
+ *   Accumulation is float32; out has the input dtype.
+ * Workspace: td_tree_verify_attn_workspace(...) bytes, 16-byte aligned, no
+ *   initialisation needed.
+ */
+size_t td_tree_verify_attn_workspace(int32_t batch, int32_t nq_max, int32_t hq, int32_t hkv,
+                                     int32_t head_dim, int64_t total_ctx, int64_t max_ctx);
+td_status td_tree_verify_attn(const void *q, const void *k_ctx, const void *v_ctx,
+                              const int64_t *ctx_offsets, int64_t total_ctx, int64_t max_ctx,
+                              const void *k_tree, const void *v_tree, const uint64_t *mask,
+                              const int32_t *n_nodes, int32_t batch, int32_t nq_max, int32_t hq,
+                              int32_t hkv, int32_t head_dim, float scale, td_dtype dtype,
+                              void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * td_accept -- stage (d).
+ * Greedy verification at temperature 0 (Experimental results: greedy
+ * decoding): from the root, step to the child whose token equals the
+ * target's greedy token at the current node, while one exists.  The number
+ * of steps is the accepted length A; the target's token at the last
+ * accepted node is the bonus token (the correct token at the first
+ * rejection point).
+ * Inputs:  node_token, node_parent [batch][n_max+1], n_nodes [batch] as
+ *          written by td_build_tree (siblings carry distinct tokens);
+ *          target_token [batch][n_max+1]: the target's greedy token at every
+ *          node 0..n_nodes[b].
+ * Outputs: accept_len [batch]; accept_path [batch][block+1]: node indices,
+ *          root first, -1 padded; bonus_token [batch].
+ */
+td_status td_accept(const int32_t *node_token, const int32_t *node_parent, const int32_t *n_nodes,
+                    const int32_t *target_token, int32_t batch, int32_t n_max, int32_t block,
+                    int32_t *accept_len, int32_t *accept_path, int32_t *bonus_token,
+                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREEDRAFT_H */

@@ -1,0 +1,121 @@
+"""Shared test utilities: oracle pipelines on workload inputs and the tree
+comparison with the near-tie exclusion.
+
+Tree parity rule: node sets and insertion order must match the oracle
+exactly, except where the oracle's own scores leave the order undecided to
+within the tolerance: two nodes whose oracle log rho differ by less than
+TIE (1e-5) may swap (which may renumber their subtrees), and the stop index
+may differ where the oracle's ln S changes by less than TIE.  Trees are
+compared by token path, so renumbering is harmless.
+"""
+import math
+
+import numpy as np
+
+import oracle
+from tree_draft_build_amd import workload as wl
+
+TIE = 1e-5          # near-tie band for log rho and ln S
+LOGRHO_TOL = 1e-5   # |log rho_gpu - log rho_oracle|
+
+
+def cost_of(cfg):
+    return (cfg.cost_a, cfg.cost_b, cfg.cost_c, cfg.cost_knee)
+
+
+def oracle_front(cfg, logits):
+    """Oracle stages (a) and (b) on stored logits: returns topk tables and
+    the stopped tree plus the fixed-budget tree (for the near-tie rules)."""
+    ids, lq, lse = oracle.draft_topk(logits, cfg.topk)
+    tree = oracle.build_tree(ids, lq, cfg.n_max, cfg.use_stop, cost_of(cfg), cfg.l_ar, cfg.ahat0)
+    full = oracle.build_tree(ids, lq, cfg.n_max, False, cost_of(cfg), cfg.l_ar, cfg.ahat0,
+                             want_curve=True)
+    return dict(ids=ids, lq=lq, lse=lse, tree=tree, full=full)
+
+
+def paths_of(node_token, node_parent, n):
+    paths = [()]
+    for j in range(1, n + 1):
+        p = int(node_parent[j])
+        assert 0 <= p < j, f"parent {p} of node {j} is not an earlier node"
+        paths.append(paths[p] + (int(node_token[j]),))
+    return paths
+
+
+def oracle_logrho_of_path(ids, lq, path):
+    """log rho of a token path under the oracle's top-K tables (None if a
+    token is not in its position's top-K)."""
+    lr = 0.0
+    for d, tok in enumerate(path):
+        row = list(ids[d])
+        if tok not in row:
+            return None
+        lr = lr + lq[d][row.index(tok)]
+    return lr
+
+
+def compare_tree(b, gpu, orc, stop: bool):
+    """Compare the GPU tree of sequence b with the oracle.
+    gpu: dict of numpy node arrays; orc: oracle_front() result.
+    Returns the number of near-tie exemptions used."""
+    ids, lq = orc["ids"][b], orc["lq"][b]
+    full = orc["full"]
+    n_full = int(full["n_nodes"][b])
+    po = paths_of(full["node_token"][b], full["node_parent"][b], n_full)
+    lro = full["node_logrho"][b]
+    n_o = int(orc["tree"]["n_nodes"][b]) if stop else n_full
+    n_g = int(gpu["n_nodes"][b])
+    pg = paths_of(gpu["node_token"][b], gpu["node_parent"][b], n_g)
+    exemptions = 0
+    # stop index
+    if n_g != n_o:
+        assert stop, f"seq {b}: fixed budget but n_nodes {n_g} != {n_o}"
+        S = full["s_curve"][b]
+        for n in range(min(n_g, n_o), max(n_g, n_o)):
+            assert abs(math.log(S[n + 1]) - math.log(S[n])) < TIE, \
+                f"seq {b}: stop at {n_g} vs oracle {n_o}, S step at {n} is not a near tie"
+        exemptions += 1
+    # every GPU node: depth, scores, and its slot in the oracle's order
+    for k in range(1, n_g + 1):
+        assert int(gpu["node_depth"][b][k]) == len(pg[k])
+        lr_o = oracle_logrho_of_path(ids, lq, pg[k])
+        assert lr_o is not None, f"seq {b}: node {k} path {pg[k]} leaves the top-K"
+        assert abs(gpu["node_logrho"][b][k] - lr_o) < LOGRHO_TOL, \
+            f"seq {b}: node {k} log rho {gpu['node_logrho'][b][k]} vs {lr_o}"
+        if k <= n_full and pg[k] != po[k]:
+            assert abs(lr_o - lro[k]) < TIE, \
+                f"seq {b}: node {k} is {pg[k]} (lr {lr_o}) but the oracle has {po[k]} (lr {lro[k]})"
+            exemptions += 1
+    # node sets: anything missing from the oracle prefix must sit at a near tie
+    set_g, set_o = set(pg[1:]), set(po[1:n_g + 1])
+    if set_g != set_o and n_g < n_full:
+        cut = lro[n_g]
+        for p in set_g ^ set_o:
+            lr_p = oracle_logrho_of_path(ids, lq, p)
+            assert abs(lr_p - cut) < TIE, f"seq {b}: node {p} differs away from the cut"
+        exemptions += 1
+    # padding
+    assert np.all(gpu["node_token"][b][n_g + 1:] == -1)
+    assert np.all(gpu["node_parent"][b][n_g + 1:] == -1)
+    return exemptions
+
+
+def targets_by_path(cfg, logits_f64, gpu_tree, seqs=None):
+    """Synthetic target tokens for the GPU tree's nodes (keyed by path)."""
+    return wl.target_tokens(cfg, logits_f64, gpu_tree["node_token"], gpu_tree["node_parent"],
+                            gpu_tree["n_nodes"], seqs=seqs)
+
+
+def attn_close(got, want, dtype, what=""):
+    """Attention parity: absolute bound (2e-2 bf16, 1e-4 f32) and, as extra
+    evidence, a relative Frobenius bound per (row, head) block."""
+    atol = 2e-2 if dtype == "bf16" else 1e-4
+    rel = 1e-2 if dtype == "bf16" else 1e-5
+    err = np.abs(got - want)
+    assert err.max() <= atol, f"{what}: max abs err {err.max():.3g} > {atol}"
+    num = np.sqrt((err ** 2).sum(-1))
+    den = np.sqrt((want ** 2).sum(-1))
+    ok = den > 0
+    worst = (num[ok] / den[ok]).max() if ok.any() else 0.0
+    assert worst <= rel, f"{what}: relative Frobenius error {worst:.3g} > {rel}"
+    assert np.all(got[~ok] == 0), f"{what}: rows that must be zero are not"

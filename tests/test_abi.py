@@ -1,0 +1,100 @@
+"""The C-ABI library on the host: it loads, exports every function declared
+in include/treedraft.h, and its argument validation rejects bad calls before
+any GPU work is enqueued (no GPU needed: validation runs first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "treedraft.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(td_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def b():
+    from tree_draft_build_amd import binding
+    return binding
+
+
+def test_every_declared_symbol_is_exported(b):
+    names = declared_functions()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(b.lib, n), n
+    assert sorted(b.EXPORTED) == names
+
+
+def test_abi_version(b):
+    assert b.lib.td_abi_version() == 1
+
+
+def test_workspace_queries(b):
+    assert b.draft_topk_workspace(1, 16, 151936, 8) > 0
+    assert b.draft_topk_workspace(0, 16, 151936, 8) == 0
+    w1 = b.tree_verify_attn_workspace(1, 65, 32, 8, 128, 4096, 4096)
+    w2 = b.tree_verify_attn_workspace(1, 65, 32, 8, 128, 8192, 8192)
+    assert 0 < w1 <= w2
+    assert b.tree_verify_attn_workspace(1, 65, 32, 7, 128, 4096, 4096) == 0  # hq % hkv
+
+
+P = ctypes.c_void_p
+FAKE = P(4096)          # never dereferenced: validation fails before any launch
+FAKE8 = P(4096 + 8)     # 8-byte but not 16-byte aligned
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    ((None, 1, 1, 16, 1000, 1000, 8, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), 1, "null"),
+    ((FAKE, 1, 1, 16, 1000, 1000, 0, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), 1, "positive"),
+    ((FAKE, 1, 1, 16, 1000, 1000, 33, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), 2, "TD_MAX_TOPK"),
+    ((FAKE, 1, 1, 16, 4, 4, 8, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), 1, "exceeds"),
+    ((FAKE, 1, 1, 33, 1000, 1000, 8, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), 2, "block"),
+    ((FAKE, 7, 1, 16, 1000, 1000, 8, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), 3, "dtype"),
+    ((FAKE, 1, 1, 16, 1000, 999, 8, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), 1, "pos_stride"),
+    ((P(4097), 1, 1, 16, 1000, 1000, 8, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), 1, "element"),
+    ((P(4098), 0, 1, 16, 1000, 1000, 8, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), 1, "element"),
+    ((FAKE, 1, 1, 16, 1000, 1000, 8, FAKE, FAKE, FAKE, FAKE, 16, None), 1, "workspace"),
+])
+def test_draft_topk_validation(b, args, status, needle):
+    assert b.lib.td_draft_topk(*args) == status
+    assert needle in b.last_error()
+
+
+def test_build_tree_validation(b):
+    base = [FAKE, FAKE, 1, 16, 8, 64, 1, 1.0, 0.005, 0.03, 32, 1.0, 1.0, None, FAKE, FAKE, FAKE,
+            FAKE, FAKE, None, None, None]
+    bad = list(base); bad[5] = 256
+    assert b.lib.td_build_tree(*bad) == 2 and "capacity" in b.last_error()
+    bad = list(base); bad[0] = None
+    assert b.lib.td_build_tree(*bad) == 1
+    bad = list(base); bad[5] = -1
+    assert b.lib.td_build_tree(*bad) == 1
+
+
+def test_mask_accept_validation(b):
+    assert b.lib.td_tree_mask(FAKE, FAKE, 1, 257, FAKE, None) == 2
+    assert b.lib.td_tree_mask(FAKE, FAKE, 1, 65, P(4097), None) == 1     # misaligned mask
+    assert b.lib.td_accept(FAKE, FAKE, FAKE, None, 1, 64, 16, FAKE, FAKE, FAKE, None) == 1
+    assert b.lib.td_accept(FAKE, FAKE, FAKE, FAKE, 1, 64, 33, FAKE, FAKE, FAKE, None) == 2
+
+
+def test_attention_validation(b):
+    ws = b.tree_verify_attn_workspace(1, 65, 32, 8, 128, 4096, 4096)
+    base = [FAKE, FAKE, FAKE, FAKE, 4096, 4096, FAKE, FAKE, FAKE, FAKE, 1, 65, 32, 8, 128,
+            0.088, 1, FAKE, FAKE, ws, None]
+    bad = list(base); bad[13] = 7
+    assert b.lib.td_tree_verify_attn(*bad) == 1 and "multiple" in b.last_error()
+    bad = list(base); bad[14] = 96
+    assert b.lib.td_tree_verify_attn(*bad) == 3
+    bad = list(base); bad[19] = ws - 1
+    assert b.lib.td_tree_verify_attn(*bad) == 1 and "workspace" in b.last_error()
+    bad = list(base); bad[0] = FAKE8
+    assert b.lib.td_tree_verify_attn(*bad) == 1
+    bad = list(base); bad[11] = 257
+    assert b.lib.td_tree_verify_attn(*bad) == 2

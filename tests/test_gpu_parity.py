@@ -1,0 +1,354 @@
+"""GPU parity: every stage of the HIP library against the CPU oracle, through
+the C ABI, on seeded synthetic inputs.
+
+Bars: top-K ids, tree node sets/order (near-tie rule in helpers.compare_tree),
+masks and acceptance bit-exact; log q, lse and log rho within 1e-5;
+attention within 2e-2 (bf16) / 1e-4 (f32) absolute plus a relative
+Frobenius bound per row.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import attn_close, compare_tree, cost_of, oracle_front, paths_of, targets_by_path
+from tree_draft_build_amd import workload as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def td():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tree_draft_build_amd import binding
+    return binding
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_logits(x):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(x).to(DEV)
+
+
+def dev_attn(x):
+    return dev_logits(np.ascontiguousarray(x))
+
+
+def host_out(t, dtype):
+    if dtype == "bf16":
+        return wl.bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def np_tree(t):
+    return {k: v.cpu().numpy() for k, v in t.items()}
+
+
+# ---------------------------------------------------------------------------
+# stage (a)
+# ---------------------------------------------------------------------------
+
+def check_topk(ids_g, lq_g, lse_g, ids_o, lq_o, lse_o):
+    np.testing.assert_array_equal(ids_g, ids_o)
+    assert np.abs(lse_g - lse_o).max() < 1e-5
+    assert np.abs(lq_g - lq_o).max() < 1e-5
+
+
+@pytest.mark.parametrize("name,seqs", [("tiny", None), ("qwen3_8b", None), ("llama31_8b", None),
+                                       ("batched", [0, 7, 15]), ("long", [0, 33, 63])])
+def test_topk_configs(td, name, seqs):
+    cfg = wl.CONFIGS[name]
+    say("topk", name, seqs)
+    x = wl.make_logits(cfg) if seqs is None or cfg.batch <= 4 else None
+    if x is None:
+        full = wl.make_logits(cfg)
+        sub = full[seqs]
+    else:
+        full = sub = x
+        seqs = list(range(cfg.batch))
+    ids, lq, lse = td.draft_topk(dev_logits(full), cfg.topk)
+    torch.cuda.synchronize()
+    ids_o, lq_o, lse_o = oracle.draft_topk(sub, cfg.topk)
+    check_topk(ids.cpu().numpy()[seqs], lq.cpu().numpy()[seqs], lse.cpu().numpy()[seqs], ids_o,
+               lq_o, lse_o)
+
+
+@pytest.mark.parametrize("V", [8, 1000, 4099, 33000])
+@pytest.mark.parametrize("K", [1, 4, 8, 13, 32])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_topk_ragged_and_ties(td, V, K, dtype):
+    if K > V:
+        pytest.skip("K > V")
+    say("topk ragged", V, K, dtype)
+    rng = np.random.default_rng(V * 7 + K)
+    x = np.round(rng.standard_normal((3, 5, V)) * 2, 1).astype(np.float32)  # many ties
+    x[0, 0] = 1.5                                                           # all tied
+    x[1, 1, -3:] = 40.0                                                     # tied top at the tail
+    if dtype == "bf16":
+        x = wl.f32_to_bf16_bits(x)
+    ids, lq, lse = td.draft_topk(dev_logits(x), K)
+    torch.cuda.synchronize()
+    check_topk(ids.cpu().numpy(), lq.cpu().numpy(), lse.cpu().numpy(), *oracle.draft_topk(x, K))
+
+
+def test_topk_pos_stride(td):
+    """Rows placed with a stride larger than the vocabulary (padded rows)."""
+    say("topk pos_stride")
+    rng = np.random.default_rng(3)
+    V, S = 1000, 1024
+    big = wl.f32_to_bf16_bits(rng.standard_normal((2, 4, S)).astype(np.float32) * 3)
+    dev = dev_logits(big)
+    K = 8
+    ids = torch.empty((2, 4, K), dtype=torch.int32, device=DEV)
+    lq = torch.empty((2, 4, K), dtype=torch.float64, device=DEV)
+    lse = torch.empty((2, 4), dtype=torch.float64, device=DEV)
+    ws = torch.empty(td.draft_topk_workspace(2, 4, V, K), dtype=torch.uint8, device=DEV)
+    st = td.lib.td_draft_topk(td._ptr(dev), td.TD_BF16, 2, 4, V, S, K, td._ptr(ids), td._ptr(lq),
+                              td._ptr(lse), td._ptr(ws), ws.numel(), td._stream())
+    assert st == 0, td.last_error()
+    torch.cuda.synchronize()
+    check_topk(ids.cpu().numpy(), lq.cpu().numpy(), lse.cpu().numpy(),
+               *oracle.draft_topk(np.ascontiguousarray(big[:, :, :V]), K))
+
+
+# ---------------------------------------------------------------------------
+# stage (b), (b'), (d) with identical inputs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_fixed", "qwen3_8b", "qwen3_8b_stress",
+                                  "llama31_8b", "batched"])
+def test_build_tree_same_inputs(td, name):
+    cfg = wl.CONFIGS[name]
+    say("build_tree", name)
+    x = wl.make_logits(cfg, list(range(min(cfg.batch, 4))))
+    orc = oracle_front(cfg, x)
+    ids = torch.from_numpy(orc["ids"]).to(DEV)
+    lq = torch.from_numpy(orc["lq"]).to(DEV)
+    root = torch.arange(x.shape[0], dtype=torch.int32, device=DEV) + 100
+    t = np_tree(td.build_tree(ids, lq, cfg.n_max, cfg.use_stop, cost_of(cfg), cfg.l_ar, cfg.ahat0,
+                              root_token=root))
+    for b in range(x.shape[0]):
+        compare_tree(b, t, orc, cfg.use_stop)
+        assert t["node_token"][b, 0] == 100 + b
+        n = int(t["n_nodes"][b])
+        assert t["ahat"][b] == pytest.approx(cfg.ahat0 + np.exp(t["node_logrho"][b, 1:n + 1]).sum(),
+                                             rel=1e-12)
+    # with identical inputs and no near ties the trees are identical
+    same = all(np.array_equal(t[k], orc["tree"][k]) for k in ("n_nodes", "node_token",
+                                                               "node_parent", "node_depth"))
+    if same:
+        np.testing.assert_array_equal(t["node_logrho"], orc["tree"]["node_logrho"])
+
+
+@pytest.mark.parametrize("n_max", [0, 1, 63, 64, 127, 255])
+@pytest.mark.parametrize("K", [1, 3, 8, 32])
+def test_build_tree_capacity_edges(td, n_max, K):
+    """Fixed budgets up to the cap, K up to the cap, peaked and flat tables."""
+    say("build_tree edges", n_max, K)
+    rng = np.random.default_rng(n_max * 40 + K)
+    B, V = 16, 64
+    x = (rng.standard_normal((2, B, V)) * 1.5).astype(np.float32)
+    x[1, :, 5] += 12.0       # peaked sequence: deep chains
+    ids, lq, _ = oracle.draft_topk(x, K)
+    cfg = wl.CONFIGS["tiny_fixed"].replace(block=B, vocab=V, topk=K, n_max=n_max)
+    orc = dict(ids=ids, lq=lq,
+               tree=oracle.build_tree(ids, lq, n_max, False),
+               full=oracle.build_tree(ids, lq, n_max, False, want_curve=True))
+    t = np_tree(td.build_tree(torch.from_numpy(ids).to(DEV), torch.from_numpy(lq).to(DEV), n_max,
+                              False))
+    for b in range(2):
+        compare_tree(b, t, orc, False)
+        avail = sum(K ** d for d in range(1, B + 1)) if K > 1 else B
+        assert t["n_nodes"][b] == min(n_max, avail)
+
+
+def test_tree_mask_same_inputs(td):
+    say("tree_mask")
+    rng = np.random.default_rng(11)
+    for nq in (1, 2, 17, 64, 65, 129, 256):
+        b = 5
+        n_nodes = np.array([nq - 1, rng.integers(0, nq), 0, nq // 2, 1 if nq > 1 else 0], np.int32)
+        par = np.full((b, nq), -1, np.int32)
+        for bi in range(b):
+            for i in range(1, int(n_nodes[bi]) + 1):
+                par[bi, i] = rng.integers(0, i)
+        m = td.tree_mask(torch.from_numpy(par).to(DEV), torch.from_numpy(n_nodes).to(DEV))
+        torch.cuda.synchronize()
+        want = oracle.tree_mask(par, n_nodes)
+        np.testing.assert_array_equal(m.cpu().numpy().view(np.uint64), want)
+
+
+def test_accept_same_inputs(td):
+    say("accept")
+    cfg = wl.CONFIGS["qwen3_8b_stress"].replace(batch=1)
+    x = wl.make_logits(cfg)
+    orc = oracle_front(cfg, x)
+    tree = orc["tree"]
+    lf = wl.logits_as_f64(x, "bf16")
+    W = cfg.n_max + 1
+    rows = []
+    for seed in range(64):               # many target draws over one tree
+        rows.append(wl.target_tokens(cfg, lf, tree["node_token"], tree["node_parent"],
+                                     tree["n_nodes"], seed=seed)[0])
+    tg = np.stack(rows)
+    rep = lambda a: np.repeat(a, 64, axis=0)
+    args_np = (rep(tree["node_token"]), rep(tree["node_parent"]), rep(tree["n_nodes"]), tg)
+    alen, path, bonus = td.accept(*[torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+                                    for a in args_np], cfg.block)
+    torch.cuda.synchronize()
+    a_o, p_o, b_o = oracle.accept(*args_np, cfg.block)
+    np.testing.assert_array_equal(alen.cpu().numpy(), a_o)
+    np.testing.assert_array_equal(path.cpu().numpy(), p_o)
+    np.testing.assert_array_equal(bonus.cpu().numpy(), b_o)
+    assert a_o.max() > 1                  # some deep acceptances happened
+
+
+# ---------------------------------------------------------------------------
+# stage (c) with identical inputs
+# ---------------------------------------------------------------------------
+
+def run_attn(td, cfg, inp, par, n_nodes):
+    mask = oracle.tree_mask(par, n_nodes)
+    dq = dev_attn(inp["q"])
+    kc, vc = dev_attn(inp["k_ctx"]), dev_attn(inp["v_ctx"])
+    kt, vt = dev_attn(inp["k_tree"]), dev_attn(inp["v_tree"])
+    off = torch.from_numpy(inp["ctx_offsets"]).to(DEV)
+    total = int(inp["ctx_offsets"][-1])
+    maxc = int(inp["ctx_len"].max()) if len(inp["ctx_len"]) else 0
+    out = td.tree_verify_attn(dq, kc, vc, off, total, maxc, kt, vt,
+                              torch.from_numpy(mask.view(np.int64)).to(DEV),
+                              torch.from_numpy(n_nodes).to(DEV), wl.attn_scale(cfg))
+    torch.cuda.synchronize()
+    return host_out(out, cfg.attn_dtype), mask
+
+
+def random_parents(rng, n_nodes, nq):
+    par = np.full((len(n_nodes), nq), -1, np.int32)
+    for b, n in enumerate(n_nodes):
+        for i in range(1, int(n) + 1):
+            par[b, i] = rng.integers(max(0, i - 4), i)     # deep-ish random trees
+    return par
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (8, 8), (4, 1)])
+def test_attention_small_ragged(td, dtype, d, hq, hkv):
+    say("attn small", dtype, d, hq, hkv)
+    cfg = wl.CONFIGS["qwen3_8b"].replace(name="s", index=50, batch=5, n_max=20, hq=hq, hkv=hkv,
+                                         head_dim=d, attn_dtype=dtype, ctx_law="uniform",
+                                         ctx_p0=0, ctx_p1=700)
+    inp = wl.make_attn_inputs(cfg)
+    rng = np.random.default_rng(hq + d)
+    n_nodes = np.array([20, 0, 7, 1, 13], np.int32)
+    par = random_parents(rng, n_nodes, cfg.nq_max)
+    got, mask = run_attn(td, cfg, inp, par, n_nodes)
+    want = oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
+                            inp["k_tree"], inp["v_tree"], mask, n_nodes, hq, hkv, d,
+                            wl.attn_scale(cfg))
+    attn_close(got, want, dtype, f"attn {dtype} d{d} {hq}/{hkv}")
+
+
+def test_attention_empty_context(td):
+    say("attn empty ctx")
+    cfg = wl.CONFIGS["qwen3_8b"].replace(name="e", index=51, batch=3, n_max=5, ctx_law="fixed",
+                                         ctx_p0=0)
+    inp = wl.make_attn_inputs(cfg)
+    n_nodes = np.array([5, 0, 2], np.int32)
+    par = random_parents(np.random.default_rng(0), n_nodes, cfg.nq_max)
+    got, mask = run_attn(td, cfg, inp, par, n_nodes)
+    want = oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
+                            inp["k_tree"], inp["v_tree"], mask, n_nodes, cfg.hq, cfg.hkv,
+                            cfg.head_dim, wl.attn_scale(cfg))
+    attn_close(got, want, "bf16", "empty context")
+
+
+@pytest.mark.parametrize("name", ["tiny_masksens", "qwen3_8b_masksens"])
+def test_attention_mask_sensitive(td, name):
+    """Tree keys dominate the softmax, so one wrong mask bit would move a row
+    by far more than the tolerance."""
+    cfg = wl.CONFIGS[name]
+    say("attn mask-sensitive", name)
+    x = wl.make_logits(cfg)
+    orc = oracle_front(cfg, x)
+    tree = orc["tree"]
+    inp = wl.make_attn_inputs(cfg)
+    got, mask = run_attn(td, cfg, inp, tree["node_parent"], tree["n_nodes"])
+    want = oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
+                            inp["k_tree"], inp["v_tree"], mask, tree["n_nodes"], cfg.hq, cfg.hkv,
+                            cfg.head_dim, wl.attn_scale(cfg))
+    attn_close(got, want, cfg.attn_dtype, name)
+    assert int(tree["n_nodes"][0]) == cfg.n_max
+
+
+# ---------------------------------------------------------------------------
+# end to end: the whole path on the GPU vs the whole path in the oracle
+# ---------------------------------------------------------------------------
+
+def gpu_pipeline(td, cfg, x, inp):
+    ids, lq, lse = td.draft_topk(dev_logits(x), cfg.topk)
+    t = td.build_tree(ids, lq, cfg.n_max, cfg.use_stop, cost_of(cfg), cfg.l_ar, cfg.ahat0)
+    mask = td.tree_mask(t["node_parent"], t["n_nodes"])
+    off = torch.from_numpy(inp["ctx_offsets"]).to(DEV)
+    total = int(inp["ctx_offsets"][-1])
+    out = td.tree_verify_attn(dev_attn(inp["q"]), dev_attn(inp["k_ctx"]), dev_attn(inp["v_ctx"]),
+                              off, total, int(inp["ctx_len"].max()), dev_attn(inp["k_tree"]),
+                              dev_attn(inp["v_tree"]), mask, t["n_nodes"], wl.attn_scale(cfg))
+    torch.cuda.synchronize()
+    return dict(ids=ids.cpu().numpy(), lq=lq.cpu().numpy(), lse=lse.cpu().numpy(), tree=np_tree(t),
+                mask=mask.cpu().numpy().view(np.uint64), out=host_out(out, cfg.attn_dtype),
+                t_dev=t)
+
+
+@pytest.mark.parametrize("name,sample", [("tiny", None), ("tiny_fixed", None), ("qwen3_8b", None),
+                                         ("qwen3_8b_stress", None), ("llama31_8b", [0, 3]),
+                                         ("batched", [0, 9]), ("long", [5, 40])])
+def test_pipeline(td, name, sample):
+    cfg = wl.CONFIGS[name]
+    say("pipeline", name, sample)
+    x = wl.make_logits(cfg)
+    inp = wl.make_attn_inputs(cfg)
+    g = gpu_pipeline(td, cfg, x, inp)
+    seqs = list(range(cfg.batch)) if sample is None else sample
+    orc = oracle_front(cfg, x[seqs])
+    check_topk(g["ids"][seqs], g["lq"][seqs], g["lse"][seqs], orc["ids"], orc["lq"], orc["lse"])
+    sub_tree = {k: v[seqs] for k, v in g["tree"].items()}
+    for i in range(len(seqs)):
+        compare_tree(i, sub_tree, orc, cfg.use_stop)
+    # mask of the GPU tree, checked against the oracle's mask of the same tree
+    np.testing.assert_array_equal(g["mask"][seqs],
+                                  oracle.tree_mask(sub_tree["node_parent"], sub_tree["n_nodes"]))
+    # attention of the GPU tree (sampled sequences; rows limited for long contexts)
+    row_limit = 3 if name == "long" else -1
+    for b in seqs:
+        want = oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
+                                inp["k_tree"], inp["v_tree"], g["mask"], g["tree"]["n_nodes"],
+                                cfg.hq, cfg.hkv, cfg.head_dim, wl.attn_scale(cfg), seqs=(b, b + 1),
+                                row_limit=row_limit)
+        got = g["out"][b:b + 1]
+        if row_limit >= 0:
+            got = got.copy()
+            got[:, row_limit + 1:] = 0
+        attn_close(got, want, cfg.attn_dtype, f"{name} seq {b}")
+    # acceptance on the GPU tree with the synthetic target
+    lf = wl.logits_as_f64(x, cfg.logit_dtype)
+    tg = targets_by_path(cfg, lf, g["tree"])
+    alen, path, bonus = td.accept(g["t_dev"]["node_token"], g["t_dev"]["node_parent"],
+                                  g["t_dev"]["n_nodes"], torch.from_numpy(tg).to(DEV), cfg.block)
+    torch.cuda.synchronize()
+    a_o, p_o, b_o = oracle.accept(g["tree"]["node_token"], g["tree"]["node_parent"],
+                                  g["tree"]["n_nodes"], tg, cfg.block)
+    np.testing.assert_array_equal(alen.cpu().numpy(), a_o)
+    np.testing.assert_array_equal(path.cpu().numpy(), p_o)
+    np.testing.assert_array_equal(bonus.cpu().numpy(), b_o)
+    assert np.all(a_o <= np.maximum(0, g["tree"]["node_depth"].max(axis=1)))

@@ -1,0 +1,281 @@
+"""Verify-step throughput of the MI355X path on a synthetic workload.
+
+One step = the whole verify-side path over one batch:
+  draft_topk -> build_tree (S(N) stop) -> tree_mask -> tree_verify_attn -> accept
+with every input already resident in HBM.  Inputs are rotated over enough
+distinct device copies (>= --rotate-mb in total) that the 256 MB Infinity
+Cache cannot serve a step from the previous one.
+
+Prints one JSON line (rank 0, one GPU):
+  value        verify steps per second over the K timed steps
+  roofline     the dominant kernel's algorithmic bytes / its average launch
+               time measured with HIP events on the launch stream
+  cpu_baseline the CPU oracle timed on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_TFLOPS = 2500.0      # dense bf16 MFMA, vendor figure
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="qwen3_8b")
+    ap.add_argument("--rotate-mb", type=float, default=1024.0)
+    ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--stage-detail", action="store_true", help="print per-stage timings to stderr")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from tree_draft_build_amd import binding as td
+    from tree_draft_build_amd import workload as wl
+
+    cfg = wl.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------- inputs (host generation, one upload, device copies) ----
+    x = wl.make_logits(cfg)
+    inp = wl.make_attn_inputs(cfg)
+    tdt = torch.bfloat16 if cfg.attn_dtype == "bf16" else torch.float32
+
+    def up(a, dtype):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev).to(dtype) if dtype is not None else torch.from_numpy(a).to(dev)
+
+    base = dict(logits=up(x, None), q=up(inp["q"], tdt), k_ctx=up(inp["k_ctx"], tdt),
+                v_ctx=up(inp["v_ctx"], tdt), k_tree=up(inp["k_tree"], tdt),
+                v_tree=up(inp["v_tree"], tdt))
+    off = torch.from_numpy(inp["ctx_offsets"]).to(dev)
+    total_ctx = int(inp["ctx_offsets"][-1])
+    max_ctx = int(inp["ctx_len"].max())
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    n_sets = max(1, int(math.ceil(args.rotate_mb * 1e6 / set_bytes)))
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_sets - 1)]
+
+    b, B, K, V = cfg.batch, cfg.block, cfg.topk, cfg.vocab
+    cost = (cfg.cost_a, cfg.cost_b, cfg.cost_c, cfg.cost_knee)
+    scale = wl.attn_scale(cfg)
+
+    # ---------------- outputs and workspaces (allocated once) ----------------
+    topk_out = (torch.empty((b, B, K), dtype=torch.int32, device=dev),
+                torch.empty((b, B, K), dtype=torch.float64, device=dev),
+                torch.empty((b, B), dtype=torch.float64, device=dev))
+    ws_topk = td.draft_topk_alloc_workspace(b, B, V, K, dev)
+    tree = td.alloc_tree(b, cfg.n_max, dev)
+    nq = cfg.nq_max
+    mask = torch.empty((b, nq, (nq + 63) // 64), dtype=torch.int64, device=dev)
+    attn_out = torch.empty((b, nq, cfg.hq, cfg.head_dim), dtype=tdt, device=dev)
+    ws_attn = td.tree_verify_attn_alloc_workspace(b, nq, cfg.hq, cfg.hkv, cfg.head_dim, total_ctx,
+                                                  max_ctx, dev)
+    acc_out = (torch.empty(b, dtype=torch.int32, device=dev),
+               torch.empty((b, B + 1), dtype=torch.int32, device=dev),
+               torch.empty(b, dtype=torch.int32, device=dev))
+    target = torch.full((b, nq), -1, dtype=torch.int32, device=dev)
+
+    def stage_a(s):
+        td.draft_topk(s["logits"], K, out=topk_out, workspace=ws_topk)
+
+    def stage_b():
+        td.build_tree(topk_out[0], topk_out[1], cfg.n_max, cfg.use_stop, cost, cfg.l_ar, cfg.ahat0,
+                      out=tree)
+        td.tree_mask(tree["node_parent"], tree["n_nodes"], out=mask)
+
+    def stage_c(s):
+        td.tree_verify_attn(s["q"], s["k_ctx"], s["v_ctx"], off, total_ctx, max_ctx, s["k_tree"],
+                            s["v_tree"], mask, tree["n_nodes"], scale, out=attn_out,
+                            workspace=ws_attn)
+
+    def stage_d():
+        td.accept(tree["node_token"], tree["node_parent"], tree["n_nodes"], target, B, out=acc_out)
+
+    def step(i):
+        s = sets[i % n_sets]
+        stage_a(s)
+        stage_b()
+        stage_c(s)
+        stage_d()
+
+    # The tree is a deterministic function of the logits: build it once,
+    # untimed, and give the acceptance stage the synthetic target's tokens.
+    step(0)
+    torch.cuda.synchronize()
+    tnp = {k: v.cpu().numpy() for k, v in tree.items()}
+    tg = wl.target_tokens(cfg, wl.logits_as_f64(x, cfg.logit_dtype), tnp["node_token"],
+                          tnp["node_parent"], tnp["n_nodes"])
+    target.copy_(torch.from_numpy(tg))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    use_graph = not args.no_graph
+    graphs = []
+    if use_graph:
+        for i in range(n_sets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if use_graph:
+            graphs[i % n_sets].replay()
+        else:
+            step(i)
+
+    # ---------------- timed region ----------------
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        run(args.warmup + i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_per_step = ms_total / args.steps
+
+    # ---------------- per-stage launch times (HIP events, eager) -------------
+    # Each stage call is bracketed by events on the stream it launches on;
+    # averaged over the same number of steps, rotating the same input sets.
+    names = ["draft_topk", "build_tree+tree_mask", "tree_verify_attn", "accept"]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in names] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        s = sets[i % n_sets]
+        e = ev[i]
+        e[0][0].record(stream); stage_a(s); e[0][1].record(stream)
+        e[1][0].record(stream); stage_b(); e[1][1].record(stream)
+        e[2][0].record(stream); stage_c(s); e[2][1].record(stream)
+        e[3][0].record(stream); stage_d(); e[3][1].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = [float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)]))
+                for j in range(len(names))]
+
+    # ---------------- algorithmic work ----------------
+    nn = tnp["n_nodes"].astype(np.int64)
+    rows = nn + 1
+    L = inp["ctx_len"].astype(np.int64)
+    esz = 2 if cfg.attn_dtype == "bf16" else 4
+    lsz = 2 if cfg.logit_dtype == "bf16" else 4
+    bytes_a = b * B * V * lsz + b * B * K * 12 + b * B * 8
+    bytes_c = int((2 * cfg.hkv * cfg.head_dim * esz * (L + rows)).sum()
+                  + 2 * (rows.sum()) * cfg.hq * cfg.head_dim * esz)
+    depth = tnp["node_depth"]
+    anc = int(sum((depth[i, :rows[i]] + 1).sum() for i in range(b)))
+    flops_c = int(4 * cfg.hq * cfg.head_dim * (rows * L).sum() + 4 * cfg.hq * cfg.head_dim * anc)
+    stage_bytes = {"draft_topk": bytes_a, "tree_verify_attn": bytes_c}
+    j_dom = int(np.argmax([stage_ms[0], -1, stage_ms[2], -1]))
+    dom = names[j_dom]
+    dom_ms = stage_ms[j_dom]
+    intensity = flops_c / bytes_c
+    if dom == "tree_verify_attn" and intensity > MFMA_BF16_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        achieved = flops_c / (dom_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / MFMA_BF16_TFLOPS, 4), traffic=None)
+    else:
+        achieved = stage_bytes[dom] / (dom_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
+    roof["kernel"] = dom
+    roof["bytes_per_launch"] = stage_bytes[dom]
+    roof["avg_launch_us"] = round(dom_ms * 1e3, 2)
+
+    result = {
+        "metric": "verify steps/s (logits->tree->tree-attn->accept) + % HBM/MFMA peak, "
+                  "Qwen3-8B shape" if cfg.name == "qwen3_8b" else f"verify steps/s ({cfg.name})",
+        "value": round(1e3 / ms_per_step, 1),
+        "unit": "verify steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.logit_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": b, "block": B, "vocab": V, "topk": K,
+                   "n_max": cfg.n_max, "stop": "S(N)" if cfg.use_stop else "fixed",
+                   "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": cfg.head_dim,
+                   "ctx_total": total_ctx, "n_nodes": [int(v) for v in nn[:8]],
+                   "graph": use_graph, "input_sets": n_sets, "parallelism": "single GPU"},
+        "roofline": roof,
+        "stages_us": {n: round(t * 1e3, 2) for n, t in zip(names, stage_ms)},
+        "stage_roofline": {
+            "draft_topk": {"bytes": bytes_a, "GB/s": round(bytes_a / (stage_ms[0] * 1e-3) / 1e9, 1)},
+            "tree_verify_attn": {"bytes": bytes_c, "flops": flops_c,
+                                 "GB/s": round(bytes_c / (stage_ms[2] * 1e-3) / 1e9, 1),
+                                 "TFLOP/s": round(flops_c / (stage_ms[2] * 1e-3) / 1e12, 3)}},
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(cfg, x, inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, x, inp, budget_s):
+    """The CPU oracle, as it stands, on whole verify steps of the same
+    workload: as many full steps as fit in about budget_s seconds."""
+    import oracle
+    from tree_draft_build_amd import workload as wl
+
+    cost = (cfg.cost_a, cfg.cost_b, cfg.cost_c, cfg.cost_knee)
+    scale = wl.attn_scale(cfg)
+    lf = wl.logits_as_f64(x, cfg.logit_dtype)
+    steps = 0
+    t0 = time.perf_counter()
+    tg = None
+    while True:
+        ids, lq, lse = oracle.draft_topk(x, cfg.topk)
+        tr = oracle.build_tree(ids, lq, cfg.n_max, cfg.use_stop, cost, cfg.l_ar, cfg.ahat0)
+        m = oracle.tree_mask(tr["node_parent"], tr["n_nodes"])
+        oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"], inp["k_tree"],
+                         inp["v_tree"], m, tr["n_nodes"], cfg.hq, cfg.hkv, cfg.head_dim, scale)
+        if tg is None:   # target tokens are an input, made once outside the count
+            t_pause = time.perf_counter()
+            tg = wl.target_tokens(cfg, lf, tr["node_token"], tr["node_parent"], tr["n_nodes"])
+            t0 += time.perf_counter() - t_pause
+        oracle.accept(tr["node_token"], tr["node_parent"], tr["n_nodes"], tg, cfg.block)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 1000:
+            break
+    return {"value": round(steps / el, 3), "unit": "verify steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} whole verify steps of {cfg.name} in {el:.1f} s, single thread"}
+
+
+if __name__ == "__main__":
+    main()

@@ -80,8 +80,10 @@ const char *td_last_error(void);
  *               to the element size (rows aligned to 16 bytes stream fastest).
  *   1 <= K <= min(TD_MAX_TOPK, vocab); 1 <= block <= TD_MAX_BLOCK.
  * Workspace: at least td_draft_topk_workspace(batch, block, vocab, K) bytes
- *   of device memory, 16-byte aligned; contents need no initialisation and
- *   are garbage afterwards.
+ *   of device memory, 16-byte aligned.  It must be ZERO-FILLED before its
+ *   first use (it holds per-row arrival counters); every call leaves those
+ *   counters zero again, so a workspace is zeroed once and then reused.
+ *   Calls that overlap in time must not share a workspace.
  */
 size_t td_draft_topk_workspace(int32_t batch, int32_t block, int32_t vocab, int32_t K);
 td_status td_draft_topk(const void *logits, td_dtype dtype, int32_t batch, int32_t block,
@@ -155,8 +157,10 @@ td_status td_tree_mask(const int32_t *node_parent, const int32_t *n_nodes, int32
  *   mask     as written by td_tree_mask; n_nodes [batch].
  *   dtype TD_BF16 or TD_F32 (all of q/k/v/out); head_dim 64 or 128.
  *   Accumulation is float32; out has the input dtype.
- * Workspace: td_tree_verify_attn_workspace(...) bytes, 16-byte aligned, no
- *   initialisation needed.
+ * Workspace: td_tree_verify_attn_workspace(...) bytes, 16-byte aligned.  It
+ *   must be ZERO-FILLED before its first use (it holds arrival counters);
+ *   every call leaves the counters zero again.  Calls that overlap in time
+ *   must not share a workspace.
  */
 size_t td_tree_verify_attn_workspace(int32_t batch, int32_t nq_max, int32_t hq, int32_t hkv,
                                      int32_t head_dim, int64_t total_ctx, int64_t max_ctx);

@@ -113,7 +113,7 @@ def test_topk_pos_stride(td):
     ids = torch.empty((2, 4, K), dtype=torch.int32, device=DEV)
     lq = torch.empty((2, 4, K), dtype=torch.float64, device=DEV)
     lse = torch.empty((2, 4), dtype=torch.float64, device=DEV)
-    ws = torch.empty(td.draft_topk_workspace(2, 4, V, K), dtype=torch.uint8, device=DEV)
+    ws = td.draft_topk_alloc_workspace(2, 4, V, K, DEV)
     st = td.lib.td_draft_topk(td._ptr(dev), td.TD_BF16, 2, 4, V, S, K, td._ptr(ids), td._ptr(lq),
                               td._ptr(lse), td._ptr(ws), ws.numel(), td._stream())
     assert st == 0, td.last_error()

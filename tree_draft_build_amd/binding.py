@@ -107,6 +107,13 @@ def draft_topk_workspace(batch, block, vocab, K) -> int:
     return int(lib.td_draft_topk_workspace(batch, block, vocab, K))
 
 
+def draft_topk_alloc_workspace(batch, block, vocab, K, device):
+    """Zero-filled workspace (its arrival counters must start at zero; each
+    call leaves them zero, so the buffer can be reused)."""
+    return torch.zeros(max(16, draft_topk_workspace(batch, block, vocab, K)), dtype=torch.uint8,
+                       device=device)
+
+
 def draft_topk(logits, K, out=None, workspace=None, stream=None):
     """logits [batch][block][vocab] (bf16 or f32, device).  Returns
     (topk_id int32[b][B][K], topk_logq f64[b][B][K], lse f64[b][B])."""
@@ -119,8 +126,7 @@ def draft_topk(logits, K, out=None, workspace=None, stream=None):
                torch.empty((b, B), dtype=torch.float64, device=dev))
     ids, lq, lse = out
     if workspace is None:
-        workspace = torch.empty(max(16, draft_topk_workspace(b, B, V, K)), dtype=torch.uint8,
-                                device=dev)
+        workspace = draft_topk_alloc_workspace(b, B, V, K, dev)
     _check(lib.td_draft_topk(_ptr(logits), _dt(logits), b, B, V, V, K, _ptr(ids), _ptr(lq),
                              _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
     return ids, lq, lse
@@ -170,6 +176,14 @@ def tree_verify_attn_workspace(batch, nq_max, hq, hkv, head_dim, total_ctx, max_
                                                  max_ctx))
 
 
+def tree_verify_attn_alloc_workspace(batch, nq_max, hq, hkv, head_dim, total_ctx, max_ctx, device):
+    """Zero-filled workspace (arrival counters start at zero and every call
+    leaves them zero, so the buffer can be reused)."""
+    return torch.zeros(max(16, tree_verify_attn_workspace(batch, nq_max, hq, hkv, head_dim,
+                                                          total_ctx, max_ctx)),
+                       dtype=torch.uint8, device=device)
+
+
 def tree_verify_attn(q, k_ctx, v_ctx, ctx_offsets, total_ctx, max_ctx, k_tree, v_tree, mask,
                      n_nodes, scale, out=None, workspace=None, stream=None):
     """q [b][nq][hq][d]; k_ctx/v_ctx [total][hkv][d]; k_tree/v_tree [b][nq][hkv][d]."""
@@ -185,9 +199,8 @@ def tree_verify_attn(q, k_ctx, v_ctx, ctx_offsets, total_ctx, max_ctx, k_tree, v
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
-        workspace = torch.empty(max(16, tree_verify_attn_workspace(b, nq, hq, hkv, d, total_ctx,
-                                                                   max_ctx)),
-                                dtype=torch.uint8, device=q.device)
+        workspace = tree_verify_attn_alloc_workspace(b, nq, hq, hkv, d, total_ctx, max_ctx,
+                                                     q.device)
     _check(lib.td_tree_verify_attn(_ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_offsets), total_ctx,
                                    max_ctx, _ptr(k_tree), _ptr(v_tree), _ptr(mask), _ptr(n_nodes), b,
                                    nq, hq, hkv, d, float(scale), _dt(q), _ptr(out), _ptr(workspace),

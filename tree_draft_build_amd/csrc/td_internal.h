@@ -50,15 +50,79 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
-// Wave-wide max / sum over the 64 lanes of a wavefront.
+// ---------------------------------------------------------------------------
+// Register-only lane exchanges (no LDS round trip).  Level L of a 6-level
+// butterfly pairs every lane with one lane of a disjoint group:
+//   L=0: lane ^ 1            (DPP quad_perm [1,0,3,2])
+//   L=1: lane ^ 2            (DPP quad_perm [2,3,0,1])
+//   L=2: 7 - lane within 8   (DPP row_half_mirror)
+//   L=3: 15 - lane within 16 (DPP row_mirror)
+//   L=4: lane ^ 16           (v_permlane16_swap, gfx950)
+//   L=5: lane ^ 32           (v_permlane32_swap, gfx950)
+// After levels 0..k every lane of an aligned group of 2^(k+1) lanes has
+// combined the whole group, so any associative, commutative merge applied at
+// levels 0..5 leaves the full wave's result in every lane.  Levels 0..3 stay
+// inside 16-lane rows.
+// ---------------------------------------------------------------------------
+template <int L>
+__device__ __forceinline__ uint32_t xchg(uint32_t x) {
+    if constexpr (L == 0) return __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false);
+    else if constexpr (L == 1) return __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false);
+    else if constexpr (L == 2) return __builtin_amdgcn_update_dpp(0u, x, 0x141, 0xF, 0xF, false);
+    else if constexpr (L == 3) return __builtin_amdgcn_update_dpp(0u, x, 0x140, 0xF, 0xF, false);
+    else if constexpr (L == 4) {
+        auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return ((__lane_id() >> 4) & 1) ? r[0] : r[1];
+    } else {
+        auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (__lane_id() >> 5) ? r[0] : r[1];
+    }
+}
+template <int L> __device__ __forceinline__ int xchg_i(int x) {
+    return static_cast<int>(xchg<L>(static_cast<uint32_t>(x)));
+}
+template <int L> __device__ __forceinline__ float xchg_f(float x) {
+    return __uint_as_float(xchg<L>(__float_as_uint(x)));
+}
+template <int L> __device__ __forceinline__ double xchg_d(double x) {
+    const uint64_t u = __double_as_longlong(x);
+    const uint64_t lo = xchg<L>(static_cast<uint32_t>(u));
+    const uint64_t hi = xchg<L>(static_cast<uint32_t>(u >> 32));
+    return __longlong_as_double(static_cast<long long>(lo | (hi << 32)));
+}
+
+// Wave-wide max / sum over the 64 lanes of a wavefront (every lane gets it).
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    v = fmaxf(v, xchg_f<0>(v));
+    v = fmaxf(v, xchg_f<1>(v));
+    v = fmaxf(v, xchg_f<2>(v));
+    v = fmaxf(v, xchg_f<3>(v));
+    v = fmaxf(v, xchg_f<4>(v));
+    v = fmaxf(v, xchg_f<5>(v));
     return v;
 }
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    v += xchg_d<0>(v);
+    v += xchg_d<1>(v);
+    v += xchg_d<2>(v);
+    v += xchg_d<3>(v);
+    v += xchg_d<4>(v);
+    v += xchg_d<5>(v);
+    return v;
+}
+// max / sum over the 16 lanes of a row (levels 0..3)
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, xchg_f<0>(v));
+    v = fmaxf(v, xchg_f<1>(v));
+    v = fmaxf(v, xchg_f<2>(v));
+    v = fmaxf(v, xchg_f<3>(v));
+    return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += xchg_f<0>(v);
+    v += xchg_f<1>(v);
+    v += xchg_f<2>(v);
+    v += xchg_f<3>(v);
     return v;
 }
 

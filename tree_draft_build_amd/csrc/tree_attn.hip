@@ -6,30 +6,38 @@
 // i <= n_nodes[b], the admitted keys are the whole context of b plus the
 // tree nodes on the root path of i.  The context part is dense and carries
 // almost all bytes and flops; the tree part is sparse (at most depth+1 keys
-// per row).  Two kernels:
+// per row).  The G heads of a KV group times the tree rows form the M
+// dimension (row r = i * G + hh), cut into row groups of 16.  Two kernels:
 //
-//  attn_ctx_split   split-KV over the context.  Work item = (KV head g, row
-//                   group of 16 query rows, context chunk).  The G heads of a
-//                   group times the tree rows form the M dimension (row
-//                   r = i * G + hh).  Each of the 4 waves takes 32-key tiles
-//                   of the chunk; per tile
-//                      S^T (32 keys x 16 rows) = K Q^T   2 x (D/32) MFMA 16x16x32
-//                      online softmax in base 2 on S^T
-//                      O^T (D x 16 rows) += V^T P^T      D/16 MFMA 16x16x32
-//                   K comes straight from HBM in the MFMA A layout (16-byte
-//                   loads, head_dim contiguous); V is staged in LDS and read
-//                   key-strided for the A operand of the second product.  The
-//                   4 waves then merge through LDS and one (m, l, O) partial
-//                   per row is written.
-//  attn_tree_combine one workgroup per (b, g, row group): merges the
-//                   context partials, adds the ancestor-masked tree keys
-//                   (sparse: one dot product per set mask bit) and writes
-//                   the normalised output; rows beyond the tree are zeroed.
+//  attn_ctx_split   split-KV over the context.  Work item = (key chunk of one
+//                   sequence, KV head); a sequence with an empty context still
+//                   gets one chunk with no keys.  The chunk's first KV loads
+//                   are issued before the tree size and the queries arrive.
+//                   The chunk streams through LDS in sub-chunks of CH keys:
+//                   K stored key-major (MFMA A operand of S^T = K Q^T, one
+//                   16-byte LDS read per lane and step), V stored transposed
+//                   (A operand of O^T += V^T P^T, two 8-byte reads), with the
+//                   next sub-chunk's global loads in flight during the
+//                   compute.  Row blocks of up to 8 row groups are processed
+//                   in turn; within a block waves own row groups, or, when it
+//                   has fewer than 4, split the keys of each sub-chunk and
+//                   merge through LDS.  Softmax is online in base 2.  One
+//                   (m, l, O) partial per tree row and chunk is stored.
+//  attn_tree_combine one wave per output row: merges the chunk partials
+//                   (every load in flight at once), adds the ancestor-masked
+//                   tree keys (sparse: one dot product per set mask bit) and
+//                   writes the normalised row; rows beyond the tree get zeros.
 //
 // MFMA 16x16x32 bf16 operand layout (wave64): A (16 x 32): lane l holds row
 // l % 16, k = 8 (l / 16) .. +7; B (32 x 16): lane l holds column l % 16, the
 // same k; C (16 x 16): lane l holds column l % 16, rows 4 (l / 16) .. +3.
 // The f32 variant uses MFMA 16x16x4 (A/B: lane l holds k = l / 16).
+// Keys inside a 32-key tile are taken by the PV product in the order the S^T
+// product leaves them in registers: lane slot t of lane group h is key
+// 4h + t (t < 4) or 16 + 4h + t - 4 (t >= 4); the contraction is invariant
+// under that permutation.
+
+#include <algorithm>
 
 #include "td_internal.h"
 
@@ -45,64 +53,69 @@ constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = 4;
 constexpr int kRowsPerGroup = 16;
 constexpr int kKeyTile = 32;
+constexpr int kRowBlock = 8;  // row groups per work item
 constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T> struct Sub;
+template <> struct Sub<uint16_t> { static constexpr int CH = 128; };
+template <> struct Sub<float> { static constexpr int CH = 64; };
 
 // ---------------------------------------------------------------------------
 // split plan (host and device agree on it)
 // ---------------------------------------------------------------------------
 struct AttnPlan {
-    int group;     // G = hq / hkv
-    int n_rg;      // row groups of 16 per (b, g)
-    int chunk;     // keys per work item (multiple of kAttnWaves * kKeyTile)
+    int group;         // G = hq / hkv
+    int n_rg;          // row groups of 16 per (b, g) at nq_max rows
+    int n_rb;          // row blocks of kRowBlock row groups
+    int chunk;         // keys per work item (a multiple of the sub-chunk)
     int64_t n_chunks;  // upper bound of sum_b ceil(L_b / chunk)
-    int64_t items;     // hkv * n_rg * n_chunks
+    int64_t items;     // n_chunks * hkv split work items
 };
 
-inline AttnPlan attn_plan(int batch, int nq_max, int hq, int hkv, int64_t total_ctx) {
+inline AttnPlan attn_plan(int batch, int nq_max, int hq, int hkv, int64_t total_ctx, int CH) {
     AttnPlan p;
     p.group = hq / hkv;
     p.n_rg = (p.group * nq_max + kRowsPerGroup - 1) / kRowsPerGroup;
-    // aim at ~1024 work items over the whole context
+    p.n_rb = (p.n_rg + kRowBlock - 1) / kRowBlock;
+    // about 1024 work items over the context; longer chunks keep the partial
+    // traffic small when the context is long
     const int64_t work = std::max<int64_t>(1, total_ctx) * hkv;
-    int chunk = kAttnWaves * kKeyTile;
-    while (chunk < 4096 && work / chunk > 1024) chunk *= 2;
+    int chunk = CH;
+    while (chunk < 32 * CH && work / chunk > 1024) chunk *= 2;
     p.chunk = chunk;
     p.n_chunks = (total_ctx + chunk - 1) / chunk + batch;
-    p.items = static_cast<int64_t>(hkv) * p.n_rg * p.n_chunks;
+    p.items = static_cast<int64_t>(hkv) * p.n_chunks;
     return p;
 }
 
-inline size_t attn_ws_bytes(const AttnPlan &p, int D) {
-    const int64_t rows = p.items * kRowsPerGroup;
-    return static_cast<size_t>(rows) * (2 + D) * sizeof(float);
-}
-
-struct AttnWs {
-    float *m;  // [items][16]
-    float *l;  // [items][16]
-    float *o;  // [items][16][D]
-};
-
-__host__ __device__ inline AttnWs attn_ws(void *base, int64_t items, int D) {
-    AttnWs w;
-    w.m = static_cast<float *>(base);
-    w.l = w.m + items * kRowsPerGroup;
-    w.o = w.l + items * kRowsPerGroup;
-    return w;
+// Workspace: partial rows [n_chunks][hkv][n_rg][16]: m (float32), then l,
+// then O[D]; row r of a (chunk, KV head) lives at prow_index(...).
+__device__ __forceinline__ int64_t prow_index(int64_t c, int g, int rg, int row, int hkv, int n_rg) {
+    return ((c * hkv + g) * n_rg + rg) * kRowsPerGroup + row;
 }
 
 // Locate chunk c of the ragged concatenation: sequence b and its key range.
-// Returns false if c lies beyond the last sequence's chunks.
+// Sequence b owns max(1, ceil(L_b / chunk)) chunks (an empty context has one
+// chunk with no keys, so the tree keys are still attended).
+__device__ __forceinline__ int64_t chunks_of(int64_t L, int chunk) {
+    return L > 0 ? (L + chunk - 1) / chunk : 1;
+}
+
+// Locate chunk c of the ragged concatenation: sequence b, its key range, its
+// first chunk index and its chunk count.
 __device__ __forceinline__ bool find_chunk(const int64_t *__restrict__ off, int batch, int chunk,
-                                           int64_t c, int &b, int64_t &k0, int64_t &k1) {
+                                           int64_t c, int &b, int64_t &k0, int64_t &k1,
+                                           int64_t &cbase, int &nch) {
     int64_t acc = 0;
     for (int s = 0; s < batch; ++s) {
         const int64_t L = off[s + 1] - off[s];
-        const int64_t n = (L + chunk - 1) / chunk;
+        const int64_t n = chunks_of(L, chunk);
         if (c < acc + n) {
             b = s;
             k0 = (c - acc) * chunk;
             k1 = std::min<int64_t>(L, k0 + chunk);
+            cbase = acc;
+            nch = static_cast<int>(n);
             return true;
         }
         acc += n;
@@ -110,407 +123,530 @@ __device__ __forceinline__ bool find_chunk(const int64_t *__restrict__ off, int 
     return false;
 }
 
-// first global chunk index of sequence b
-__device__ __forceinline__ int64_t chunk_base(const int64_t *__restrict__ off, int b, int chunk) {
-    int64_t acc = 0;
-    for (int s = 0; s < b; ++s) acc += (off[s + 1] - off[s] + chunk - 1) / chunk;
-    return acc;
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) { return f32_to_bf16(x); }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 
-// ---------------------------------------------------------------------------
-// dtype-specific fragments
-// ---------------------------------------------------------------------------
-template <typename T, int D> struct Frag;
-
-// bf16: MFMA 16x16x32.  A lane's k-slice for step s is d = 32 s + 8 (l/16) .. +7.
-template <int D> struct Frag<uint16_t, D> {
-    static constexpr int kSteps = D / 32;
-    typedef bf16x8 QK;  // one operand register group per step
-
-    __device__ __forceinline__ static QK load8(const uint16_t *p) {
-        u32x4 w = *reinterpret_cast<const u32x4 *>(p);
-        return __builtin_bit_cast(bf16x8, w);
-    }
-    __device__ __forceinline__ static QK zero() { return __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0}); }
-    // operand for step s of the row/key `ptr` points at (head_dim contiguous)
-    __device__ __forceinline__ static QK qk_operand(const uint16_t *row, int s, int lane) {
-        return load8(row + 32 * s + 8 * (lane >> 4));
-    }
-    __device__ __forceinline__ static f32x4 mma_qk(QK a, QK b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-    // P^T operand: lane (row, h) holds its 8 probabilities in slot order
-    // t<4 -> key 4h+t, t>=4 -> key 16+4h+t-4.
-    __device__ __forceinline__ static QK p_operand(const float (&p)[8]) {
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            w[k] = static_cast<uint32_t>(f32_to_bf16(p[2 * k])) |
-                   (static_cast<uint32_t>(f32_to_bf16(p[2 * k + 1])) << 16);
-        return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-    }
-    // V^T operand for d-tile dt from the key-major LDS tile (pitch in elements).
-    __device__ __forceinline__ static QK v_operand(const uint16_t *sv, int pitch, int dt, int lane) {
-        const int d = 16 * dt + (lane & 15);
-        const int h = lane >> 4;
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int t0 = 2 * k, t1 = 2 * k + 1;
-            const int k0 = t0 < 4 ? 4 * h + t0 : 16 + 4 * h + (t0 - 4);
-            const int k1 = t1 < 4 ? 4 * h + t1 : 16 + 4 * h + (t1 - 4);
-            w[k] = static_cast<uint32_t>(sv[k0 * pitch + d]) |
-                   (static_cast<uint32_t>(sv[k1 * pitch + d]) << 16);
-        }
-        return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-    }
-    __device__ __forceinline__ static f32x4 mma_pv(QK a, QK b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-    __device__ __forceinline__ static float to_f32(uint16_t x) {
-        return __uint_as_float(static_cast<uint32_t>(x) << 16);
-    }
-    __device__ __forceinline__ static uint16_t from_f32(float x) { return f32_to_bf16(x); }
-};
-
-// f32: MFMA 16x16x4.  A lane holds head_dim run d = h*(D/4) .. +D/4-1 and uses
-// element s of it at step s; the contraction covers every d exactly once.
-template <int D> struct Frag<float, D> {
-    static constexpr int kSteps = D / 4;
-    struct QK {
-        float v[D / 4];
-    };
-    __device__ __forceinline__ static QK qk_all(const float *row, int lane) {
-        QK q;
-        const float *p = row + (lane >> 4) * (D / 4);
-#pragma unroll
-        for (int k = 0; k < D / 16; ++k) {
-            u32x4 w = *reinterpret_cast<const u32x4 *>(p + 4 * k);
-            q.v[4 * k + 0] = __uint_as_float(w.x);
-            q.v[4 * k + 1] = __uint_as_float(w.y);
-            q.v[4 * k + 2] = __uint_as_float(w.z);
-            q.v[4 * k + 3] = __uint_as_float(w.w);
-        }
-        return q;
-    }
-    __device__ __forceinline__ static QK zero() {
-        QK q;
-#pragma unroll
-        for (int k = 0; k < D / 4; ++k) q.v[k] = 0.f;
-        return q;
-    }
-    __device__ __forceinline__ static float to_f32(float x) { return x; }
-    __device__ __forceinline__ static float from_f32(float x) { return x; }
-};
+__device__ __forceinline__ int slot_key(int h4, int t) { return t < 4 ? 4 * h4 + t : 12 + 4 * h4 + t; }
 
 // ---------------------------------------------------------------------------
 // attn_ctx_split
 // ---------------------------------------------------------------------------
 
-// LDS: per wave a V tile of 32 keys (pitch D + 8 elements); after the key
-// loop the same memory holds the per-wave (m, l, O) for the merge.
+template <typename T, int D> struct Lds;
+template <int D> struct Lds<uint16_t, D> {
+    static constexpr int CH = Sub<uint16_t>::CH;
+    static constexpr int KP = D + 8;    // sK pitch (elements): 16-byte aligned rows
+    static constexpr int VP = CH + 4;   // sVt pitch (elements): 8-byte aligned rows
+    static constexpr int bytes_kv = (CH * KP + D * VP) * 2;
+};
+template <int D> struct Lds<float, D> {
+    static constexpr int CH = Sub<float>::CH;
+    static constexpr int KP = D + 4;
+    static constexpr int VP = D + 4;    // sV key-major for f32
+    static constexpr int bytes_kv = (CH * KP + CH * VP) * 4;
+};
+
 template <typename T, int D>
-constexpr int ctx_lds_bytes() {
-    constexpr int vt = kAttnWaves * kKeyTile * (D + 8) * static_cast<int>(sizeof(T));
+constexpr int split_lds_bytes() {
+    constexpr int kv = Lds<T, D>::bytes_kv;
     constexpr int mg = kAttnWaves * kRowsPerGroup * (D + 2) * 4;
-    return vt > mg ? vt : mg;
+    return kv > mg ? kv : mg;
 }
+
+// Per row group state of a wave: running max, lane-partial sum, O^T tiles.
+template <int D>
+struct RowState {
+    float m;
+    float l;
+    f32x4 o[D / 16];
+    __device__ __forceinline__ void init() {
+        m = -INFINITY;
+        l = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+};
+
+// One 32-key tile for one row group: S^T, online softmax, O^T update.
+// kt: tile index inside the LDS sub-chunk; valid: keys of the sub-chunk.
+template <int D>
+__device__ __forceinline__ void tile_bf16(const uint16_t *sK, const uint16_t *sVt, const bf16x8 (&qf)[D / 32],
+                                          int kt, int valid, float scale2, int lane, RowState<D> &st) {
+    using L = Lds<uint16_t, D>;
+    const int col = lane & 15;
+    const int h4 = lane >> 4;
+    f32x4 s[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const uint16_t *krow = sK + (kt * kKeyTile + 16 * hf + col) * L::KP + 8 * h4;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(krow + 32 * ks));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc, 0, 0, 0);
+        }
+        s[hf] = acc;
+    }
+    float sc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const float v = (t < 4 ? s[0][t] : s[1][t - 4]) * scale2;
+        sc[t] = kt * kKeyTile + slot_key(h4, t) < valid ? v : -INFINITY;
+    }
+    float tmax = sc[0];
+#pragma unroll
+    for (int t = 1; t < 8; ++t) tmax = fmaxf(tmax, sc[t]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(st.m, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    float p[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        p[t] = __builtin_amdgcn_exp2f(sc[t] - m_new);
+        ps += p[t];
+    }
+    st.l = st.l * alpha + ps;
+    st.m = m_new;
+    uint32_t pw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        pw[k] = static_cast<uint32_t>(f32_to_bf16(p[2 * k])) |
+                (static_cast<uint32_t>(f32_to_bf16(p[2 * k + 1])) << 16);
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+        const uint16_t *vrow = sVt + (16 * dt + col) * L::VP + kt * kKeyTile + 4 * h4;
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow);
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 16);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, st.o[dt] * alpha, 0, 0, 0);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void tile_f32(const float *sK, const float *sV, const float (&qa)[D / 4],
+                                         int kt, int valid, float scale2, int lane, RowState<D> &st) {
+    using L = Lds<float, D>;
+    const int col = lane & 15;
+    const int h4 = lane >> 4;
+    f32x4 s[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const float *krow = sK + (kt * kKeyTile + 16 * hf + col) * L::KP + h4 * (D / 4);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k4 = 0; k4 < D / 16; ++k4) {
+            const f32x4 kv = *reinterpret_cast<const f32x4 *>(krow + 4 * k4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[e], qa[4 * k4 + e], acc, 0, 0, 0);
+        }
+        s[hf] = acc;
+    }
+    float sc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const float v = (t < 4 ? s[0][t] : s[1][t - 4]) * scale2;
+        sc[t] = kt * kKeyTile + slot_key(h4, t) < valid ? v : -INFINITY;
+    }
+    float tmax = sc[0];
+#pragma unroll
+    for (int t = 1; t < 8; ++t) tmax = fmaxf(tmax, sc[t]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(st.m, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    float p[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        p[t] = __builtin_amdgcn_exp2f(sc[t] - m_new);
+        ps += p[t];
+    }
+    st.l = st.l * alpha + ps;
+    st.m = m_new;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+        f32x4 acc = st.o[dt] * alpha;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float a = sV[(kt * kKeyTile + slot_key(h4, t)) * L::VP + 16 * dt + col];
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, p[t], acc, 0, 0, 0);
+        }
+        st.o[dt] = acc;
+    }
+}
+
+// Global -> register staging of one sub-chunk (keys clamped into range).
+template <typename T, int D> struct Stage;
+
+template <int D> struct Stage<uint16_t, D> {
+    using L = Lds<uint16_t, D>;
+    static constexpr int kKPieces = L::CH * D / 8 / kAttnThreads;           // 16-byte K pieces per thread
+    static constexpr int kVUnits = (L::CH / 4) * (D / 8) / kAttnThreads;    // (4 keys x 8 d) V units
+    u32x4 k[kKPieces];
+    u32x4 v[kVUnits][4];
+
+    __device__ __forceinline__ void load(const uint16_t *kbase, const uint16_t *vbase, int64_t kstride,
+                                         int valid, int tid) {
+#pragma unroll
+        for (int r = 0; r < kKPieces; ++r) {
+            const int p = tid + kAttnThreads * r;
+            const int key = min(p / (D / 8), valid - 1);
+            k[r] = *reinterpret_cast<const u32x4 *>(kbase + key * kstride + (p % (D / 8)) * 8);
+        }
+#pragma unroll
+        for (int r = 0; r < kVUnits; ++r) {
+            const int u = tid + kAttnThreads * r;
+            const int kg = u / (D / 8);
+            const int db = u % (D / 8);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int key = min(4 * kg + j, valid - 1);
+                v[r][j] = *reinterpret_cast<const u32x4 *>(vbase + key * kstride + db * 8);
+            }
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t *sK, uint16_t *sVt, int tid) const {
+#pragma unroll
+        for (int r = 0; r < kKPieces; ++r) {
+            const int p = tid + kAttnThreads * r;
+            *reinterpret_cast<u32x4 *>(sK + (p / (D / 8)) * L::KP + (p % (D / 8)) * 8) = k[r];
+        }
+#pragma unroll
+        for (int r = 0; r < kVUnits; ++r) {
+            const int u = tid + kAttnThreads * r;
+            const int kg = u / (D / 8);
+            const int db = u % (D / 8);
+            // 8 d values x 4 keys -> 8 rows of sVt, 4 keys each
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int w = t >> 1;
+                const int sh = (t & 1) * 16;
+                const uint32_t e0 = (v[r][0][w] >> sh) & 0xffffu;
+                const uint32_t e1 = (v[r][1][w] >> sh) & 0xffffu;
+                const uint32_t e2 = (v[r][2][w] >> sh) & 0xffffu;
+                const uint32_t e3 = (v[r][3][w] >> sh) & 0xffffu;
+                *reinterpret_cast<u32x2 *>(sVt + (db * 8 + t) * L::VP + 4 * kg) =
+                    u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+            }
+        }
+    }
+};
+
+template <int D> struct Stage<float, D> {
+    using L = Lds<float, D>;
+    static constexpr int kPieces = L::CH * D / 4 / kAttnThreads;
+    u32x4 k[kPieces];
+    u32x4 v[kPieces];
+
+    __device__ __forceinline__ void load(const float *kbase, const float *vbase, int64_t kstride,
+                                         int valid, int tid) {
+#pragma unroll
+        for (int r = 0; r < kPieces; ++r) {
+            const int p = tid + kAttnThreads * r;
+            const int key = min(p / (D / 4), valid - 1);
+            k[r] = *reinterpret_cast<const u32x4 *>(kbase + key * kstride + (p % (D / 4)) * 4);
+            v[r] = *reinterpret_cast<const u32x4 *>(vbase + key * kstride + (p % (D / 4)) * 4);
+        }
+    }
+    __device__ __forceinline__ void store(float *sK, float *sV, int tid) const {
+#pragma unroll
+        for (int r = 0; r < kPieces; ++r) {
+            const int p = tid + kAttnThreads * r;
+            const int off = (p / (D / 4)) * L::KP + (p % (D / 4)) * 4;
+            *reinterpret_cast<u32x4 *>(sK + off) = k[r];
+            *reinterpret_cast<u32x4 *>(sV + off) = v[r];
+        }
+    }
+};
 
 template <typename T, int D>
 __global__ __launch_bounds__(kAttnThreads) void attn_ctx_split(
     const T *__restrict__ q, const T *__restrict__ k_ctx, const T *__restrict__ v_ctx,
     const int64_t *__restrict__ ctx_offsets, const int32_t *__restrict__ n_nodes, int batch,
-    int nq_max, int hq, int hkv, int group, int n_rg, int chunk, int64_t n_chunks, float scale2,
-    void *ws, int64_t items) {
-    using F = Frag<T, D>;
-    constexpr int kPitch = D + 8;
-    __shared__ __attribute__((aligned(16))) char lds[ctx_lds_bytes<T, D>()];
+    int nq_max, int hq, int hkv, int group, int n_rg, int chunk, float scale2, float *__restrict__ ws,
+    int64_t prow_total) {
+    using L = Lds<T, D>;
+    constexpr bool kBF = sizeof(T) == 2;
+    constexpr int CH = L::CH;
+    __shared__ __attribute__((aligned(16))) char lds[split_lds_bytes<T, D>()];
+    T *sK = reinterpret_cast<T *>(lds);
+    T *sV = sK + CH * L::KP;
 
-    const int64_t item = blockIdx.x;
-    const int rg = static_cast<int>(item % n_rg);
-    const int g = static_cast<int>((item / n_rg) % hkv);
-    const int64_t c = item / (static_cast<int64_t>(n_rg) * hkv);
-    int b;
-    int64_t k0, k1;
-    if (!find_chunk(ctx_offsets, batch, chunk, c, b, k0, k1)) return;
-    // rows of this sequence; n_nodes beyond nq_max - 1 is clamped (bad input)
-    const int rows_b = group * min(n_nodes[b] + 1, nq_max);
-    if (rg * kRowsPerGroup >= rows_b) return;
+    const int64_t c = blockIdx.x / hkv;
+    const int g = static_cast<int>(blockIdx.x % hkv);
+    int b, nch;
+    int64_t k0, k1, cbase;
+    if (!find_chunk(ctx_offsets, batch, chunk, c, b, k0, k1, cbase, nch)) return;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int col = lane & 15;  // this lane's query row within the group (C/B layout)
+    const int col = lane & 15;
     const int h4 = lane >> 4;
 
-    // query row of this lane
-    const int r = rg * kRowsPerGroup + col;
-    const bool row_ok = r < rows_b;
-    const int qi = row_ok ? r / group : 0;
-    const int qh = g * group + (row_ok ? r % group : 0);
-    const T *qrow = q + ((static_cast<int64_t>(b) * nq_max + qi) * hq + qh) * D;
-
+    // the KV stream goes first: its loads fly while the tree size and the
+    // queries arrive
     const int64_t ctx0 = ctx_offsets[b];
-    const int64_t kstride = static_cast<int64_t>(hkv) * D;  // elements between keys
+    const int64_t kstride = static_cast<int64_t>(hkv) * D;
     const T *kbase = k_ctx + (ctx0 * hkv + g) * D;
     const T *vbase = v_ctx + (ctx0 * hkv + g) * D;
-    T *sv = reinterpret_cast<T *>(lds) + wave * kKeyTile * kPitch;
+    const int n_sub = static_cast<int>((k1 - k0 + CH - 1) / CH);
+    Stage<T, D> stage;
+    if (n_sub > 0) {
+        const int valid0 = static_cast<int>(std::min<int64_t>(CH, k1 - k0));
+        stage.load(kbase + k0 * kstride, vbase + k0 * kstride, kstride, valid0, tid);
+    }
+    const int rows_b = group * min(n_nodes[b] + 1, nq_max);
+    const int n_rg_b = (rows_b + kRowsPerGroup - 1) / kRowsPerGroup;
+    const T *qb = q + static_cast<int64_t>(b) * nq_max * hq * D;
 
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-    f32x4 o[D / 16];
+    for (int rb0 = 0; rb0 < n_rg_b; rb0 += kRowBlock) {
+        const int nrg = min(kRowBlock, n_rg_b - rb0);
+        // wave -> (row groups, key tiles) assignment
+        //   nrg >= 4: wave w owns row groups w and w + 4 of the block, all keys
+        //   nrg <  4: p2 = 1, 2 or 4 row slots; waves share a row group's keys
+        const int p2 = nrg >= 4 ? 4 : (nrg == 1 ? 1 : (nrg == 2 ? 2 : 4));
+        const int kt_step = kAttnWaves / p2;
+        const int kt_first = wave / p2;
+        constexpr int kMaxOwn = kRowBlock / kAttnWaves;  // 2
+        int own_rg[kMaxOwn];
+        int n_own = 0;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int64_t nkeys = k1 - k0;
-    const int ntiles = static_cast<int>((nkeys + kKeyTile - 1) / kKeyTile);
-
-    if constexpr (sizeof(T) == 2) {
-        typename F::QK qf[F::kSteps];
-#pragma unroll
-        for (int s = 0; s < F::kSteps; ++s) qf[s] = row_ok ? F::qk_operand(qrow, s, lane) : F::zero();
-
-        for (int t = wave; t < ntiles; t += kAttnWaves) {
-            const int64_t t0 = k0 + static_cast<int64_t>(t) * kKeyTile;
-            const int valid = static_cast<int>(std::min<int64_t>(kKeyTile, k1 - t0));
-            // K operands for both 16-key halves (key index clamped in range)
-            typename F::QK kf[2][F::kSteps];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int kk = std::min(16 * hf + col, valid - 1);
-                const T *krow = kbase + (t0 + kk) * kstride;
-#pragma unroll
-                for (int s = 0; s < F::kSteps; ++s) kf[hf][s] = F::qk_operand(krow, s, lane);
-            }
-            // V tile -> LDS (key-major), 16-byte pieces, clamped keys
-            constexpr int kPieces = kKeyTile * D / 8;
-#pragma unroll
-            for (int p0 = 0; p0 < kPieces; p0 += 64) {
-                const int p = p0 + lane;
-                const int key = p / (D / 8);
-                const int db = p % (D / 8);
-                const int kk = std::min(key, valid - 1);
-                u32x4 w = *reinterpret_cast<const u32x4 *>(vbase + (t0 + kk) * kstride + db * 8);
-                *reinterpret_cast<u32x4 *>(sv + key * kPitch + db * 8) = w;
-            }
-            // S^T = K Q^T
-            f32x4 st[2];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < F::kSteps; ++s) acc = F::mma_qk(kf[hf][s], qf[s], acc);
-                st[hf] = acc;
-            }
-            // this lane's 8 scores in slot order; keys beyond the chunk -> -inf
-            float sc[8];
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt) {
-                const int key = tt < 4 ? 4 * h4 + tt : 16 + 4 * h4 + (tt - 4);
-                const float v = (tt < 4 ? st[0][tt] : st[1][tt - 4]) * scale2;
-                sc[tt] = key < valid ? v : -INFINITY;
-            }
-            float tmax = sc[0];
-#pragma unroll
-            for (int tt = 1; tt < 8; ++tt) tmax = fmaxf(tmax, sc[tt]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            const float m_new = fmaxf(m_run, tmax);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            float p[8];
-            float ps = 0.f;
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt) {
-                p[tt] = __builtin_amdgcn_exp2f(sc[tt] - m_new);
-                ps += p[tt];
-            }
-            l_run = l_run * alpha + ps;
-            m_run = m_new;
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
-            const typename F::QK pf = F::p_operand(p);
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)
-                o[dt] = F::mma_pv(F::v_operand(sv, kPitch, dt, lane), pf, o[dt]);
-            __builtin_amdgcn_wave_barrier();
+        for (int j = 0; j < kMaxOwn; ++j) {
+            const int rl = (nrg >= 4) ? wave + kAttnWaves * j : (j == 0 ? wave % p2 : nrg);
+            own_rg[j] = rl;
+            n_own += rl < nrg ? 1 : 0;
         }
-    } else {
-        // f32 inputs: MFMA 16x16x4
-        const typename F::QK qa = row_ok ? F::qk_all(qrow, lane) : F::zero();
-        for (int t = wave; t < ntiles; t += kAttnWaves) {
-            const int64_t t0 = k0 + static_cast<int64_t>(t) * kKeyTile;
-            const int valid = static_cast<int>(std::min<int64_t>(kKeyTile, k1 - t0));
-            f32x4 st[2];
+        const bool split_mode = nrg < 4;
+
+        // queries of the owned row groups (B operand layout); rows past the
+        // tree read row 0 of the group and are never published
+        RowState<D> st[kMaxOwn];
+        typedef typename std::conditional<kBF, bf16x8, float>::type QE;
+        constexpr int kQN = kBF ? D / 32 : D / 4;
+        QE qf[kMaxOwn][kQN];
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int kk = std::min(16 * hf + col, valid - 1);
-                const typename F::QK ka = F::qk_all(kbase + (t0 + kk) * kstride, lane);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < kMaxOwn; ++j) {
+            st[j].init();
+            const int r = (rb0 + own_rg[j]) * kRowsPerGroup + col;
+            const bool ok = j < n_own && r < rows_b;
+            const int qi = ok ? r / group : 0;
+            const int qh = g * group + (ok ? r % group : 0);
+            const T *qrow = qb + (static_cast<int64_t>(qi) * hq + qh) * D;
+            if constexpr (kBF) {
 #pragma unroll
-                for (int s = 0; s < F::kSteps; ++s)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.v[s], qa.v[s], acc, 0, 0, 0);
-                st[hf] = acc;
-            }
-            constexpr int kPieces = kKeyTile * D / 4;
+                for (int ks = 0; ks < kQN; ++ks) {
+                    u32x4 w = *reinterpret_cast<const u32x4 *>(qrow + 32 * ks + 8 * h4);
+                    qf[j][ks] = __builtin_bit_cast(bf16x8, w);
+                }
+            } else {
 #pragma unroll
-            for (int p0 = 0; p0 < kPieces; p0 += 64) {
-                const int pp = p0 + lane;
-                const int key = pp / (D / 4);
-                const int db = pp % (D / 4);
-                const int kk = std::min(key, valid - 1);
-                u32x4 w = *reinterpret_cast<const u32x4 *>(vbase + (t0 + kk) * kstride + db * 4);
-                *reinterpret_cast<u32x4 *>(sv + key * kPitch + db * 4) = w;
-            }
-            float sc[8];
+                for (int k4 = 0; k4 < D / 16; ++k4) {
+                    f32x4 w = *reinterpret_cast<const f32x4 *>(qrow + h4 * (D / 4) + 4 * k4);
 #pragma unroll
-            for (int tt = 0; tt < 8; ++tt) {
-                const int key = tt < 4 ? 4 * h4 + tt : 16 + 4 * h4 + (tt - 4);
-                const float v = (tt < 4 ? st[0][tt] : st[1][tt - 4]) * scale2;
-                sc[tt] = key < valid ? v : -INFINITY;
-            }
-            float tmax = sc[0];
-#pragma unroll
-            for (int tt = 1; tt < 8; ++tt) tmax = fmaxf(tmax, sc[tt]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            const float m_new = fmaxf(m_run, tmax);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            float p[8];
-            float ps = 0.f;
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt) {
-                p[tt] = __builtin_amdgcn_exp2f(sc[tt] - m_new);
-                ps += p[tt];
-            }
-            l_run = l_run * alpha + ps;
-            m_run = m_new;
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
-            // O^T += V^T P^T, 8 steps of 4 keys; step u uses key
-            // u<4 -> 4h+u, u>=4 -> 16+4h+u-4 (this lane's p[u])
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) {
-                const int d = 16 * dt + col;
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int key = u < 4 ? 4 * h4 + u : 16 + 4 * h4 + (u - 4);
-                    o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sv[key * kPitch + d], p[u], o[dt],
-                                                                 0, 0, 0);
+                    for (int e = 0; e < 4; ++e) qf[j][4 * k4 + e] = w[e];
                 }
             }
-            __builtin_amdgcn_wave_barrier();
+        }
+        if (rb0 > 0 && n_sub > 0) {  // another row block: stream the chunk again
+            const int valid0 = static_cast<int>(std::min<int64_t>(CH, k1 - k0));
+            stage.load(kbase + k0 * kstride, vbase + k0 * kstride, kstride, valid0, tid);
+        }
+        for (int sc = 0; sc < n_sub; ++sc) {
+            const int64_t s0 = k0 + static_cast<int64_t>(sc) * CH;
+            const int valid = static_cast<int>(std::min<int64_t>(CH, k1 - s0));
+            stage.store(sK, sV, tid);
+            __syncthreads();
+            if (sc + 1 < n_sub) {  // next sub-chunk's loads fly during the compute
+                const int64_t s1 = s0 + CH;
+                const int valid1 = static_cast<int>(std::min<int64_t>(CH, k1 - s1));
+                stage.load(kbase + s1 * kstride, vbase + s1 * kstride, kstride, valid1, tid);
+            }
+            const int ntiles = (valid + kKeyTile - 1) / kKeyTile;
+#pragma unroll
+            for (int j = 0; j < kMaxOwn; ++j) {
+                if (j >= n_own) break;
+                for (int kt = split_mode ? kt_first : 0; kt < ntiles; kt += split_mode ? kt_step : 1) {
+                    if constexpr (kBF)
+                        tile_bf16<D>(sK, sV, qf[j], kt, valid, scale2, lane, st[j]);
+                    else
+                        tile_f32<D>(sK, sV, qf[j], kt, valid, scale2, lane, st[j]);
+                }
+            }
+            __syncthreads();
+        }
+
+        // row sums over the four lane groups
+#pragma unroll
+        for (int j = 0; j < kMaxOwn; ++j) {
+            st[j].l += xchg_f<4>(st[j].l);
+            st[j].l += xchg_f<5>(st[j].l);
+        }
+
+        float *wm = ws;
+        float *wl = ws + prow_total;
+        float *wo = ws + 2 * prow_total;
+        if (!split_mode || kt_step == 1) {
+            // each owned row group is complete in this wave: store its rows
+#pragma unroll
+            for (int j = 0; j < kMaxOwn; ++j) {
+                if (j >= n_own) break;
+                const int rg = rb0 + own_rg[j];
+                if (rg * kRowsPerGroup + col >= rows_b) continue;
+                const int64_t pr = prow_index(c, g, rg, col, hkv, n_rg);
+                if (h4 == 0) {
+                    wm[pr] = st[j].m;
+                    wl[pr] = st[j].l;
+                }
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt)
+                    *reinterpret_cast<f32x4 *>(&wo[pr * D + 16 * dt + 4 * h4]) = st[j].o[dt];
+            }
+        } else {
+            // split mode: kt_step waves per row group merge through LDS
+            float *mw = reinterpret_cast<float *>(lds);        // [4][16]
+            float *lw = mw + kAttnWaves * kRowsPerGroup;       // [4][16]
+            float *ow = lw + kAttnWaves * kRowsPerGroup;       // [4][16][D]
+            if (n_own > 0) {
+                if (h4 == 0) {
+                    mw[wave * kRowsPerGroup + col] = st[0].m;
+                    lw[wave * kRowsPerGroup + col] = st[0].l;
+                }
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt)
+                    *reinterpret_cast<f32x4 *>(&ow[(wave * kRowsPerGroup + col) * D + 16 * dt + 4 * h4]) =
+                        st[0].o[dt];
+            }
+            __syncthreads();
+            // 16 threads per (row slot, row), each a D/16 slice; slot s merges
+            // waves s, s + p2, ...
+            constexpr int kPer = D / 16;
+            for (int idx = tid; idx < p2 * kRowsPerGroup * 16; idx += kAttnThreads) {
+                const int sl = idx / (kRowsPerGroup * 16);
+                const int r = (idx / 16) % kRowsPerGroup;
+                if (sl >= nrg || (rb0 + sl) * kRowsPerGroup + r >= rows_b) continue;
+                const int ds = (idx % 16) * kPer;
+                float M = -INFINITY;
+                for (int v = sl; v < kAttnWaves; v += p2) M = fmaxf(M, mw[v * kRowsPerGroup + r]);
+                float Ls = 0.f;
+                float acc[kPer];
+#pragma unroll
+                for (int k = 0; k < kPer; ++k) acc[k] = 0.f;
+                for (int v = sl; v < kAttnWaves; v += p2) {
+                    const float mv = mw[v * kRowsPerGroup + r];
+                    const float f = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+                    Ls += f * lw[v * kRowsPerGroup + r];
+#pragma unroll
+                    for (int k = 0; k < kPer; ++k) acc[k] += f * ow[(v * kRowsPerGroup + r) * D + ds + k];
+                }
+                const int64_t pr = prow_index(c, g, rb0 + sl, r, hkv, n_rg);
+                if ((idx % 16) == 0) {
+                    wm[pr] = M;
+                    wl[pr] = Ls;
+                }
+#pragma unroll
+                for (int k = 0; k < kPer; k += 4)
+                    *reinterpret_cast<f32x4 *>(&wo[pr * D + ds + k]) =
+                        f32x4{acc[k], acc[k + 1], acc[k + 2], acc[k + 3]};
+            }
+            __syncthreads();  // LDS is reused by the next row block
         }
     }
-
-    // l: sum of the four key-slices of this row
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
-
-    // ---- merge the 4 waves through LDS ----
-    __syncthreads();  // V tiles are dead
-    float *sm = reinterpret_cast<float *>(lds);
-    float *mw = sm;                                          // [4][16]
-    float *lw = mw + kAttnWaves * kRowsPerGroup;             // [4][16]
-    float *ow = lw + kAttnWaves * kRowsPerGroup;             // [4][16][D]
-    if (h4 == 0) {
-        mw[wave * kRowsPerGroup + col] = m_run;
-        lw[wave * kRowsPerGroup + col] = l_run;
-    }
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            ow[(wave * kRowsPerGroup + col) * D + 16 * dt + 4 * h4 + k] = o[dt][k];
-    __syncthreads();
-
-    AttnWs w = attn_ws(ws, items, D);
-    const int row = tid >> 4;           // 0..15
-    const int dsub = (tid & 15) * (D / 16);
-    float M = -INFINITY;
-#pragma unroll
-    for (int wv = 0; wv < kAttnWaves; ++wv) M = fmaxf(M, mw[wv * kRowsPerGroup + row]);
-    float L = 0.f;
-    float acc[D / 16];
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) acc[k] = 0.f;
-#pragma unroll
-    for (int wv = 0; wv < kAttnWaves; ++wv) {
-        const float mv = mw[wv * kRowsPerGroup + row];
-        const float f = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
-        L += f * lw[wv * kRowsPerGroup + row];
-#pragma unroll
-        for (int k = 0; k < D / 16; ++k) acc[k] += f * ow[(wv * kRowsPerGroup + row) * D + dsub + k];
-    }
-    const int64_t prow = item * kRowsPerGroup + row;
-    if ((tid & 15) == 0) {
-        w.m[prow] = M;
-        w.l[prow] = L;
-    }
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) w.o[prow * D + dsub + k] = acc[k];
 }
 
 // ---------------------------------------------------------------------------
-// attn_tree_combine
+// attn_tree_combine: one wave per output row.  Lane j owns dims
+// 16 (j / 8) .. +15 and chunks c = j % 8 (mod 8): all partial loads of a row
+// are in flight at once, and the chunk groups are summed by the register
+// butterfly levels 0..2 (within 8 lanes).  Tree keys: each lane dots its 16
+// dims, levels 3..5 sum the 8 dim slices.
 // ---------------------------------------------------------------------------
+constexpr int kCombineRows = kAttnThreads / kWave;  // rows per workgroup
+
 template <typename T, int D>
 __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     const T *__restrict__ q, const int64_t *__restrict__ ctx_offsets, const T *__restrict__ k_tree,
     const T *__restrict__ v_tree, const uint64_t *__restrict__ mask,
-    const int32_t *__restrict__ n_nodes, int batch, int nq_max, int hq, int hkv, int group,
-    int n_rg, int chunk, float scale2, const void *ws, int64_t items, T *__restrict__ out) {
-    using F = Frag<T, D>;
-    constexpr int kPer = D / 16;  // output dims per thread
-    const int rg = blockIdx.x % n_rg;
-    const int g = (blockIdx.x / n_rg) % hkv;
-    const int b = blockIdx.x / (n_rg * hkv);
-    const int tid = threadIdx.x;
-    const int row = tid >> 4;
-    const int dsub = (tid & 15) * kPer;
-    const int r = rg * kRowsPerGroup + row;
+    const int32_t *__restrict__ n_nodes, int nq_max, int hq, int hkv, int group, int n_rg,
+    int chunk, float scale2, const float *__restrict__ ws, int64_t prow_total, T *__restrict__ out) {
+    constexpr int kSlice = D / 8;  // dims per lane group
+    const int rows_per_bg = group * nq_max;
+    const int blocks_per_bg = (rows_per_bg + kCombineRows - 1) / kCombineRows;
+    const int blk = blockIdx.x % blocks_per_bg;
+    const int g = (blockIdx.x / blocks_per_bg) % hkv;
+    const int b = blockIdx.x / (blocks_per_bg * hkv);
+    const int lane = threadIdx.x & 63;
+    const int r = blk * kCombineRows + (threadIdx.x >> 6);
+    if (r >= rows_per_bg) return;
     const int i = r / group;
-    const int hh = r % group;
-    if (i >= nq_max) return;
-    const int h = g * group + hh;
-    T *orow = out + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + dsub;
+    const int h = g * group + r % group;
+    const int slice = lane >> 3;
+    const int cg = lane & 7;
+    T *orow = out + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + slice * kSlice;
     const int n = min(n_nodes[b], nq_max - 1);
-    if (i > n) {
+    if (i > n) {  // a row beyond the tree: zeros
+        if (cg == 0) {
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) orow[k] = F::from_f32(0.f);
+            for (int k = 0; k < kSlice; ++k) orow[k] = from_f32<T>(0.f);
+        }
         return;
     }
 
     // context partials of this row
-    AttnWs w = attn_ws(const_cast<void *>(ws), items, D);
-    const int64_t L = ctx_offsets[b + 1] - ctx_offsets[b];
-    const int64_t nch = (L + chunk - 1) / chunk;
-    const int64_t cb = chunk_base(ctx_offsets, b, chunk);
-    float M = -INFINITY, Lsum = 0.f;
-    float acc[kPer];
+    int64_t cb = 0;
+    for (int s2 = 0; s2 < b; ++s2) cb += chunks_of(ctx_offsets[s2 + 1] - ctx_offsets[s2], chunk);
+    const int nch = static_cast<int>(chunks_of(ctx_offsets[b + 1] - ctx_offsets[b], chunk));
+    const int rg = r / kRowsPerGroup;
+    const int rr = r % kRowsPerGroup;
+    const float *wm = ws;
+    const float *wl = ws + prow_total;
+    const float *wo = ws + 2 * prow_total;
+    float M = -INFINITY;
+    for (int cc = cg; cc < nch; cc += 8) M = fmaxf(M, wm[prow_index(cb + cc, g, rg, rr, hkv, n_rg)]);
+    M = wave_max(M);
+    float Lsum = 0.f;
+    float acc[kSlice];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) acc[k] = 0.f;
-    for (int64_t c = cb; c < cb + nch; ++c) {
-        const int64_t item = (c * hkv + g) * n_rg + rg;
-        const int64_t prow = item * kRowsPerGroup + row;
-        const float mc = w.m[prow];
-        const float Mn = fmaxf(M, mc);
-        const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-        const float fn = __builtin_amdgcn_exp2f(mc - Mn);
-        Lsum = Lsum * fo + w.l[prow] * fn;
+    for (int k = 0; k < kSlice; ++k) acc[k] = 0.f;
+#pragma unroll 2
+    for (int cc = cg; cc < nch; cc += 8) {
+        const int64_t pr = prow_index(cb + cc, g, rg, rr, hkv, n_rg);
+        const float mc = wm[pr];
+        const float f = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+        Lsum += wl[pr] * f;
+        const f32x4 *op = reinterpret_cast<const f32x4 *>(&wo[pr * D + slice * kSlice]);
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) acc[k] = acc[k] * fo + w.o[prow * D + dsub + k] * fn;
-        M = Mn;
+        for (int k4 = 0; k4 < kSlice / 4; ++k4) {
+            const f32x4 o4 = op[k4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[4 * k4 + e] += o4[e] * f;
+        }
+    }
+    Lsum += xchg_f<0>(Lsum);
+    Lsum += xchg_f<1>(Lsum);
+    Lsum += xchg_f<2>(Lsum);
+#pragma unroll
+    for (int k = 0; k < kSlice; ++k) {
+        acc[k] += xchg_f<0>(acc[k]);
+        acc[k] += xchg_f<1>(acc[k]);
+        acc[k] += xchg_f<2>(acc[k]);
     }
 
     // tree keys on the root path of i (mask row), one dot product per bit
-    const T *qrow = q + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + dsub;
-    float qv[kPer];
+    const T *qrow = q + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + slice * kSlice;
+    float qv[kSlice];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) qv[k] = F::to_f32(qrow[k]);
+    for (int k = 0; k < kSlice; ++k) qv[k] = to_f32<T>(qrow[k]);
     const int words = (nq_max + 63) / 64;
     const uint64_t *mrow = mask + (static_cast<int64_t>(b) * nq_max + i) * words;
     for (int wd = 0; wd < words; ++wd) {
@@ -519,28 +655,28 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
             const int j = wd * 64 + __ffsll(static_cast<long long>(bits)) - 1;
             bits &= bits - 1;
             if (j >= nq_max) break;  // bits beyond the tree rows are ignored
-            const int64_t kv = ((static_cast<int64_t>(b) * nq_max + j) * hkv + g) * D + dsub;
+            const int64_t kv = ((static_cast<int64_t>(b) * nq_max + j) * hkv + g) * D + slice * kSlice;
             float dot = 0.f;
 #pragma unroll
-            for (int k = 0; k < kPer; ++k) dot += qv[k] * F::to_f32(k_tree[kv + k]);
-            // reduce over the 16 threads of this row
-            dot += __shfl_xor(dot, 1, 64);
-            dot += __shfl_xor(dot, 2, 64);
-            dot += __shfl_xor(dot, 4, 64);
-            dot += __shfl_xor(dot, 8, 64);
-            const float s = dot * scale2;
-            const float Mn = fmaxf(M, s);
+            for (int k = 0; k < kSlice; ++k) dot += qv[k] * to_f32<T>(k_tree[kv + k]);
+            dot += xchg_f<3>(dot);
+            dot += xchg_f<4>(dot);
+            dot += xchg_f<5>(dot);
+            const float sc = dot * scale2;
+            const float Mn = fmaxf(M, sc);
             const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-            const float fn = __builtin_amdgcn_exp2f(s - Mn);
+            const float fn = __builtin_amdgcn_exp2f(sc - Mn);
             Lsum = Lsum * fo + fn;
 #pragma unroll
-            for (int k = 0; k < kPer; ++k) acc[k] = acc[k] * fo + F::to_f32(v_tree[kv + k]) * fn;
+            for (int k = 0; k < kSlice; ++k) acc[k] = acc[k] * fo + to_f32<T>(v_tree[kv + k]) * fn;
             M = Mn;
         }
     }
-    const float inv = 1.f / Lsum;
+    if (cg == 0) {
+        const float inv = 1.f / Lsum;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) orow[k] = F::from_f32(acc[k] * inv);
+        for (int k = 0; k < kSlice; ++k) orow[k] = from_f32<T>(acc[k] * inv);
+    }
 }
 
 template <typename T, int D>
@@ -549,23 +685,39 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
                  const int32_t *n_nodes, int batch, int nq_max, int hq, int hkv, float scale,
                  const AttnPlan &pl, void *ws, void *out, hipStream_t st) {
     const float scale2 = scale * kLog2e;
-    if (pl.items > 0)
-        hipLaunchKernelGGL((attn_ctx_split<T, D>), dim3(static_cast<unsigned>(pl.items)),
-                           dim3(kAttnThreads), 0, st, static_cast<const T *>(q),
-                           static_cast<const T *>(k_ctx), static_cast<const T *>(v_ctx), off, n_nodes,
-                           batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, pl.n_chunks, scale2,
-                           ws, pl.items);
+    const int64_t prow_total = pl.n_chunks * hkv * pl.n_rg * kRowsPerGroup;
+    hipLaunchKernelGGL((attn_ctx_split<T, D>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)),
+                       dim3(kAttnThreads), 0, st, static_cast<const T *>(q),
+                       static_cast<const T *>(k_ctx), static_cast<const T *>(v_ctx), off, n_nodes,
+                       batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,
+                       static_cast<float *>(ws), prow_total);
+    const int blocks_per_bg = (pl.group * nq_max + kCombineRows - 1) / kCombineRows;
     hipLaunchKernelGGL((attn_tree_combine<T, D>),
-                       dim3(static_cast<unsigned>(batch * hkv * pl.n_rg)), dim3(kAttnThreads), 0,
-                       st, static_cast<const T *>(q), off, static_cast<const T *>(k_tree),
-                       static_cast<const T *>(v_tree), mask, n_nodes, batch, nq_max, hq, hkv,
-                       pl.group, pl.n_rg, pl.chunk, scale2, ws, pl.items, static_cast<T *>(out));
+                       dim3(static_cast<unsigned>(static_cast<int64_t>(batch) * hkv * blocks_per_bg)),
+                       dim3(kAttnThreads), 0, st, static_cast<const T *>(q), off,
+                       static_cast<const T *>(k_tree), static_cast<const T *>(v_tree), mask, n_nodes,
+                       nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,
+                       static_cast<const float *>(ws), prow_total, static_cast<T *>(out));
+}
+
+inline int sub_chunk(td_dtype dt) { return dt == TD_BF16 ? Sub<uint16_t>::CH : Sub<float>::CH; }
+
+inline size_t attn_ws_size(const AttnPlan &pl, int batch, int hkv, int D) {
+    (void)batch;
+    const int64_t prow_total = pl.n_chunks * hkv * pl.n_rg * kRowsPerGroup;
+    return static_cast<size_t>(prow_total) * (2 + D) * sizeof(float);
 }
 
 }  // namespace
 }  // namespace td
 
 using namespace td;
+
+static size_t attn_workspace(int32_t batch, int32_t nq_max, int32_t hq, int32_t hkv,
+                             int32_t head_dim, int64_t total_ctx, td_dtype dt) {
+    AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, sub_chunk(dt));
+    return std::max<size_t>(16, attn_ws_size(pl, batch, hkv, head_dim));
+}
 
 extern "C" size_t td_tree_verify_attn_workspace(int32_t batch, int32_t nq_max, int32_t hq,
                                                 int32_t hkv, int32_t head_dim, int64_t total_ctx,
@@ -574,8 +726,9 @@ extern "C" size_t td_tree_verify_attn_workspace(int32_t batch, int32_t nq_max, i
     if (batch <= 0 || nq_max <= 0 || hq <= 0 || hkv <= 0 || hq % hkv || head_dim <= 0 ||
         total_ctx < 0)
         return 0;
-    AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx);
-    return std::max<size_t>(16, attn_ws_bytes(pl, head_dim));
+    // the larger of the two dtypes' plans, so one size serves both
+    return std::max(attn_workspace(batch, nq_max, hq, hkv, head_dim, total_ctx, TD_BF16),
+                    attn_workspace(batch, nq_max, hq, hkv, head_dim, total_ctx, TD_F32));
 }
 
 extern "C" td_status td_tree_verify_attn(const void *q, const void *k_ctx, const void *v_ctx,
@@ -606,10 +759,9 @@ extern "C" td_status td_tree_verify_attn(const void *q, const void *k_ctx, const
     if (workspace_bytes <
         td_tree_verify_attn_workspace(batch, nq_max, hq, hkv, head_dim, total_ctx, max_ctx))
         return fail(TD_EINVAL, "td_tree_verify_attn: workspace too small");
-    AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx);
+    AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, sub_chunk(dtype));
     if (pl.items > 0x7fffffffLL || static_cast<int64_t>(batch) * hkv * pl.n_rg > 0x7fffffffLL)
         return fail(TD_ECAPACITY, "td_tree_verify_attn: grid too large");
-    if (total_ctx == 0) pl.items = 0;
     hipStream_t st = as_stream(stream);
     const bool bf = dtype == TD_BF16;
 #define TD_ATTN(T, DD)                                                                          \

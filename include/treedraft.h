@@ -191,6 +191,59 @@ td_status td_accept(const int32_t *node_token, const int32_t *node_parent, const
                     int32_t *accept_len, int32_t *accept_path, int32_t *bonus_token,
                     void *stream);
 
+/* ------------------------------------------------------------------------
+ * td_verify_step -- the whole verify step, stages (a) to (d), in three
+ * kernels instead of the five calls' seven: (1) top-K of every position,
+ * then, by the last position of each sequence to finish, that sequence's
+ * tree and mask rows; (2) the split-KV context attention; (3) the partial
+ * merge with the tree keys, and the acceptance walk.  Every result equals
+ * what the five calls above produce on the same inputs, into the same
+ * output arrays (the fields below use their names, layouts and rules).
+ * nq_max = n_max + 1.  target_token [batch][n_max+1] is an input: the
+ * target's greedy token at every node of the tree this step builds.
+ * Workspace: td_verify_step_workspace(args) bytes, 16-byte aligned,
+ * ZERO-FILLED before its first use; every call leaves it ready for the next.
+ * Calls that overlap in time must not share a workspace.
+ */
+typedef struct {
+    /* stage (a) */
+    const void *logits;
+    td_dtype logits_dtype;
+    int32_t batch, block, vocab;
+    int64_t pos_stride;
+    int32_t topk;
+    /* stage (b) */
+    int32_t n_max, use_stop;
+    double cost_a, cost_b, cost_c;
+    int32_t cost_knee;
+    double l_ar, ahat0;
+    const int32_t *root_token; /* may be NULL */
+    /* stage (c) */
+    const void *q, *k_ctx, *v_ctx;
+    const int64_t *ctx_offsets;
+    int64_t total_ctx, max_ctx;
+    const void *k_tree, *v_tree;
+    int32_t hq, hkv, head_dim;
+    float scale;
+    td_dtype attn_dtype;
+    /* stage (d) */
+    const int32_t *target_token;
+    /* outputs */
+    int32_t *topk_id;
+    double *topk_logq, *lse;
+    int32_t *n_nodes, *node_token, *node_parent, *node_depth;
+    double *node_logrho, *ahat, *speedup; /* ahat, speedup may be NULL */
+    uint64_t *mask;
+    void *out;
+    int32_t *accept_len, *accept_path, *bonus_token;
+} td_step_args;
+
+/* sizeof(td_step_args), for bindings that lay the struct out themselves */
+size_t td_step_args_bytes(void);
+size_t td_verify_step_workspace(const td_step_args *args);
+td_status td_verify_step(const td_step_args *args, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ def b():
 
 def test_every_declared_symbol_is_exported(b):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 12
     for n in names:
         assert hasattr(b.lib, n), n
     assert sorted(b.EXPORTED) == names
@@ -98,3 +98,30 @@ def test_attention_validation(b):
     assert b.lib.td_tree_verify_attn(*bad) == 1
     bad = list(base); bad[11] = 257
     assert b.lib.td_tree_verify_attn(*bad) == 2
+
+
+def test_step_args_layout_and_validation(b):
+    assert b.lib.td_step_args_bytes() == ctypes.sizeof(b.StepArgs)
+    a = b.StepArgs()
+    assert b.lib.td_verify_step(None, FAKE, 1 << 20, None) == 1
+    assert b.lib.td_verify_step(ctypes.byref(a), FAKE, 1 << 20, None) == 1   # all null
+    assert b.lib.td_verify_step_workspace(ctypes.byref(a)) == 0
+    a.batch, a.block, a.vocab, a.pos_stride, a.topk = 1, 16, 151936, 151936, 8
+    a.n_max, a.hq, a.hkv, a.head_dim, a.total_ctx, a.max_ctx = 64, 32, 8, 128, 4096, 4096
+    assert b.lib.td_verify_step_workspace(ctypes.byref(a)) > 0
+    for f in ("logits", "q", "k_ctx", "v_ctx", "ctx_offsets", "k_tree", "v_tree", "target_token",
+              "topk_id", "topk_logq", "lse", "n_nodes", "node_token", "node_parent", "node_depth",
+              "node_logrho", "mask", "out", "accept_len", "accept_path", "bonus_token"):
+        setattr(a, f, 4096)
+    a.logits_dtype = a.attn_dtype = 1
+    a.topk = 33
+    assert b.lib.td_verify_step(ctypes.byref(a), FAKE, 1 << 30, None) == 2
+    a.topk = 8
+    a.n_max = 300
+    assert b.lib.td_verify_step(ctypes.byref(a), FAKE, 1 << 30, None) == 2
+    a.n_max = 64
+    a.hkv = 7
+    assert b.lib.td_verify_step(ctypes.byref(a), FAKE, 1 << 30, None) == 1
+    a.hkv = 8
+    assert b.lib.td_verify_step(ctypes.byref(a), FAKE, 16, None) == 1
+    assert "workspace" in b.last_error()

@@ -1,0 +1,150 @@
+"""GPU: the fused verify step (td_verify_step, three kernels) produces exactly
+what the five stage calls produce on the same inputs, on every workload, and
+keeps doing so over repeated calls on one workspace (its arrival counters
+reset themselves).  The stage calls are checked against the oracle in
+test_gpu_parity.py; here the oracle also checks the step's attention and
+acceptance directly on one workload."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import attn_close, cost_of, targets_by_path
+from tree_draft_build_amd import workload as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def td():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tree_draft_build_amd import binding
+    return binding
+
+
+def dev(x):
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(x).to(DEV)
+
+
+def modular(td, cfg, d, tg):
+    ids, lq, lse = td.draft_topk(d["logits"], cfg.topk)
+    t = td.build_tree(ids, lq, cfg.n_max, cfg.use_stop, cost_of(cfg), cfg.l_ar, cfg.ahat0)
+    mask = td.tree_mask(t["node_parent"], t["n_nodes"])
+    out = td.tree_verify_attn(d["q"], d["k_ctx"], d["v_ctx"], d["off"], d["total"], d["maxc"],
+                              d["k_tree"], d["v_tree"], mask, t["n_nodes"], wl.attn_scale(cfg))
+    res = dict(topk_id=ids, topk_logq=lq, lse=lse, mask=mask, out=out, **t)
+    if tg is not None:
+        a, p, bo = td.accept(t["node_token"], t["node_parent"], t["n_nodes"], tg, cfg.block)
+        res.update(accept_len=a, accept_path=p, bonus_token=bo)
+    torch.cuda.synchronize()
+    return {k: v.cpu() for k, v in res.items()}
+
+
+def make_step(td, cfg, d):
+    s = td.VerifyStep(batch=cfg.batch, block=cfg.block, vocab=cfg.vocab, topk=cfg.topk,
+                      n_max=cfg.n_max, use_stop=cfg.use_stop, cost=cost_of(cfg), l_ar=cfg.l_ar,
+                      ahat0=cfg.ahat0, hq=cfg.hq, hkv=cfg.hkv, head_dim=cfg.head_dim,
+                      scale=wl.attn_scale(cfg),
+                      logits_dtype=td.TD_BF16 if cfg.logit_dtype == "bf16" else td.TD_F32,
+                      attn_dtype=td.TD_BF16 if cfg.attn_dtype == "bf16" else td.TD_F32,
+                      total_ctx=d["total"], max_ctx=d["maxc"], device=DEV)
+    return s
+
+
+def step_outputs(s):
+    res = dict(topk_id=s.topk_id, topk_logq=s.topk_logq, lse=s.lse, mask=s.mask, out=s.out,
+               accept_len=s.accept_len, accept_path=s.accept_path, bonus_token=s.bonus_token,
+               **s.tree)
+    return {k: v.cpu() for k, v in res.items()}
+
+
+def inputs(cfg):
+    x = wl.make_logits(cfg)
+    inp = wl.make_attn_inputs(cfg)
+    return x, inp, dict(logits=dev(x), q=dev(inp["q"]), k_ctx=dev(inp["k_ctx"]),
+                        v_ctx=dev(inp["v_ctx"]), k_tree=dev(inp["k_tree"]),
+                        v_tree=dev(inp["v_tree"]), off=dev(inp["ctx_offsets"]),
+                        total=int(inp["ctx_offsets"][-1]), maxc=int(inp["ctx_len"].max()))
+
+
+def assert_same(a, b, what):
+    for k in a:
+        assert torch.equal(a[k], b[k]), f"{what}: {k} differs"
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_fixed", "qwen3_8b", "qwen3_8b_stress",
+                                  "qwen3_8b_masksens", "llama31_8b", "batched", "long"])
+def test_step_equals_stage_calls(td, name):
+    cfg = wl.CONFIGS[name]
+    print("[case] step vs stages", name, flush=True)
+    x, inp, d = inputs(cfg)
+    ref = modular(td, cfg, d, None)
+    tree_np = {k: ref[k].numpy() for k in ("node_token", "node_parent", "n_nodes")}
+    tg = dev(targets_by_path(cfg, wl.logits_as_f64(x, cfg.logit_dtype), tree_np))
+    ref = modular(td, cfg, d, tg)
+    s = make_step(td, cfg, d)
+    s.set_inputs(d["logits"], d["q"], d["k_ctx"], d["v_ctx"], d["off"], d["k_tree"], d["v_tree"], tg)
+    for rep in range(3):  # the workspace must be ready again after every call
+        s.run()
+        torch.cuda.synchronize()
+        assert_same(ref, step_outputs(s), f"{name} call {rep}")
+
+
+def test_step_alternating_inputs(td):
+    """Two workloads of one shape through one step object, alternating."""
+    cfg_a = wl.CONFIGS["qwen3_8b_stress"]
+    cfg_b = cfg_a.replace(index=31)
+    print("[case] step alternating", flush=True)
+    xa, ia, da = inputs(cfg_a)
+    xb, ib, db = inputs(cfg_b)
+    assert da["total"] == db["total"]
+    refs, tgs = [], []
+    for cfg, x, d in ((cfg_a, xa, da), (cfg_b, xb, db)):
+        r = modular(td, cfg, d, None)
+        tree_np = {k: r[k].numpy() for k in ("node_token", "node_parent", "n_nodes")}
+        tg = dev(targets_by_path(cfg, wl.logits_as_f64(x, cfg.logit_dtype), tree_np))
+        refs.append(modular(td, cfg, d, tg))
+        tgs.append(tg)
+    s = make_step(td, cfg_a, da)
+    for rep in range(6):
+        j = rep % 2
+        d = (da, db)[j]
+        s.set_inputs(d["logits"], d["q"], d["k_ctx"], d["v_ctx"], d["off"], d["k_tree"],
+                     d["v_tree"], tgs[j])
+        s.run()
+        torch.cuda.synchronize()
+        assert_same(refs[j], step_outputs(s), f"alternating call {rep}")
+
+
+def test_step_against_oracle(td):
+    cfg = wl.CONFIGS["qwen3_8b_stress"]
+    print("[case] step vs oracle", flush=True)
+    x, inp, d = inputs(cfg)
+    ids, lq, _ = oracle.draft_topk(x, cfg.topk)
+    tr = oracle.build_tree(ids, lq, cfg.n_max, cfg.use_stop, cost_of(cfg), cfg.l_ar, cfg.ahat0)
+    tg_np = wl.target_tokens(cfg, wl.logits_as_f64(x, "bf16"), tr["node_token"], tr["node_parent"],
+                             tr["n_nodes"])
+    s = make_step(td, cfg, d)
+    s.set_inputs(d["logits"], d["q"], d["k_ctx"], d["v_ctx"], d["off"], d["k_tree"], d["v_tree"],
+                 dev(tg_np))
+    s.run()
+    torch.cuda.synchronize()
+    out = step_outputs(s)
+    for k in ("n_nodes", "node_token", "node_parent", "node_depth"):
+        np.testing.assert_array_equal(out[k].numpy(), tr[k])
+    m = oracle.tree_mask(tr["node_parent"], tr["n_nodes"])
+    np.testing.assert_array_equal(out["mask"].numpy().view(np.uint64), m)
+    want = oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"], inp["k_tree"],
+                            inp["v_tree"], m, tr["n_nodes"], cfg.hq, cfg.hkv, cfg.head_dim,
+                            wl.attn_scale(cfg))
+    got = wl.bf16_bits_to_f32(out["out"].view(torch.int16).numpy().view(np.uint16)).astype(np.float64)
+    attn_close(got, want, "bf16", "step attention")
+    a_o, p_o, b_o = oracle.accept(tr["node_token"], tr["node_parent"], tr["n_nodes"], tg_np, cfg.block)
+    np.testing.assert_array_equal(out["accept_len"].numpy(), a_o)
+    np.testing.assert_array_equal(out["accept_path"].numpy(), p_o)
+    np.testing.assert_array_equal(out["bonus_token"].numpy(), b_o)

@@ -24,7 +24,29 @@ STATUS_NAMES = {0: "TD_OK", 1: "TD_EINVAL", 2: "TD_ECAPACITY", 3: "TD_EUNSUPPORT
 # every symbol declared in include/treedraft.h
 EXPORTED = ["td_abi_version", "td_last_error", "td_draft_topk_workspace", "td_draft_topk",
             "td_build_tree", "td_tree_mask", "td_tree_verify_attn_workspace",
-            "td_tree_verify_attn", "td_accept"]
+            "td_tree_verify_attn", "td_accept", "td_step_args_bytes", "td_verify_step_workspace",
+            "td_verify_step"]
+
+
+class StepArgs(ctypes.Structure):
+    """td_step_args, field for field."""
+    _fields_ = [
+        ("logits", c_void_p), ("logits_dtype", c_int), ("batch", c_int32), ("block", c_int32),
+        ("vocab", c_int32), ("pos_stride", c_int64), ("topk", c_int32),
+        ("n_max", c_int32), ("use_stop", c_int32), ("cost_a", c_double), ("cost_b", c_double),
+        ("cost_c", c_double), ("cost_knee", c_int32), ("l_ar", c_double), ("ahat0", c_double),
+        ("root_token", c_void_p),
+        ("q", c_void_p), ("k_ctx", c_void_p), ("v_ctx", c_void_p), ("ctx_offsets", c_void_p),
+        ("total_ctx", c_int64), ("max_ctx", c_int64), ("k_tree", c_void_p), ("v_tree", c_void_p),
+        ("hq", c_int32), ("hkv", c_int32), ("head_dim", c_int32), ("scale", c_float),
+        ("attn_dtype", c_int),
+        ("target_token", c_void_p),
+        ("topk_id", c_void_p), ("topk_logq", c_void_p), ("lse", c_void_p),
+        ("n_nodes", c_void_p), ("node_token", c_void_p), ("node_parent", c_void_p),
+        ("node_depth", c_void_p), ("node_logrho", c_void_p), ("ahat", c_void_p),
+        ("speedup", c_void_p), ("mask", c_void_p), ("out", c_void_p),
+        ("accept_len", c_void_p), ("accept_path", c_void_p), ("bonus_token", c_void_p),
+    ]
 
 
 class TreedraftError(RuntimeError):
@@ -54,9 +76,15 @@ def _load():
     lib.td_tree_verify_attn.argtypes = [P, P, P, P, c_int64, c_int64, P, P, P, P, c_int32, c_int32,
                                         c_int32, c_int32, c_int32, c_float, c_int, P, P, c_size_t, P]
     lib.td_accept.argtypes = [P, P, P, P, c_int32, c_int32, c_int32, P, P, P, P]
+    lib.td_step_args_bytes.restype = c_size_t
+    lib.td_verify_step_workspace.argtypes = [ctypes.POINTER(StepArgs)]
+    lib.td_verify_step_workspace.restype = c_size_t
+    lib.td_verify_step.argtypes = [ctypes.POINTER(StepArgs), P, c_size_t, P]
     for name in ("td_draft_topk", "td_build_tree", "td_tree_mask", "td_tree_verify_attn",
-                 "td_accept"):
+                 "td_accept", "td_verify_step"):
         getattr(lib, name).restype = c_int
+    if lib.td_step_args_bytes() != ctypes.sizeof(StepArgs):
+        raise ImportError("td_step_args layout differs between the library and this binding")
     return lib
 
 
@@ -223,3 +251,64 @@ def accept(node_token, node_parent, n_nodes, target_token, block, out=None, stre
     _check(lib.td_accept(_ptr(node_token), _ptr(node_parent), _ptr(n_nodes), _ptr(target_token), b,
                          W - 1, block, _ptr(alen), _ptr(path), _ptr(bonus), _stream(stream)))
     return alen, path, bonus
+
+
+# ---------------------------------------------------------------------------
+# the fused verify step
+
+class VerifyStep:
+    """Argument block and buffers of td_verify_step for one fixed problem.
+
+    All tensors are device tensors; outputs and the (zero-filled) workspace
+    are allocated once, so repeated calls allocate nothing and can be
+    captured in a HIP graph."""
+
+    def __init__(self, *, batch, block, vocab, topk, n_max, use_stop, cost, l_ar, ahat0, hq, hkv,
+                 head_dim, scale, logits_dtype, attn_dtype, total_ctx, max_ctx, device):
+        dev = device
+        W = n_max + 1
+        self.topk_id = torch.empty((batch, block, topk), dtype=torch.int32, device=dev)
+        self.topk_logq = torch.empty((batch, block, topk), dtype=torch.float64, device=dev)
+        self.lse = torch.empty((batch, block), dtype=torch.float64, device=dev)
+        self.tree = alloc_tree(batch, n_max, dev)
+        self.mask = torch.empty((batch, W, (W + 63) // 64), dtype=torch.int64, device=dev)
+        adt = torch.bfloat16 if attn_dtype == TD_BF16 else torch.float32
+        self.out = torch.empty((batch, W, hq, head_dim), dtype=adt, device=dev)
+        self.accept_len = torch.empty(batch, dtype=torch.int32, device=dev)
+        self.accept_path = torch.empty((batch, block + 1), dtype=torch.int32, device=dev)
+        self.bonus_token = torch.empty(batch, dtype=torch.int32, device=dev)
+        a = StepArgs()
+        a.logits_dtype, a.batch, a.block, a.vocab, a.pos_stride, a.topk = (
+            logits_dtype, batch, block, vocab, vocab, topk)
+        a.n_max, a.use_stop = n_max, int(bool(use_stop))
+        a.cost_a, a.cost_b, a.cost_c, a.cost_knee = float(cost[0]), float(cost[1]), float(cost[2]), int(cost[3])
+        a.l_ar, a.ahat0 = float(l_ar), float(ahat0)
+        a.total_ctx, a.max_ctx = int(total_ctx), int(max_ctx)
+        a.hq, a.hkv, a.head_dim, a.scale, a.attn_dtype = hq, hkv, head_dim, float(scale), attn_dtype
+        t = self.tree
+        for name, ten in (("topk_id", self.topk_id), ("topk_logq", self.topk_logq),
+                          ("lse", self.lse), ("n_nodes", t["n_nodes"]),
+                          ("node_token", t["node_token"]), ("node_parent", t["node_parent"]),
+                          ("node_depth", t["node_depth"]), ("node_logrho", t["node_logrho"]),
+                          ("ahat", t["ahat"]), ("speedup", t["speedup"]), ("mask", self.mask),
+                          ("out", self.out), ("accept_len", self.accept_len),
+                          ("accept_path", self.accept_path), ("bonus_token", self.bonus_token)):
+            setattr(a, name, ten.data_ptr())
+        self.args = a
+        self.workspace = torch.zeros(max(16, int(lib.td_verify_step_workspace(ctypes.byref(a)))),
+                                     dtype=torch.uint8, device=dev)
+
+    def set_inputs(self, logits, q, k_ctx, v_ctx, ctx_offsets, k_tree, v_tree, target_token,
+                   root_token=None):
+        a = self.args
+        a.logits = logits.data_ptr()
+        a.q, a.k_ctx, a.v_ctx = q.data_ptr(), k_ctx.data_ptr(), v_ctx.data_ptr()
+        a.ctx_offsets = ctx_offsets.data_ptr()
+        a.k_tree, a.v_tree = k_tree.data_ptr(), v_tree.data_ptr()
+        a.target_token = target_token.data_ptr()
+        a.root_token = None if root_token is None else root_token.data_ptr()
+        self._keep = (logits, q, k_ctx, v_ctx, ctx_offsets, k_tree, v_tree, target_token, root_token)
+
+    def run(self, stream=None):
+        _check(lib.td_verify_step(ctypes.byref(self.args), _ptr(self.workspace),
+                                  self.workspace.numel(), _stream(stream)))

@@ -31,7 +31,9 @@
 
 #include <algorithm>
 
+#include "step_launch.h"
 #include "td_internal.h"
+#include "tree_core.h"
 
 namespace td {
 namespace {
@@ -135,10 +137,11 @@ __device__ __forceinline__ void wave_select(KeyList<KW> &l, int K, uint64_t (&wi
     }
 }
 
-// Workspace layout: for R rows and P = rows * splits partials
-//   uint32 count[R] | double s[P] | float m[P] | uint64 key[P][K]
-// (each 16-byte aligned).  count[] must be zero before the first call and is
-// zero again after every call.
+// Workspace layout: for R rows, P = rows * splits partials and B sequences
+//   uint32 count[R + B] | double s[P] | float m[P] | uint64 key[P][K]
+// (each 16-byte aligned; the B sequence counters serve the fused step).
+// count[] must be zero before the first call and is zero again after every
+// call.
 struct TopkWs {
     unsigned int *count;
     double *s;
@@ -149,14 +152,15 @@ struct TopkWs {
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
 inline size_t topk_ws_bytes(int64_t rows, int64_t parts, int K) {
-    return align16(rows * 4) + align16(parts * 8) + align16(parts * 4) + align16(parts * K * 8);
+    return align16(rows * 4 + rows * 4) + align16(parts * 8) + align16(parts * 4) +
+           align16(parts * K * 8);
 }
 
 __host__ __device__ inline TopkWs topk_ws(void *base, int64_t rows, int64_t parts, int K) {
     char *p = static_cast<char *>(base);
     TopkWs w;
     w.count = reinterpret_cast<unsigned int *>(p);
-    p += align16(rows * 4);
+    p += align16(rows * 4 + rows * 4);  // row counters, then (up to rows) sequence counters
     w.s = reinterpret_cast<double *>(p);
     p += align16(parts * 8);
     w.m = reinterpret_cast<float *>(p);
@@ -268,14 +272,18 @@ __device__ __forceinline__ void rank_select(const uint64_t *buf, int C, int K, u
     }
 }
 
-template <typename T, int KM>
+// FUSE: the verify step's first kernel.  The row outputs are then written
+// with agent-scope atomic stores, and the last row of each sequence to finish
+// builds that sequence's tree (and mask rows) from them in wave 0.
+template <typename T, int KM, bool FUSE, int SLOTS>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict__ logits,
                                                             int vocab, int64_t pos_stride,
                                                             int slice, int splits, int K, void *ws,
                                                             int64_t parts,
                                                             int32_t *__restrict__ topk_id,
                                                             double *__restrict__ topk_logq,
-                                                            double *__restrict__ lse_out) {
+                                                            double *__restrict__ lse_out,
+                                                            TreeParams tp, TreeOut to) {
     constexpr int N = Vec<T>::N;
     const int sp = blockIdx.x;
     const int row = blockIdx.y;
@@ -504,12 +512,41 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     const double lse = static_cast<double>(M) + log(S);
     if (lane < K) {
         const uint64_t k = sm_win[lane];
-        topk_id[static_cast<int64_t>(row) * K + lane] = key_id(k);
-        topk_logq[static_cast<int64_t>(row) * K + lane] = static_cast<double>(key_value(k)) - lse;
+        const int32_t id = key_id(k);
+        const double lq = static_cast<double>(key_value(k)) - lse;
+        if constexpr (FUSE) {
+            publish(&topk_id[static_cast<int64_t>(row) * K + lane], id);
+            publish(&topk_logq[static_cast<int64_t>(row) * K + lane], lq);
+        } else {
+            topk_id[static_cast<int64_t>(row) * K + lane] = id;
+            topk_logq[static_cast<int64_t>(row) * K + lane] = lq;
+        }
     }
     if (lane == 0) {
         lse_out[row] = lse;
         ws_.count[row] = 0u;  // ready for the next call
+    }
+    if constexpr (FUSE) {
+        // sequence completion: the last of its rows builds the tree
+        __shared__ TreeLds tl;
+        const int b = row / tp.block;
+        unsigned int *seq_count = ws_.count + rows;
+        __builtin_amdgcn_s_waitcnt(0);  // this row's outputs are complete
+        int last = 0;
+        if (lane == 0)
+            last = __hip_atomic_fetch_add(&seq_count[b], 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) ==
+                   static_cast<unsigned>(tp.block - 1);
+        last = __builtin_amdgcn_readfirstlane(last);
+        if (!last) return;
+        const int BK = tp.block * K;
+        for (int e = lane; e < BK; e += kWave) {
+            tl.ids[e] = fetch(&topk_id[static_cast<int64_t>(b) * BK + e]);
+            tl.lq[e] = fetch(&topk_logq[static_cast<int64_t>(b) * BK + e]);
+        }
+        wave_lds_sync();
+        build_tree_wave<SLOTS>(tl, tp, to, b, lane);
+        if (lane == 0) seq_count[b] = 0u;
     }
 }
 
@@ -533,40 +570,109 @@ inline TopkPlan topk_plan(int64_t rows, int vocab) {
     return {splits, slice};
 }
 
-template <typename T, int KM>
+template <typename T, int KM, bool FUSE, int SLOTS>
 void launch_topk(const void *logits, int rows, int vocab, int64_t pos_stride, int K,
                  const TopkPlan &pl, void *ws, int32_t *topk_id, double *topk_logq, double *lse,
-                 hipStream_t st) {
+                 const TreeParams &tp, const TreeOut &to, hipStream_t st) {
     const int64_t parts = static_cast<int64_t>(rows) * pl.splits;
-    hipLaunchKernelGGL((topk_kernel<T, KM>), dim3(pl.splits, rows), dim3(kTopkThreads), 0, st,
-                       static_cast<const T *>(logits), vocab, pos_stride, pl.slice, pl.splits, K,
-                       ws, parts, topk_id, topk_logq, lse);
+    hipLaunchKernelGGL((topk_kernel<T, KM, FUSE, SLOTS>), dim3(pl.splits, rows), dim3(kTopkThreads),
+                       0, st, static_cast<const T *>(logits), vocab, pos_stride, pl.slice, pl.splits,
+                       K, ws, parts, topk_id, topk_logq, lse, tp, to);
 }
 
-template <typename T>
+template <typename T, bool FUSE, int SLOTS>
 void launch_topk_k(const void *logits, int rows, int vocab, int64_t pos_stride, int K,
                    const TopkPlan &pl, void *ws, int32_t *topk_id, double *topk_logq, double *lse,
-                   hipStream_t st) {
+                   const TreeParams &tp, const TreeOut &to, hipStream_t st) {
     if (K <= 4)
-        launch_topk<T, 4>(logits, rows, vocab, pos_stride, K, pl, ws, topk_id, topk_logq, lse, st);
+        launch_topk<T, 4, FUSE, SLOTS>(logits, rows, vocab, pos_stride, K, pl, ws, topk_id, topk_logq,
+                                       lse, tp, to, st);
     else if (K <= 8)
-        launch_topk<T, 8>(logits, rows, vocab, pos_stride, K, pl, ws, topk_id, topk_logq, lse, st);
+        launch_topk<T, 8, FUSE, SLOTS>(logits, rows, vocab, pos_stride, K, pl, ws, topk_id, topk_logq,
+                                       lse, tp, to, st);
     else if (K <= 16)
-        launch_topk<T, 16>(logits, rows, vocab, pos_stride, K, pl, ws, topk_id, topk_logq, lse, st);
+        launch_topk<T, 16, FUSE, SLOTS>(logits, rows, vocab, pos_stride, K, pl, ws, topk_id,
+                                        topk_logq, lse, tp, to, st);
     else
-        launch_topk<T, 32>(logits, rows, vocab, pos_stride, K, pl, ws, topk_id, topk_logq, lse, st);
+        launch_topk<T, 32, FUSE, SLOTS>(logits, rows, vocab, pos_stride, K, pl, ws, topk_id,
+                                        topk_logq, lse, tp, to, st);
+}
+
+template <bool FUSE, int SLOTS>
+void launch_topk_dt(const void *logits, td_dtype dtype, int rows, int vocab, int64_t pos_stride,
+                    int K, void *ws, int32_t *topk_id, double *topk_logq, double *lse,
+                    const TreeParams &tp, const TreeOut &to, hipStream_t st) {
+    const TopkPlan pl = topk_plan(rows, vocab);
+    if (dtype == TD_BF16)
+        launch_topk_k<uint16_t, FUSE, SLOTS>(logits, rows, vocab, pos_stride, K, pl, ws, topk_id,
+                                             topk_logq, lse, tp, to, st);
+    else
+        launch_topk_k<float, FUSE, SLOTS>(logits, rows, vocab, pos_stride, K, pl, ws, topk_id,
+                                          topk_logq, lse, tp, to, st);
 }
 
 }  // namespace
+
+size_t topk_workspace_bytes(int batch, int block, int vocab, int K) {
+    const int64_t rows = static_cast<int64_t>(batch) * block;
+    const TopkPlan pl = topk_plan(rows, vocab);
+    return topk_ws_bytes(rows, rows * pl.splits, K);
+}
+
+void launch_topk_tree(const void *logits, td_dtype dtype, int batch, int block, int vocab,
+                      int64_t pos_stride, int K, void *ws, int32_t *topk_id, double *topk_logq,
+                      double *lse, const TreeParams &tp, const TreeOut &to, hipStream_t st) {
+    const int rows = batch * block;
+    switch (tree_slots(tp.n_max)) {
+    case 1:
+        launch_topk_dt<true, 1>(logits, dtype, rows, vocab, pos_stride, K, ws, topk_id, topk_logq,
+                                lse, tp, to, st);
+        break;
+    case 2:
+        launch_topk_dt<true, 2>(logits, dtype, rows, vocab, pos_stride, K, ws, topk_id, topk_logq,
+                                lse, tp, to, st);
+        break;
+    case 4:
+        launch_topk_dt<true, 4>(logits, dtype, rows, vocab, pos_stride, K, ws, topk_id, topk_logq,
+                                lse, tp, to, st);
+        break;
+    default:
+        launch_topk_dt<true, 8>(logits, dtype, rows, vocab, pos_stride, K, ws, topk_id, topk_logq,
+                                lse, tp, to, st);
+        break;
+    }
+}
+
 }  // namespace td
 
 using namespace td;
 
 extern "C" size_t td_draft_topk_workspace(int32_t batch, int32_t block, int32_t vocab, int32_t K) {
     if (batch <= 0 || block <= 0 || vocab <= 0 || K <= 0) return 0;
-    const int64_t rows = static_cast<int64_t>(batch) * block;
-    TopkPlan pl = topk_plan(rows, vocab);
-    return topk_ws_bytes(rows, rows * pl.splits, K);
+    return topk_workspace_bytes(batch, block, vocab, K);
+}
+
+td_status td::check_topk_args(const void *logits, td_dtype dtype, int32_t batch, int32_t block,
+                             int32_t vocab, int64_t pos_stride, int32_t K, const int32_t *topk_id,
+                             const double *topk_logq, const double *lse) {
+    if (!logits || !topk_id || !topk_logq || !lse)
+        return fail(TD_EINVAL, "draft_topk: null pointer argument");
+    if (batch <= 0 || block <= 0 || vocab <= 0 || K <= 0)
+        return fail(TD_EINVAL, "draft_topk: batch, block, vocab and K must be positive");
+    if (K > vocab) return fail(TD_EINVAL, "draft_topk: K exceeds the vocabulary");
+    if (K > TD_MAX_TOPK) return fail(TD_ECAPACITY, "draft_topk: K above TD_MAX_TOPK");
+    if (block > TD_MAX_BLOCK) return fail(TD_ECAPACITY, "draft_topk: block above TD_MAX_BLOCK");
+    if (batch > TD_MAX_BATCH) return fail(TD_ECAPACITY, "draft_topk: batch above TD_MAX_BATCH");
+    if (vocab > TD_MAX_VOCAB) return fail(TD_ECAPACITY, "draft_topk: vocab above TD_MAX_VOCAB");
+    if (dtype != TD_F32 && dtype != TD_BF16)
+        return fail(TD_EUNSUPPORTED, "draft_topk: dtype must be TD_F32 or TD_BF16");
+    if (pos_stride < vocab) return fail(TD_EINVAL, "draft_topk: pos_stride < vocab");
+    const int esz = dtype == TD_F32 ? 4 : 2;
+    if ((reinterpret_cast<uintptr_t>(logits) % esz) != 0)
+        return fail(TD_EINVAL, "draft_topk: logits must be aligned to the element size");
+    if (!aligned8(topk_logq) || !aligned8(lse))
+        return fail(TD_EINVAL, "draft_topk: misaligned float64 output");
+    return TD_OK;
 }
 
 extern "C" td_status td_draft_topk(const void *logits, td_dtype dtype, int32_t batch, int32_t block,
@@ -574,33 +680,16 @@ extern "C" td_status td_draft_topk(const void *logits, td_dtype dtype, int32_t b
                                    double *topk_logq, double *lse, void *workspace,
                                    size_t workspace_bytes, void *stream) {
     clear_error();
-    if (!logits || !topk_id || !topk_logq || !lse || !workspace)
-        return fail(TD_EINVAL, "td_draft_topk: null pointer argument");
-    if (batch <= 0 || block <= 0 || vocab <= 0 || K <= 0)
-        return fail(TD_EINVAL, "td_draft_topk: batch, block, vocab and K must be positive");
-    if (K > vocab) return fail(TD_EINVAL, "td_draft_topk: K exceeds the vocabulary");
-    if (K > TD_MAX_TOPK) return fail(TD_ECAPACITY, "td_draft_topk: K above TD_MAX_TOPK");
-    if (block > TD_MAX_BLOCK) return fail(TD_ECAPACITY, "td_draft_topk: block above TD_MAX_BLOCK");
-    if (batch > TD_MAX_BATCH) return fail(TD_ECAPACITY, "td_draft_topk: batch above TD_MAX_BATCH");
-    if (vocab > TD_MAX_VOCAB) return fail(TD_ECAPACITY, "td_draft_topk: vocab above TD_MAX_VOCAB");
-    if (dtype != TD_F32 && dtype != TD_BF16)
-        return fail(TD_EUNSUPPORTED, "td_draft_topk: dtype must be TD_F32 or TD_BF16");
-    if (pos_stride < vocab) return fail(TD_EINVAL, "td_draft_topk: pos_stride < vocab");
-    const int esz = dtype == TD_F32 ? 4 : 2;
-    if ((reinterpret_cast<uintptr_t>(logits) % esz) != 0)
-        return fail(TD_EINVAL, "td_draft_topk: logits must be aligned to the element size");
-    if (!aligned16(workspace) || !aligned8(topk_logq) || !aligned8(lse))
-        return fail(TD_EINVAL, "td_draft_topk: misaligned workspace or output");
+    const td_status st =
+        check_topk_args(logits, dtype, batch, block, vocab, pos_stride, K, topk_id, topk_logq, lse);
+    if (st != TD_OK) return st;
+    if (!workspace || !aligned16(workspace))
+        return fail(TD_EINVAL, "td_draft_topk: null or misaligned workspace");
     if (workspace_bytes < td_draft_topk_workspace(batch, block, vocab, K))
         return fail(TD_EINVAL, "td_draft_topk: workspace too small");
-    const int rows = batch * block;
-    TopkPlan pl = topk_plan(rows, vocab);
-    hipStream_t st = as_stream(stream);
-    if (dtype == TD_BF16)
-        launch_topk_k<uint16_t>(logits, rows, vocab, pos_stride, K, pl, workspace, topk_id,
-                                topk_logq, lse, st);
-    else
-        launch_topk_k<float>(logits, rows, vocab, pos_stride, K, pl, workspace, topk_id, topk_logq,
-                             lse, st);
+    const TreeParams tp{};
+    const TreeOut to{};
+    launch_topk_dt<false, 1>(logits, dtype, batch * block, vocab, pos_stride, K, workspace, topk_id,
+                             topk_logq, lse, tp, to, as_stream(stream));
     return check_launch("td_draft_topk");
 }

@@ -1,0 +1,58 @@
+// Launchers shared between translation units (internal, not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "treedraft.h"
+
+namespace td {
+
+struct TreeParams;
+struct TreeOut;
+
+// top-K workspace bytes (row and sequence arrival counters + partials)
+size_t topk_workspace_bytes(int batch, int block, int vocab, int K);
+
+// The verify step's first kernel: top-K of every position, then each
+// sequence's tree and mask rows (TreeOut::mask must be set).
+void launch_topk_tree(const void *logits, td_dtype dtype, int batch, int block, int vocab,
+                      int64_t pos_stride, int K, void *ws, int32_t *topk_id, double *topk_logq,
+                      double *lse, const TreeParams &tp, const TreeOut &to, hipStream_t st);
+
+// Tree attention; with accept_* set, the combine kernel also runs the
+// acceptance walk of every sequence.
+struct AcceptArgs {
+    const int32_t *node_token, *node_parent, *target_token;
+    int n_max, block;
+    int32_t *accept_len, *accept_path, *bonus_token;
+};
+size_t attn_workspace_bytes(int batch, int nq_max, int hq, int hkv, int head_dim,
+                            int64_t total_ctx, td_dtype dtype);
+void launch_attention(const void *q, const void *k_ctx, const void *v_ctx, const int64_t *off,
+                      int64_t total_ctx, const void *k_tree, const void *v_tree,
+                      const uint64_t *mask, const int32_t *n_nodes, int batch, int nq_max, int hq,
+                      int hkv, int head_dim, float scale, td_dtype dtype, void *ws, void *out,
+                      const AcceptArgs *acc, hipStream_t st);
+
+// Argument checks shared by the per-stage entry points and the fused step
+// (they record td_last_error text and return the status).
+td_status check_topk_args(const void *logits, td_dtype dtype, int32_t batch, int32_t block,
+                          int32_t vocab, int64_t pos_stride, int32_t K, const int32_t *topk_id,
+                          const double *topk_logq, const double *lse);
+td_status check_tree_args(const int32_t *topk_id, const double *topk_logq, int32_t batch,
+                          int32_t block, int32_t K, int32_t n_max, const int32_t *n_nodes,
+                          const int32_t *node_token, const int32_t *node_parent,
+                          const int32_t *node_depth, const double *node_logrho);
+td_status check_attn_args(const void *q, const void *k_ctx, const void *v_ctx,
+                          const int64_t *ctx_offsets, int64_t total_ctx, int64_t max_ctx,
+                          const void *k_tree, const void *v_tree, const uint64_t *mask,
+                          const int32_t *n_nodes, int32_t batch, int32_t nq_max, int32_t hq,
+                          int32_t hkv, int32_t head_dim, td_dtype dtype, const void *out);
+td_status check_accept_args(const int32_t *node_token, const int32_t *node_parent,
+                            const int32_t *n_nodes, const int32_t *target_token, int32_t batch,
+                            int32_t n_max, int32_t block, const int32_t *accept_len,
+                            const int32_t *accept_path, const int32_t *bonus_token);
+
+}  // namespace td

@@ -39,7 +39,9 @@
 
 #include <algorithm>
 
+#include "step_launch.h"
 #include "td_internal.h"
+#include "tree_core.h"
 
 namespace td {
 namespace {
@@ -573,15 +575,29 @@ __global__ __launch_bounds__(kAttnThreads) void attn_ctx_split(
 // ---------------------------------------------------------------------------
 constexpr int kCombineRows = kAttnThreads / kWave;  // rows per workgroup
 
-template <typename T, int D>
+// ACC: the grid carries one more workgroup per sequence, whose wave 0 runs
+// the acceptance walk (the verify step's last kernel).
+template <typename T, int D, bool ACC>
 __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     const T *__restrict__ q, const int64_t *__restrict__ ctx_offsets, const T *__restrict__ k_tree,
     const T *__restrict__ v_tree, const uint64_t *__restrict__ mask,
-    const int32_t *__restrict__ n_nodes, int nq_max, int hq, int hkv, int group, int n_rg,
-    int chunk, float scale2, const float *__restrict__ ws, int64_t prow_total, T *__restrict__ out) {
+    const int32_t *__restrict__ n_nodes, int batch, int nq_max, int hq, int hkv, int group, int n_rg,
+    int chunk, float scale2, const float *__restrict__ ws, int64_t prow_total, T *__restrict__ out,
+    AcceptArgs accept) {
     constexpr int kSlice = D / 8;  // dims per lane group
     const int rows_per_bg = group * nq_max;
     const int blocks_per_bg = (rows_per_bg + kCombineRows - 1) / kCombineRows;
+    if constexpr (ACC) {
+        const int64_t first_acc = static_cast<int64_t>(batch) * hkv * blocks_per_bg;
+        if (blockIdx.x >= first_acc) {
+            if (threadIdx.x < kWave)
+                accept_wave(accept.node_token, accept.node_parent, n_nodes, accept.target_token,
+                            accept.n_max, accept.block, accept.accept_len, accept.accept_path,
+                            accept.bonus_token,
+                            static_cast<int>(blockIdx.x - first_acc), threadIdx.x);
+            return;
+        }
+    }
     const int blk = blockIdx.x % blocks_per_bg;
     const int g = (blockIdx.x / blocks_per_bg) % hkv;
     const int b = blockIdx.x / (blocks_per_bg * hkv);
@@ -683,7 +699,7 @@ template <typename T, int D>
 void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int64_t *off,
                  const void *k_tree, const void *v_tree, const uint64_t *mask,
                  const int32_t *n_nodes, int batch, int nq_max, int hq, int hkv, float scale,
-                 const AttnPlan &pl, void *ws, void *out, hipStream_t st) {
+                 const AttnPlan &pl, void *ws, void *out, const AcceptArgs *acc, hipStream_t st) {
     const float scale2 = scale * kLog2e;
     const int64_t prow_total = pl.n_chunks * hkv * pl.n_rg * kRowsPerGroup;
     hipLaunchKernelGGL((attn_ctx_split<T, D>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)),
@@ -692,12 +708,20 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
                        batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,
                        static_cast<float *>(ws), prow_total);
     const int blocks_per_bg = (pl.group * nq_max + kCombineRows - 1) / kCombineRows;
-    hipLaunchKernelGGL((attn_tree_combine<T, D>),
-                       dim3(static_cast<unsigned>(static_cast<int64_t>(batch) * hkv * blocks_per_bg)),
-                       dim3(kAttnThreads), 0, st, static_cast<const T *>(q), off,
-                       static_cast<const T *>(k_tree), static_cast<const T *>(v_tree), mask, n_nodes,
-                       nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,
-                       static_cast<const float *>(ws), prow_total, static_cast<T *>(out));
+    const int64_t blocks = static_cast<int64_t>(batch) * hkv * blocks_per_bg;
+    if (acc)
+        hipLaunchKernelGGL((attn_tree_combine<T, D, true>), dim3(static_cast<unsigned>(blocks + batch)),
+                           dim3(kAttnThreads), 0, st, static_cast<const T *>(q), off,
+                           static_cast<const T *>(k_tree), static_cast<const T *>(v_tree), mask,
+                           n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,
+                           static_cast<const float *>(ws), prow_total, static_cast<T *>(out), *acc);
+    else
+        hipLaunchKernelGGL((attn_tree_combine<T, D, false>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(kAttnThreads), 0, st, static_cast<const T *>(q), off,
+                           static_cast<const T *>(k_tree), static_cast<const T *>(v_tree), mask,
+                           n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,
+                           static_cast<const float *>(ws), prow_total, static_cast<T *>(out),
+                           AcceptArgs{});
 }
 
 inline int sub_chunk(td_dtype dt) { return dt == TD_BF16 ? Sub<uint16_t>::CH : Sub<float>::CH; }
@@ -709,15 +733,37 @@ inline size_t attn_ws_size(const AttnPlan &pl, int batch, int hkv, int D) {
 }
 
 }  // namespace
+
+size_t attn_workspace_bytes(int batch, int nq_max, int hq, int hkv, int head_dim,
+                            int64_t total_ctx, td_dtype dtype) {
+    const AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, sub_chunk(dtype));
+    return std::max<size_t>(16, attn_ws_size(pl, batch, hkv, head_dim));
+}
+
+void launch_attention(const void *q, const void *k_ctx, const void *v_ctx, const int64_t *off,
+                      int64_t total_ctx, const void *k_tree, const void *v_tree,
+                      const uint64_t *mask, const int32_t *n_nodes, int batch, int nq_max, int hq,
+                      int hkv, int head_dim, float scale, td_dtype dtype, void *ws, void *out,
+                      const AcceptArgs *acc, hipStream_t st) {
+    const AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, sub_chunk(dtype));
+    const bool bf = dtype == TD_BF16;
+#define TD_ATTN(T, DD)                                                                          \
+    launch_attn<T, DD>(q, k_ctx, v_ctx, off, k_tree, v_tree, mask, n_nodes, batch, nq_max, hq,  \
+                       hkv, scale, pl, ws, out, acc, st)
+    if (bf && head_dim == 128)
+        TD_ATTN(uint16_t, 128);
+    else if (bf)
+        TD_ATTN(uint16_t, 64);
+    else if (head_dim == 128)
+        TD_ATTN(float, 128);
+    else
+        TD_ATTN(float, 64);
+#undef TD_ATTN
+}
+
 }  // namespace td
 
 using namespace td;
-
-static size_t attn_workspace(int32_t batch, int32_t nq_max, int32_t hq, int32_t hkv,
-                             int32_t head_dim, int64_t total_ctx, td_dtype dt) {
-    AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, sub_chunk(dt));
-    return std::max<size_t>(16, attn_ws_size(pl, batch, hkv, head_dim));
-}
 
 extern "C" size_t td_tree_verify_attn_workspace(int32_t batch, int32_t nq_max, int32_t hq,
                                                 int32_t hkv, int32_t head_dim, int64_t total_ctx,
@@ -727,8 +773,36 @@ extern "C" size_t td_tree_verify_attn_workspace(int32_t batch, int32_t nq_max, i
         total_ctx < 0)
         return 0;
     // the larger of the two dtypes' plans, so one size serves both
-    return std::max(attn_workspace(batch, nq_max, hq, hkv, head_dim, total_ctx, TD_BF16),
-                    attn_workspace(batch, nq_max, hq, hkv, head_dim, total_ctx, TD_F32));
+    return std::max(attn_workspace_bytes(batch, nq_max, hq, hkv, head_dim, total_ctx, TD_BF16),
+                    attn_workspace_bytes(batch, nq_max, hq, hkv, head_dim, total_ctx, TD_F32));
+}
+
+td_status td::check_attn_args(const void *q, const void *k_ctx, const void *v_ctx,
+                             const int64_t *ctx_offsets, int64_t total_ctx, int64_t max_ctx,
+                             const void *k_tree, const void *v_tree, const uint64_t *mask,
+                             const int32_t *n_nodes, int32_t batch, int32_t nq_max, int32_t hq,
+                             int32_t hkv, int32_t head_dim, td_dtype dtype, const void *out) {
+    if (!q || !k_tree || !v_tree || !ctx_offsets || !mask || !n_nodes || !out)
+        return fail(TD_EINVAL, "tree_verify_attn: null pointer argument");
+    if (total_ctx > 0 && (!k_ctx || !v_ctx))
+        return fail(TD_EINVAL, "tree_verify_attn: null context K/V with total_ctx > 0");
+    if (batch <= 0 || nq_max <= 0 || hq <= 0 || hkv <= 0 || total_ctx < 0 || max_ctx < 0)
+        return fail(TD_EINVAL, "tree_verify_attn: sizes must be positive");
+    if (hq % hkv != 0) return fail(TD_EINVAL, "tree_verify_attn: hq must be a multiple of hkv");
+    if (nq_max > TD_MAX_NODES + 1 || batch > TD_MAX_BATCH)
+        return fail(TD_ECAPACITY, "tree_verify_attn: nq_max or batch above capacity");
+    if (dtype != TD_F32 && dtype != TD_BF16)
+        return fail(TD_EUNSUPPORTED, "tree_verify_attn: dtype must be TD_F32 or TD_BF16");
+    if (head_dim != 64 && head_dim != 128)
+        return fail(TD_EUNSUPPORTED, "tree_verify_attn: head_dim must be 64 or 128");
+    if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out) ||
+        (k_ctx && !aligned16(k_ctx)) || (v_ctx && !aligned16(v_ctx)) || !aligned8(mask) ||
+        !aligned8(ctx_offsets))
+        return fail(TD_EINVAL, "tree_verify_attn: buffers must be 16-byte aligned");
+    const AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, sub_chunk(dtype));
+    if (pl.items > 0x7fffffffLL || static_cast<int64_t>(batch) * hkv * pl.n_rg * 4 > 0x7fffffffLL)
+        return fail(TD_ECAPACITY, "tree_verify_attn: grid too large");
+    return TD_OK;
 }
 
 extern "C" td_status td_tree_verify_attn(const void *q, const void *k_ctx, const void *v_ctx,
@@ -739,42 +813,17 @@ extern "C" td_status td_tree_verify_attn(const void *q, const void *k_ctx, const
                                          int32_t head_dim, float scale, td_dtype dtype, void *out,
                                          void *workspace, size_t workspace_bytes, void *stream) {
     clear_error();
-    if (!q || !k_tree || !v_tree || !ctx_offsets || !mask || !n_nodes || !out || !workspace)
-        return fail(TD_EINVAL, "td_tree_verify_attn: null pointer argument");
-    if (total_ctx > 0 && (!k_ctx || !v_ctx))
-        return fail(TD_EINVAL, "td_tree_verify_attn: null context K/V with total_ctx > 0");
-    if (batch <= 0 || nq_max <= 0 || hq <= 0 || hkv <= 0 || total_ctx < 0 || max_ctx < 0)
-        return fail(TD_EINVAL, "td_tree_verify_attn: sizes must be positive");
-    if (hq % hkv != 0) return fail(TD_EINVAL, "td_tree_verify_attn: hq must be a multiple of hkv");
-    if (nq_max > TD_MAX_NODES + 1 || batch > TD_MAX_BATCH)
-        return fail(TD_ECAPACITY, "td_tree_verify_attn: nq_max or batch above capacity");
-    if (dtype != TD_F32 && dtype != TD_BF16)
-        return fail(TD_EUNSUPPORTED, "td_tree_verify_attn: dtype must be TD_F32 or TD_BF16");
-    if (head_dim != 64 && head_dim != 128)
-        return fail(TD_EUNSUPPORTED, "td_tree_verify_attn: head_dim must be 64 or 128");
-    if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out) ||
-        !aligned16(workspace) || (k_ctx && !aligned16(k_ctx)) || (v_ctx && !aligned16(v_ctx)) ||
-        !aligned8(mask) || !aligned8(ctx_offsets))
-        return fail(TD_EINVAL, "td_tree_verify_attn: buffers must be 16-byte aligned");
+    const td_status chk = check_attn_args(q, k_ctx, v_ctx, ctx_offsets, total_ctx, max_ctx, k_tree,
+                                          v_tree, mask, n_nodes, batch, nq_max, hq, hkv, head_dim,
+                                          dtype, out);
+    if (chk != TD_OK) return chk;
+    if (!workspace || !aligned16(workspace))
+        return fail(TD_EINVAL, "td_tree_verify_attn: null or misaligned workspace");
     if (workspace_bytes <
         td_tree_verify_attn_workspace(batch, nq_max, hq, hkv, head_dim, total_ctx, max_ctx))
         return fail(TD_EINVAL, "td_tree_verify_attn: workspace too small");
-    AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, sub_chunk(dtype));
-    if (pl.items > 0x7fffffffLL || static_cast<int64_t>(batch) * hkv * pl.n_rg > 0x7fffffffLL)
-        return fail(TD_ECAPACITY, "td_tree_verify_attn: grid too large");
-    hipStream_t st = as_stream(stream);
-    const bool bf = dtype == TD_BF16;
-#define TD_ATTN(T, DD)                                                                          \
-    launch_attn<T, DD>(q, k_ctx, v_ctx, ctx_offsets, k_tree, v_tree, mask, n_nodes, batch,     \
-                       nq_max, hq, hkv, scale, pl, workspace, out, st)
-    if (bf && head_dim == 128)
-        TD_ATTN(uint16_t, 128);
-    else if (bf)
-        TD_ATTN(uint16_t, 64);
-    else if (head_dim == 128)
-        TD_ATTN(float, 128);
-    else
-        TD_ATTN(float, 64);
-#undef TD_ATTN
+    launch_attention(q, k_ctx, v_ctx, ctx_offsets, total_ctx, k_tree, v_tree, mask, n_nodes, batch,
+                     nq_max, hq, hkv, head_dim, scale, dtype, workspace, out, nullptr,
+                     as_stream(stream));
     return check_launch("td_tree_verify_attn");
 }

@@ -1,0 +1,290 @@
+// Device cores of stage (b) best-first tree construction with the online
+// budget stop, stage (b') ancestor masks and stage (d) greedy acceptance,
+// shared by the stand-alone kernels and the fused verify step.
+//
+// BASTION, "Methodik" §2: the tree grows by repeatedly adding the valid
+// candidate of largest path score rho; §3: growth stops when the estimated
+// speedup S(N) = A_hat(T_N) L_AR / C(N) stops rising.
+//
+// One wavefront builds one sequence's tree.  The frontier is spread over the
+// 64 lanes (entry e lives in slot e/64 of lane e%64).  Children are pushed
+// lazily: inserting the node (parent p, rank j, depth d) pushes only
+//   - its next sibling (p, rank j+1), and
+//   - its first child (rank 0 at depth d+1).
+// Every other candidate c has a predecessor that precedes it in the order
+// (the previous sibling, whose score is >= c's, or the parent, whose score is
+// >= c's at smaller depth), and c is pushed when that predecessor is
+// inserted, so the frontier maximum is always the global maximum over all
+// valid candidates and at most 1 + 2 N entries are ever live.
+// The order is (log rho desc, depth asc, token asc, parent index asc); the
+// last three keys are packed into one 32-bit word compared ascending:
+//   depth << 26 | token << 8 | parent.
+#pragma once
+
+#include "td_internal.h"
+
+namespace td {
+
+constexpr uint32_t kEmptyKey = 0xffffffffu;
+
+// LDS ordering inside one wavefront: LDS operations of a wave complete in
+// issue order; this keeps the compiler from moving them and waits for them.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), other counters untouched
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ uint32_t pack_key(int depth, int token, int parent) {
+    return (static_cast<uint32_t>(depth) << 26) | (static_cast<uint32_t>(token) << 8) |
+           static_cast<uint32_t>(parent);
+}
+
+// a precedes b
+__device__ __forceinline__ bool precedes(double la, uint32_t ka, double lb, uint32_t kb) {
+    return la > lb || (la == lb && ka < kb);
+}
+
+__device__ __forceinline__ double cost_model(int n, double a, double b, double c, int knee) {
+#pragma clang fp contract(off)
+    double over = n - knee > 0 ? static_cast<double>(n - knee) : 0.0;
+    return a + b * static_cast<double>(n) + c * over;
+}
+
+struct TreeParams {
+    int block, K, n_max, use_stop;
+    double ca, cb, cc;
+    int knee;
+    double l_ar, ahat0;
+    const int32_t *root_token;  // may be null
+};
+
+struct TreeOut {
+    int32_t *n_nodes, *node_token, *node_parent, *node_depth;
+    double *node_logrho, *ahat, *speedup;  // ahat / speedup may be null
+    uint64_t *mask;                        // null: no mask rows
+};
+
+// LDS of one tree build: the top-K tables and the inserted nodes
+struct TreeLds {
+    int ids[TD_MAX_BLOCK * TD_MAX_TOPK];
+    double lq[TD_MAX_BLOCK * TD_MAX_TOPK];
+    int tok[TD_MAX_NODES + 1];
+    int par[TD_MAX_NODES + 1];
+    int dep[TD_MAX_NODES + 1];
+    double lr[TD_MAX_NODES + 1];
+};
+
+// Frontier slots per lane for a budget of n_max nodes (1 + 2 n_max entries).
+__host__ __device__ inline int tree_slots(int n_max) {
+    const int need = 1 + 2 * n_max;
+    return need <= 64 ? 1 : need <= 128 ? 2 : need <= 256 ? 4 : 8;
+}
+
+// Build sequence b's tree with one wavefront from the tables in t.ids/t.lq
+// (already in LDS, ordered by (position, rank)).  Writes every output array
+// of sequence b, and its mask rows when o.mask is set.
+template <int SLOTS>
+__device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &o, int b, int lane) {
+#pragma clang fp contract(off)
+    const int K = P.K;
+    // frontier slots of this lane
+    double f_lr[SLOTS];
+    uint32_t f_key[SLOTS];
+    int f_rank[SLOTS];
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+        f_lr[s] = -INFINITY;
+        f_key[s] = kEmptyKey;
+        f_rank[s] = 0;
+    }
+    // entry 0: the best child of the root (rank 0 of position 1)
+    if (lane == 0) {
+        f_lr[0] = t.lq[0];
+        f_key[0] = pack_key(1, t.ids[0], 0);
+        f_rank[0] = 0;
+    }
+    int count = 1;  // entries ever pushed (uniform across lanes)
+
+    int n = 0;
+    double ahat = P.ahat0;
+    double s_now = ahat * P.l_ar / cost_model(0, P.ca, P.cb, P.cc, P.knee);
+    if (lane == 0) {
+        t.tok[0] = P.root_token ? P.root_token[b] : -1;
+        t.par[0] = -1;
+        t.dep[0] = 0;
+        t.lr[0] = 0.0;
+    }
+
+    while (n < P.n_max) {
+        // lane-local best slot
+        double bl = f_lr[0];
+        uint32_t bk = f_key[0];
+#pragma unroll
+        for (int s = 1; s < SLOTS; ++s)
+            if (precedes(f_lr[s], f_key[s], bl, bk)) {
+                bl = f_lr[s];
+                bk = f_key[s];
+            }
+        // wave-wide best (register butterfly)
+        double wl = bl;
+        uint32_t wk = bk;
+#define TD_TREE_LEVEL(L)                                       \
+        {                                                      \
+            const double ol = xchg_d<L>(wl);                   \
+            const uint32_t ok = xchg<L>(wk);                   \
+            const bool take = precedes(ol, ok, wl, wk);        \
+            wl = take ? ol : wl;                               \
+            wk = take ? ok : wk;                               \
+        }
+        TD_TREE_LEVEL(0)
+        TD_TREE_LEVEL(1)
+        TD_TREE_LEVEL(2)
+        TD_TREE_LEVEL(3)
+        TD_TREE_LEVEL(4)
+        TD_TREE_LEVEL(5)
+#undef TD_TREE_LEVEL
+        if (wk == kEmptyKey) break;  // no valid candidate left
+
+        const double ahat_next = ahat + exp(wl);
+        const double s_next = ahat_next * P.l_ar / cost_model(n + 1, P.ca, P.cb, P.cc, P.knee);
+        if (P.use_stop && !(s_next > s_now)) break;
+
+        // the owner lane removes the entry and publishes its rank
+        const bool owner = (bk == wk) && (bl == wl);
+        int my_rank = 0;
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s)
+            if (owner && f_key[s] == wk) {
+                my_rank = f_rank[s];
+                f_lr[s] = -INFINITY;
+                f_key[s] = kEmptyKey;
+            }
+        const unsigned long long ob = __ballot(owner);
+        const int owner_lane = __ffsll(static_cast<long long>(ob)) - 1;
+        const int rank = __builtin_amdgcn_readlane(my_rank, owner_lane);
+
+        const int depth = static_cast<int>(wk >> 26);
+        const int token = static_cast<int>((wk >> 8) & 0x3ffffu);
+        const int parent = static_cast<int>(wk & 0xffu);
+        ++n;
+        if (lane == 0) {
+            t.tok[n] = token;
+            t.par[n] = parent;
+            t.dep[n] = depth;
+            t.lr[n] = wl;
+        }
+        wave_lds_sync();  // t.lr[parent] is read by every lane below
+        ahat = ahat_next;
+        s_now = s_next;
+
+        // lazy pushes: next sibling, then first child
+        if (rank + 1 < K) {
+            const int e = count++;
+            const int j = (depth - 1) * K + rank + 1;
+            const double plr = parent == 0 ? 0.0 : t.lr[parent];
+            if (lane == (e & (kWave - 1))) {
+#pragma unroll
+                for (int s = 0; s < SLOTS; ++s)
+                    if (s == (e >> 6)) {
+                        f_lr[s] = plr + t.lq[j];
+                        f_key[s] = pack_key(depth, t.ids[j], parent);
+                        f_rank[s] = rank + 1;
+                    }
+            }
+        }
+        if (depth < P.block) {
+            const int e = count++;
+            const int j = depth * K;
+            if (lane == (e & (kWave - 1))) {
+#pragma unroll
+                for (int s = 0; s < SLOTS; ++s)
+                    if (s == (e >> 6)) {
+                        f_lr[s] = wl + t.lq[j];
+                        f_key[s] = pack_key(depth + 1, t.ids[j], n);
+                        f_rank[s] = 0;
+                    }
+            }
+        }
+    }
+    wave_lds_sync();
+
+    const int W = P.n_max + 1;
+    const int64_t base = static_cast<int64_t>(b) * W;
+    for (int i = lane; i < W; i += kWave) {
+        const bool in = i <= n;
+        o.node_token[base + i] = in ? t.tok[i] : -1;
+        o.node_parent[base + i] = in ? t.par[i] : -1;
+        o.node_depth[base + i] = in ? t.dep[i] : -1;
+        o.node_logrho[base + i] = in ? t.lr[i] : 0.0;
+    }
+    if (o.mask) {
+        // ancestor-or-self rows from the parents in LDS (depth <= block steps)
+        const int words = (W + 63) / 64;
+        for (int i = lane; i < W; i += kWave) {
+            uint64_t w[4] = {0, 0, 0, 0};
+            if (i <= n) {
+                int u = i;
+                for (int step = 0; step <= P.block; ++step) {
+                    const uint64_t bit = 1ull << (u & 63);
+                    const int qw = u >> 6;
+                    w[0] |= qw == 0 ? bit : 0;
+                    w[1] |= qw == 1 ? bit : 0;
+                    w[2] |= qw == 2 ? bit : 0;
+                    w[3] |= qw == 3 ? bit : 0;
+                    if (u == 0) break;
+                    u = t.par[u];
+                }
+            }
+            uint64_t *row = o.mask + (base + i) * words;
+            for (int k = 0; k < words; ++k) row[k] = k == 0 ? w[0] : k == 1 ? w[1] : k == 2 ? w[2] : w[3];
+        }
+    }
+    if (lane == 0) {
+        o.n_nodes[b] = n;
+        if (o.ahat) o.ahat[b] = ahat;
+        if (o.speedup) o.speedup[b] = s_now;
+    }
+}
+
+// Greedy acceptance of sequence b with one wavefront: from the root, step to
+// the child carrying the target's greedy token while one exists.
+__device__ __forceinline__ void accept_wave(const int32_t *__restrict__ node_token,
+                                            const int32_t *__restrict__ node_parent,
+                                            const int32_t *__restrict__ n_nodes,
+                                            const int32_t *__restrict__ target_token, int n_max,
+                                            int block, int32_t *__restrict__ accept_len,
+                                            int32_t *__restrict__ accept_path,
+                                            int32_t *__restrict__ bonus_token, int b, int lane) {
+    const int W = n_max + 1;
+    const int64_t base = static_cast<int64_t>(b) * W;
+    const int n = min(n_nodes[b], n_max);
+    int32_t *path = accept_path + static_cast<int64_t>(b) * (block + 1);
+    for (int t = lane; t <= block; t += kWave) path[t] = t == 0 ? 0 : -1;
+    int u = 0;
+    int A = 0;
+    // the tree has depth <= block, so at most block steps
+    for (int step = 0; step < block; ++step) {
+        const int want = target_token[base + u];
+        int next = 0x7fffffff;
+        for (int c0 = 1; c0 <= n; c0 += kWave) {
+            const int c = c0 + lane;
+            const bool hit = c <= n && node_parent[base + c] == u && node_token[base + c] == want;
+            const unsigned long long m = __ballot(hit);
+            if (m) {
+                next = c0 + __ffsll(static_cast<long long>(m)) - 1;
+                break;
+            }
+        }
+        if (next == 0x7fffffff) break;
+        u = next;
+        ++A;
+        if (lane == 0) path[A] = u;
+    }
+    if (lane == 0) {
+        accept_len[b] = A;
+        bonus_token[b] = target_token[base + u];
+    }
+}
+
+}  // namespace td

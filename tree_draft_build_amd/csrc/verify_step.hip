@@ -1,0 +1,81 @@
+// td_verify_step: the verify step of budget-aware tree speculative decoding
+// (BASTION, "Methodik" §1-§3) as three kernels.  Kernel boundaries cost a few
+// microseconds each on this GPU, which at batch 1 is as much as the stages'
+// own memory time, so the step fuses what the five stage calls keep apart:
+//   1. top-K of every position; the last position of each sequence to finish
+//      builds the sequence's tree and mask rows in the same kernel;
+//   2. split-KV context attention;
+//   3. partial merge with the ancestor-masked tree keys, plus the acceptance
+//      walk of every sequence.
+// The device code is the stage calls' own.
+
+#include <algorithm>
+
+#include "step_launch.h"
+#include "td_internal.h"
+#include "tree_core.h"
+
+using namespace td;
+
+namespace {
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t topk_part(const td_step_args *a) {
+    return round_up(topk_workspace_bytes(a->batch, a->block, a->vocab, a->topk), 256);
+}
+
+}  // namespace
+
+extern "C" size_t td_step_args_bytes(void) { return sizeof(td_step_args); }
+
+extern "C" size_t td_verify_step_workspace(const td_step_args *a) {
+    if (!a || a->batch <= 0 || a->block <= 0 || a->vocab <= 0 || a->topk <= 0 || a->n_max < 0 ||
+        a->hq <= 0 || a->hkv <= 0 || a->hq % a->hkv || a->total_ctx < 0)
+        return 0;
+    const int nq_max = a->n_max + 1;
+    const size_t attn = std::max(
+        attn_workspace_bytes(a->batch, nq_max, a->hq, a->hkv, a->head_dim, a->total_ctx, TD_BF16),
+        attn_workspace_bytes(a->batch, nq_max, a->hq, a->hkv, a->head_dim, a->total_ctx, TD_F32));
+    return topk_part(a) + attn;
+}
+
+extern "C" td_status td_verify_step(const td_step_args *a, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+    clear_error();
+    if (!a) return fail(TD_EINVAL, "td_verify_step: null args");
+    td_status st = check_topk_args(a->logits, a->logits_dtype, a->batch, a->block, a->vocab,
+                                   a->pos_stride, a->topk, a->topk_id, a->topk_logq, a->lse);
+    if (st != TD_OK) return st;
+    st = check_tree_args(a->topk_id, a->topk_logq, a->batch, a->block, a->topk, a->n_max,
+                         a->n_nodes, a->node_token, a->node_parent, a->node_depth, a->node_logrho);
+    if (st != TD_OK) return st;
+    const int nq_max = a->n_max + 1;
+    st = check_attn_args(a->q, a->k_ctx, a->v_ctx, a->ctx_offsets, a->total_ctx, a->max_ctx,
+                         a->k_tree, a->v_tree, a->mask, a->n_nodes, a->batch, nq_max, a->hq,
+                         a->hkv, a->head_dim, a->attn_dtype, a->out);
+    if (st != TD_OK) return st;
+    st = check_accept_args(a->node_token, a->node_parent, a->n_nodes, a->target_token, a->batch,
+                           a->n_max, a->block, a->accept_len, a->accept_path, a->bonus_token);
+    if (st != TD_OK) return st;
+    if (!a->mask || !aligned8(a->mask)) return fail(TD_EINVAL, "td_verify_step: mask must be set");
+    if (!workspace || !aligned16(workspace))
+        return fail(TD_EINVAL, "td_verify_step: null or misaligned workspace");
+    if (workspace_bytes < td_verify_step_workspace(a))
+        return fail(TD_EINVAL, "td_verify_step: workspace too small");
+
+    hipStream_t s = as_stream(stream);
+    char *ws = static_cast<char *>(workspace);
+    const TreeParams tp{a->block, a->topk, a->n_max, a->use_stop, a->cost_a, a->cost_b, a->cost_c,
+                        a->cost_knee, a->l_ar, a->ahat0, a->root_token};
+    const TreeOut to{a->n_nodes, a->node_token, a->node_parent, a->node_depth, a->node_logrho,
+                     a->ahat, a->speedup, a->mask};
+    launch_topk_tree(a->logits, a->logits_dtype, a->batch, a->block, a->vocab, a->pos_stride,
+                     a->topk, ws, a->topk_id, a->topk_logq, a->lse, tp, to, s);
+    const AcceptArgs acc{a->node_token, a->node_parent, a->target_token, a->n_max, a->block,
+                         a->accept_len, a->accept_path, a->bonus_token};
+    launch_attention(a->q, a->k_ctx, a->v_ctx, a->ctx_offsets, a->total_ctx, a->k_tree, a->v_tree,
+                     a->mask, a->n_nodes, a->batch, nq_max, a->hq, a->hkv, a->head_dim, a->scale,
+                     a->attn_dtype, ws + topk_part(a), a->out, &acc, s);
+    return check_launch("td_verify_step");
+}

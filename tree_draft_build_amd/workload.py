@@ -112,6 +112,10 @@ CONFIGS: dict[str, Config] = {
         ctx_cap=32768, target_seed=103),
 }
 
+# 64 independent sequences of the Qwen3-8B shape in one step: the streaming
+# rate of the same per-sequence work (one cold batch-1 step is latency-bound).
+CONFIGS["qwen3_8b_x64"] = CONFIGS["qwen3_8b"].replace(name="qwen3_8b_x64", index=5, batch=64)
+
 # Variants used only as parity cases.
 CONFIGS["tiny_fixed"] = CONFIGS["tiny"].replace(name="tiny_fixed", use_stop=False)
 # Peaked marginals: S-stop trees reach the budget cap and the full block depth.

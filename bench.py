@@ -41,7 +41,10 @@ def parse():
     ap.add_argument("--graph-steps", type=int, default=8, help="steps captured per HIP graph")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--stage-detail", action="store_true", help="print per-stage timings to stderr")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run plain copies of MIB MiB (profiler byte-counter reference)")
+    ap.add_argument("--no-streaming", dest="streaming", action="store_false",
+                    help="skip the 64-sequence streaming measurement")
     return ap.parse_args()
 
 
@@ -54,12 +57,37 @@ def main():
         sys.exit(2)
     import torch
 
+    from tree_draft_build_amd import workload as wl
+
+    torch.cuda.set_device(torch.device("cuda:0"))
+    if args.calibrate_copy:
+        copy_calibration(args.calibrate_copy)
+        return
+    cfg = wl.CONFIGS[args.config]
+    result, x, inp = measure(cfg, args, args.steps, args.warmup)
+    if args.streaming and cfg.name == "qwen3_8b":
+        # the same per-sequence work, 64 independent sequences per step
+        scfg = wl.CONFIGS["qwen3_8b_x64"]
+        sres, _, _ = measure(scfg, args, max(10, args.steps // 4), max(2, args.warmup // 4))
+        result["streaming"] = {
+            "workload": scfg.name, "batch": scfg.batch,
+            "value": sres["value"], "unit": "verify steps/s",
+            "sequence_steps_per_s": round(sres["value"] * scfg.batch, 1),
+            "ms_per_step": sres["ms_per_step"], "steps": sres["steps"],
+            "kernels_us": sres["kernels_us"], "roofline": sres["roofline"],
+            "stage_roofline": sres["stage_roofline"]}
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(cfg, x, inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def measure(cfg, args, steps, warmup):
+    import torch
+
     from tree_draft_build_amd import binding as td
     from tree_draft_build_amd import workload as wl
 
-    cfg = wl.CONFIGS[args.config]
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
 
     # ---------------- inputs (host generation, one upload, device copies) ----
     x = wl.make_logits(cfg)
@@ -80,13 +108,15 @@ def main():
     max_ctx = int(inp["ctx_len"].max())
     set_bytes = sum(t.numel() * t.element_size() for t in base.values())
     n_sets = max(1, int(math.ceil(args.rotate_mb * 1e6 / set_bytes)))
+    if n_sets == 1 and set_bytes < 4 * 256e6:
+        n_sets = 2
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_sets - 1)]
 
     b, B, K, V = cfg.batch, cfg.block, cfg.topk, cfg.vocab
     cost = (cfg.cost_a, cfg.cost_b, cfg.cost_c, cfg.cost_knee)
     scale = wl.attn_scale(cfg)
 
-    # ---------------- outputs and workspaces (allocated once) ----------------
+    # ---------------- stage calls: outputs and workspaces (allocated once) ----
     topk_out = (torch.empty((b, B, K), dtype=torch.int32, device=dev),
                 torch.empty((b, B, K), dtype=torch.float64, device=dev),
                 torch.empty((b, B), dtype=torch.float64, device=dev))
@@ -151,69 +181,80 @@ def main():
         args_per_set.append(td.StepArgs.from_buffer_copy(vs.args))
     use_graph = not args.no_graph
 
-    def fused(i):
+    def fused(i, stages=0):
         vs.args = args_per_set[i % n_sets]
-        vs.run()
+        vs.run(stages=stages)
 
     # HIP graphs of G consecutive steps (cycling the input sets) so that the
     # host's launch cost is paid once per G steps; single-step graphs cover
-    # the remainder, so the timed region runs exactly --steps steps
+    # the remainder, so a timed region runs exactly the steps it names
     G = max(1, min(args.graph_steps, n_sets))
-    multi, single = [], []
-    if use_graph:
-        for i in range(0, n_sets, G):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for j in range(G):
-                    fused(i + j)
-            multi.append(g)
-        for i in range(n_sets):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                fused(i)
-            single.append(g)
+
+    def make_runner(stages):
+        multi, single = [], []
+        if use_graph:
+            for i in range(0, n_sets - G + 1, G):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for j in range(G):
+                        fused(i + j, stages)
+                multi.append(g)
+            for i in range(n_sets):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    fused(i, stages)
+                single.append(g)
+            torch.cuda.synchronize()
+
+        def run_steps(first, count):
+            """Steps first .. first+count-1 (input set = step index mod n_sets)."""
+            i = first
+            end = first + count
+            while i < end:
+                k = i % n_sets
+                if use_graph and k % G == 0 and k // G < len(multi) and i + G <= end:
+                    multi[k // G].replay()
+                    i += G
+                elif use_graph:
+                    single[k].replay()
+                    i += 1
+                else:
+                    fused(i, stages)
+                    i += 1
+        return run_steps
+
+    def timed(run_steps, count):
+        run_steps(0, warmup)
         torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        run_steps(warmup, count)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / count
 
-    def run_steps(first, count):
-        """Run steps first .. first+count-1 (input set = step index mod n_sets)."""
-        i = first
-        end = first + count
-        while i < end:
-            if use_graph and i % G == 0 and i + G <= end and (i % n_sets) + G <= n_sets:
-                multi[(i % n_sets) // G].replay()
-                i += G
-            elif use_graph:
-                single[i % n_sets].replay()
-                i += 1
-            else:
-                fused(i)
-                i += 1
-
-    # ---------------- timed region ----------------
-    run_steps(0, args.warmup)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    run_steps(args.warmup, args.steps)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_total = t0.elapsed_time(t1)
-    ms_per_step = ms_total / args.steps
+    # ---------------- timed region: whole steps ----------------
+    ms_per_step = timed(make_runner(0), steps)
     # the step's results equal the stage calls' (checked by the test-suite);
     # keep one cheap guard here that the timed path ran
     assert int(vs.tree["n_nodes"][0]) == int(tnp["n_nodes"][0])
 
-    # ---------------- per-stage launch times (HIP events, eager) -------------
-    # Each stage call is bracketed by events on the stream it launches on;
-    # averaged over the same number of steps, rotating the same input sets.
+    # ---------------- the step's kernels, timed apart ----------------
+    # Kernel 1 (top-K + tree + mask) alone, and kernels 2-3 (attention +
+    # acceptance) alone, each over the same number of launches with HIP events
+    # on the launch stream; the average launch time is the loop time / count.
+    k1_ms = timed(make_runner(td.TD_STEP_DRAFT), steps)
+    k23_ms = timed(make_runner(td.TD_STEP_VERIFY), steps)
+
+    # ---------------- per-stage calls (HIP events, eager) ----------------
     names = ["draft_topk", "build_tree+tree_mask", "tree_verify_attn", "accept"]
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in names] for _ in range(args.steps)]
-    for i in range(args.warmup):
+           for _ in names] for _ in range(steps)]
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    for i in range(args.steps):
+    for i in range(steps):
         s = sets[i % n_sets]
         e = ev[i]
         e[0][0].record(stream); stage_a(s); e[0][1].record(stream)
@@ -221,37 +262,48 @@ def main():
         e[2][0].record(stream); stage_c(s); e[2][1].record(stream)
         e[3][0].record(stream); stage_d(); e[3][1].record(stream)
     torch.cuda.synchronize()
-    stage_ms = [float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)]))
+    stage_ms = [float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)]))
                 for j in range(len(names))]
 
     # ---------------- algorithmic work ----------------
     nn = tnp["n_nodes"].astype(np.int64)
     rows = nn + 1
+    W = (nq + 63) // 64
     L = inp["ctx_len"].astype(np.int64)
     esz = 2 if cfg.attn_dtype == "bf16" else 4
     lsz = 2 if cfg.logit_dtype == "bf16" else 4
+    # (a): logits read once; top-K ids (4 B) + log q (8 B) and lse (8 B) written
     bytes_a = b * B * V * lsz + b * B * K * 12 + b * B * 8
+    # (b)+(b'): node arrays (token, parent, depth 4 B; log rho 8 B) + mask rows
+    bytes_b = b * nq * (20 + 8 * W)
+    # (c): K/V of context and tree read once, q read and out written once
     bytes_c = int((2 * cfg.hkv * cfg.head_dim * esz * (L + rows)).sum()
                   + 2 * (rows.sum()) * cfg.hq * cfg.head_dim * esz)
     depth = tnp["node_depth"]
     anc = int(sum((depth[i, :rows[i]] + 1).sum() for i in range(b)))
     flops_c = int(4 * cfg.hq * cfg.head_dim * (rows * L).sum() + 4 * cfg.hq * cfg.head_dim * anc)
-    stage_bytes = {"draft_topk": bytes_a, "tree_verify_attn": bytes_c}
-    j_dom = int(np.argmax([stage_ms[0], -1, stage_ms[2], -1]))
-    dom = names[j_dom]
-    dom_ms = stage_ms[j_dom]
-    intensity = flops_c / bytes_c
-    if dom == "tree_verify_attn" and intensity > MFMA_BF16_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        achieved = flops_c / (dom_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_TFLOPS,
-                    unit="TFLOP/s", frac=round(achieved / MFMA_BF16_TFLOPS, 4), traffic=None)
-    else:
-        achieved = stage_bytes[dom] / (dom_ms * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
-    roof["kernel"] = dom
-    roof["bytes_per_launch"] = stage_bytes[dom]
-    roof["avg_launch_us"] = round(dom_ms * 1e3, 2)
+    ridge = MFMA_BF16_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+
+    def roofline(kernel, ms, nbytes, nflops):
+        if nflops / nbytes > ridge:
+            ach = nflops / (ms * 1e-3) / 1e12
+            r = dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_TFLOPS,
+                     unit="TFLOP/s", frac=round(ach / MFMA_BF16_TFLOPS, 4), traffic=None)
+        else:
+            ach = nbytes / (ms * 1e-3) / 1e9
+            r = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                     frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
+        r.update(kernel=kernel, bytes_per_launch=int(nbytes), flops_per_launch=int(nflops),
+                 avg_launch_us=round(ms * 1e3, 2))
+        return r
+
+    k1 = roofline("topk_tree (kernel 1: top-K + tree + mask)", k1_ms, bytes_a + bytes_b, 0)
+    k23 = roofline("attention + acceptance (kernels 2-3)", k23_ms, bytes_c, flops_c)
+    measured = hbm_traffic(cfg.name)
+    if measured:
+        k1["traffic"] = measured.get("topk_tree")
+        k23["traffic"] = measured.get("attention+accept")
+    roof = k1 if k1_ms >= k23_ms else k23
 
     result = {
         "metric": "verify steps/s (logits->tree->tree-attn->accept) + % HBM/MFMA peak, "
@@ -259,8 +311,8 @@ def main():
         "value": round(1e3 / ms_per_step, 1),
         "unit": "verify steps/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -274,6 +326,8 @@ def main():
                    "step": "td_verify_step (3 kernels)", "graph": use_graph, "graph_steps": G,
                    "input_sets": n_sets, "parallelism": "single GPU"},
         "roofline": roof,
+        "kernels_us": {"topk_tree": round(k1_ms * 1e3, 2), "attention+accept": round(k23_ms * 1e3, 2)},
+        "kernel_roofline": {"topk_tree": k1, "attention+accept": k23},
         "stages_us": {n: round(t * 1e3, 2) for n, t in zip(names, stage_ms)},
         "stage_roofline": {
             "draft_topk": {"bytes": bytes_a, "GB/s": round(bytes_a / (stage_ms[0] * 1e-3) / 1e9, 1)},
@@ -281,9 +335,50 @@ def main():
                                  "GB/s": round(bytes_c / (stage_ms[2] * 1e-3) / 1e9, 1),
                                  "TFLOP/s": round(flops_c / (stage_ms[2] * 1e-3) / 1e12, 3)}},
     }
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(cfg, x, inp, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    return result, x, inp
+
+
+def source_digest():
+    """Digest of the library's sources: profiler counts are only reported for
+    the kernels they were taken on."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "tree_draft_build_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "treedraft.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def hbm_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary of this workload (scaled by the plain-copy
+    calibration), or None when it is missing or was taken on other sources."""
+    path = os.path.join(ROOT, "profiles", f"verify_step_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("traffic_bytes")
+
+
+def copy_calibration(mib):
+    """Plain device-to-device copies of a known size, as the reference point
+    for the HBM byte counters of a profiler run: each copy reads and writes
+    exactly mib MiB."""
+    import torch
+    n = int(mib) << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": int(mib), "copies": 5}), flush=True)
 
 
 def cpu_baseline(cfg, x, inp, budget_s):

@@ -204,7 +204,16 @@ td_status td_accept(const int32_t *node_token, const int32_t *node_parent, const
  * Workspace: td_verify_step_workspace(args) bytes, 16-byte aligned,
  * ZERO-FILLED before its first use; every call leaves it ready for the next.
  * Calls that overlap in time must not share a workspace.
+ * stages selects the kernels a call enqueues: TD_STEP_DRAFT (kernel 1: top-K,
+ * tree, mask), TD_STEP_VERIFY (kernels 2 and 3: attention and acceptance),
+ * or 0 for both.  A serving loop builds the tree with TD_STEP_DRAFT, runs the
+ * target model over the tree's tokens to obtain q, k_tree, v_tree and the
+ * target tokens, then calls TD_STEP_VERIFY with the same argument block and
+ * workspace; a TD_STEP_VERIFY call reads the tree arrays and mask rows that
+ * the earlier TD_STEP_DRAFT call wrote.  Only the fields of the selected
+ * stages are checked.
  */
+enum { TD_STEP_DRAFT = 1, TD_STEP_VERIFY = 2 };
 typedef struct {
     /* stage (a) */
     const void *logits;
@@ -236,6 +245,7 @@ typedef struct {
     uint64_t *mask;
     void *out;
     int32_t *accept_len, *accept_path, *bonus_token;
+    int32_t stages; /* TD_STEP_DRAFT | TD_STEP_VERIFY; 0 means both */
 } td_step_args;
 
 /* sizeof(td_step_args), for bindings that lay the struct out themselves */

@@ -125,3 +125,15 @@ def test_step_args_layout_and_validation(b):
     a.hkv = 8
     assert b.lib.td_verify_step(ctypes.byref(a), FAKE, 16, None) == 1
     assert "workspace" in b.last_error()
+    a.stages = 4
+    assert b.lib.td_verify_step(ctypes.byref(a), FAKE, 1 << 30, None) == 1
+    assert "stages" in b.last_error()
+    # a verify-only call checks only the attention and acceptance fields
+    a.stages = b.TD_STEP_VERIFY
+    a.topk = 33
+    a.hkv = 7
+    assert b.lib.td_verify_step(ctypes.byref(a), FAKE, 1 << 30, None) == 1
+    assert "hkv" in b.last_error() or "hq" in b.last_error()
+    a.hkv = 8
+    a.stages = b.TD_STEP_DRAFT
+    assert b.lib.td_verify_step(ctypes.byref(a), FAKE, 1 << 30, None) == 2

@@ -148,3 +148,31 @@ def test_step_against_oracle(td):
     np.testing.assert_array_equal(out["accept_len"].numpy(), a_o)
     np.testing.assert_array_equal(out["accept_path"].numpy(), p_o)
     np.testing.assert_array_equal(out["bonus_token"].numpy(), b_o)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_8b_stress", "batched"])
+def test_step_in_two_calls(td, name):
+    """A draft-only call followed by a verify-only call on the same argument
+    block and workspace gives the one-call step's results."""
+    cfg = wl.CONFIGS[name]
+    print("[case] step in two calls", name, flush=True)
+    x, inp, d = inputs(cfg)
+    ref = modular(td, cfg, d, None)
+    tree_np = {k: ref[k].numpy() for k in ("node_token", "node_parent", "n_nodes")}
+    tg = dev(targets_by_path(cfg, wl.logits_as_f64(x, cfg.logit_dtype), tree_np))
+    ref = modular(td, cfg, d, tg)
+    s = make_step(td, cfg, d)
+    s.set_inputs(d["logits"], d["q"], d["k_ctx"], d["v_ctx"], d["off"], d["k_tree"], d["v_tree"], tg)
+    for rep in range(2):
+        s.out.fill_(0)
+        s.accept_len.fill_(-7)
+        s.run(stages=td.TD_STEP_DRAFT)
+        torch.cuda.synchronize()
+        got = step_outputs(s)
+        for k in ("topk_id", "topk_logq", "lse", "mask", "n_nodes", "node_token", "node_parent",
+                  "node_depth", "node_logrho"):
+            assert torch.equal(ref[k], got[k]), f"{name} draft call {rep}: {k} differs"
+        assert int(got["accept_len"][0]) == -7      # verify kernels did not run
+        s.run(stages=td.TD_STEP_VERIFY)
+        torch.cuda.synchronize()
+        assert_same(ref, step_outputs(s), f"{name} two calls {rep}")

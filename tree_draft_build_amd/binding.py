@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libtreedraft.so")
 
 TD_OK, TD_EINVAL, TD_ECAPACITY, TD_EUNSUPPORTED, TD_EHIP = range(5)
 TD_F32, TD_BF16 = 0, 1
+TD_STEP_DRAFT, TD_STEP_VERIFY = 1, 2
 STATUS_NAMES = {0: "TD_OK", 1: "TD_EINVAL", 2: "TD_ECAPACITY", 3: "TD_EUNSUPPORTED", 4: "TD_EHIP"}
 
 # every symbol declared in include/treedraft.h
@@ -46,6 +47,7 @@ class StepArgs(ctypes.Structure):
         ("node_depth", c_void_p), ("node_logrho", c_void_p), ("ahat", c_void_p),
         ("speedup", c_void_p), ("mask", c_void_p), ("out", c_void_p),
         ("accept_len", c_void_p), ("accept_path", c_void_p), ("bonus_token", c_void_p),
+        ("stages", c_int32),
     ]
 
 
@@ -309,6 +311,8 @@ class VerifyStep:
         a.root_token = None if root_token is None else root_token.data_ptr()
         self._keep = (logits, q, k_ctx, v_ctx, ctx_offsets, k_tree, v_tree, target_token, root_token)
 
-    def run(self, stream=None):
+    def run(self, stream=None, stages=0):
+        """Enqueue the step (stages: TD_STEP_DRAFT | TD_STEP_VERIFY, 0 = both)."""
+        self.args.stages = stages
         _check(lib.td_verify_step(ctypes.byref(self.args), _ptr(self.workspace),
                                   self.workspace.numel(), _stream(stream)))

@@ -44,20 +44,34 @@ extern "C" td_status td_verify_step(const td_step_args *a, void *workspace, size
                                     void *stream) {
     clear_error();
     if (!a) return fail(TD_EINVAL, "td_verify_step: null args");
-    td_status st = check_topk_args(a->logits, a->logits_dtype, a->batch, a->block, a->vocab,
-                                   a->pos_stride, a->topk, a->topk_id, a->topk_logq, a->lse);
-    if (st != TD_OK) return st;
-    st = check_tree_args(a->topk_id, a->topk_logq, a->batch, a->block, a->topk, a->n_max,
-                         a->n_nodes, a->node_token, a->node_parent, a->node_depth, a->node_logrho);
-    if (st != TD_OK) return st;
+    const int stages = a->stages == 0 ? (TD_STEP_DRAFT | TD_STEP_VERIFY) : a->stages;
+    if (stages & ~(TD_STEP_DRAFT | TD_STEP_VERIFY))
+        return fail(TD_EINVAL, "td_verify_step: stages must be a mask of TD_STEP_DRAFT, TD_STEP_VERIFY");
+    const bool draft = stages & TD_STEP_DRAFT;
+    const bool verify = stages & TD_STEP_VERIFY;
+    td_status st = TD_OK;
+    if (draft) {
+        st = check_topk_args(a->logits, a->logits_dtype, a->batch, a->block, a->vocab,
+                             a->pos_stride, a->topk, a->topk_id, a->topk_logq, a->lse);
+        if (st != TD_OK) return st;
+        st = check_tree_args(a->topk_id, a->topk_logq, a->batch, a->block, a->topk, a->n_max,
+                             a->n_nodes, a->node_token, a->node_parent, a->node_depth,
+                             a->node_logrho);
+        if (st != TD_OK) return st;
+    }
     const int nq_max = a->n_max + 1;
-    st = check_attn_args(a->q, a->k_ctx, a->v_ctx, a->ctx_offsets, a->total_ctx, a->max_ctx,
-                         a->k_tree, a->v_tree, a->mask, a->n_nodes, a->batch, nq_max, a->hq,
-                         a->hkv, a->head_dim, a->attn_dtype, a->out);
-    if (st != TD_OK) return st;
-    st = check_accept_args(a->node_token, a->node_parent, a->n_nodes, a->target_token, a->batch,
-                           a->n_max, a->block, a->accept_len, a->accept_path, a->bonus_token);
-    if (st != TD_OK) return st;
+    if (verify) {
+        if (a->n_max < 0 || a->n_max > TD_MAX_NODES)
+            return fail(TD_ECAPACITY, "td_verify_step: n_max out of range");
+        st = check_attn_args(a->q, a->k_ctx, a->v_ctx, a->ctx_offsets, a->total_ctx, a->max_ctx,
+                             a->k_tree, a->v_tree, a->mask, a->n_nodes, a->batch, nq_max, a->hq,
+                             a->hkv, a->head_dim, a->attn_dtype, a->out);
+        if (st != TD_OK) return st;
+        st = check_accept_args(a->node_token, a->node_parent, a->n_nodes, a->target_token,
+                               a->batch, a->n_max, a->block, a->accept_len, a->accept_path,
+                               a->bonus_token);
+        if (st != TD_OK) return st;
+    }
     if (!a->mask || !aligned8(a->mask)) return fail(TD_EINVAL, "td_verify_step: mask must be set");
     if (!workspace || !aligned16(workspace))
         return fail(TD_EINVAL, "td_verify_step: null or misaligned workspace");
@@ -66,16 +80,20 @@ extern "C" td_status td_verify_step(const td_step_args *a, void *workspace, size
 
     hipStream_t s = as_stream(stream);
     char *ws = static_cast<char *>(workspace);
-    const TreeParams tp{a->block, a->topk, a->n_max, a->use_stop, a->cost_a, a->cost_b, a->cost_c,
-                        a->cost_knee, a->l_ar, a->ahat0, a->root_token};
-    const TreeOut to{a->n_nodes, a->node_token, a->node_parent, a->node_depth, a->node_logrho,
-                     a->ahat, a->speedup, a->mask};
-    launch_topk_tree(a->logits, a->logits_dtype, a->batch, a->block, a->vocab, a->pos_stride,
-                     a->topk, ws, a->topk_id, a->topk_logq, a->lse, tp, to, s);
-    const AcceptArgs acc{a->node_token, a->node_parent, a->target_token, a->n_max, a->block,
-                         a->accept_len, a->accept_path, a->bonus_token};
-    launch_attention(a->q, a->k_ctx, a->v_ctx, a->ctx_offsets, a->total_ctx, a->k_tree, a->v_tree,
-                     a->mask, a->n_nodes, a->batch, nq_max, a->hq, a->hkv, a->head_dim, a->scale,
-                     a->attn_dtype, ws + topk_part(a), a->out, &acc, s);
+    if (draft) {
+        const TreeParams tp{a->block, a->topk, a->n_max, a->use_stop, a->cost_a, a->cost_b,
+                            a->cost_c, a->cost_knee, a->l_ar, a->ahat0, a->root_token};
+        const TreeOut to{a->n_nodes, a->node_token, a->node_parent, a->node_depth,
+                         a->node_logrho, a->ahat, a->speedup, a->mask};
+        launch_topk_tree(a->logits, a->logits_dtype, a->batch, a->block, a->vocab, a->pos_stride,
+                         a->topk, ws, a->topk_id, a->topk_logq, a->lse, tp, to, s);
+    }
+    if (verify) {
+        const AcceptArgs acc{a->node_token, a->node_parent, a->target_token, a->n_max, a->block,
+                             a->accept_len, a->accept_path, a->bonus_token};
+        launch_attention(a->q, a->k_ctx, a->v_ctx, a->ctx_offsets, a->total_ctx, a->k_tree,
+                         a->v_tree, a->mask, a->n_nodes, a->batch, nq_max, a->hq, a->hkv,
+                         a->head_dim, a->scale, a->attn_dtype, ws + topk_part(a), a->out, &acc, s);
+    }
     return check_launch("td_verify_step");
 }

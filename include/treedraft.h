@@ -81,8 +81,9 @@ const char *td_last_error(void);
  *   1 <= K <= min(TD_MAX_TOPK, vocab); 1 <= block <= TD_MAX_BLOCK.
  * Workspace: at least td_draft_topk_workspace(batch, block, vocab, K) bytes
  *   of device memory, 16-byte aligned.  It must be ZERO-FILLED before its
- *   first use (it holds per-row arrival counters); every call leaves those
- *   counters zero again, so a workspace is zeroed once and then reused.
+ *   first use and again whenever batch, block, vocab or K change (it holds
+ *   the workgroups' call epochs, which tag the partial results they hand
+ *   over); every call leaves it ready for the next call of the same shape.
  *   Calls that overlap in time must not share a workspace.
  */
 size_t td_draft_topk_workspace(int32_t batch, int32_t block, int32_t vocab, int32_t K);
@@ -157,10 +158,9 @@ td_status td_tree_mask(const int32_t *node_parent, const int32_t *n_nodes, int32
  *   mask     as written by td_tree_mask; n_nodes [batch].
  *   dtype TD_BF16 or TD_F32 (all of q/k/v/out); head_dim 64 or 128.
  *   Accumulation is float32; out has the input dtype.
- * Workspace: td_tree_verify_attn_workspace(...) bytes, 16-byte aligned.  It
- *   must be ZERO-FILLED before its first use (it holds arrival counters);
- *   every call leaves the counters zero again.  Calls that overlap in time
- *   must not share a workspace.
+ * Workspace: td_tree_verify_attn_workspace(...) bytes, 16-byte aligned
+ *   (per-chunk partial results; no state is kept between calls).  Calls
+ *   that overlap in time must not share a workspace.
  */
 size_t td_tree_verify_attn_workspace(int32_t batch, int32_t nq_max, int32_t hq, int32_t hkv,
                                      int32_t head_dim, int64_t total_ctx, int64_t max_ctx);
@@ -202,8 +202,10 @@ td_status td_accept(const int32_t *node_token, const int32_t *node_parent, const
  * nq_max = n_max + 1.  target_token [batch][n_max+1] is an input: the
  * target's greedy token at every node of the tree this step builds.
  * Workspace: td_verify_step_workspace(args) bytes, 16-byte aligned,
- * ZERO-FILLED before its first use; every call leaves it ready for the next.
- * Calls that overlap in time must not share a workspace.
+ * ZERO-FILLED before its first use and again whenever the shape fields
+ * (batch, block, vocab, topk, n_max, hq, hkv, head_dim, total_ctx) change;
+ * every call leaves it ready for the next call of the same shape.  Calls
+ * that overlap in time must not share a workspace.
  * stages selects the kernels a call enqueues: TD_STEP_DRAFT (kernel 1: top-K,
  * tree, mask), TD_STEP_VERIFY (kernels 2 and 3: attention and acceptance),
  * or 0 for both.  A serving loop builds the tree with TD_STEP_DRAFT, runs the

@@ -44,6 +44,9 @@ constexpr int kTopkThreads = 256;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kBatch = 4;  // 16-byte vectors per thread in flight
 constexpr int kCandCap = 512;  // candidates ranked in LDS by counting
+// Words of a row's partials held by the merger: splits * (2K + 3) with
+// splits <= min(64, 1024 / K) is at most 2240 for every K <= 32.
+constexpr int kMergeWords = 2304;
 constexpr int kWaveCap = kCandCap / kTopkWaves;  // per wave
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -137,48 +140,86 @@ __device__ __forceinline__ void wave_select(KeyList<KW> &l, int K, uint64_t (&wi
     }
 }
 
-// Workspace layout: for R rows, P = rows * splits partials and B sequences
-//   uint32 count[R + B] | double s[P] | float m[P] | uint64 key[P][K]
-// (each 16-byte aligned; the B sequence counters serve the fused step).
-// count[] must be zero before the first call and is zero again after every
-// call.
+// Workspace layout for R rows of `splits` partials each (zero-filled once,
+// and again whenever the problem's shape changes):
+//   uint64 part[R][splits][2K + 4]  per workgroup: its epoch (word 0), then
+//          the tagged words of its partial: key j low/high halves (1 + 2j,
+//          2 + 2j), log2 max (2K + 1), float64 sum (2K + 2, 2K + 3)
+//   uint64 rowrec[R][3K]            tagged row results for the fused tree
+//          build: id j (j), log q j low/high halves (K + 2j, K + 2j + 1)
+// Each workgroup reads only its own epoch word and advances it when done,
+// so every epoch of a workspace counts the calls made with it.  A tagged
+// word carries 32 data bits under a 32-bit tag (the epoch plus one) and is
+// written and read as one 8-byte atomic, so a reader takes a word only once
+// the word of this call has landed.
 struct TopkWs {
-    unsigned int *count;
-    double *s;
-    float *m;
-    uint64_t *key;
+    uint64_t *part;
+    uint64_t *rowrec;
 };
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+__host__ __device__ inline int part_words(int K) { return 2 * K + 3; }  // data words
 
 inline size_t topk_ws_bytes(int64_t rows, int64_t parts, int K) {
-    return align16(rows * 4 + rows * 4) + align16(parts * 8) + align16(parts * 4) +
-           align16(parts * K * 8);
+    return align16(parts * (part_words(K) + 1) * 8) + align16(rows * 3 * K * 8);
 }
 
 __host__ __device__ inline TopkWs topk_ws(void *base, int64_t rows, int64_t parts, int K) {
     char *p = static_cast<char *>(base);
     TopkWs w;
-    w.count = reinterpret_cast<unsigned int *>(p);
-    p += align16(rows * 4 + rows * 4);  // row counters, then (up to rows) sequence counters
-    w.s = reinterpret_cast<double *>(p);
-    p += align16(parts * 8);
-    w.m = reinterpret_cast<float *>(p);
-    p += align16(parts * 4);
-    w.key = reinterpret_cast<uint64_t *>(p);
-    (void)K;
+    w.part = reinterpret_cast<uint64_t *>(p);
+    p += align16(parts * (part_words(K) + 1) * 8);
+    w.rowrec = reinterpret_cast<uint64_t *>(p);
+    (void)rows;
     return w;
 }
 
-// Cross-workgroup hand-off through the workspace: agent-scope relaxed
-// atomic stores and loads (coherent without L2 write-back/invalidate).
+// Agent-scope relaxed atomics: coherent across the chip's L2 caches by
+// themselves (no cache write-back or invalidate).
+template <typename V>
+__device__ __forceinline__ V fetch(const V *p) {
+    return __hip_atomic_load(const_cast<V *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 template <typename V>
 __device__ __forceinline__ void publish(V *p, V x) {
     __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-template <typename V>
-__device__ __forceinline__ V fetch(const V *p) {
-    return __hip_atomic_load(const_cast<V *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void put_word(uint64_t *p, uint32_t data, uint32_t tag) {
+    publish(p, (static_cast<uint64_t>(tag) << 32) | data);
+}
+
+// Polls of words whose writers have not landed them yet, per get_words call.
+// Every awaited word comes from a workgroup of lower index in the same
+// launch, which the dispatcher has started before the waiting one, so the
+// wait is a few microseconds; the bound only guards against a broken
+// protocol (the outputs then carry NaN or -1).
+constexpr int kSpinLimit = 1 << 16;
+
+// Reads n <= NW tagged words p[idx[u]] (all loads in flight at once) into
+// out[u]; returns false if some word never carried the tag.
+template <int NW>
+__device__ __forceinline__ bool get_words(const uint64_t *p, const int (&idx)[NW], int n,
+                                          uint32_t tag, uint32_t (&out)[NW]) {
+    uint64_t v[NW];
+#pragma unroll
+    for (int u = 0; u < NW; ++u)
+        if (u < n) v[u] = fetch(p + idx[u]);
+    bool ok = true;
+    int spins = 0;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) {
+        out[u] = 0;
+        if (u < n) {
+            while (static_cast<uint32_t>(v[u] >> 32) != tag && spins < kSpinLimit) {
+                __builtin_amdgcn_s_sleep(1);
+                v[u] = fetch(p + idx[u]);
+                ++spins;
+            }
+            ok = ok && static_cast<uint32_t>(v[u] >> 32) == tag;
+            out[u] = static_cast<uint32_t>(v[u]);
+        }
+    }
+    return ok;
 }
 
 // Elements per 16-byte vector.
@@ -204,30 +245,44 @@ template <> struct Vec<float> {
     __device__ __forceinline__ static float scalar(const float *p) { return *p; }
 };
 
-// Lane state: running max m, float64 sum s of exp(x - m), candidate list.
+// Lane state: running max m (and ml = m log2 e), float64 sum s of
+// 2^(x log2 e - ml) = exp(x - m), and the candidate list.
 template <int KM>
 struct LaneAcc {
-    float m;
+    float m, ml;
     double s;
     KeyList<KM> top;
 
+    __device__ __forceinline__ void init() {
+        m = -INFINITY;
+        ml = -INFINITY;
+        s = 0.0;
+        top.init();
+    }
     template <int N>
-    __device__ __forceinline__ void add_exp(const float (&x)[N]) {
-        float vmax = x[0];
+    __device__ __forceinline__ static float vmax(const float (&x)[N]) {
+        float v = x[0];
 #pragma unroll
-        for (int j = 1; j < N; ++j) vmax = fmaxf(vmax, x[j]);
-        if (vmax > m) {  // rescale the running sum to the new max
-            s *= static_cast<double>(__builtin_amdgcn_exp2f((m - vmax) * kLog2e));
-            m = vmax;
+        for (int j = 1; j < N; ++j) v = fmaxf(v, x[j]);
+        return v;
+    }
+    template <int N>
+    __device__ __forceinline__ void add_exp(const float (&x)[N], float vm) {
+        if (vm > m) {  // rescale the running sum to the new max
+            const float nl = vm * kLog2e;
+            s *= static_cast<double>(__builtin_amdgcn_exp2f(ml - nl));
+            m = vm;
+            ml = nl;
         }
-        float ls = 0.f;
+        if (m != -INFINITY) {  // elements of -inf add nothing
+            float ls = 0.f;
 #pragma unroll
-        for (int j = 0; j < N; ++j) ls += __builtin_amdgcn_exp2f((x[j] - m) * kLog2e);
-        s += static_cast<double>(ls);
+            for (int j = 0; j < N; ++j) ls += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -ml));
+            s += static_cast<double>(ls);
+        }
     }
     // candidates: every element >= tau (the list keeps the lane's best KM).
-    // One insertion per loop trip over the lane's pending elements, so the
-    // wave pays for max-over-lanes insertions rather than for every element.
+    // One insertion per loop trip over the lane's pending elements.
     template <int N>
     __device__ __forceinline__ void add_cand(const float (&x)[N], int base_id, float tau) {
         uint32_t pend = 0;
@@ -272,14 +327,59 @@ __device__ __forceinline__ void rank_select(const uint64_t *buf, int C, int K, u
     }
 }
 
-// FUSE: the verify step's first kernel.  The row outputs are then written
-// with agent-scope atomic stores, and the last row of each sequence to finish
-// builds that sequence's tree (and mask rows) from them in wave 0.
+__device__ __forceinline__ uint64_t readlane64(uint64_t x, int j) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x)), j);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x >> 32)), j);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Rank by counting in registers: lanes below C hold one key each (distinct
+// when nonzero); the nonzero key beaten by exactly r others is the (r+1)-th
+// best and goes to out[r] when r < K.
+__device__ __forceinline__ void rank_in_wave(uint64_t c, int C, int K, uint64_t *out, int lane) {
+    int rank = 0;
+    for (int j = 0; j < C; ++j) rank += readlane64(c, j) > c;
+    if (lane < C && c != 0 && rank < K) out[rank] = c;
+}
+
+// Exclusive prefix sum over the wave's lanes of v in [0, 2^BITS), and the
+// wave's total, from one ballot per bit.
+template <int BITS>
+__device__ __forceinline__ int wave_prefix(int v, int lane, int &total) {
+    const uint64_t below = (1ull << lane) - 1;
+    int off = 0;
+    total = 0;
+#pragma unroll
+    for (int bit = 0; bit < BITS; ++bit) {
+        const uint64_t m = __ballot((v >> bit) & 1);
+        off += __popcll(m & below) << bit;
+        total += __popcll(m) << bit;
+    }
+    return off;
+}
+
+template <typename T>
+__device__ __forceinline__ void load_batch(u32x4 (&w)[kBatch], const u32x4 *vp, int i0, int nvec) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int i = i0 + u * kTopkThreads;
+        if (i < nvec) w[u] = __builtin_nontemporal_load(vp + i);
+    }
+}
+
+// Hand-off protocol (no writer ever waits for its own stores, and no word is
+// contended): every workgroup reads its epoch with its first loads in
+// flight and leaves its partial as tagged words; the row's last slice
+// (highest workgroup index of the row) merges the row, polling the other
+// partials until they carry this call's tag.
+//
+// FUSE: the verify step's first kernel.  The row mergers also leave their
+// row's results as tagged words, and the merger of each sequence's last row
+// gathers them and builds that sequence's tree (and mask rows) in wave 0.
 template <typename T, int KM, bool FUSE, int SLOTS>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict__ logits,
                                                             int vocab, int64_t pos_stride,
                                                             int slice, int splits, int K, void *ws,
-                                                            int64_t parts,
                                                             int32_t *__restrict__ topk_id,
                                                             double *__restrict__ topk_logq,
                                                             double *__restrict__ lse_out,
@@ -287,28 +387,27 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     constexpr int N = Vec<T>::N;
     const int sp = blockIdx.x;
     const int row = blockIdx.y;
+    const int rows = gridDim.y;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int lo = sp * slice;
     const int hi = min(vocab, lo + slice);
     const T *rowp = logits + static_cast<int64_t>(row) * pos_stride;
+    const TopkWs W = topk_ws(ws, rows, static_cast<int64_t>(rows) * splits, K);
+    const int PW = part_words(K);
 
-    __shared__ int sm_wcnt[kTopkWaves];
     __shared__ float sm_m[kTopkWaves];
     __shared__ double sm_s[kTopkWaves];
     __shared__ uint64_t sm_cand[kCandCap];
     __shared__ uint64_t sm_wave[kTopkWaves][KM];
     __shared__ uint64_t sm_win[KM];
-    __shared__ uint64_t sm_head[64];
-    __shared__ uint64_t sm_tau_key;
-    __shared__ int sm_cnt;
-    __shared__ int sm_last;
+    __shared__ uint32_t sm_part[kMergeWords];
+    __shared__ uint32_t sm_epoch;
+    __shared__ int sm_fail;
 
     LaneAcc<KM> acc;
-    acc.m = -INFINITY;
-    acc.s = 0.0;
-    acc.top.init();
+    acc.init();
 
     // scalar head up to the first 16-byte boundary (rows need only element
     // alignment), full 16-byte vectors, then a scalar tail
@@ -318,92 +417,103 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     const int nvec = (hi - vlo) / N;
     const int tail0 = vlo + nvec * N;
     const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + vlo);
+    constexpr int kStep = kBatch * kTopkThreads;
 
-    // ---- first batch: loads in flight, exp sums, then the pre-filter ----
+    // ---- first two batches in flight, then the row ticket ----
     float hx[1] = {-INFINITY};
     const bool has_head = tid < vlo - lo;
     const int head_id = lo + tid;
     if (has_head) hx[0] = Vec<T>::scalar(rowp + head_id);
-    u32x4 w[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        const int i = tid + u * kTopkThreads;
-        if (i < nvec) w[u] = __builtin_nontemporal_load(vp + i);
-    }
-    float lmax = has_head ? hx[0] : -INFINITY;
-    if (has_head) acc.add_exp(hx);
+    u32x4 wa[kBatch], wb[kBatch];
+    load_batch<T>(wa, vp, tid, nvec);
+    load_batch<T>(wb, vp, tid + kStep, nvec);
+    const bool merger = sp == splits - 1;
+    const int PS = PW + 1;  // words per workgroup slot
+    uint64_t *slot = W.part + (static_cast<int64_t>(row) * splits + sp) * PS;
+    uint64_t r_ep = 0;
+    if (tid == 0) r_ep = fetch(slot);
+
+    // ---- batch 0: exp sums, then the pre-filter bound ----
+    float lmax = hx[0];
+    if (has_head) acc.add_exp(hx, hx[0]);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
         const int i = tid + u * kTopkThreads;
         if (i < nvec) {
             float x[N];
-            Vec<T>::unpack(w[u], x);
-            acc.add_exp(x);
-#pragma unroll
-            for (int j = 0; j < N; ++j) lmax = fmaxf(lmax, x[j]);
+            Vec<T>::unpack(wa[u], x);
+            const float vm = LaneAcc<KM>::vmax(x);
+            acc.add_exp(x, vm);
+            lmax = fmaxf(lmax, vm);
         }
     }
     // Pre-filter bound: cut the wave into KM groups of 64/KM lanes; tau = the
     // smallest of the groups' maxima.  The KM group maxima are KM >= K
     // distinct elements >= tau, so the slice's K-th largest is >= tau.
     const float tau = group_max_min<KM>(lmax);
-    if (has_head) acc.add_cand(hx, head_id, tau);
+    if (has_head && hx[0] >= tau) acc.add_cand(hx, head_id, tau);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
         const int i = tid + u * kTopkThreads;
         if (i < nvec) {
             float x[N];
-            Vec<T>::unpack(w[u], x);
-            acc.add_cand(x, vlo + i * N, tau);
+            Vec<T>::unpack(wa[u], x);
+            if (LaneAcc<KM>::vmax(x) >= tau) acc.add_cand(x, vlo + i * N, tau);
         }
     }
-    // ---- remaining batches ----
-    for (int i0 = tid + kBatch * kTopkThreads; i0 < nvec; i0 += kBatch * kTopkThreads) {
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int i = i0 + u * kTopkThreads;
-            if (i < nvec) w[u] = __builtin_nontemporal_load(vp + i);
-        }
+
+    // ---- remaining batches, the next batch's loads in flight ----
+    auto process = [&](const u32x4 (&w)[kBatch], int i0) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int i = i0 + u * kTopkThreads;
             if (i < nvec) {
                 float x[N];
                 Vec<T>::unpack(w[u], x);
-                acc.add_exp(x);
-                acc.add_cand(x, vlo + i * N, tau);
+                const float vm = LaneAcc<KM>::vmax(x);
+                acc.add_exp(x, vm);
+                if (vm >= tau) acc.add_cand(x, vlo + i * N, tau);
             }
         }
+    };
+    for (int i = tid + kStep; i < nvec;) {
+        load_batch<T>(wa, vp, i + kStep, nvec);
+        process(wb, i);
+        i += kStep;
+        if (i >= nvec) break;
+        load_batch<T>(wb, vp, i + kStep, nvec);
+        process(wa, i);
+        i += kStep;
     }
     for (int e = tail0 + tid; e < hi; e += kTopkThreads) {
         float x[1] = {Vec<T>::scalar(rowp + e)};
-        acc.add_exp(x);
-        acc.add_cand(x, e, tau);
+        acc.add_exp(x, x[0]);
+        if (x[0] >= tau) acc.add_cand(x, e, tau);
     }
 
-    // ---- workgroup partial: (m, s) and the top K of the lanes' lists ----
-    const float wm = wave_max(acc.m);
+    // ---- workgroup partial: (log2 max, sum) and the top K of the lanes' lists ----
+    const float wml = wave_max(acc.ml);
     const double contrib =
-        (acc.m == -INFINITY) ? 0.0
-                             : acc.s * static_cast<double>(__builtin_amdgcn_exp2f((acc.m - wm) * kLog2e));
+        (acc.m == -INFINITY) ? 0.0 : acc.s * static_cast<double>(__builtin_amdgcn_exp2f(acc.ml - wml));
     const double ws_sum = wave_sum(contrib);
     // per wave: compact the lanes' candidates into LDS and rank them
     int n_l = 0;
 #pragma unroll
     for (int j = 0; j < KM; ++j) n_l += acc.top.k[j] != 0;
+    constexpr int kCountBits = KM <= 4 ? 3 : KM <= 8 ? 4 : KM <= 16 ? 5 : 6;
+    int Cw = 0;
+    const int off = wave_prefix<kCountBits>(n_l, lane, Cw);
     uint64_t *wcand = &sm_cand[wave * kWaveCap];
-    if (lane == 0) sm_wcnt[wave] = 0;
     if (lane < KM) sm_wave[wave][lane] = 0;
-    __builtin_amdgcn_wave_barrier();
-    const int off = atomicAdd(&sm_wcnt[wave], n_l);
-    __builtin_amdgcn_wave_barrier();
-    const int Cw = sm_wcnt[wave];  // same for every lane of the wave
     if (Cw <= kWaveCap) {
 #pragma unroll
         for (int j = 0; j < KM; ++j)
             if (j < n_l) wcand[off + j] = acc.top.k[j];
-        __builtin_amdgcn_wave_barrier();
-        rank_select(wcand, Cw, K, sm_wave[wave], lane, kWave);
+        wave_lds_sync();
+        if (Cw <= kWave)
+            rank_in_wave(lane < Cw ? wcand[lane] : 0, Cw, K, sm_wave[wave], lane);
+        else
+            rank_select(wcand, Cw, K, sm_wave[wave], lane, kWave);
     } else {
         // many equal logits: a K-round tournament over the lane lists
         uint64_t win[KM];
@@ -413,27 +523,37 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
             for (int j = 0; j < KM; ++j) sm_wave[wave][j] = win[j];
     }
     if (lane == 0) {
-        sm_m[wave] = wm;
+        sm_m[wave] = wml;
         sm_s[wave] = ws_sum;
     }
+    if (tid == 0) {
+        sm_epoch = static_cast<uint32_t>(r_ep);
+        sm_fail = 0;
+    }
     __syncthreads();
-    // the 4 waves' winners (distinct keys) ranked the same way
-    if (tid < KM) sm_win[tid] = 0;
-    __syncthreads();
+    // the 4 waves' winners (distinct keys) ranked the same way by wave 0
     if (wave == 0) {
-        uint64_t *all = &sm_wave[0][0];
-        rank_select_nz(all, kTopkWaves * KM, K, sm_win, lane, kWave);
+        if (lane < KM) sm_win[lane] = 0;
+        if constexpr (kTopkWaves * KM <= kWave) {
+            rank_in_wave(lane < kTopkWaves * KM ? sm_wave[lane / KM][lane % KM] : 0,
+                         kTopkWaves * KM, K, sm_win, lane);
+        } else {
+            wave_lds_sync();
+            rank_select_nz(&sm_wave[0][0], kTopkWaves * KM, K, sm_win, lane, kWave);
+        }
     }
     __syncthreads();
 
-    const int64_t rows = gridDim.y;
-    TopkWs ws_ = topk_ws(ws, rows, parts, K);
-    const int64_t part = static_cast<int64_t>(row) * splits + sp;
-    // publish with agent-scope atomic stores (coherent across the chip's L2
-    // caches by themselves); each wave waits for its own stores, then one
-    // thread counts in
-    if (tid < K) publish(&ws_.key[part * K + tid], sm_win[tid]);
-    if (tid == 0) {
+    // ---- this workgroup's partial: tagged words, or the merger's own LDS ----
+    const uint32_t tag = sm_epoch + 1u;
+    uint64_t *mypart = slot + 1;
+    uint32_t *ownp = &sm_part[sp * PW];
+    if (tid < 2 * K) {
+        const uint64_t k = sm_win[tid >> 1];
+        const uint32_t v = static_cast<uint32_t>((tid & 1) ? (k >> 32) : k);
+        if (merger) ownp[tid] = v;
+        else put_word(mypart + tid, v, tag);
+    } else if (tid == 2 * K) {
         float M = sm_m[0];
 #pragma unroll
         for (int q = 1; q < kTopkWaves; ++q) M = fmaxf(M, sm_m[q]);
@@ -441,112 +561,171 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
 #pragma unroll
         for (int q = 0; q < kTopkWaves; ++q)
             if (sm_m[q] != -INFINITY)
-                S += sm_s[q] * static_cast<double>(__builtin_amdgcn_exp2f((sm_m[q] - M) * kLog2e));
-        publish(&ws_.m[part], M);
-        publish(&ws_.s[part], S);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0)
-        sm_last = __hip_atomic_fetch_add(&ws_.count[row], 1u, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT) == static_cast<unsigned>(splits - 1);
-    __syncthreads();
-    if (!sm_last) return;
-
-    // ---- last workgroup of the row: merge the row's partials ----
-    // tau_key = K-th best of the partials' heads bounds the row's K-th best
-    // from below; only keys >= tau_key can be in the row's top K.
-    const int PK = splits * K;
-    if (tid < splits) sm_head[tid] = fetch(&ws_.key[(static_cast<int64_t>(row) * splits + tid) * K]);
-    if (tid == 0) {
-        sm_cnt = 0;
-        sm_tau_key = 0;
-    }
-    if (tid < KM) sm_win[tid] = 0;
-    __syncthreads();
-    if (tid < splits && splits >= K) {
-        const uint64_t h = sm_head[tid];
-        int rank = 0;
-        for (int u = 0; u < splits; ++u) rank += sm_head[u] > h;
-        if (rank == K - 1) sm_tau_key = h;
-    }
-    __syncthreads();
-    const uint64_t tau_key = sm_tau_key;
-    for (int e = tid; e < PK; e += kTopkThreads) {
-        const uint64_t k = fetch(&ws_.key[static_cast<int64_t>(row) * PK + e]);
-        if (k != 0 && k >= tau_key) {
-            const int o = atomicAdd(&sm_cnt, 1);
-            if (o < kCandCap) sm_cand[o] = k;
+                S += sm_s[q] * static_cast<double>(__builtin_amdgcn_exp2f(sm_m[q] - M));
+        const uint64_t sb = static_cast<uint64_t>(__double_as_longlong(S));
+        if (merger) {
+            ownp[2 * K] = __float_as_uint(M);
+            ownp[2 * K + 1] = static_cast<uint32_t>(sb);
+            ownp[2 * K + 2] = static_cast<uint32_t>(sb >> 32);
+        } else {
+            put_word(mypart + 2 * K, __float_as_uint(M), tag);
+            put_word(mypart + 2 * K + 1, static_cast<uint32_t>(sb), tag);
+            put_word(mypart + 2 * K + 2, static_cast<uint32_t>(sb >> 32), tag);
         }
     }
+    if (tid == 0) publish(slot, static_cast<uint64_t>(tag));  // the next call's epoch
+    if (!merger) return;
+
+    // ---- the row merger: gather every partial of the row ----
+    // (the merger's own words, split splits - 1, are the last PW and in LDS)
+    const uint64_t *rp = W.part + static_cast<int64_t>(row) * splits * PS;
+    const int nw = (splits - 1) * PW;
+    for (int w0 = 0; w0 < nw; w0 += 4 * kTopkThreads) {
+        int idx[4];
+        uint32_t val[4];
+        int n = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int w = w0 + tid + u * kTopkThreads;
+            idx[u] = (w / PW) * PS + 1 + w % PW;  // data word w % PW of slot w / PW
+            if (w < nw) n = u + 1;
+        }
+        if (n > 0 && !get_words(rp, idx, n, tag, val)) sm_fail = 1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (u < n) sm_part[w0 + tid + u * kTopkThreads] = val[u];
+    }
     __syncthreads();
-    const int C2 = sm_cnt;
-    if (C2 <= kCandCap) {
-        rank_select(sm_cand, C2, K, sm_win, tid, kTopkThreads);
-    } else if (wave == 0) {
+    if (wave != 0) return;
+
+    // ---- the row's top K from the partials (wave 0, registers and LDS) ----
+    auto part_key = [&](int s, int j) -> uint64_t {
+        const uint32_t *w = &sm_part[s * PW + 2 * j];
+        return static_cast<uint64_t>(w[0]) | (static_cast<uint64_t>(w[1]) << 32);
+    };
+    // tau_key = K-th best of the partials' heads bounds the row's K-th best
+    // from below; only keys >= tau_key can be in the row's top K.
+    uint64_t tau_key = 0;
+    if (splits >= K) {
+        const uint64_t hd = lane < splits ? part_key(lane, 0) : 0;
+        int rank = 0;
+        for (int j = 0; j < splits; ++j) rank += readlane64(hd, j) > hd;
+        const uint64_t at = __ballot(lane < splits && rank == K - 1);
+        if (at) tau_key = readlane64(hd, __ffsll(static_cast<long long>(at)) - 1);
+    }
+    const uint64_t below = (1ull << lane) - 1;
+    const int PK = splits * K;
+    int C2 = 0;
+    for (int e0 = 0; e0 < PK; e0 += kWave) {
+        const int e = e0 + lane;
+        const uint64_t k = e < PK ? part_key(e / K, e % K) : 0;
+        const bool take = k != 0 && k >= tau_key;
+        const uint64_t m = __ballot(take);
+        const int o = C2 + __popcll(m & below);
+        if (take && o < kCandCap) sm_cand[o] = k;
+        C2 += __popcll(m);
+    }
+    if (lane < KM) sm_win[lane] = 0;
+    wave_lds_sync();
+    if (C2 <= kWave) {
+        rank_in_wave(lane < C2 ? sm_cand[lane] : 0, C2, K, sm_win, lane);
+    } else if (C2 <= kCandCap) {
+        rank_select(sm_cand, C2, K, sm_win, lane, kWave);
+    } else {
         // many equal logits: tournament over the partial lists
         KeyList<KM> t;
         t.init();
         if (lane < splits)
 #pragma unroll
             for (int j = 0; j < KM; ++j)
-                if (j < K) t.k[j] = fetch(&ws_.key[(static_cast<int64_t>(row) * splits + lane) * K + j]);
+                if (j < K) t.k[j] = part_key(lane, j);
         uint64_t win[KM];
         wave_select<KM, KM>(t, K, win);
         if (lane == 0)
 #pragma unroll
             for (int j = 0; j < KM; ++j) sm_win[j] = win[j];
     }
-    __syncthreads();
-    if (wave != 0) return;
-    float m = -INFINITY;
+    wave_lds_sync();
+
+    // ---- the row's normaliser and outputs (wave 0) ----
+    float ml = -INFINITY;
     double ssum = 0.0;
     if (lane < splits) {
-        const int64_t pt = static_cast<int64_t>(row) * splits + lane;
-        m = fetch(&ws_.m[pt]);
-        ssum = fetch(&ws_.s[pt]);
+        const uint32_t *w = &sm_part[lane * PW + 2 * K];
+        ml = __uint_as_float(w[0]);
+        ssum = __longlong_as_double(static_cast<long long>(
+            static_cast<uint64_t>(w[1]) | (static_cast<uint64_t>(w[2]) << 32)));
     }
-    const float M = wave_max(m);
-    const double c = (m == -INFINITY) ? 0.0 : ssum * exp(static_cast<double>(m) - static_cast<double>(M));
+    const float M = wave_max(ml);
+    const double c = (ml == -INFINITY) ? 0.0
+                                       : ssum * exp2(static_cast<double>(ml) - static_cast<double>(M));
     const double S = wave_sum(c);
-    const double lse = static_cast<double>(M) + log(S);
+    constexpr double kLn2 = 0.6931471805599453;
+    const double lse = sm_fail ? NAN : static_cast<double>(M) * kLn2 + log(S);
+    int32_t id = -1;
+    double lq = 0.0;
     if (lane < K) {
         const uint64_t k = sm_win[lane];
-        const int32_t id = key_id(k);
-        const double lq = static_cast<double>(key_value(k)) - lse;
-        if constexpr (FUSE) {
-            publish(&topk_id[static_cast<int64_t>(row) * K + lane], id);
-            publish(&topk_logq[static_cast<int64_t>(row) * K + lane], lq);
-        } else {
-            topk_id[static_cast<int64_t>(row) * K + lane] = id;
-            topk_logq[static_cast<int64_t>(row) * K + lane] = lq;
-        }
+        id = key_id(k);
+        lq = static_cast<double>(key_value(k)) - lse;
+        topk_id[static_cast<int64_t>(row) * K + lane] = id;
+        topk_logq[static_cast<int64_t>(row) * K + lane] = lq;
     }
-    if (lane == 0) {
-        lse_out[row] = lse;
-        ws_.count[row] = 0u;  // ready for the next call
-    }
+    if (lane == 0) lse_out[row] = lse;
     if constexpr (FUSE) {
-        // sequence completion: the last of its rows builds the tree
+        // leave the row's results for the sequence's tree builder (the merger
+        // of the sequence's last row, which keeps its own row in LDS)
         __shared__ TreeLds tl;
+        const uint32_t stag = tag;  // every slot of a workspace holds the same epoch
         const int b = row / tp.block;
-        unsigned int *seq_count = ws_.count + rows;
-        __builtin_amdgcn_s_waitcnt(0);  // this row's outputs are complete
-        int last = 0;
-        if (lane == 0)
-            last = __hip_atomic_fetch_add(&seq_count[b], 1u, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT) ==
-                   static_cast<unsigned>(tp.block - 1);
-        last = __builtin_amdgcn_readfirstlane(last);
-        if (!last) return;
-        const int BK = tp.block * K;
-        for (int e = lane; e < BK; e += kWave) {
-            tl.ids[e] = fetch(&topk_id[static_cast<int64_t>(b) * BK + e]);
-            tl.lq[e] = fetch(&topk_logq[static_cast<int64_t>(b) * BK + e]);
+        const int rl = row - b * tp.block;
+        if (rl != tp.block - 1) {
+            uint64_t *rr = W.rowrec + static_cast<int64_t>(row) * 3 * K;
+            if (lane < K) {
+                const uint64_t qb = static_cast<uint64_t>(__double_as_longlong(lq));
+                put_word(rr + lane, static_cast<uint32_t>(id), stag);
+                put_word(rr + K + 2 * lane, static_cast<uint32_t>(qb), stag);
+                put_word(rr + K + 2 * lane + 1, static_cast<uint32_t>(qb >> 32), stag);
+            }
+            return;
+        }
+        if (lane < K) {
+            tl.ids[rl * K + lane] = id;
+            tl.lq[rl * K + lane] = lq;
+        }
+
+        // the sequence's tree builder: gather the other rows, build the tree
+        const int BK = (tp.block - 1) * K;
+        const uint64_t *sr = W.rowrec + static_cast<int64_t>(b) * tp.block * 3 * K;
+        bool ok = true;
+        // two entries per lane and trip: id, log q low and high words each
+        for (int e0 = lane; e0 < BK; e0 += 2 * kWave) {
+            int idx[6];
+            uint32_t v[6];
+            int n = 0;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int e = e0 + u * kWave;
+                const int r = e / K, j = e % K;
+                idx[3 * u] = r * 3 * K + j;
+                idx[3 * u + 1] = r * 3 * K + K + 2 * j;
+                idx[3 * u + 2] = r * 3 * K + K + 2 * j + 1;
+                if (e < BK) n = 3 * (u + 1);
+            }
+            ok = get_words(sr, idx, n, stag, v) && ok;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int e = e0 + u * kWave;
+                if (e < BK) {
+                    tl.ids[e] = static_cast<int>(v[3 * u]);
+                    tl.lq[e] = __longlong_as_double(static_cast<long long>(
+                        static_cast<uint64_t>(v[3 * u + 1]) | (static_cast<uint64_t>(v[3 * u + 2]) << 32)));
+                }
+            }
         }
         wave_lds_sync();
         build_tree_wave<SLOTS>(tl, tp, to, b, lane);
-        if (lane == 0) seq_count[b] = 0u;
+        if (lane == 0 && !ok) to.n_nodes[b] = -1;
     }
 }
 
@@ -560,10 +739,11 @@ struct TopkPlan {
     int slice;
 };
 
-inline TopkPlan topk_plan(int64_t rows, int vocab) {
+inline TopkPlan topk_plan(int64_t rows, int vocab, int K) {
     int64_t want = (kTargetWgs + rows - 1) / rows;
     int64_t cap = (vocab + kMinSlice - 1) / kMinSlice;
-    int splits = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>({want, cap, 64})));
+    int64_t most = std::min<int64_t>(64, 1024 / K);
+    int splits = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>({want, cap, most})));
     int slice = (vocab + splits - 1) / splits;
     slice = (slice + 7) & ~7;  // 16-byte aligned slices for both element types
     splits = (vocab + slice - 1) / slice;
@@ -574,10 +754,9 @@ template <typename T, int KM, bool FUSE, int SLOTS>
 void launch_topk(const void *logits, int rows, int vocab, int64_t pos_stride, int K,
                  const TopkPlan &pl, void *ws, int32_t *topk_id, double *topk_logq, double *lse,
                  const TreeParams &tp, const TreeOut &to, hipStream_t st) {
-    const int64_t parts = static_cast<int64_t>(rows) * pl.splits;
     hipLaunchKernelGGL((topk_kernel<T, KM, FUSE, SLOTS>), dim3(pl.splits, rows), dim3(kTopkThreads),
                        0, st, static_cast<const T *>(logits), vocab, pos_stride, pl.slice, pl.splits,
-                       K, ws, parts, topk_id, topk_logq, lse, tp, to);
+                       K, ws, topk_id, topk_logq, lse, tp, to);
 }
 
 template <typename T, bool FUSE, int SLOTS>
@@ -602,7 +781,7 @@ template <bool FUSE, int SLOTS>
 void launch_topk_dt(const void *logits, td_dtype dtype, int rows, int vocab, int64_t pos_stride,
                     int K, void *ws, int32_t *topk_id, double *topk_logq, double *lse,
                     const TreeParams &tp, const TreeOut &to, hipStream_t st) {
-    const TopkPlan pl = topk_plan(rows, vocab);
+    const TopkPlan pl = topk_plan(rows, vocab, K);
     if (dtype == TD_BF16)
         launch_topk_k<uint16_t, FUSE, SLOTS>(logits, rows, vocab, pos_stride, K, pl, ws, topk_id,
                                              topk_logq, lse, tp, to, st);
@@ -615,7 +794,7 @@ void launch_topk_dt(const void *logits, td_dtype dtype, int rows, int vocab, int
 
 size_t topk_workspace_bytes(int batch, int block, int vocab, int K) {
     const int64_t rows = static_cast<int64_t>(batch) * block;
-    const TopkPlan pl = topk_plan(rows, vocab);
+    const TopkPlan pl = topk_plan(rows, vocab, K);
     return topk_ws_bytes(rows, rows * pl.splits, K);
 }
 

@@ -15,7 +15,8 @@ from ctypes import c_double, c_float, c_int, c_int32, c_int64, c_size_t, c_void_
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtreedraft.so")
+# TREEDRAFT_LIB selects another build of the library (e.g. for A/B timing).
+LIB_PATH = os.environ.get("TREEDRAFT_LIB") or os.path.join(_HERE, "libtreedraft.so")
 
 TD_OK, TD_EINVAL, TD_ECAPACITY, TD_EUNSUPPORTED, TD_EHIP = range(5)
 TD_F32, TD_BF16 = 0, 1

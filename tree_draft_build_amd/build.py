@@ -19,7 +19,10 @@ ARCH = os.environ.get("TD_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # matrix-core accumulators in ordinary VGPRs: the online softmax
+         # rescales them with vector ALU ops, which cannot address AGPRs
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Wall",
          "-Wno-unused-function"]
 
 

@@ -9,20 +9,21 @@
 // per row).  The G heads of a KV group times the tree rows form the M
 // dimension (row r = i * G + hh), cut into row groups of 16.  Two kernels:
 //
-//  attn_ctx_split   split-KV over the context.  Work item = (key chunk of one
-//                   sequence, KV head); a sequence with an empty context still
-//                   gets one chunk with no keys.  The chunk's first KV loads
-//                   are issued before the tree size and the queries arrive.
-//                   The chunk streams through LDS in sub-chunks of CH keys:
-//                   K stored key-major (MFMA A operand of S^T = K Q^T, one
-//                   16-byte LDS read per lane and step), V stored transposed
-//                   (A operand of O^T += V^T P^T, two 8-byte reads), with the
-//                   next sub-chunk's global loads in flight during the
-//                   compute.  Row blocks of up to 8 row groups are processed
-//                   in turn; within a block waves own row groups, or, when it
-//                   has fewer than 4, split the keys of each sub-chunk and
-//                   merge through LDS.  Softmax is online in base 2.  One
-//                   (m, l, O) partial per tree row and chunk is stored.
+//  split            split-KV over the context (attn_split_bf16 streams keys
+//                   straight into LDS and reads V transposed from there;
+//                   attn_split_f32 stages through registers).  Work item =
+//                   (key chunk of one sequence, KV head); a sequence with an
+//                   empty context still gets one chunk with no keys.  The
+//                   chunk's first loads are issued before the tree size and
+//                   the queries arrive, and each next sub-chunk's loads fly
+//                   during the compute.  A wave owns up to OWN row groups
+//                   (queries and O^T accumulators in registers) and shares
+//                   each K and V fragment it reads from LDS among them; row
+//                   blocks of 4 OWN row groups are processed in turn; a block
+//                   of fewer than 4 row groups splits the keys of each
+//                   sub-chunk over the waves, which merge through LDS.
+//                   Softmax is online in base 2.  One (m, l, O) partial per
+//                   tree row and chunk is stored.
 //  attn_tree_combine one wave per output row: merges the chunk partials
 //                   (every load in flight at once), adds the ancestor-masked
 //                   tree keys (sparse: one dot product per set mask bit) and
@@ -55,7 +56,12 @@ constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = 4;
 constexpr int kRowsPerGroup = 16;
 constexpr int kKeyTile = 32;
-constexpr int kRowBlock = 8;  // row groups per work item
+// Row groups a wave may own: its query fragments and O^T accumulators live
+// in registers (about 54 per row group at D = 128, 30 at D = 64).
+template <typename T, int D>
+constexpr int max_own() {
+    return sizeof(T) == 4 ? 2 : (D == 128 ? 3 : 5);
+}
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <typename T> struct Sub;
@@ -68,7 +74,7 @@ template <> struct Sub<float> { static constexpr int CH = 64; };
 struct AttnPlan {
     int group;         // G = hq / hkv
     int n_rg;          // row groups of 16 per (b, g) at nq_max rows
-    int n_rb;          // row blocks of kRowBlock row groups
+    int own;           // row groups per wave and row block (block = 4 own), uncapped
     int chunk;         // keys per work item (a multiple of the sub-chunk)
     int64_t n_chunks;  // upper bound of sum_b ceil(L_b / chunk)
     int64_t items;     // n_chunks * hkv split work items
@@ -78,7 +84,9 @@ inline AttnPlan attn_plan(int batch, int nq_max, int hq, int hkv, int64_t total_
     AttnPlan p;
     p.group = hq / hkv;
     p.n_rg = (p.group * nq_max + kRowsPerGroup - 1) / kRowsPerGroup;
-    p.n_rb = (p.n_rg + kRowBlock - 1) / kRowBlock;
+    // one row block holds 4 own row groups: as many as the registers allow,
+    // so that a chunk's keys stream once for every tree row where they can
+    p.own = std::max(1, (p.n_rg + kAttnWaves - 1) / kAttnWaves);
     // about 1024 work items over the context; longer chunks keep the partial
     // traffic small when the context is long
     const int64_t work = std::max<int64_t>(1, total_ctx) * hkv;
@@ -140,13 +148,8 @@ __device__ __forceinline__ int slot_key(int h4, int t) { return t < 4 ? 4 * h4 +
 // attn_ctx_split
 // ---------------------------------------------------------------------------
 
+// float32 split kernel: K and V key-major in LDS, one sub-chunk at a time.
 template <typename T, int D> struct Lds;
-template <int D> struct Lds<uint16_t, D> {
-    static constexpr int CH = Sub<uint16_t>::CH;
-    static constexpr int KP = D + 8;    // sK pitch (elements): 16-byte aligned rows
-    static constexpr int VP = CH + 4;   // sVt pitch (elements): 8-byte aligned rows
-    static constexpr int bytes_kv = (CH * KP + D * VP) * 2;
-};
 template <int D> struct Lds<float, D> {
     static constexpr int CH = Sub<float>::CH;
     static constexpr int KP = D + 4;
@@ -174,64 +177,6 @@ struct RowState {
         for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 };
-
-// One 32-key tile for one row group: S^T, online softmax, O^T update.
-// kt: tile index inside the LDS sub-chunk; valid: keys of the sub-chunk.
-template <int D>
-__device__ __forceinline__ void tile_bf16(const uint16_t *sK, const uint16_t *sVt, const bf16x8 (&qf)[D / 32],
-                                          int kt, int valid, float scale2, int lane, RowState<D> &st) {
-    using L = Lds<uint16_t, D>;
-    const int col = lane & 15;
-    const int h4 = lane >> 4;
-    f32x4 s[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-        const uint16_t *krow = sK + (kt * kKeyTile + 16 * hf + col) * L::KP + 8 * h4;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(krow + 32 * ks));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc, 0, 0, 0);
-        }
-        s[hf] = acc;
-    }
-    float sc[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const float v = (t < 4 ? s[0][t] : s[1][t - 4]) * scale2;
-        sc[t] = kt * kKeyTile + slot_key(h4, t) < valid ? v : -INFINITY;
-    }
-    float tmax = sc[0];
-#pragma unroll
-    for (int t = 1; t < 8; ++t) tmax = fmaxf(tmax, sc[t]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(st.m, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-    float p[8];
-    float ps = 0.f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        p[t] = __builtin_amdgcn_exp2f(sc[t] - m_new);
-        ps += p[t];
-    }
-    st.l = st.l * alpha + ps;
-    st.m = m_new;
-    uint32_t pw[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        pw[k] = static_cast<uint32_t>(f32_to_bf16(p[2 * k])) |
-                (static_cast<uint32_t>(f32_to_bf16(p[2 * k + 1])) << 16);
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-        const uint16_t *vrow = sVt + (16 * dt + col) * L::VP + kt * kKeyTile + 4 * h4;
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow);
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 16);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-        st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, st.o[dt] * alpha, 0, 0, 0);
-    }
-}
 
 template <int D>
 __device__ __forceinline__ void tile_f32(const float *sK, const float *sV, const float (&qa)[D / 4],
@@ -262,8 +207,8 @@ __device__ __forceinline__ void tile_f32(const float *sK, const float *sV, const
     float tmax = sc[0];
 #pragma unroll
     for (int t = 1; t < 8; ++t) tmax = fmaxf(tmax, sc[t]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = fmaxf(tmax, xchg_f<4>(tmax));
+    tmax = fmaxf(tmax, xchg_f<5>(tmax));
     const float m_new = fmaxf(st.m, tmax);
     const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
     float p[8];
@@ -289,60 +234,6 @@ __device__ __forceinline__ void tile_f32(const float *sK, const float *sV, const
 
 // Global -> register staging of one sub-chunk (keys clamped into range).
 template <typename T, int D> struct Stage;
-
-template <int D> struct Stage<uint16_t, D> {
-    using L = Lds<uint16_t, D>;
-    static constexpr int kKPieces = L::CH * D / 8 / kAttnThreads;           // 16-byte K pieces per thread
-    static constexpr int kVUnits = (L::CH / 4) * (D / 8) / kAttnThreads;    // (4 keys x 8 d) V units
-    u32x4 k[kKPieces];
-    u32x4 v[kVUnits][4];
-
-    __device__ __forceinline__ void load(const uint16_t *kbase, const uint16_t *vbase, int64_t kstride,
-                                         int valid, int tid) {
-#pragma unroll
-        for (int r = 0; r < kKPieces; ++r) {
-            const int p = tid + kAttnThreads * r;
-            const int key = min(p / (D / 8), valid - 1);
-            k[r] = *reinterpret_cast<const u32x4 *>(kbase + key * kstride + (p % (D / 8)) * 8);
-        }
-#pragma unroll
-        for (int r = 0; r < kVUnits; ++r) {
-            const int u = tid + kAttnThreads * r;
-            const int kg = u / (D / 8);
-            const int db = u % (D / 8);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int key = min(4 * kg + j, valid - 1);
-                v[r][j] = *reinterpret_cast<const u32x4 *>(vbase + key * kstride + db * 8);
-            }
-        }
-    }
-    __device__ __forceinline__ void store(uint16_t *sK, uint16_t *sVt, int tid) const {
-#pragma unroll
-        for (int r = 0; r < kKPieces; ++r) {
-            const int p = tid + kAttnThreads * r;
-            *reinterpret_cast<u32x4 *>(sK + (p / (D / 8)) * L::KP + (p % (D / 8)) * 8) = k[r];
-        }
-#pragma unroll
-        for (int r = 0; r < kVUnits; ++r) {
-            const int u = tid + kAttnThreads * r;
-            const int kg = u / (D / 8);
-            const int db = u % (D / 8);
-            // 8 d values x 4 keys -> 8 rows of sVt, 4 keys each
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int w = t >> 1;
-                const int sh = (t & 1) * 16;
-                const uint32_t e0 = (v[r][0][w] >> sh) & 0xffffu;
-                const uint32_t e1 = (v[r][1][w] >> sh) & 0xffffu;
-                const uint32_t e2 = (v[r][2][w] >> sh) & 0xffffu;
-                const uint32_t e3 = (v[r][3][w] >> sh) & 0xffffu;
-                *reinterpret_cast<u32x2 *>(sVt + (db * 8 + t) * L::VP + 4 * kg) =
-                    u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
-            }
-        }
-    }
-};
 
 template <int D> struct Stage<float, D> {
     using L = Lds<float, D>;
@@ -371,14 +262,17 @@ template <int D> struct Stage<float, D> {
     }
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(kAttnThreads) void attn_ctx_split(
-    const T *__restrict__ q, const T *__restrict__ k_ctx, const T *__restrict__ v_ctx,
+// The float32 split kernel (see attn_split_bf16 for the bf16 one): each
+// sub-chunk is staged through registers into LDS while the previous one is
+// computed on.
+template <int D, int OWN>
+__global__ __launch_bounds__(kAttnThreads) void attn_split_f32(
+    const float *__restrict__ q, const float *__restrict__ k_ctx, const float *__restrict__ v_ctx,
     const int64_t *__restrict__ ctx_offsets, const int32_t *__restrict__ n_nodes, int batch,
     int nq_max, int hq, int hkv, int group, int n_rg, int chunk, float scale2, float *__restrict__ ws,
     int64_t prow_total) {
+    using T = float;
     using L = Lds<T, D>;
-    constexpr bool kBF = sizeof(T) == 2;
     constexpr int CH = L::CH;
     __shared__ __attribute__((aligned(16))) char lds[split_lds_bytes<T, D>()];
     T *sK = reinterpret_cast<T *>(lds);
@@ -412,15 +306,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_ctx_split(
     const int n_rg_b = (rows_b + kRowsPerGroup - 1) / kRowsPerGroup;
     const T *qb = q + static_cast<int64_t>(b) * nq_max * hq * D;
 
-    for (int rb0 = 0; rb0 < n_rg_b; rb0 += kRowBlock) {
-        const int nrg = min(kRowBlock, n_rg_b - rb0);
+    // row blocks of at most 4 OWN row groups, balanced
+    constexpr int kBlock = kAttnWaves * OWN;
+    const int n_blk = (n_rg_b + kBlock - 1) / kBlock;
+    const int per_blk = n_blk > 0 ? (n_rg_b + n_blk - 1) / n_blk : 1;
+    for (int rb0 = 0; rb0 < n_rg_b; rb0 += per_blk) {
+        const int nrg = min(per_blk, n_rg_b - rb0);
         // wave -> (row groups, key tiles) assignment
         //   nrg >= 4: wave w owns row groups w and w + 4 of the block, all keys
         //   nrg <  4: p2 = 1, 2 or 4 row slots; waves share a row group's keys
         const int p2 = nrg >= 4 ? 4 : (nrg == 1 ? 1 : (nrg == 2 ? 2 : 4));
         const int kt_step = kAttnWaves / p2;
         const int kt_first = wave / p2;
-        constexpr int kMaxOwn = kRowBlock / kAttnWaves;  // 2
+        constexpr int kMaxOwn = OWN;
         int own_rg[kMaxOwn];
         int n_own = 0;
 #pragma unroll
@@ -434,9 +332,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_ctx_split(
         // queries of the owned row groups (B operand layout); rows past the
         // tree read row 0 of the group and are never published
         RowState<D> st[kMaxOwn];
-        typedef typename std::conditional<kBF, bf16x8, float>::type QE;
-        constexpr int kQN = kBF ? D / 32 : D / 4;
-        QE qf[kMaxOwn][kQN];
+        float qf[kMaxOwn][D / 4];
 #pragma unroll
         for (int j = 0; j < kMaxOwn; ++j) {
             st[j].init();
@@ -445,19 +341,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_ctx_split(
             const int qi = ok ? r / group : 0;
             const int qh = g * group + (ok ? r % group : 0);
             const T *qrow = qb + (static_cast<int64_t>(qi) * hq + qh) * D;
-            if constexpr (kBF) {
 #pragma unroll
-                for (int ks = 0; ks < kQN; ++ks) {
-                    u32x4 w = *reinterpret_cast<const u32x4 *>(qrow + 32 * ks + 8 * h4);
-                    qf[j][ks] = __builtin_bit_cast(bf16x8, w);
-                }
-            } else {
+            for (int k4 = 0; k4 < D / 16; ++k4) {
+                f32x4 w = *reinterpret_cast<const f32x4 *>(qrow + h4 * (D / 4) + 4 * k4);
 #pragma unroll
-                for (int k4 = 0; k4 < D / 16; ++k4) {
-                    f32x4 w = *reinterpret_cast<const f32x4 *>(qrow + h4 * (D / 4) + 4 * k4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) qf[j][4 * k4 + e] = w[e];
-                }
+                for (int e = 0; e < 4; ++e) qf[j][4 * k4 + e] = w[e];
             }
         }
         if (rb0 > 0 && n_sub > 0) {  // another row block: stream the chunk again
@@ -475,15 +363,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_ctx_split(
                 stage.load(kbase + s1 * kstride, vbase + s1 * kstride, kstride, valid1, tid);
             }
             const int ntiles = (valid + kKeyTile - 1) / kKeyTile;
+            for (int kt = split_mode ? kt_first : 0; kt < ntiles; kt += split_mode ? kt_step : 1) {
 #pragma unroll
-            for (int j = 0; j < kMaxOwn; ++j) {
-                if (j >= n_own) break;
-                for (int kt = split_mode ? kt_first : 0; kt < ntiles; kt += split_mode ? kt_step : 1) {
-                    if constexpr (kBF)
-                        tile_bf16<D>(sK, sV, qf[j], kt, valid, scale2, lane, st[j]);
-                    else
-                        tile_f32<D>(sK, sV, qf[j], kt, valid, scale2, lane, st[j]);
-                }
+                for (int j = 0; j < kMaxOwn; ++j)
+                    if (j < n_own) tile_f32<D>(sK, sV, qf[j], kt, valid, scale2, lane, st[j]);
             }
             __syncthreads();
         }
@@ -564,6 +447,383 @@ __global__ __launch_bounds__(kAttnThreads) void attn_ctx_split(
             __syncthreads();  // LDS is reused by the next row block
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// attn_split_bf16: the bf16 split kernel.  Sub-chunks of kSubB keys stream
+// straight from HBM into one of two LDS buffers (global_load_lds, 16 bytes
+// per lane) while the other buffer is computed on, so no register holds
+// staged data.  K and V sit key-major in LDS, each key row padded:
+//   K rows of D/8 + 1 16-byte pieces: S^T = K Q^T reads 16 consecutive key
+//     rows at one piece (A operand), and those fall in distinct banks;
+//   V rows of D/8 + 2 pieces: O^T += V^T P^T needs V transposed, which
+//     ds_read_b64_tr_b16 delivers.  Within a group of 16 lanes it hands lane
+//     i, as element j, element i % 4 of the 4 elements at the address of lane
+//     4 j + i / 4, so lane m of group G addresses 4 head dims of key
+//     4 G + m / 4: lane i then holds head dim i of keys 4 G .. 4 G + 3 (and,
+//     from a second read, of keys 16 + 4 G ..), the order in which S^T leaves
+//     P in registers.  The 4 keys' 32-byte reads fall in distinct banks.
+// The pad pieces of a row load a copy of its last piece (same instruction,
+// no extra HBM traffic).
+// ---------------------------------------------------------------------------
+constexpr int kSubB = 128;  // keys per LDS sub-chunk (bf16): 4 tiles, one per wave in split mode
+
+template <int D> constexpr int rk_pieces() { return D / 8 + 1; }
+template <int D> constexpr int rv_pieces() { return D / 8 + 2; }
+template <int D> constexpr int sub_elems() { return kSubB * (rk_pieces<D>() + rv_pieces<D>()) * 8; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef unsigned u2_t __attribute__((ext_vector_type(2)));
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at lds + 16 l (lds must be the same for the whole wave).
+__device__ __forceinline__ void lds_dma16(const void *g, void *lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void *)p));
+}
+
+// Enqueue the direct loads of one sub-chunk's K or V rows (LDS rows of R
+// pieces; rows at or past `valid` repeat key valid - 1 and are masked later).
+template <int D, int R>
+__device__ __forceinline__ void issue_rows(const uint16_t *gbase, int ks32, int valid, uint16_t *lds,
+                                           int wave, int lane) {
+    constexpr int P = D / 8;
+    constexpr int kSlots = kSubB * R;
+    constexpr int kRounds = (kSlots + kAttnThreads - 1) / kAttnThreads;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+        const int slot0 = (r * kAttnWaves + wave) * kWave;  // first slot of this wave (uniform)
+        if (slot0 >= kSlots) break;
+        const int sl = slot0 + lane;
+        if (sl < kSlots) {
+            const int row = sl / R;
+            const int piece = min(sl % R, P - 1);
+            lds_dma16(gbase + min(row, valid - 1) * ks32 + 8 * piece, lds + 8 * slot0);
+        }
+    }
+}
+
+// V^T fragments of one 32-key tile, all reads in flight before one wait.
+// The LDS reads are issued from assembly: the compiler's own transposing-read
+// builtin makes it wait for the other buffer's loads first.
+template <int D>
+__device__ __forceinline__ void read_vt(const uint16_t *sV, int kt, int lane, bf16x8 (&fv)[D / 16]) {
+    constexpr int RV = rv_pieces<D>();
+    const int G = lane >> 4;
+    const int m = lane & 15;
+    const int key0 = kt * kKeyTile + 4 * G + (m >> 2);
+    const uint32_t a0 = lds_addr(sV + key0 * RV * 8 + 4 * (m & 3));
+    const uint32_t a1 = lds_addr(sV + (key0 + 16) * RV * 8 + 4 * (m & 3));
+    u2_t t[2 * (D / 16)];
+    if constexpr (D == 128) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %16\n"
+            "ds_read_b64_tr_b16 %1, %17\n"
+            "ds_read_b64_tr_b16 %2, %16 offset:32\n"
+            "ds_read_b64_tr_b16 %3, %17 offset:32\n"
+            "ds_read_b64_tr_b16 %4, %16 offset:64\n"
+            "ds_read_b64_tr_b16 %5, %17 offset:64\n"
+            "ds_read_b64_tr_b16 %6, %16 offset:96\n"
+            "ds_read_b64_tr_b16 %7, %17 offset:96\n"
+            "ds_read_b64_tr_b16 %8, %16 offset:128\n"
+            "ds_read_b64_tr_b16 %9, %17 offset:128\n"
+            "ds_read_b64_tr_b16 %10, %16 offset:160\n"
+            "ds_read_b64_tr_b16 %11, %17 offset:160\n"
+            "ds_read_b64_tr_b16 %12, %16 offset:192\n"
+            "ds_read_b64_tr_b16 %13, %17 offset:192\n"
+            "ds_read_b64_tr_b16 %14, %16 offset:224\n"
+            "ds_read_b64_tr_b16 %15, %17 offset:224\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]),
+              "=&v"(t[6]), "=&v"(t[7]), "=&v"(t[8]), "=&v"(t[9]), "=&v"(t[10]), "=&v"(t[11]),
+              "=&v"(t[12]), "=&v"(t[13]), "=&v"(t[14]), "=&v"(t[15])
+            : "v"(a0), "v"(a1));
+    } else {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n"
+            "ds_read_b64_tr_b16 %1, %9\n"
+            "ds_read_b64_tr_b16 %2, %8 offset:32\n"
+            "ds_read_b64_tr_b16 %3, %9 offset:32\n"
+            "ds_read_b64_tr_b16 %4, %8 offset:64\n"
+            "ds_read_b64_tr_b16 %5, %9 offset:64\n"
+            "ds_read_b64_tr_b16 %6, %8 offset:96\n"
+            "ds_read_b64_tr_b16 %7, %9 offset:96\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]),
+              "=&v"(t[6]), "=&v"(t[7])
+            : "v"(a0), "v"(a1));
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+        fv[dt] = __builtin_bit_cast(bf16x8, u32x4{t[2 * dt].x, t[2 * dt].y, t[2 * dt + 1].x, t[2 * dt + 1].y});
+}
+
+// One 32-key tile for the n_own row groups a wave owns: S^T = K Q^T (K rows
+// read from LDS once for all of them), online softmax in base 2, then
+// O^T += V^T P^T (V^T fragments read once).  valid: keys of the sub-chunk
+// (keys at or past it are masked).
+template <int D, int OWN>
+__device__ __forceinline__ void tile_dma(const uint16_t *sK, const uint16_t *sV,
+                                         const bf16x8 (&qf)[OWN][D / 32], int n_own, int kt,
+                                         int valid, float scale2, int lane, RowState<D> (&st)[OWN]) {
+    constexpr int RK = rk_pieces<D>();
+    const int col = lane & 15;
+    const int h4 = lane >> 4;
+    bf16x8 pf[OWN];
+    float alpha[OWN];
+    {
+        bf16x8 fk[2][D / 32];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const uint16_t *krow = sK + (kt * kKeyTile + 16 * hf + col) * RK * 8 + 8 * h4;
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks)
+                fk[hf][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(krow + 32 * ks));
+        }
+        const bool ragged = kt * kKeyTile + kKeyTile > valid;
+#pragma unroll
+        for (int j = 0; j < OWN; ++j) {
+            if (j >= n_own) break;
+            float sc[8];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk[hf][ks], qf[j][ks], acc, 0, 0, 0);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) sc[4 * hf + t] = acc[t] * scale2;
+            }
+            if (ragged) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    sc[t] = kt * kKeyTile + slot_key(h4, t) < valid ? sc[t] : -INFINITY;
+            }
+            float tmax = sc[0];
+#pragma unroll
+            for (int t = 1; t < 8; ++t) tmax = fmaxf(tmax, sc[t]);
+            tmax = fmaxf(tmax, xchg_f<4>(tmax));
+            tmax = fmaxf(tmax, xchg_f<5>(tmax));
+            const float m_new = fmaxf(st[j].m, tmax);
+            alpha[j] = __builtin_amdgcn_exp2f(st[j].m - m_new);
+            float ps = 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float p = __builtin_amdgcn_exp2f(sc[t] - m_new);
+                ps += p;
+                pf[j][t] = static_cast<__bf16>(p);  // round to nearest even
+            }
+            st[j].l = st[j].l * alpha[j] + ps;
+            st[j].m = m_new;
+        }
+    }
+    bf16x8 fv[D / 16];
+    read_vt<D>(sV, kt, lane, fv);
+#pragma unroll
+    for (int j = 0; j < OWN; ++j) {
+        if (j >= n_own) break;
+        // the running max rarely moves after the first tiles: rescale only then
+        if (__ballot(alpha[j] != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) st[j].o[dt] *= alpha[j];
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+            st[j].o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fv[dt], pf[j], st[j].o[dt], 0, 0, 0);
+    }
+}
+
+template <int D, int OWN>
+__global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_ctx,
+    const uint16_t *__restrict__ v_ctx, const int64_t *__restrict__ ctx_offsets,
+    const int32_t *__restrict__ n_nodes, int batch, int nq_max, int hq, int hkv, int group, int n_rg,
+    int chunk, float scale2, float *__restrict__ ws, int64_t prow_total) {
+    // two buffers, each K then V of one sub-chunk; the merge scratch of
+    // split mode reuses them once no load is in flight
+    __shared__ __attribute__((aligned(16))) uint16_t sbuf0[sub_elems<D>()];
+    __shared__ __attribute__((aligned(16))) uint16_t sbuf1[sub_elems<D>()];
+    static_assert(sub_elems<D>() * 2 * 2 >= kAttnWaves * kRowsPerGroup * (D + 2) * 4, "merge scratch");
+    constexpr int kVOff = kSubB * rk_pieces<D>() * 8;  // V rows follow the K rows
+
+    const int64_t c = blockIdx.x / hkv;
+    const int g = static_cast<int>(blockIdx.x % hkv);
+    int b, nch;
+    int64_t k0, k1, cbase;
+    if (!find_chunk(ctx_offsets, batch, chunk, c, b, k0, k1, cbase, nch)) return;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15;
+    const int h4 = lane >> 4;
+
+    // the KV stream goes first: its loads fly while the tree size and the
+    // queries arrive
+    const int64_t ctx0 = ctx_offsets[b];
+    const int64_t kstride = static_cast<int64_t>(hkv) * D;
+    const uint16_t *kbase = k_ctx + (ctx0 * hkv + g) * D;
+    const uint16_t *vbase = v_ctx + (ctx0 * hkv + g) * D;
+    const int n_sub = static_cast<int>((k1 - k0 + kSubB - 1) / kSubB);
+    // sub-chunk sc: keys k0 + sc kSubB .., `valid` of them
+#define TD_SUB_VALID(sc) \
+    static_cast<int>(std::min<int64_t>(kSubB, k1 - k0 - static_cast<int64_t>(sc) * kSubB))
+#define TD_ISSUE(sc, buf)                                                                      \
+    {                                                                                          \
+        const int64_t s0_ = (k0 + static_cast<int64_t>(sc) * kSubB) * kstride;               \
+        issue_rows<D, rk_pieces<D>()>(kbase + s0_, static_cast<int>(kstride), TD_SUB_VALID(sc), \
+                                      buf, wave, lane);                                        \
+        issue_rows<D, rv_pieces<D>()>(vbase + s0_, static_cast<int>(kstride), TD_SUB_VALID(sc), \
+                                      buf + kVOff, wave, lane);                                \
+    }
+    if (n_sub > 0) TD_ISSUE(0, sbuf0);
+    const int rows_b = group * min(n_nodes[b] + 1, nq_max);
+    const int n_rg_b = (rows_b + kRowsPerGroup - 1) / kRowsPerGroup;
+    const uint16_t *qb = q + static_cast<int64_t>(b) * nq_max * hq * D;
+
+    // row blocks of at most 4 OWN row groups, balanced
+    constexpr int kBlock = kAttnWaves * OWN;
+    const int n_blk = (n_rg_b + kBlock - 1) / kBlock;
+    const int per_blk = n_blk > 0 ? (n_rg_b + n_blk - 1) / n_blk : 1;
+    for (int rb0 = 0; rb0 < n_rg_b; rb0 += per_blk) {
+        if (rb0 > 0 && n_sub > 0) TD_ISSUE(0, sbuf0);  // another row block: stream the chunk again
+        const int nrg = min(per_blk, n_rg_b - rb0);
+        // wave -> (row groups, key tiles) assignment
+        //   nrg >= 4: wave w owns row groups w, w + 4, ... of the block, all keys
+        //   nrg <  4: p2 = 1, 2 or 4 row slots; waves share a row group's keys
+        const int p2 = nrg >= 4 ? 4 : (nrg == 1 ? 1 : (nrg == 2 ? 2 : 4));
+        const int kt_step = kAttnWaves / p2;
+        const int kt_first = wave / p2;
+        int own_rg[OWN];
+        int n_own = 0;
+#pragma unroll
+        for (int j = 0; j < OWN; ++j) {
+            const int rl = (nrg >= 4) ? wave + kAttnWaves * j : (j == 0 ? wave % p2 : nrg);
+            own_rg[j] = rl;
+            n_own += rl < nrg ? 1 : 0;
+        }
+        const bool split_mode = nrg < 4;
+
+        // queries of the owned row groups (B operand layout); rows past the
+        // tree read row 0 of the group and are never published
+        RowState<D> st[OWN];
+        bf16x8 qf[OWN][D / 32];
+#pragma unroll
+        for (int j = 0; j < OWN; ++j) {
+            st[j].init();
+            const int r = (rb0 + own_rg[j]) * kRowsPerGroup + col;
+            const bool ok = j < n_own && r < rows_b;
+            const int qi = ok ? r / group : 0;
+            const int qh = g * group + (ok ? r % group : 0);
+            const uint16_t *qrow = qb + (static_cast<int64_t>(qi) * hq + qh) * D;
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks)
+                qf[j][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 32 * ks + 8 * h4));
+        }
+
+#define TD_COMPUTE(buf, sc)                                                                    \
+    {                                                                                          \
+        const int valid = TD_SUB_VALID(sc);                                                    \
+        const int ntiles = (valid + kKeyTile - 1) / kKeyTile;                                  \
+        for (int kt = split_mode ? kt_first : 0; kt < ntiles; kt += split_mode ? kt_step : 1) \
+            tile_dma<D, OWN>(buf, buf + kVOff, qf, n_own, kt, valid, scale2, lane, st);        \
+    }
+        // sub-chunk sc sits in buffer sc % 2; the next one streams meanwhile
+        for (int sc = 0; sc < n_sub; sc += 2) {
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of sub-chunk sc have landed
+            __syncthreads();                // everyone's have; buffer 1 is free
+            if (sc + 1 < n_sub) TD_ISSUE(sc + 1, sbuf1);
+            TD_COMPUTE(sbuf0, sc);
+            if (sc + 1 >= n_sub) break;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (sc + 2 < n_sub) TD_ISSUE(sc + 2, sbuf0);
+            TD_COMPUTE(sbuf1, sc + 1);
+        }
+#undef TD_COMPUTE
+        __syncthreads();  // every wave is done with both buffers
+
+        // row sums over the four lane groups
+#pragma unroll
+        for (int j = 0; j < OWN; ++j) {
+            st[j].l += xchg_f<4>(st[j].l);
+            st[j].l += xchg_f<5>(st[j].l);
+        }
+
+        float *wm = ws;
+        float *wl = ws + prow_total;
+        float *wo = ws + 2 * prow_total;
+        if (!split_mode || kt_step == 1) {
+            // each owned row group is complete in this wave: store its rows
+#pragma unroll
+            for (int j = 0; j < OWN; ++j) {
+                if (j >= n_own) break;
+                const int rg = rb0 + own_rg[j];
+                if (rg * kRowsPerGroup + col >= rows_b) continue;
+                const int64_t pr = prow_index(c, g, rg, col, hkv, n_rg);
+                if (h4 == 0) {
+                    wm[pr] = st[j].m;
+                    wl[pr] = st[j].l;
+                }
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt)
+                    *reinterpret_cast<f32x4 *>(&wo[pr * D + 16 * dt + 4 * h4]) = st[j].o[dt];
+            }
+        } else {
+            // split mode: kt_step waves per row group merge through LDS
+            float *mw = reinterpret_cast<float *>(sbuf0);      // [4][16]
+            float *lw = mw + kAttnWaves * kRowsPerGroup;       // [4][16]
+            float *ow = lw + kAttnWaves * kRowsPerGroup;       // [4][16][D]
+            if (n_own > 0) {
+                if (h4 == 0) {
+                    mw[wave * kRowsPerGroup + col] = st[0].m;
+                    lw[wave * kRowsPerGroup + col] = st[0].l;
+                }
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt)
+                    *reinterpret_cast<f32x4 *>(&ow[(wave * kRowsPerGroup + col) * D + 16 * dt + 4 * h4]) =
+                        st[0].o[dt];
+            }
+            __syncthreads();
+            // 16 threads per (row slot, row), each a D/16 slice; slot s merges
+            // waves s, s + p2, ...
+            constexpr int kPer = D / 16;
+            for (int idx = tid; idx < p2 * kRowsPerGroup * 16; idx += kAttnThreads) {
+                const int sl = idx / (kRowsPerGroup * 16);
+                const int r = (idx / 16) % kRowsPerGroup;
+                if (sl >= nrg || (rb0 + sl) * kRowsPerGroup + r >= rows_b) continue;
+                const int ds = (idx % 16) * kPer;
+                float M = -INFINITY;
+                for (int v = sl; v < kAttnWaves; v += p2) M = fmaxf(M, mw[v * kRowsPerGroup + r]);
+                float Ls = 0.f;
+                float acc[kPer];
+#pragma unroll
+                for (int k = 0; k < kPer; ++k) acc[k] = 0.f;
+                for (int v = sl; v < kAttnWaves; v += p2) {
+                    const float mv = mw[v * kRowsPerGroup + r];
+                    const float f = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+                    Ls += f * lw[v * kRowsPerGroup + r];
+#pragma unroll
+                    for (int k = 0; k < kPer; ++k) acc[k] += f * ow[(v * kRowsPerGroup + r) * D + ds + k];
+                }
+                const int64_t pr = prow_index(c, g, rb0 + sl, r, hkv, n_rg);
+                if ((idx % 16) == 0) {
+                    wm[pr] = M;
+                    wl[pr] = Ls;
+                }
+#pragma unroll
+                for (int k = 0; k < kPer; k += 4)
+                    *reinterpret_cast<f32x4 *>(&wo[pr * D + ds + k]) =
+                        f32x4{acc[k], acc[k + 1], acc[k + 2], acc[k + 3]};
+            }
+            __syncthreads();  // LDS is reused by the next row block
+        }
+    }
+#undef TD_ISSUE
+#undef TD_SUB_VALID
 }
 
 // ---------------------------------------------------------------------------
@@ -702,11 +962,39 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
                  const AttnPlan &pl, void *ws, void *out, const AcceptArgs *acc, hipStream_t st) {
     const float scale2 = scale * kLog2e;
     const int64_t prow_total = pl.n_chunks * hkv * pl.n_rg * kRowsPerGroup;
-    hipLaunchKernelGGL((attn_ctx_split<T, D>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)),
-                       dim3(kAttnThreads), 0, st, static_cast<const T *>(q),
-                       static_cast<const T *>(k_ctx), static_cast<const T *>(v_ctx), off, n_nodes,
-                       batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,
-                       static_cast<float *>(ws), prow_total);
+#define TD_SPLIT(OWN)                                                                          \
+    hipLaunchKernelGGL((attn_split_f32<D, OWN>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)), \
+                       dim3(kAttnThreads), 0, st, static_cast<const float *>(q),                \
+                       static_cast<const float *>(k_ctx), static_cast<const float *>(v_ctx), off, n_nodes, \
+                       batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,             \
+                       static_cast<float *>(ws), prow_total)
+#define TD_SPLIT_BF(OWN)                                                                       \
+    hipLaunchKernelGGL((attn_split_bf16<D, OWN>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)), \
+                       dim3(kAttnThreads), 0, st, static_cast<const uint16_t *>(q),             \
+                       static_cast<const uint16_t *>(k_ctx), static_cast<const uint16_t *>(v_ctx), \
+                       off, n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2, \
+                       static_cast<float *>(ws), prow_total)
+    const int own = std::min(pl.own, max_own<T, D>());
+    if constexpr (max_own<T, D>() == 5) {
+        switch (own) {
+        case 1: TD_SPLIT_BF(1); break;
+        case 2: TD_SPLIT_BF(2); break;
+        case 3: TD_SPLIT_BF(3); break;
+        case 4: TD_SPLIT_BF(4); break;
+        default: TD_SPLIT_BF(5); break;
+        }
+    } else if constexpr (max_own<T, D>() == 3) {
+        switch (own) {
+        case 1: TD_SPLIT_BF(1); break;
+        case 2: TD_SPLIT_BF(2); break;
+        default: TD_SPLIT_BF(3); break;
+        }
+    } else {
+        if (own <= 1) TD_SPLIT(1);
+        else TD_SPLIT(2);
+    }
+#undef TD_SPLIT
+#undef TD_SPLIT_BF
     const int blocks_per_bg = (pl.group * nq_max + kCombineRows - 1) / kCombineRows;
     const int64_t blocks = static_cast<int64_t>(batch) * hkv * blocks_per_bg;
     if (acc)

@@ -358,13 +358,13 @@ __device__ __forceinline__ int wave_prefix(int v, int lane, int &total) {
     return off;
 }
 
+// kBatch vectors per thread; indices past the slice repeat its last vector
+// (same cache lines), so every load is issued and the loads in flight can
+// be counted exactly.  Requires last >= 0.
 template <typename T>
-__device__ __forceinline__ void load_batch(u32x4 (&w)[kBatch], const u32x4 *vp, int i0, int nvec) {
+__device__ __forceinline__ void load_batch(u32x4 (&w)[kBatch], const u32x4 *vp, int i0, int last) {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        const int i = i0 + u * kTopkThreads;
-        if (i < nvec) w[u] = __builtin_nontemporal_load(vp + i);
-    }
+    for (int u = 0; u < kBatch; ++u) w[u] = __builtin_nontemporal_load(vp + min(i0 + u * kTopkThreads, last));
 }
 
 // Hand-off protocol (no writer ever waits for its own stores, and no word is
@@ -425,8 +425,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     const int head_id = lo + tid;
     if (has_head) hx[0] = Vec<T>::scalar(rowp + head_id);
     u32x4 wa[kBatch], wb[kBatch];
-    load_batch<T>(wa, vp, tid, nvec);
-    load_batch<T>(wb, vp, tid + kStep, nvec);
+    const int last = nvec - 1;
+    if (nvec > 0) {
+        load_batch<T>(wa, vp, tid, last);
+        load_batch<T>(wb, vp, tid + kStep, last);
+    }
     const bool merger = sp == splits - 1;
     const int PS = PW + 1;  // words per workgroup slot
     uint64_t *slot = W.part + (static_cast<int64_t>(row) * splits + sp) * PS;
@@ -450,7 +453,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     // Pre-filter bound: cut the wave into KM groups of 64/KM lanes; tau = the
     // smallest of the groups' maxima.  The KM group maxima are KM >= K
     // distinct elements >= tau, so the slice's K-th largest is >= tau.
-    const float tau = group_max_min<KM>(lmax);
+    float tau = group_max_min<KM>(lmax);
     if (has_head && hx[0] >= tau) acc.add_cand(hx, head_id, tau);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -476,14 +479,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
             }
         }
     };
-    for (int i = tid + kStep; i < nvec;) {
-        load_batch<T>(wa, vp, i + kStep, nvec);
-        process(wb, i);
-        i += kStep;
-        if (i >= nvec) break;
-        load_batch<T>(wb, vp, i + kStep, nvec);
-        process(wa, i);
-        i += kStep;
+    // The loop runs in step for the whole wave (its lanes' indices differ by
+    // less than kStep), so the bound can be tightened with lane exchanges:
+    // the KM group maxima of the lanes' best candidates are KM distinct
+    // elements seen so far, so the slice's K-th largest is >= their minimum.
+    auto tighten = [&]() {
+        const float head = acc.top.k[0] ? key_value(acc.top.k[0]) : -INFINITY;
+        tau = fmaxf(tau, group_max_min<KM>(head));
+    };
+    // Batch k sits in wb for odd k / kStep, wa for even; each buffer is
+    // refilled with the batch two ahead as soon as it has been processed
+    // (unconditionally: past the slice the loads repeat its last vector).
+    const int wbase = tid & ~(kWave - 1);
+    if (wbase + kStep < nvec) {
+        load_batch<T>(wa, vp, tid + 2 * kStep, last);
+        for (int k = kStep;;) {
+            process(wb, tid + k);
+            load_batch<T>(wb, vp, tid + k + 2 * kStep, last);
+            tighten();
+            k += kStep;
+            if (wbase + k >= nvec) break;
+            process(wa, tid + k);
+            load_batch<T>(wa, vp, tid + k + 2 * kStep, last);
+            tighten();
+            k += kStep;
+            if (wbase + k >= nvec) break;
+        }
     }
     for (int e = tail0 + tid; e < hi; e += kTopkThreads) {
         float x[1] = {Vec<T>::scalar(rowp + e)};

@@ -835,6 +835,39 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
 // ---------------------------------------------------------------------------
 constexpr int kCombineRows = kAttnThreads / kWave;  // rows per workgroup
 
+// N consecutive elements (16-byte aligned) widened to float.
+template <typename T, int N>
+__device__ __forceinline__ void load_slice(const T *p, float (&x)[N]) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int k8 = 0; k8 < N / 8; ++k8) {
+            const u32x4 w = reinterpret_cast<const u32x4 *>(p)[k8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[8 * k8 + 2 * e] = bf16_lo(w[e]);
+                x[8 * k8 + 2 * e + 1] = bf16_hi(w[e]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k4 = 0; k4 < N / 4; ++k4) {
+            const f32x4 w = reinterpret_cast<const f32x4 *>(p)[k4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[4 * k4 + e] = w[e];
+        }
+    }
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+    v += xchg_i<0>(v);
+    v += xchg_i<1>(v);
+    v += xchg_i<2>(v);
+    v += xchg_i<3>(v);
+    v += xchg_i<4>(v);
+    v += xchg_i<5>(v);
+    return v;
+}
+
 // ACC: the grid carries one more workgroup per sequence, whose wave 0 runs
 // the acceptance walk (the verify step's last kernel).
 template <typename T, int D, bool ACC>
@@ -877,75 +910,129 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
         }
         return;
     }
+    // Everything this row needs that does not depend on other loads goes out
+    // first: the query slice, the mask row and the root's key and value
+    // (the root is on every row's path).
+    const T *qrow = q + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + slice * kSlice;
+    const int64_t kv0 = (static_cast<int64_t>(b) * nq_max * hkv + g) * D + slice * kSlice;
+    float qv[kSlice], k0v[kSlice], v0v[kSlice];
+    load_slice<T, kSlice>(qrow, qv);
+    load_slice<T, kSlice>(k_tree + kv0, k0v);
+    load_slice<T, kSlice>(v_tree + kv0, v0v);
+    const int words = (nq_max + 63) / 64;
+    const uint64_t *mrow = mask + (static_cast<int64_t>(b) * nq_max + i) * words;
+    uint64_t mw[4];
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) mw[wd] = wd < words ? mrow[wd] : 0;
 
-    // context partials of this row
-    int64_t cb = 0;
-    for (int s2 = 0; s2 < b; ++s2) cb += chunks_of(ctx_offsets[s2 + 1] - ctx_offsets[s2], chunk);
+    // chunk base of sequence b: the lanes count the chunks of sequences < b
+    int cbl = 0;
+    for (int s2 = lane; s2 < b; s2 += kWave)
+        cbl += static_cast<int>(chunks_of(ctx_offsets[s2 + 1] - ctx_offsets[s2], chunk));
+    const int64_t cb = wave_sum_i(cbl);
     const int nch = static_cast<int>(chunks_of(ctx_offsets[b + 1] - ctx_offsets[b], chunk));
     const int rg = r / kRowsPerGroup;
     const int rr = r % kRowsPerGroup;
     const float *wm = ws;
     const float *wl = ws + prow_total;
     const float *wo = ws + 2 * prow_total;
+
+    // context partials: lane group cg takes chunks cg, cg + 8, ...; up to
+    // kCB of them per trip with all their loads in flight, merged online
+    constexpr int kCB = 4;
     float M = -INFINITY;
-    for (int cc = cg; cc < nch; cc += 8) M = fmaxf(M, wm[prow_index(cb + cc, g, rg, rr, hkv, n_rg)]);
-    M = wave_max(M);
     float Lsum = 0.f;
     float acc[kSlice];
 #pragma unroll
     for (int k = 0; k < kSlice; ++k) acc[k] = 0.f;
-#pragma unroll 2
-    for (int cc = cg; cc < nch; cc += 8) {
-        const int64_t pr = prow_index(cb + cc, g, rg, rr, hkv, n_rg);
-        const float mc = wm[pr];
-        const float f = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
-        Lsum += wl[pr] * f;
-        const f32x4 *op = reinterpret_cast<const f32x4 *>(&wo[pr * D + slice * kSlice]);
+    for (int c0 = 0; c0 < nch; c0 += 8 * kCB) {
+        float mv[kCB], lv[kCB];
+        f32x4 ov[kCB][kSlice / 4];
 #pragma unroll
-        for (int k4 = 0; k4 < kSlice / 4; ++k4) {
-            const f32x4 o4 = op[k4];
+        for (int u = 0; u < kCB; ++u) {
+            const int cc = min(c0 + cg + 8 * u, nch - 1);  // in range; repeats are dropped below
+            const int64_t pr = prow_index(cb + cc, g, rg, rr, hkv, n_rg);
+            mv[u] = wm[pr];
+            lv[u] = wl[pr];
+            const f32x4 *op = reinterpret_cast<const f32x4 *>(&wo[pr * D + slice * kSlice]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[4 * k4 + e] += o4[e] * f;
+            for (int k4 = 0; k4 < kSlice / 4; ++k4) ov[u][k4] = op[k4];
+        }
+        float mb = M;
+#pragma unroll
+        for (int u = 0; u < kCB; ++u)
+            if (c0 + cg + 8 * u < nch) mb = fmaxf(mb, mv[u]);
+        if (mb != -INFINITY) {
+            const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mb);
+            Lsum *= fo;
+#pragma unroll
+            for (int k = 0; k < kSlice; ++k) acc[k] *= fo;
+#pragma unroll
+            for (int u = 0; u < kCB; ++u) {
+                if (c0 + cg + 8 * u >= nch || mv[u] == -INFINITY) continue;
+                const float f = __builtin_amdgcn_exp2f(mv[u] - mb);
+                Lsum += f * lv[u];
+#pragma unroll
+                for (int k4 = 0; k4 < kSlice / 4; ++k4)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[4 * k4 + e] += f * ov[u][k4][e];
+            }
+            M = mb;
         }
     }
-    Lsum += xchg_f<0>(Lsum);
-    Lsum += xchg_f<1>(Lsum);
-    Lsum += xchg_f<2>(Lsum);
+    // merge the 8 chunk groups (levels 0..2 of the lane exchanges)
+    {
+        float Mg = M;
+        Mg = fmaxf(Mg, xchg_f<0>(Mg));
+        Mg = fmaxf(Mg, xchg_f<1>(Mg));
+        Mg = fmaxf(Mg, xchg_f<2>(Mg));
+        const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mg);
+        Lsum *= f;
+        Lsum += xchg_f<0>(Lsum);
+        Lsum += xchg_f<1>(Lsum);
+        Lsum += xchg_f<2>(Lsum);
 #pragma unroll
-    for (int k = 0; k < kSlice; ++k) {
-        acc[k] += xchg_f<0>(acc[k]);
-        acc[k] += xchg_f<1>(acc[k]);
-        acc[k] += xchg_f<2>(acc[k]);
+        for (int k = 0; k < kSlice; ++k) {
+            acc[k] *= f;
+            acc[k] += xchg_f<0>(acc[k]);
+            acc[k] += xchg_f<1>(acc[k]);
+            acc[k] += xchg_f<2>(acc[k]);
+        }
+        M = Mg;
     }
 
-    // tree keys on the root path of i (mask row), one dot product per bit
-    const T *qrow = q + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + slice * kSlice;
-    float qv[kSlice];
+    // tree keys on the root path of i (mask row), one dot product per bit;
+    // the root's key and value are already in registers
+    auto add_key = [&](const float (&kk)[kSlice], const float (&vv)[kSlice]) {
+        float dot = 0.f;
 #pragma unroll
-    for (int k = 0; k < kSlice; ++k) qv[k] = to_f32<T>(qrow[k]);
-    const int words = (nq_max + 63) / 64;
-    const uint64_t *mrow = mask + (static_cast<int64_t>(b) * nq_max + i) * words;
-    for (int wd = 0; wd < words; ++wd) {
-        uint64_t bits = mrow[wd];
+        for (int k = 0; k < kSlice; ++k) dot += qv[k] * kk[k];
+        dot += xchg_f<3>(dot);
+        dot += xchg_f<4>(dot);
+        dot += xchg_f<5>(dot);
+        const float sc = dot * scale2;
+        const float Mn = fmaxf(M, sc);
+        const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        const float fn = __builtin_amdgcn_exp2f(sc - Mn);
+        Lsum = Lsum * fo + fn;
+#pragma unroll
+        for (int k = 0; k < kSlice; ++k) acc[k] = acc[k] * fo + vv[k] * fn;
+        M = Mn;
+    };
+    if (mw[0] & 1ull) add_key(k0v, v0v);
+    mw[0] &= ~1ull;
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+        uint64_t bits = mw[wd];
         while (bits) {
             const int j = wd * 64 + __ffsll(static_cast<long long>(bits)) - 1;
             bits &= bits - 1;
             if (j >= nq_max) break;  // bits beyond the tree rows are ignored
             const int64_t kv = ((static_cast<int64_t>(b) * nq_max + j) * hkv + g) * D + slice * kSlice;
-            float dot = 0.f;
-#pragma unroll
-            for (int k = 0; k < kSlice; ++k) dot += qv[k] * to_f32<T>(k_tree[kv + k]);
-            dot += xchg_f<3>(dot);
-            dot += xchg_f<4>(dot);
-            dot += xchg_f<5>(dot);
-            const float sc = dot * scale2;
-            const float Mn = fmaxf(M, sc);
-            const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-            const float fn = __builtin_amdgcn_exp2f(sc - Mn);
-            Lsum = Lsum * fo + fn;
-#pragma unroll
-            for (int k = 0; k < kSlice; ++k) acc[k] = acc[k] * fo + to_f32<T>(v_tree[kv + k]) * fn;
-            M = Mn;
+            float kk[kSlice], vv[kSlice];
+            load_slice<T, kSlice>(k_tree + kv, kk);
+            load_slice<T, kSlice>(v_tree + kv, vv);
+            add_key(kk, vv);
         }
     }
     if (cg == 0) {

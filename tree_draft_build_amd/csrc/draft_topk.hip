@@ -679,7 +679,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     }
     const float M = wave_max(ml);
     const double c = (ml == -INFINITY) ? 0.0
-                                       : ssum * exp2(static_cast<double>(ml) - static_cast<double>(M));
+                                       : ssum * static_cast<double>(__builtin_amdgcn_exp2f(ml - M));
     const double S = wave_sum(c);
     constexpr double kLn2 = 0.6931471805599453;
     const double lse = sm_fail ? NAN : static_cast<double>(M) * kLn2 + log(S);
@@ -753,7 +753,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
 // Split plan: enough workgroups to cover the chip, at least kMinSlice
 // elements per workgroup, at most one partial per lane of the merge wave.
 constexpr int kTargetWgs = 1024;
-constexpr int kMinSlice = 4096;
+constexpr int kMinSlice = 8192;
 
 struct TopkPlan {
     int splits;

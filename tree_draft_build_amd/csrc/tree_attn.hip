@@ -493,15 +493,21 @@ __device__ __forceinline__ void issue_rows(const uint16_t *gbase, int ks32, int 
     constexpr int P = D / 8;
     constexpr int kSlots = kSubB * R;
     constexpr int kRounds = (kSlots + kAttnThreads - 1) / kAttnThreads;
+    // slot of this lane in round r: (r 4 + wave) 64 + lane; its (row, piece)
+    // advance by (256 / R, 256 % R) per round
+    int row = (wave * kWave + lane) / R;
+    int piece = (wave * kWave + lane) % R;
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
         const int slot0 = (r * kAttnWaves + wave) * kWave;  // first slot of this wave (uniform)
         if (slot0 >= kSlots) break;
-        const int sl = slot0 + lane;
-        if (sl < kSlots) {
-            const int row = sl / R;
-            const int piece = min(sl % R, P - 1);
-            lds_dma16(gbase + min(row, valid - 1) * ks32 + 8 * piece, lds + 8 * slot0);
+        if (slot0 + lane < kSlots)
+            lds_dma16(gbase + min(row, valid - 1) * ks32 + 8 * min(piece, P - 1), lds + 8 * slot0);
+        row += kAttnThreads / R;
+        piece += kAttnThreads % R;
+        if (piece >= R) {
+            piece -= R;
+            ++row;
         }
     }
 }
@@ -679,10 +685,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
         issue_rows<D, rv_pieces<D>()>(vbase + s0_, static_cast<int>(kstride), TD_SUB_VALID(sc), \
                                       buf + kVOff, wave, lane);                                \
     }
-    if (n_sub > 0) TD_ISSUE(0, sbuf0);
-    const int rows_b = group * min(n_nodes[b] + 1, nq_max);
-    const int n_rg_b = (rows_b + kRowsPerGroup - 1) / kRowsPerGroup;
+    const int nn_b = n_nodes[b];  // in flight while the first loads are issued
     const uint16_t *qb = q + static_cast<int64_t>(b) * nq_max * hq * D;
+    // Row group 0 (tree rows of the root onwards) always has work: its
+    // queries load now rather than after the tree size arrives.
+    bf16x8 q0[D / 32];
+    {
+        const int qi = min(col / group, nq_max - 1);
+        const uint16_t *qrow = qb + (static_cast<int64_t>(qi) * hq + g * group + col % group) * D;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            q0[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 32 * ks + 8 * h4));
+    }
+    if (n_sub > 0) TD_ISSUE(0, sbuf0);
+    const int rows_b = group * min(nn_b + 1, nq_max);
+    const int n_rg_b = (rows_b + kRowsPerGroup - 1) / kRowsPerGroup;
 
     // row blocks of at most 4 OWN row groups, balanced
     constexpr int kBlock = kAttnWaves * OWN;
@@ -714,6 +731,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
 #pragma unroll
         for (int j = 0; j < OWN; ++j) {
             st[j].init();
+            if (rb0 + own_rg[j] == 0) {  // already loaded
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks) qf[j][ks] = q0[ks];
+                continue;
+            }
             const int r = (rb0 + own_rg[j]) * kRowsPerGroup + col;
             const bool ok = j < n_own && r < rows_b;
             const int qi = ok ? r / group : 0;

@@ -338,9 +338,34 @@ def measure(cfg, args, steps, warmup):
     return result, x, inp
 
 
+def _code_tokens(text):
+    """C/C++ source with comments removed and runs of whitespace folded, so
+    that editing a comment does not change the digest."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest():
-    """Digest of the library's sources: profiler counts are only reported for
-    the kernels they were taken on."""
+    """Digest of the library's code (comments and layout ignored): profiler
+    counts are only reported for the kernels they were taken on."""
     import glob
     import hashlib
     h = hashlib.sha256()
@@ -348,8 +373,8 @@ def source_digest():
     files.append(os.path.join(ROOT, "include", "treedraft.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

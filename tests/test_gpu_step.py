@@ -1,7 +1,7 @@
 """GPU: the fused verify step (td_verify_step, three kernels) produces exactly
 what the five stage calls produce on the same inputs, on every workload, and
-keeps doing so over repeated calls on one workspace (its arrival counters
-reset themselves).  The stage calls are checked against the oracle in
+keeps doing so over repeated calls on one workspace (its epoch words advance
+by themselves).  The stage calls are checked against the oracle in
 test_gpu_parity.py; here the oracle also checks the step's attention and
 acceptance directly on one workload."""
 import numpy as np

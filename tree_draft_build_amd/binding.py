@@ -139,8 +139,9 @@ def draft_topk_workspace(batch, block, vocab, K) -> int:
 
 
 def draft_topk_alloc_workspace(batch, block, vocab, K, device):
-    """Zero-filled workspace (its arrival counters must start at zero; each
-    call leaves them zero, so the buffer can be reused)."""
+    """Zero-filled workspace.  It holds per-workgroup epoch words, so one
+    buffer serves any number of calls of the same shape; zero it again
+    before a call with a different batch, block, vocab or K."""
     return torch.zeros(max(16, draft_topk_workspace(batch, block, vocab, K)), dtype=torch.uint8,
                        device=device)
 
@@ -208,8 +209,8 @@ def tree_verify_attn_workspace(batch, nq_max, hq, hkv, head_dim, total_ctx, max_
 
 
 def tree_verify_attn_alloc_workspace(batch, nq_max, hq, hkv, head_dim, total_ctx, max_ctx, device):
-    """Zero-filled workspace (arrival counters start at zero and every call
-    leaves them zero, so the buffer can be reused)."""
+    """Workspace for the per-chunk partials (no state is kept between calls;
+    zero-filled only for tidiness)."""
     return torch.zeros(max(16, tree_verify_attn_workspace(batch, nq_max, hq, hkv, head_dim,
                                                           total_ctx, max_ctx)),
                        dtype=torch.uint8, device=device)

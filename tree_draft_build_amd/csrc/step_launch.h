@@ -12,7 +12,7 @@ namespace td {
 struct TreeParams;
 struct TreeOut;
 
-// top-K workspace bytes (row and sequence arrival counters + partials)
+// top-K workspace bytes (per-workgroup epoch-tagged partials + row records)
 size_t topk_workspace_bytes(int batch, int block, int vocab, int K);
 
 // The verify step's first kernel: top-K of every position, then each

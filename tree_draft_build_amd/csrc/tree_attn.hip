@@ -145,7 +145,7 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 __device__ __forceinline__ int slot_key(int h4, int t) { return t < 4 ? 4 * h4 + t : 12 + 4 * h4 + t; }
 
 // ---------------------------------------------------------------------------
-// attn_ctx_split
+// attn_split_f32 / attn_split_bf16: one key chunk of one KV head
 // ---------------------------------------------------------------------------
 
 // float32 split kernel: K and V key-major in LDS, one sub-chunk at a time.

@@ -16,13 +16,14 @@ __global__ __launch_bounds__(kWave) void build_tree_kernel(const int32_t *__rest
     __shared__ TreeLds t;
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
+    const int root_tok = P.root_token ? P.root_token[b] : -1;
     const int BK = P.block * P.K;
     for (int e = lane; e < BK; e += kWave) {
         t.ids[e] = topk_id[static_cast<int64_t>(b) * BK + e];
         t.lq[e] = topk_logq[static_cast<int64_t>(b) * BK + e];
     }
     wave_lds_sync();
-    build_tree_wave<SLOTS>(t, P, o, b, lane);
+    build_tree_wave<SLOTS>(t, P, o, b, lane, root_tok);
 }
 
 // One thread per (sequence, row): walk the parent chain and set the bits.

@@ -23,11 +23,11 @@
 // wave 0 then ranks the 4 waves' winners.  Should a wave hold more than
 // kWaveCap candidates (rows of many equal logits), a K-round tournament over
 // its lane lists (wave-wide key max per round) takes over.  The
-// workgroup publishes its (m, s, K keys) with agent-scope atomic stores and
-// counts in; the last workgroup of the row bounds the row's K-th key from
-// below by the K-th best partial head, ranks the partial keys above that
-// bound the same way, writes lse = M + log(sum_s s_s exp(m_s - M))
-// (float64), the ids and log q = l - lse, and resets the row's counter.
+// workgroup publishes its (m, s, K keys) as epoch-tagged words; the row's
+// highest slice waits for every tag, bounds the row's K-th key from below by
+// the K-th best partial head, ranks the partial keys above that bound the
+// same way, and writes lse = M + log(sum_s s_s exp(m_s - M)) (float64), the
+// ids and log q = l - lse.
 
 #include <algorithm>
 
@@ -48,6 +48,7 @@ constexpr int kCandCap = 512;  // candidates ranked in LDS by counting
 // splits <= min(64, 1024 / K) is at most 2240 for every K <= 32.
 constexpr int kMergeWords = 2304;
 constexpr int kWaveCap = kCandCap / kTopkWaves;  // per wave
+static_assert(kWaveCap == 2 * kWave, "a wave ranks at most two candidates per lane");
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Order key: larger key = larger logit, then smaller id.  -0 becomes +0 first
@@ -336,10 +337,36 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t x, int j) {
 // Rank by counting in registers: lanes below C hold one key each (distinct
 // when nonzero); the nonzero key beaten by exactly r others is the (r+1)-th
 // best and goes to out[r] when r < K.
-__device__ __forceinline__ void rank_in_wave(uint64_t c, int C, int K, uint64_t *out, int lane) {
+// Lanes C..63 must hold 0 (never counted), so the count runs in unrolled
+// groups of 8 lanes; requires C <= 64.
+__device__ __forceinline__ int count_above(uint64_t c, int C) {
     int rank = 0;
-    for (int j = 0; j < C; ++j) rank += readlane64(c, j) > c;
+    for (int j0 = 0; j0 < C; j0 += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += readlane64(c, j0 + u) > c;
+    }
+    return rank;
+}
+__device__ __forceinline__ void rank_in_wave(uint64_t c, int C, int K, uint64_t *out, int lane) {
+    const int rank = count_above(c, C);
     if (lane < C && c != 0 && rank < K) out[rank] = c;
+}
+// The same for 64 < C <= 128 keys, two per lane: key lane in c0, key
+// 64 + lane in c1 (0 where the key index is >= C).
+__device__ __forceinline__ void rank_in_wave2(uint64_t c0, uint64_t c1, int C, int K, uint64_t *out,
+                                              int lane) {
+    int r0 = 0, r1 = 0;
+#pragma unroll 8
+    for (int j = 0; j < kWave; ++j) {
+        const uint64_t a = readlane64(c0, j);
+        const uint64_t b = readlane64(c1, j);
+        r0 += (a > c0) + (b > c0);
+        r1 += (a > c1) + (b > c1);
+    }
+    if (c0 != 0 && r0 < K) out[r0] = c0;
+    if (c1 != 0 && r1 < K) out[r1] = c1;
+    (void)C;
+    (void)lane;
 }
 
 // Exclusive prefix sum over the wave's lanes of v in [0, 2^BITS), and the
@@ -431,6 +458,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
         load_batch<T>(wb, vp, tid + kStep, last);
     }
     const bool merger = sp == splits - 1;
+    int root_tok = -1;  // the tree builder's root token, wanted only at its end
+    if constexpr (FUSE) {
+        if (merger && row % tp.block == tp.block - 1 && tp.root_token) root_tok = tp.root_token[row / tp.block];
+    }
     const int PS = PW + 1;  // words per workgroup slot
     uint64_t *slot = W.part + (static_cast<int64_t>(row) * splits + sp) * PS;
     uint64_t r_ep = 0;
@@ -533,8 +564,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
         wave_lds_sync();
         if (Cw <= kWave)
             rank_in_wave(lane < Cw ? wcand[lane] : 0, Cw, K, sm_wave[wave], lane);
-        else
-            rank_select(wcand, Cw, K, sm_wave[wave], lane, kWave);
+        else  // Cw <= kWaveCap = 2 * kWave
+            rank_in_wave2(wcand[lane], lane + kWave < Cw ? wcand[lane + kWave] : 0, Cw, K, sm_wave[wave],
+                          lane);
     } else {
         // many equal logits: a K-round tournament over the lane lists
         uint64_t win[KM];
@@ -617,9 +649,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
             if (u < n) sm_part[w0 + tid + u * kTopkThreads] = val[u];
     }
     __syncthreads();
-    if (wave != 0) return;
+
+    // ---- wave 1: the row's normaliser, while wave 0 selects the row's top K ----
+    __shared__ double sm_lse;
+    if (wave == 1) {
+        float ml = -INFINITY;
+        double ssum = 0.0;
+        if (lane < splits) {
+            const uint32_t *w = &sm_part[lane * PW + 2 * K];
+            ml = __uint_as_float(w[0]);
+            ssum = __longlong_as_double(static_cast<long long>(
+                static_cast<uint64_t>(w[1]) | (static_cast<uint64_t>(w[2]) << 32)));
+        }
+        const float M = wave_max(ml);
+        const double c = (ml == -INFINITY) ? 0.0
+                                           : ssum * static_cast<double>(__builtin_amdgcn_exp2f(ml - M));
+        const double S = wave_sum(c);
+        constexpr double kLn2 = 0.6931471805599453;
+        const double lse = sm_fail ? NAN : static_cast<double>(M) * kLn2 + log(S);
+        if (lane == 0) {
+            sm_lse = lse;
+            lse_out[row] = lse;
+        }
+    }
 
     // ---- the row's top K from the partials (wave 0, registers and LDS) ----
+    if (wave == 0) {
     auto part_key = [&](int s, int j) -> uint64_t {
         const uint32_t *w = &sm_part[s * PW + 2 * j];
         return static_cast<uint64_t>(w[0]) | (static_cast<uint64_t>(w[1]) << 32);
@@ -629,17 +684,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     uint64_t tau_key = 0;
     if (splits >= K) {
         const uint64_t hd = lane < splits ? part_key(lane, 0) : 0;
-        int rank = 0;
-        for (int j = 0; j < splits; ++j) rank += readlane64(hd, j) > hd;
+        const int rank = count_above(hd, splits);
         const uint64_t at = __ballot(lane < splits && rank == K - 1);
         if (at) tau_key = readlane64(hd, __ffsll(static_cast<long long>(at)) - 1);
     }
     const uint64_t below = (1ull << lane) - 1;
-    const int PK = splits * K;
+    // lane e of a trip reads key e % KM of partial e / KM (KM >= K)
+    const int PK = splits * KM;
     int C2 = 0;
     for (int e0 = 0; e0 < PK; e0 += kWave) {
         const int e = e0 + lane;
-        const uint64_t k = e < PK ? part_key(e / K, e % K) : 0;
+        const uint64_t k = (e < PK && e % KM < K) ? part_key(e / KM, e % KM) : 0;
         const bool take = k != 0 && k >= tau_key;
         const uint64_t m = __ballot(take);
         const int o = C2 + __popcll(m & below);
@@ -666,23 +721,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
 #pragma unroll
             for (int j = 0; j < KM; ++j) sm_win[j] = win[j];
     }
-    wave_lds_sync();
+    }  // wave 0
+    __syncthreads();  // every wave is still resident here
+    if (wave != 0) return;
 
-    // ---- the row's normaliser and outputs (wave 0) ----
-    float ml = -INFINITY;
-    double ssum = 0.0;
-    if (lane < splits) {
-        const uint32_t *w = &sm_part[lane * PW + 2 * K];
-        ml = __uint_as_float(w[0]);
-        ssum = __longlong_as_double(static_cast<long long>(
-            static_cast<uint64_t>(w[1]) | (static_cast<uint64_t>(w[2]) << 32)));
-    }
-    const float M = wave_max(ml);
-    const double c = (ml == -INFINITY) ? 0.0
-                                       : ssum * static_cast<double>(__builtin_amdgcn_exp2f(ml - M));
-    const double S = wave_sum(c);
-    constexpr double kLn2 = 0.6931471805599453;
-    const double lse = sm_fail ? NAN : static_cast<double>(M) * kLn2 + log(S);
+    // ---- the row's outputs (wave 0) ----
+    const double lse = sm_lse;
     int32_t id = -1;
     double lq = 0.0;
     if (lane < K) {
@@ -692,7 +736,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
         topk_id[static_cast<int64_t>(row) * K + lane] = id;
         topk_logq[static_cast<int64_t>(row) * K + lane] = lq;
     }
-    if (lane == 0) lse_out[row] = lse;
     if constexpr (FUSE) {
         // leave the row's results for the sequence's tree builder (the merger
         // of the sequence's last row, which keeps its own row in LDS)
@@ -745,7 +788,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
             }
         }
         wave_lds_sync();
-        build_tree_wave<SLOTS>(tl, tp, to, b, lane);
+        build_tree_wave<SLOTS>(tl, tp, to, b, lane, root_tok);
         if (lane == 0 && !ok) to.n_nodes[b] = -1;
     }
 }

@@ -83,9 +83,11 @@ __host__ __device__ inline int tree_slots(int n_max) {
 
 // Build sequence b's tree with one wavefront from the tables in t.ids/t.lq
 // (already in LDS, ordered by (position, rank)).  Writes every output array
-// of sequence b, and its mask rows when o.mask is set.
+// of sequence b, and its mask rows when o.mask is set.  root_tok is the
+// token of node 0 (the caller loads it early; it is needed only at the end).
 template <int SLOTS>
-__device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &o, int b, int lane) {
+__device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &o, int b, int lane,
+                                int root_tok) {
 #pragma clang fp contract(off)
     const int K = P.K;
     // frontier slots of this lane
@@ -110,7 +112,6 @@ __device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &
     double ahat = P.ahat0;
     double s_now = ahat * P.l_ar / cost_model(0, P.ca, P.cb, P.cc, P.knee);
     if (lane == 0) {
-        t.tok[0] = P.root_token ? P.root_token[b] : -1;
         t.par[0] = -1;
         t.dep[0] = 0;
         t.lr[0] = 0.0;
@@ -213,7 +214,7 @@ __device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &
     const int64_t base = static_cast<int64_t>(b) * W;
     for (int i = lane; i < W; i += kWave) {
         const bool in = i <= n;
-        o.node_token[base + i] = in ? t.tok[i] : -1;
+        o.node_token[base + i] = !in ? -1 : i == 0 ? root_tok : t.tok[i];
         o.node_parent[base + i] = in ? t.par[i] : -1;
         o.node_depth[base + i] = in ? t.dep[i] : -1;
         o.node_logrho[base + i] = in ? t.lr[i] : 0.0;

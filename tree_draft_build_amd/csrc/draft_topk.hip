@@ -17,12 +17,14 @@
 // slice's K-th largest element is >= tau and no element below tau can be in
 // the top K: only elements >= tau enter a lane's list.
 //
-// Selection: each wave compacts its lanes' surviving candidates into LDS and
-// ranks them by counting (a key's rank = number of keys that beat it; keys
-// are distinct), so its K best land in their slots in one parallel pass;
-// wave 0 then ranks the 4 waves' winners.  Should a wave hold more than
-// kWaveCap candidates (rows of many equal logits), a K-round tournament over
-// its lane lists (wave-wide key max per round) takes over.  The
+// Selection: the waves' bounds are pooled (their maximum still bounds the
+// workgroup's K-th largest from below), each wave compacts its lanes' list
+// entries above that bound into its LDS region, and every thread holding a
+// key ranks it by counting the keys that beat it (keys are distinct), so
+// the K best land in their slots in one parallel pass.  Should a wave hold
+// more than kWaveCap candidates (rows of many equal logits), a K-round
+// tournament over its lane lists (wave-wide key max per round) gives its K
+// best instead.  The
 // workgroup publishes its (m, s, K keys) as epoch-tagged words; the row's
 // highest slice waits for every tag, bounds the row's K-th key from below by
 // the K-th best partial head, ranks the partial keys above that bound the
@@ -39,6 +41,7 @@ namespace td {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTopkThreads = 256;
 constexpr int kTopkWaves = kTopkThreads / kWave;
@@ -48,7 +51,7 @@ constexpr int kCandCap = 512;  // candidates ranked in LDS by counting
 // splits <= min(64, 1024 / K) is at most 2240 for every K <= 32.
 constexpr int kMergeWords = 2304;
 constexpr int kWaveCap = kCandCap / kTopkWaves;  // per wave
-static_assert(kWaveCap == 2 * kWave, "a wave ranks at most two candidates per lane");
+static_assert(kWaveCap % 8 == 0 && kWaveCap >= 32, "regions hold whole groups of 8 keys");
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Order key: larger key = larger logit, then smaller id.  -0 becomes +0 first
@@ -303,18 +306,6 @@ struct LaneAcc {
 // Exact top-K of C distinct nonzero keys buf[0..C) (in LDS) by counting: the
 // key beaten by exactly r others is the (r+1)-th best.  out[0..K) must hold 0
 // beforehand (slots stay 0 when C < K).
-// Same, for a buffer that may hold empty (0) slots, which are skipped.
-__device__ __forceinline__ void rank_select_nz(const uint64_t *buf, int C, int K, uint64_t *out,
-                                               int tid, int nthreads) {
-    for (int e = tid; e < C; e += nthreads) {
-        const uint64_t mine = buf[e];
-        if (mine == 0) continue;
-        int rank = 0;
-        for (int u = 0; u < C; ++u) rank += buf[u] > mine;
-        if (rank < K) out[rank] = mine;
-    }
-}
-
 __device__ __forceinline__ void rank_select(const uint64_t *buf, int C, int K, uint64_t *out,
                                             int tid, int nthreads) {
     for (int e = tid; e < C; e += nthreads) {
@@ -351,24 +342,6 @@ __device__ __forceinline__ void rank_in_wave(uint64_t c, int C, int K, uint64_t 
     const int rank = count_above(c, C);
     if (lane < C && c != 0 && rank < K) out[rank] = c;
 }
-// The same for 64 < C <= 128 keys, two per lane: key lane in c0, key
-// 64 + lane in c1 (0 where the key index is >= C).
-__device__ __forceinline__ void rank_in_wave2(uint64_t c0, uint64_t c1, int C, int K, uint64_t *out,
-                                              int lane) {
-    int r0 = 0, r1 = 0;
-#pragma unroll 8
-    for (int j = 0; j < kWave; ++j) {
-        const uint64_t a = readlane64(c0, j);
-        const uint64_t b = readlane64(c1, j);
-        r0 += (a > c0) + (b > c0);
-        r1 += (a > c1) + (b > c1);
-    }
-    if (c0 != 0 && r0 < K) out[r0] = c0;
-    if (c1 != 0 && r1 < K) out[r1] = c1;
-    (void)C;
-    (void)lane;
-}
-
 // Exclusive prefix sum over the wave's lanes of v in [0, 2^BITS), and the
 // wave's total, from one ballot per bit.
 template <int BITS>
@@ -426,8 +399,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
 
     __shared__ float sm_m[kTopkWaves];
     __shared__ double sm_s[kTopkWaves];
-    __shared__ uint64_t sm_cand[kCandCap];
-    __shared__ uint64_t sm_wave[kTopkWaves][KM];
+    __shared__ __align__(16) uint64_t sm_cand[kCandCap];
+    __shared__ float sm_tau[kTopkWaves];
+    __shared__ int sm_cnt[kTopkWaves];
     __shared__ uint64_t sm_win[KM];
     __shared__ uint32_t sm_part[kMergeWords];
     __shared__ uint32_t sm_epoch;
@@ -548,51 +522,79 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     const double contrib =
         (acc.m == -INFINITY) ? 0.0 : acc.s * static_cast<double>(__builtin_amdgcn_exp2f(acc.ml - wml));
     const double ws_sum = wave_sum(contrib);
-    // per wave: compact the lanes' candidates into LDS and rank them
-    int n_l = 0;
-#pragma unroll
-    for (int j = 0; j < KM; ++j) n_l += acc.top.k[j] != 0;
-    constexpr int kCountBits = KM <= 4 ? 3 : KM <= 8 ? 4 : KM <= 16 ? 5 : 6;
-    int Cw = 0;
-    const int off = wave_prefix<kCountBits>(n_l, lane, Cw);
-    uint64_t *wcand = &sm_cand[wave * kWaveCap];
-    if (lane < KM) sm_wave[wave][lane] = 0;
-    if (Cw <= kWaveCap) {
-#pragma unroll
-        for (int j = 0; j < KM; ++j)
-            if (j < n_l) wcand[off + j] = acc.top.k[j];
-        wave_lds_sync();
-        if (Cw <= kWave)
-            rank_in_wave(lane < Cw ? wcand[lane] : 0, Cw, K, sm_wave[wave], lane);
-        else  // Cw <= kWaveCap = 2 * kWave
-            rank_in_wave2(wcand[lane], lane + kWave < Cw ? wcand[lane + kWave] : 0, Cw, K, sm_wave[wave],
-                          lane);
-    } else {
-        // many equal logits: a K-round tournament over the lane lists
-        uint64_t win[KM];
-        wave_select<KM, KM>(acc.top, K, win);
-        if (lane == 0)
-#pragma unroll
-            for (int j = 0; j < KM; ++j) sm_wave[wave][j] = win[j];
-    }
     if (lane == 0) {
         sm_m[wave] = wml;
         sm_s[wave] = ws_sum;
+        sm_tau[wave] = tau;
     }
     if (tid == 0) {
         sm_epoch = static_cast<uint32_t>(r_ep);
         sm_fail = 0;
     }
+    if (tid < KM) sm_win[tid] = 0;
     __syncthreads();
-    // the 4 waves' winners (distinct keys) ranked the same way by wave 0
-    if (wave == 0) {
-        if (lane < KM) sm_win[lane] = 0;
-        if constexpr (kTopkWaves * KM <= kWave) {
-            rank_in_wave(lane < kTopkWaves * KM ? sm_wave[lane / KM][lane % KM] : 0,
-                         kTopkWaves * KM, K, sm_win, lane);
-        } else {
-            wave_lds_sync();
-            rank_select_nz(&sm_wave[0][0], kTopkWaves * KM, K, sm_win, lane, kWave);
+    // Each wave's bound is at most the workgroup's K-th largest element, so
+    // their maximum is one too: only list entries at or above it compete.
+    float tau_wg = sm_tau[0];
+#pragma unroll
+    for (int q = 1; q < kTopkWaves; ++q) tau_wg = fmaxf(tau_wg, sm_tau[q]);
+    int n_l = 0;
+#pragma unroll
+    for (int j = 0; j < KM; ++j) n_l += acc.top.k[j] != 0 && key_value(acc.top.k[j]) >= tau_wg;
+    constexpr int kCountBits = KM <= 4 ? 3 : KM <= 8 ? 4 : KM <= 16 ? 5 : 6;
+    int Cw = 0;
+    const int off = wave_prefix<kCountBits>(n_l, lane, Cw);
+    uint64_t *wcand = &sm_cand[wave * kWaveCap];
+    if (Cw <= kWaveCap) {
+        // the lists are sorted, so the entries that compete come first
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+            if (j < n_l) wcand[off + j] = acc.top.k[j];
+    } else {
+        // many equal logits: the wave's K best by a K-round tournament
+        uint64_t win[KM];
+        wave_select<KM, KM>(acc.top, K, win);
+        if (lane == 0)
+#pragma unroll
+            for (int j = 0; j < KM; ++j) wcand[j] = win[j];
+        Cw = KM;
+    }
+    // pad the region to a multiple of 8 keys with empty (0) keys
+    const int C8 = (Cw + 7) & ~7;
+    if (lane < 8 && Cw + lane < C8) wcand[Cw + lane] = 0;
+    if (lane == 0) sm_cnt[wave] = C8;
+    __syncthreads();
+    // Rank the union by counting: the thread holding a key counts the keys
+    // that beat it (keys are distinct), reading every region with broadcast
+    // LDS loads, and a key beaten by r < K others is the (r+1)-th best.
+    {
+        int nreg[kTopkWaves];
+        int Ct = 0;
+#pragma unroll
+        for (int q = 0; q < kTopkWaves; ++q) {
+            nreg[q] = sm_cnt[q];
+            Ct += nreg[q];
+        }
+        for (int e = tid; e < Ct; e += kTopkThreads) {
+            int q = 0, i = e;
+#pragma unroll
+            for (int r = 0; r + 1 < kTopkWaves; ++r)
+                if (q == r && i >= nreg[r]) {
+                    i -= nreg[r];
+                    q = r + 1;
+                }
+            const uint64_t mine = sm_cand[q * kWaveCap + i];
+            int rank = 0;
+#pragma unroll
+            for (int r = 0; r < kTopkWaves; ++r) {
+                const u64x2 *buf = reinterpret_cast<const u64x2 *>(&sm_cand[r * kWaveCap]);
+                for (int u = 0; u < nreg[r] / 2; u += 4) {
+                    const u64x2 a = buf[u], b = buf[u + 1], c = buf[u + 2], d = buf[u + 3];
+                    rank += (a.x > mine) + (a.y > mine) + (b.x > mine) + (b.y > mine) + (c.x > mine) +
+                            (c.y > mine) + (d.x > mine) + (d.y > mine);
+                }
+            }
+            if (mine != 0 && rank < K) sm_win[rank] = mine;
         }
     }
     __syncthreads();

@@ -303,20 +303,17 @@ struct LaneAcc {
     }
 };
 
-// Exact top-K of C distinct nonzero keys buf[0..C) (in LDS) by counting: the
-// key beaten by exactly r others is the (r+1)-th best.  out[0..K) must hold 0
-// beforehand (slots stay 0 when C < K).
-__device__ __forceinline__ void rank_select(const uint64_t *buf, int C, int K, uint64_t *out,
-                                            int tid, int nthreads) {
-    for (int e = tid; e < C; e += nthreads) {
-        const uint64_t mine = buf[e];
-        int rank = 0;
-        int u = 0;
-        for (; u + 4 <= C; u += 4)
-            rank += (buf[u] > mine) + (buf[u + 1] > mine) + (buf[u + 2] > mine) + (buf[u + 3] > mine);
-        for (; u < C; ++u) rank += buf[u] > mine;
-        if (rank < K) out[rank] = mine;
+// Number of keys in buf[0..n8) that beat x: buf is 16-byte aligned LDS, n8 a
+// multiple of 8, and every lane of the wave reads the same addresses
+// (broadcast loads, no bank conflicts).
+__device__ __forceinline__ int count_above_lds(const uint64_t *buf, int n8, uint64_t x) {
+    const u64x2 *b = reinterpret_cast<const u64x2 *>(buf);
+    int r = 0;
+    for (int u = 0; u < n8 / 2; u += 4) {
+        const u64x2 a = b[u], c = b[u + 1], d = b[u + 2], e = b[u + 3];
+        r += (a.x > x) + (a.y > x) + (c.x > x) + (c.y > x) + (d.x > x) + (d.y > x) + (e.x > x) + (e.y > x);
     }
+    return r;
 }
 
 __device__ __forceinline__ uint64_t readlane64(uint64_t x, int j) {
@@ -325,23 +322,6 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t x, int j) {
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// Rank by counting in registers: lanes below C hold one key each (distinct
-// when nonzero); the nonzero key beaten by exactly r others is the (r+1)-th
-// best and goes to out[r] when r < K.
-// Lanes C..63 must hold 0 (never counted), so the count runs in unrolled
-// groups of 8 lanes; requires C <= 64.
-__device__ __forceinline__ int count_above(uint64_t c, int C) {
-    int rank = 0;
-    for (int j0 = 0; j0 < C; j0 += 8) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) rank += readlane64(c, j0 + u) > c;
-    }
-    return rank;
-}
-__device__ __forceinline__ void rank_in_wave(uint64_t c, int C, int K, uint64_t *out, int lane) {
-    const int rank = count_above(c, C);
-    if (lane < C && c != 0 && rank < K) out[rank] = c;
-}
 // Exclusive prefix sum over the wave's lanes of v in [0, 2^BITS), and the
 // wave's total, from one ballot per bit.
 template <int BITS>
@@ -401,6 +381,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     __shared__ double sm_s[kTopkWaves];
     __shared__ __align__(16) uint64_t sm_cand[kCandCap];
     __shared__ float sm_tau[kTopkWaves];
+    __shared__ __align__(16) uint64_t sm_heads[kWave];
     __shared__ int sm_cnt[kTopkWaves];
     __shared__ uint64_t sm_win[KM];
     __shared__ uint32_t sm_part[kMergeWords];
@@ -586,14 +567,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
             const uint64_t mine = sm_cand[q * kWaveCap + i];
             int rank = 0;
 #pragma unroll
-            for (int r = 0; r < kTopkWaves; ++r) {
-                const u64x2 *buf = reinterpret_cast<const u64x2 *>(&sm_cand[r * kWaveCap]);
-                for (int u = 0; u < nreg[r] / 2; u += 4) {
-                    const u64x2 a = buf[u], b = buf[u + 1], c = buf[u + 2], d = buf[u + 3];
-                    rank += (a.x > mine) + (a.y > mine) + (b.x > mine) + (b.y > mine) + (c.x > mine) +
-                            (c.y > mine) + (d.x > mine) + (d.y > mine);
-                }
-            }
+            for (int r = 0; r < kTopkWaves; ++r) rank += count_above_lds(&sm_cand[r * kWaveCap], nreg[r], mine);
             if (mine != 0 && rank < K) sm_win[rank] = mine;
         }
     }
@@ -675,54 +649,60 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
         }
     }
 
-    // ---- the row's top K from the partials (wave 0, registers and LDS) ----
+    // ---- the row's top K from the partials (wave 0, broadcast LDS counts) ----
     if (wave == 0) {
-    auto part_key = [&](int s, int j) -> uint64_t {
-        const uint32_t *w = &sm_part[s * PW + 2 * j];
-        return static_cast<uint64_t>(w[0]) | (static_cast<uint64_t>(w[1]) << 32);
-    };
-    // tau_key = K-th best of the partials' heads bounds the row's K-th best
-    // from below; only keys >= tau_key can be in the row's top K.
-    uint64_t tau_key = 0;
-    if (splits >= K) {
+        auto part_key = [&](int s, int j) -> uint64_t {
+            const uint32_t *w = &sm_part[s * PW + 2 * j];
+            return static_cast<uint64_t>(w[0]) | (static_cast<uint64_t>(w[1]) << 32);
+        };
+        // tau_key = K-th best of the partials' heads bounds the row's K-th
+        // best from below; only keys >= tau_key can be in the row's top K.
         const uint64_t hd = lane < splits ? part_key(lane, 0) : 0;
-        const int rank = count_above(hd, splits);
-        const uint64_t at = __ballot(lane < splits && rank == K - 1);
-        if (at) tau_key = readlane64(hd, __ffsll(static_cast<long long>(at)) - 1);
-    }
-    const uint64_t below = (1ull << lane) - 1;
-    // lane e of a trip reads key e % KM of partial e / KM (KM >= K)
-    const int PK = splits * KM;
-    int C2 = 0;
-    for (int e0 = 0; e0 < PK; e0 += kWave) {
-        const int e = e0 + lane;
-        const uint64_t k = (e < PK && e % KM < K) ? part_key(e / KM, e % KM) : 0;
-        const bool take = k != 0 && k >= tau_key;
-        const uint64_t m = __ballot(take);
-        const int o = C2 + __popcll(m & below);
-        if (take && o < kCandCap) sm_cand[o] = k;
-        C2 += __popcll(m);
-    }
-    if (lane < KM) sm_win[lane] = 0;
-    wave_lds_sync();
-    if (C2 <= kWave) {
-        rank_in_wave(lane < C2 ? sm_cand[lane] : 0, C2, K, sm_win, lane);
-    } else if (C2 <= kCandCap) {
-        rank_select(sm_cand, C2, K, sm_win, lane, kWave);
-    } else {
-        // many equal logits: tournament over the partial lists
-        KeyList<KM> t;
-        t.init();
-        if (lane < splits)
+        sm_heads[lane] = hd;  // splits <= 64; zeros pad to a multiple of 8
+        wave_lds_sync();
+        uint64_t tau_key = 0;
+        if (splits >= K) {
+            const int rank = count_above_lds(sm_heads, (splits + 7) & ~7, hd);
+            const uint64_t at = __ballot(lane < splits && rank == K - 1);
+            if (at) tau_key = readlane64(hd, __ffsll(static_cast<long long>(at)) - 1);
+        }
+        const uint64_t below = (1ull << lane) - 1;
+        // lane e of a trip reads key e % KM of partial e / KM (KM >= K)
+        const int PK = splits * KM;
+        int C2 = 0;
+        for (int e0 = 0; e0 < PK; e0 += kWave) {
+            const int e = e0 + lane;
+            const uint64_t k = (e < PK && e % KM < K) ? part_key(e / KM, e % KM) : 0;
+            const bool take = k != 0 && k >= tau_key;
+            const uint64_t m = __ballot(take);
+            const int o = C2 + __popcll(m & below);
+            if (take && o < kCandCap) sm_cand[o] = k;
+            C2 += __popcll(m);
+        }
+        if (lane < KM) sm_win[lane] = 0;
+        if (C2 <= kCandCap) {
+            const int C8 = (C2 + 7) & ~7;
+            for (int p = C2 + lane; p < C8; p += kWave) sm_cand[p] = 0;
+            wave_lds_sync();
+            for (int e = lane; e < C2; e += kWave) {
+                const uint64_t mine = sm_cand[e];
+                const int rank = count_above_lds(sm_cand, C8, mine);
+                if (rank < K) sm_win[rank] = mine;
+            }
+        } else {
+            // many equal logits: tournament over the partial lists
+            KeyList<KM> t;
+            t.init();
+            if (lane < splits)
 #pragma unroll
-            for (int j = 0; j < KM; ++j)
-                if (j < K) t.k[j] = part_key(lane, j);
-        uint64_t win[KM];
-        wave_select<KM, KM>(t, K, win);
-        if (lane == 0)
+                for (int j = 0; j < KM; ++j)
+                    if (j < K) t.k[j] = part_key(lane, j);
+            uint64_t win[KM];
+            wave_select<KM, KM>(t, K, win);
+            if (lane == 0)
 #pragma unroll
-            for (int j = 0; j < KM; ++j) sm_win[j] = win[j];
-    }
+                for (int j = 0; j < KM; ++j) sm_win[j] = win[j];
+        }
     }  // wave 0
     __syncthreads();  // every wave is still resident here
     if (wave != 0) return;

@@ -121,30 +121,38 @@ __device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &
         // lane-local best slot
         double bl = f_lr[0];
         uint32_t bk = f_key[0];
+        double wl;
+        uint32_t wk;
+        if (n == 0) {
+            // the frontier holds entry 0 alone (lane 0, slot 0)
+            wl = t.lq[0];
+            wk = pack_key(1, t.ids[0], 0);
+        } else {
 #pragma unroll
-        for (int s = 1; s < SLOTS; ++s)
-            if (precedes(f_lr[s], f_key[s], bl, bk)) {
-                bl = f_lr[s];
-                bk = f_key[s];
-            }
-        // wave-wide best (register butterfly)
-        double wl = bl;
-        uint32_t wk = bk;
+            for (int s = 1; s < SLOTS; ++s)
+                if (precedes(f_lr[s], f_key[s], bl, bk)) {
+                    bl = f_lr[s];
+                    bk = f_key[s];
+                }
+            // wave-wide best (register butterfly)
+            wl = bl;
+            wk = bk;
 #define TD_TREE_LEVEL(L)                                       \
-        {                                                      \
-            const double ol = xchg_d<L>(wl);                   \
-            const uint32_t ok = xchg<L>(wk);                   \
-            const bool take = precedes(ol, ok, wl, wk);        \
-            wl = take ? ol : wl;                               \
-            wk = take ? ok : wk;                               \
-        }
-        TD_TREE_LEVEL(0)
-        TD_TREE_LEVEL(1)
-        TD_TREE_LEVEL(2)
-        TD_TREE_LEVEL(3)
-        TD_TREE_LEVEL(4)
-        TD_TREE_LEVEL(5)
+            {                                                  \
+                const double ol = xchg_d<L>(wl);               \
+                const uint32_t ok = xchg<L>(wk);               \
+                const bool take = precedes(ol, ok, wl, wk);    \
+                wl = take ? ol : wl;                           \
+                wk = take ? ok : wk;                           \
+            }
+            TD_TREE_LEVEL(0)
+            TD_TREE_LEVEL(1)
+            TD_TREE_LEVEL(2)
+            TD_TREE_LEVEL(3)
+            TD_TREE_LEVEL(4)
+            TD_TREE_LEVEL(5)
 #undef TD_TREE_LEVEL
+        }
         if (wk == kEmptyKey) break;  // no valid candidate left
 
         const double ahat_next = ahat + exp(wl);
@@ -152,7 +160,7 @@ __device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &
         if (P.use_stop && !(s_next > s_now)) break;
 
         // the owner lane removes the entry and publishes its rank
-        const bool owner = (bk == wk) && (bl == wl);
+        const bool owner = n == 0 ? lane == 0 : (bk == wk) && (bl == wl);
         int my_rank = 0;
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s)

@@ -775,8 +775,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     }
 }
 
-// Split plan: enough workgroups to cover the chip, at least kMinSlice
-// elements per workgroup, at most one partial per lane of the merge wave.
+// Split plan.  When every row can be cut into slices of at most kOneRound
+// elements with one workgroup per compute unit, do that: the loads of a
+// slice then all go out at once and no compute unit serves two slices (the
+// latency-bound case of a few rows).  Otherwise enough workgroups to cover
+// the chip a few times over, at least kMinSlice elements per workgroup, and
+// at most one partial per lane of the merge wave.
+constexpr int kCUs = 256;  // compute units of the gfx950 parts
+constexpr int kOneRound = 2 * kBatch * kTopkThreads * 8;  // two batches of bf16 vectors
 constexpr int kTargetWgs = 1024;
 constexpr int kMinSlice = 8192;
 
@@ -786,10 +792,17 @@ struct TopkPlan {
 };
 
 inline TopkPlan topk_plan(int64_t rows, int vocab, int K) {
-    int64_t want = (kTargetWgs + rows - 1) / rows;
-    int64_t cap = (vocab + kMinSlice - 1) / kMinSlice;
-    int64_t most = std::min<int64_t>(64, 1024 / K);
-    int splits = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>({want, cap, most})));
+    const int64_t most = std::min<int64_t>(64, 1024 / K);
+    const int64_t per_cu = kCUs / std::max<int64_t>(1, rows);
+    int64_t want;
+    if (per_cu >= 1 && (vocab + per_cu - 1) / per_cu <= kOneRound) {
+        want = per_cu;
+    } else {
+        const int64_t cover = (kTargetWgs + rows - 1) / rows;
+        const int64_t cap = (vocab + kMinSlice - 1) / kMinSlice;
+        want = std::min(cover, cap);
+    }
+    int splits = static_cast<int>(std::max<int64_t>(1, std::min(want, most)));
     int slice = (vocab + splits - 1) / splits;
     slice = (slice + 7) & ~7;  // 16-byte aligned slices for both element types
     splits = (vocab + slice - 1) / slice;

@@ -796,9 +796,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
             }
         } else {
             // split mode: kt_step waves per row group merge through LDS
+            constexpr int kMP = D + 4;
+            static_assert((2 * kAttnWaves * kRowsPerGroup + kAttnWaves * kRowsPerGroup * kMP) * 4 <=
+                              kSubB * 2 * D * 2,
+                          "the merge area fits one sub-chunk buffer");
             float *mw = reinterpret_cast<float *>(sbuf0);      // [4][16]
             float *lw = mw + kAttnWaves * kRowsPerGroup;       // [4][16]
-            float *ow = lw + kAttnWaves * kRowsPerGroup;       // [4][16][D]
+            float *ow = lw + kAttnWaves * kRowsPerGroup;       // [4][16][kMP]
+            // rows padded by 4 floats: the 16 rows of one 16-byte store land
+            // in distinct banks
             if (n_own > 0) {
                 if (h4 == 0) {
                     mw[wave * kRowsPerGroup + col] = st[0].m;
@@ -806,7 +812,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
                 }
 #pragma unroll
                 for (int dt = 0; dt < D / 16; ++dt)
-                    *reinterpret_cast<f32x4 *>(&ow[(wave * kRowsPerGroup + col) * D + 16 * dt + 4 * h4]) =
+                    *reinterpret_cast<f32x4 *>(&ow[(wave * kRowsPerGroup + col) * kMP + 16 * dt + 4 * h4]) =
                         st[0].o[dt];
             }
             __syncthreads();
@@ -829,7 +835,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
                     const float f = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
                     Ls += f * lw[v * kRowsPerGroup + r];
 #pragma unroll
-                    for (int k = 0; k < kPer; ++k) acc[k] += f * ow[(v * kRowsPerGroup + r) * D + ds + k];
+                    for (int k = 0; k < kPer; ++k) acc[k] += f * ow[(v * kRowsPerGroup + r) * kMP + ds + k];
                 }
                 const int64_t pr = prow_index(c, g, rb0 + sl, r, hkv, n_rg);
                 if ((idx % 16) == 0) {

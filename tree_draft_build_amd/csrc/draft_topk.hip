@@ -705,7 +705,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
         }
     }  // wave 0
     __syncthreads();  // every wave is still resident here
-    if (wave != 0) return;
+    if (wave != 0) {
+        if constexpr (FUSE) {
+            if (row % tp.block == tp.block - 1) {
+                // the sequence's tree builder: while wave 0 builds, the other
+                // waves write the entries past the root as beyond the tree
+                prefill_tree_outputs(tp, to, row / tp.block, tid - kWave, kTopkThreads - kWave);
+                __builtin_amdgcn_s_waitcnt(0);  // acknowledged before wave 0 writes the tree
+                __syncthreads();
+            }
+        }
+        return;
+    }
 
     // ---- the row's outputs (wave 0) ----
     const double lse = sm_lse;
@@ -770,7 +781,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
             }
         }
         wave_lds_sync();
-        build_tree_wave<SLOTS>(tl, tp, to, b, lane, root_tok);
+        build_tree_wave<SLOTS, true>(tl, tp, to, b, lane, root_tok);
         if (lane == 0 && !ok) to.n_nodes[b] = -1;
     }
 }

@@ -85,7 +85,11 @@ __host__ __device__ inline int tree_slots(int n_max) {
 // (already in LDS, ordered by (position, rank)).  Writes every output array
 // of sequence b, and its mask rows when o.mask is set.  root_tok is the
 // token of node 0 (the caller loads it early; it is needed only at the end).
-template <int SLOTS>
+// PREFILLED: the other waves of the workgroup have written every entry and
+// mask row past the root as if beyond the tree (prefill_tree_outputs) and
+// meet this wave at a workgroup barrier before the tree's own entries are
+// written; only entries 0..n are written here then.
+template <int SLOTS, bool PREFILLED = false>
 __device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &o, int b, int lane,
                                 int root_tok) {
 #pragma clang fp contract(off)
@@ -217,10 +221,12 @@ __device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &
         }
     }
     wave_lds_sync();
+    if constexpr (PREFILLED) __syncthreads();  // the prefill stores have landed
 
     const int W = P.n_max + 1;
     const int64_t base = static_cast<int64_t>(b) * W;
-    for (int i = lane; i < W; i += kWave) {
+    const int lim = PREFILLED ? n + 1 : W;  // entries written here
+    for (int i = lane; i < lim; i += kWave) {
         const bool in = i <= n;
         o.node_token[base + i] = !in ? -1 : i == 0 ? root_tok : t.tok[i];
         o.node_parent[base + i] = in ? t.par[i] : -1;
@@ -230,7 +236,7 @@ __device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &
     if (o.mask) {
         // ancestor-or-self rows from the parents in LDS (depth <= block steps)
         const int words = (W + 63) / 64;
-        for (int i = lane; i < W; i += kWave) {
+        for (int i = lane; i < lim; i += kWave) {
             uint64_t w[4] = {0, 0, 0, 0};
             if (i <= n) {
                 int u = i;
@@ -253,6 +259,26 @@ __device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &
         o.n_nodes[b] = n;
         if (o.ahat) o.ahat[b] = ahat;
         if (o.speedup) o.speedup[b] = s_now;
+    }
+}
+
+// The outputs of sequence b past the root as if beyond the tree (token,
+// parent and depth -1, log rho 0, zero mask rows), by threads t0, t0 +
+// nthreads, ...; the tree builder then writes entries 0..n over them.
+__device__ __forceinline__ void prefill_tree_outputs(const TreeParams &P, const TreeOut &o, int b, int t0,
+                                                     int nthreads) {
+    const int W = P.n_max + 1;
+    const int64_t base = static_cast<int64_t>(b) * W;
+    for (int i = 1 + t0; i < W; i += nthreads) {
+        o.node_token[base + i] = -1;
+        o.node_parent[base + i] = -1;
+        o.node_depth[base + i] = -1;
+        o.node_logrho[base + i] = 0.0;
+    }
+    if (o.mask) {
+        const int words = (W + 63) / 64;
+        uint64_t *m = o.mask + (base + 1) * words;
+        for (int k = t0; k < (W - 1) * words; k += nthreads) m[k] = 0;
     }
 }
 

@@ -200,7 +200,9 @@ __device__ __forceinline__ void put_word(uint64_t *p, uint32_t data, uint32_t ta
 constexpr int kSpinLimit = 1 << 16;
 
 // Reads n <= NW tagged words p[idx[u]] (all loads in flight at once) into
-// out[u]; returns false if some word never carried the tag.
+// out[u]; returns false if some word never carried the tag.  Every poll
+// re-reads all words still missing at once, so a late writer costs one
+// round trip after it lands, not one per word.
 template <int NW>
 __device__ __forceinline__ bool get_words(const uint64_t *p, const int (&idx)[NW], int n,
                                           uint32_t tag, uint32_t (&out)[NW]) {
@@ -208,20 +210,22 @@ __device__ __forceinline__ bool get_words(const uint64_t *p, const int (&idx)[NW
 #pragma unroll
     for (int u = 0; u < NW; ++u)
         if (u < n) v[u] = fetch(p + idx[u]);
+    auto tagged = [&](int u) { return u >= n || static_cast<uint32_t>(v[u] >> 32) == tag; };
+    for (int spins = 0; spins < kSpinLimit; ++spins) {
+        bool all = true;
+#pragma unroll
+        for (int u = 0; u < NW; ++u) all = all && tagged(u);
+        if (all) break;
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int u = 0; u < NW; ++u)
+            if (!tagged(u)) v[u] = fetch(p + idx[u]);
+    }
     bool ok = true;
-    int spins = 0;
 #pragma unroll
     for (int u = 0; u < NW; ++u) {
-        out[u] = 0;
-        if (u < n) {
-            while (static_cast<uint32_t>(v[u] >> 32) != tag && spins < kSpinLimit) {
-                __builtin_amdgcn_s_sleep(1);
-                v[u] = fetch(p + idx[u]);
-                ++spins;
-            }
-            ok = ok && static_cast<uint32_t>(v[u] >> 32) == tag;
-            out[u] = static_cast<uint32_t>(v[u]);
-        }
+        ok = ok && tagged(u);
+        out[u] = u < n ? static_cast<uint32_t>(v[u]) : 0;
     }
     return ok;
 }

@@ -930,18 +930,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     const int slice = lane >> 3;
     const int cg = lane & 7;
     T *orow = out + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + slice * kSlice;
-    auto zero_row = [&]() {
+    const int n = min(n_nodes[b], nq_max - 1);
+    if (i > n) {  // a row beyond the tree: zeros
         if (cg == 0) {
 #pragma unroll
             for (int k = 0; k < kSlice; ++k) orow[k] = from_f32<T>(0.f);
         }
-    };
-    const int n_raw = n_nodes[b];
-    // Row 0 belongs to every tree that was built: its loads go out while the
-    // tree size is in flight (it is checked at the end).  Other rows wait
-    // for it, so that rows beyond the tree load nothing.
-    if (i > 0 && i > min(n_raw, nq_max - 1)) {  // a row beyond the tree: zeros
-        zero_row();
         return;
     }
     // Everything this row needs that does not depend on other loads goes out
@@ -960,17 +954,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     for (int wd = 0; wd < 4; ++wd) mw[wd] = wd < words ? mrow[wd] : 0;
 
     // chunk base of sequence b: the lanes count the chunks of sequences < b
-    // (none for the first sequence, whose partial loads need no other load)
-    int64_t cb = 0;
-    if (b > 0) {
-        int cbl = 0;
-        for (int s2 = lane; s2 < b; s2 += kWave)
-            cbl += static_cast<int>(chunks_of(ctx_offsets[s2 + 1] - ctx_offsets[s2], chunk));
-        cb = wave_sum_i(cbl);
-    }
+    int cbl = 0;
+    for (int s2 = lane; s2 < b; s2 += kWave)
+        cbl += static_cast<int>(chunks_of(ctx_offsets[s2 + 1] - ctx_offsets[s2], chunk));
+    const int64_t cb = wave_sum_i(cbl);
     const int nch = static_cast<int>(chunks_of(ctx_offsets[b + 1] - ctx_offsets[b], chunk));
-    // every chunk index below stays inside the workspace, whatever nch is
-    const int cmax = static_cast<int>(prow_total / (static_cast<int64_t>(hkv) * n_rg * kRowsPerGroup) - 1 - cb);
     const int rg = r / kRowsPerGroup;
     const int rr = r % kRowsPerGroup;
     const float *wm = ws;
@@ -985,13 +973,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     float acc[kSlice];
 #pragma unroll
     for (int k = 0; k < kSlice; ++k) acc[k] = 0.f;
-    // (the first trip's loads do not wait for nch: every sequence has a chunk)
-    for (int c0 = 0;; c0 += 8 * kCB) {
+    for (int c0 = 0; c0 < nch; c0 += 8 * kCB) {
         float mv[kCB], lv[kCB];
         f32x4 ov[kCB][kSlice / 4];
 #pragma unroll
         for (int u = 0; u < kCB; ++u) {
-            const int cc = min(c0 + cg + 8 * u, cmax);  // in range; chunks >= nch are dropped below
+            const int cc = min(c0 + cg + 8 * u, nch - 1);  // in range; repeats are dropped below
             const int64_t pr = prow_index(cb + cc, g, rg, rr, hkv, n_rg);
             mv[u] = wm[pr];
             lv[u] = wl[pr];
@@ -1020,7 +1007,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
             }
             M = mb;
         }
-        if (c0 + 8 * kCB >= nch) break;
     }
     // merge the 8 chunk groups (levels 0..2 of the lane exchanges)
     {
@@ -1076,10 +1062,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
             load_slice<T, kSlice>(v_tree + kv, vv);
             add_key(kk, vv);
         }
-    }
-    if (n_raw < 0) {  // no tree (its build failed): row 0 is zeros as well
-        zero_row();
-        return;
     }
     if (cg == 0) {
         const float inv = 1.f / Lsum;

@@ -385,6 +385,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     __shared__ double sm_s[kTopkWaves];
     __shared__ __align__(16) uint64_t sm_cand[kCandCap];
     __shared__ float sm_tau[kTopkWaves];
+    __shared__ __align__(16) float sm_live[kTopkWaves];
+    static_assert(kTopkWaves == 4, "the live bounds are read as one 16-byte vector");
     __shared__ __align__(16) uint64_t sm_heads[kWave];
     __shared__ int sm_cnt[kTopkWaves];
     __shared__ uint64_t sm_win[KM];
@@ -416,6 +418,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
         load_batch<T>(wa, vp, tid, last);
         load_batch<T>(wb, vp, tid + kStep, last);
     }
+    // the waves' live bounds start at -inf for everyone before anyone reads them
+    if (tid < kTopkWaves) sm_live[tid] = -INFINITY;
+    __syncthreads();
     const bool merger = sp == splits - 1;
     int root_tok = -1;  // the tree builder's root token, wanted only at its end
     if constexpr (FUSE) {
@@ -473,9 +478,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     // less than kStep), so the bound can be tightened with lane exchanges:
     // the KM group maxima of the lanes' best candidates are KM distinct
     // elements seen so far, so the slice's K-th largest is >= their minimum.
+    // Each wave's bound also bounds the workgroup's K-th largest, so the waves
+    // share them through LDS (a stale value is still a valid bound): every
+    // wave filters with the best of the four.
     auto tighten = [&]() {
         const float head = acc.top.k[0] ? key_value(acc.top.k[0]) : -INFINITY;
         tau = fmaxf(tau, group_max_min<KM>(head));
+        if (lane == 0) sm_live[wave] = tau;
+        const u32x4 lv = *reinterpret_cast<const u32x4 *>(sm_live);
+        tau = fmaxf(tau, fmaxf(fmaxf(__uint_as_float(lv.x), __uint_as_float(lv.y)),
+                               fmaxf(__uint_as_float(lv.z), __uint_as_float(lv.w))));
     };
     // Batch k sits in wb for odd k / kStep, wa for even; each buffer is
     // refilled with the batch two ahead as soon as it has been processed

@@ -470,7 +470,15 @@ constexpr int kSubB = 128;  // keys per LDS sub-chunk (bf16): 4 tiles, one per w
 
 template <int D> constexpr int rk_pieces() { return D / 8 + 1; }
 template <int D> constexpr int rv_pieces() { return D / 8 + 2; }
-template <int D> constexpr int sub_elems() { return kSubB * (rk_pieces<D>() + rv_pieces<D>()) * 8; }
+// LDS slots of one K or V region: whole rounds of 16-byte loads of the
+// workgroup, so every wave issues the same, compile-time number of direct
+// loads (the compiler can then wait for an earlier load without waiting for
+// them); the slots past the rows take copies of the last row.
+template <int R> constexpr int region_slots() {
+    return (kSubB * R + kAttnThreads - 1) / kAttnThreads * kAttnThreads;
+}
+template <int D> constexpr int sub_k_elems() { return region_slots<rk_pieces<D>()>() * 8; }
+template <int D> constexpr int sub_elems() { return (region_slots<rk_pieces<D>()>() + region_slots<rv_pieces<D>()>()) * 8; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef unsigned u2_t __attribute__((ext_vector_type(2)));
@@ -491,8 +499,7 @@ template <int D, int R>
 __device__ __forceinline__ void issue_rows(const uint16_t *gbase, int ks32, int valid, uint16_t *lds,
                                            int wave, int lane) {
     constexpr int P = D / 8;
-    constexpr int kSlots = kSubB * R;
-    constexpr int kRounds = (kSlots + kAttnThreads - 1) / kAttnThreads;
+    constexpr int kRounds = region_slots<R>() / kAttnThreads;
     // slot of this lane in round r: (r 4 + wave) 64 + lane; its (row, piece)
     // advance by (256 / R, 256 % R) per round
     int row = (wave * kWave + lane) / R;
@@ -500,9 +507,7 @@ __device__ __forceinline__ void issue_rows(const uint16_t *gbase, int ks32, int 
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
         const int slot0 = (r * kAttnWaves + wave) * kWave;  // first slot of this wave (uniform)
-        if (slot0 >= kSlots) break;
-        if (slot0 + lane < kSlots)
-            lds_dma16(gbase + min(row, valid - 1) * ks32 + 8 * min(piece, P - 1), lds + 8 * slot0);
+        lds_dma16(gbase + min(row, valid - 1) * ks32 + 8 * min(piece, P - 1), lds + 8 * slot0);
         row += kAttnThreads / R;
         piece += kAttnThreads % R;
         if (piece >= R) {
@@ -653,7 +658,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
     __shared__ __attribute__((aligned(16))) uint16_t sbuf0[sub_elems<D>()];
     __shared__ __attribute__((aligned(16))) uint16_t sbuf1[sub_elems<D>()];
     static_assert(sub_elems<D>() * 2 * 2 >= kAttnWaves * kRowsPerGroup * (D + 2) * 4, "merge scratch");
-    constexpr int kVOff = kSubB * rk_pieces<D>() * 8;  // V rows follow the K rows
+    constexpr int kVOff = sub_k_elems<D>();  // the V region follows the K region
 
     const int64_t c = blockIdx.x / hkv;
     const int g = static_cast<int>(blockIdx.x % hkv);
@@ -677,13 +682,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
     // sub-chunk sc: keys k0 + sc kSubB .., `valid` of them
 #define TD_SUB_VALID(sc) \
     static_cast<int>(std::min<int64_t>(kSubB, k1 - k0 - static_cast<int64_t>(sc) * kSubB))
+// (a chunk without keys loads copies of the first queries instead: every
+// workgroup issues its first sub-chunk's loads unconditionally)
 #define TD_ISSUE(sc, buf)                                                                      \
     {                                                                                          \
         const int64_t s0_ = (k0 + static_cast<int64_t>(sc) * kSubB) * kstride;               \
-        issue_rows<D, rk_pieces<D>()>(kbase + s0_, static_cast<int>(kstride), TD_SUB_VALID(sc), \
-                                      buf, wave, lane);                                        \
-        issue_rows<D, rv_pieces<D>()>(vbase + s0_, static_cast<int>(kstride), TD_SUB_VALID(sc), \
-                                      buf + kVOff, wave, lane);                                \
+        const int v_ = TD_SUB_VALID(sc);                                                       \
+        issue_rows<D, rk_pieces<D>()>(v_ > 0 ? kbase + s0_ : q, static_cast<int>(kstride),     \
+                                      v_ > 0 ? v_ : 1, buf, wave, lane);                       \
+        issue_rows<D, rv_pieces<D>()>(v_ > 0 ? vbase + s0_ : q, static_cast<int>(kstride),     \
+                                      v_ > 0 ? v_ : 1, buf + kVOff, wave, lane);               \
     }
     const int nn_b = n_nodes[b];  // in flight while the first loads are issued
     const uint16_t *qb = q + static_cast<int64_t>(b) * nq_max * hq * D;
@@ -697,7 +705,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
         for (int ks = 0; ks < D / 32; ++ks)
             q0[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 32 * ks + 8 * h4));
     }
-    if (n_sub > 0) TD_ISSUE(0, sbuf0);
+    TD_ISSUE(0, sbuf0);
     const int rows_b = group * min(nn_b + 1, nq_max);
     const int n_rg_b = (rows_b + kRowsPerGroup - 1) / kRowsPerGroup;
 
@@ -734,6 +742,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
             if (rb0 + own_rg[j] == 0) {  // already loaded
 #pragma unroll
                 for (int ks = 0; ks < D / 32; ++ks) qf[j][ks] = q0[ks];
+                continue;
+            }
+            if (j >= n_own) {  // no row group: never read
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks) qf[j][ks] = bf16x8{};
                 continue;
             }
             const int r = (rb0 + own_rg[j]) * kRowsPerGroup + col;

@@ -999,27 +999,29 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
 #pragma unroll
             for (int k4 = 0; k4 < kSlice / 4; ++k4) ov[u][k4] = op[k4];
         }
+        // Branch-free on purpose: every loaded value is used, so the
+        // compiler keeps all of a trip's loads in flight together instead of
+        // sinking the O loads behind the m loads.  Repeated and empty chunks
+        // get weight 0 (every partial read here was written, so finite).
         float mb = M;
 #pragma unroll
-        for (int u = 0; u < kCB; ++u)
-            if (c0 + cg + 8 * u < nch) mb = fmaxf(mb, mv[u]);
-        if (mb != -INFINITY) {
-            const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mb);
-            Lsum *= fo;
+        for (int u = 0; u < kCB; ++u) mb = fmaxf(mb, c0 + cg + 8 * u < nch ? mv[u] : -INFINITY);
+        const float base = mb == -INFINITY ? 0.f : mb;
+        const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - base);
+        Lsum *= fo;
 #pragma unroll
-            for (int k = 0; k < kSlice; ++k) acc[k] *= fo;
+        for (int k = 0; k < kSlice; ++k) acc[k] *= fo;
 #pragma unroll
-            for (int u = 0; u < kCB; ++u) {
-                if (c0 + cg + 8 * u >= nch || mv[u] == -INFINITY) continue;
-                const float f = __builtin_amdgcn_exp2f(mv[u] - mb);
-                Lsum += f * lv[u];
+        for (int u = 0; u < kCB; ++u) {
+            const bool use = c0 + cg + 8 * u < nch && mv[u] != -INFINITY;
+            const float f = use ? __builtin_amdgcn_exp2f(mv[u] - base) : 0.f;
+            Lsum += f * lv[u];
 #pragma unroll
-                for (int k4 = 0; k4 < kSlice / 4; ++k4)
+            for (int k4 = 0; k4 < kSlice / 4; ++k4)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[4 * k4 + e] += f * ov[u][k4][e];
-            }
-            M = mb;
+                for (int e = 0; e < 4; ++e) acc[4 * k4 + e] += f * ov[u][k4][e];
         }
+        M = mb;
     }
     // merge the 8 chunk groups (levels 0..2 of the lane exchanges)
     {

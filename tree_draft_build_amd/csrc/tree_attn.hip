@@ -944,12 +944,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     const int cg = lane & 7;
     T *orow = out + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + slice * kSlice;
     const int n = min(n_nodes[b], nq_max - 1);
-    // chunk base of sequence b (the lanes count the chunks of sequences < b)
-    // and its chunk count: loaded beside the tree size, not after it
-    int cbl = 0;
-    for (int s2 = lane; s2 < b; s2 += kWave)
-        cbl += static_cast<int>(chunks_of(ctx_offsets[s2 + 1] - ctx_offsets[s2], chunk));
-    const int nch = static_cast<int>(chunks_of(ctx_offsets[b + 1] - ctx_offsets[b], chunk));
     if (i > n) {  // a row beyond the tree: zeros
         if (cg == 0) {
 #pragma unroll
@@ -972,7 +966,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
 #pragma unroll
     for (int wd = 0; wd < 4; ++wd) mw[wd] = wd < words ? mrow[wd] : 0;
 
+    // chunk base of sequence b: the lanes count the chunks of sequences < b
+    int cbl = 0;
+    for (int s2 = lane; s2 < b; s2 += kWave)
+        cbl += static_cast<int>(chunks_of(ctx_offsets[s2 + 1] - ctx_offsets[s2], chunk));
     const int64_t cb = wave_sum_i(cbl);
+    const int nch = static_cast<int>(chunks_of(ctx_offsets[b + 1] - ctx_offsets[b], chunk));
     const int rg = r / kRowsPerGroup;
     const int rr = r % kRowsPerGroup;
     const float *wm = ws;

@@ -78,7 +78,8 @@ def assert_same(a, b, what):
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_fixed", "qwen3_8b", "qwen3_8b_stress",
-                                  "qwen3_8b_masksens", "llama31_8b", "batched", "long"])
+                                  "qwen3_8b_masksens", "llama31_8b", "batched", "long",
+                                  "two_seq_k4", "few_slices"])
 def test_step_equals_stage_calls(td, name):
     cfg = wl.CONFIGS[name]
     print("[case] step vs stages", name, flush=True)
@@ -93,6 +94,33 @@ def test_step_equals_stage_calls(td, name):
         s.run()
         torch.cuda.synchronize()
         assert_same(ref, step_outputs(s), f"{name} call {rep}")
+
+
+def test_step_tied_logits(td):
+    """Positions of all-equal or two-valued logits (many tied keys) through
+    the fused step at the Qwen3-8B shape, against the stage calls."""
+    cfg = wl.CONFIGS["qwen3_8b_stress"]
+    print("[case] step tied logits", flush=True)
+    x, inp, d = inputs(cfg)
+    x = x.copy()
+    x[0, 3, :] = 0x3F00                        # bf16 0.5 everywhere
+    x[0, 10, :] = 0x4000                       # bf16 2.0 ...
+    x[0, 10, 1::3] = 0x4080                    # ... and 4.0 on every third token
+    x[0, 15, :cfg.vocab // 2] = 0xBF80         # -1.0 on the first half
+    d["logits"] = dev(x)
+    ref = modular(td, cfg, d, None)
+    tree_np = {k: ref[k].numpy() for k in ("node_token", "node_parent", "n_nodes")}
+    tg = dev(targets_by_path(cfg, wl.logits_as_f64(x, cfg.logit_dtype), tree_np))
+    ref = modular(td, cfg, d, tg)
+    s = make_step(td, cfg, d)
+    s.set_inputs(d["logits"], d["q"], d["k_ctx"], d["v_ctx"], d["off"], d["k_tree"], d["v_tree"], tg)
+    for rep in range(2):
+        s.run()
+        torch.cuda.synchronize()
+        assert_same(ref, step_outputs(s), f"tied call {rep}")
+    ids = ref["topk_id"].numpy().reshape(cfg.block, cfg.topk)
+    assert list(ids[3]) == list(range(cfg.topk))                # ties go to the smaller id
+    assert list(ids[10]) == [1 + 3 * j for j in range(cfg.topk)]
 
 
 def test_step_alternating_inputs(td):
@@ -150,7 +178,7 @@ def test_step_against_oracle(td):
     np.testing.assert_array_equal(out["bonus_token"].numpy(), b_o)
 
 
-@pytest.mark.parametrize("name", ["tiny", "qwen3_8b_stress", "batched"])
+@pytest.mark.parametrize("name", ["tiny", "qwen3_8b_stress", "batched", "two_seq_k4"])
 def test_step_in_two_calls(td, name):
     """A draft-only call followed by a verify-only call on the same argument
     block and workspace gives the one-call step's results."""

@@ -39,6 +39,7 @@
 // under that permutation.
 
 #include <algorithm>
+#include <type_traits>
 
 #include "step_launch.h"
 #include "td_internal.h"
@@ -647,7 +648,10 @@ __device__ __forceinline__ void tile_dma(const uint16_t *sK, const uint16_t *sV,
     }
 }
 
-template <int D, int OWN>
+// OWN2 > OWN: a tree of more than 4 OWN row groups is processed with OWN2
+// per wave instead (one pass over the keys where OWN would need several);
+// smaller trees keep the lighter OWN code.
+template <int D, int OWN, int OWN2 = OWN>
 __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_ctx,
     const uint16_t *__restrict__ v_ctx, const int64_t *__restrict__ ctx_offsets,
@@ -709,160 +713,167 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
     const int rows_b = group * min(nn_b + 1, nq_max);
     const int n_rg_b = (rows_b + kRowsPerGroup - 1) / kRowsPerGroup;
 
-    // row blocks of at most 4 OWN row groups, balanced
-    constexpr int kBlock = kAttnWaves * OWN;
-    const int n_blk = (n_rg_b + kBlock - 1) / kBlock;
-    const int per_blk = n_blk > 0 ? (n_rg_b + n_blk - 1) / n_blk : 1;
-    for (int rb0 = 0; rb0 < n_rg_b; rb0 += per_blk) {
-        if (rb0 > 0 && n_sub > 0) TD_ISSUE(0, sbuf0);  // another row block: stream the chunk again
-        const int nrg = min(per_blk, n_rg_b - rb0);
-        // wave -> (row groups, key tiles) assignment
-        //   nrg >= 4: wave w owns row groups w, w + 4, ... of the block, all keys
-        //   nrg <  4: p2 = 1, 2 or 4 row slots; waves share a row group's keys
-        const int p2 = nrg >= 4 ? 4 : (nrg == 1 ? 1 : (nrg == 2 ? 2 : 4));
-        const int kt_step = kAttnWaves / p2;
-        const int kt_first = wave / p2;
-        int own_rg[OWN];
-        int n_own = 0;
+    auto row_blocks = [&](auto own_tag) __attribute__((always_inline)) {
+        constexpr int OWNX = decltype(own_tag)::value;
+        // row blocks of at most 4 OWNX row groups, balanced
+        constexpr int kBlock = kAttnWaves * OWNX;
+        const int n_blk = (n_rg_b + kBlock - 1) / kBlock;
+        const int per_blk = n_blk > 0 ? (n_rg_b + n_blk - 1) / n_blk : 1;
+        for (int rb0 = 0; rb0 < n_rg_b; rb0 += per_blk) {
+            if (rb0 > 0 && n_sub > 0) TD_ISSUE(0, sbuf0);  // another row block: stream the chunk again
+            const int nrg = min(per_blk, n_rg_b - rb0);
+            // wave -> (row groups, key tiles) assignment
+            //   nrg >= 4: wave w owns row groups w, w + 4, ... of the block, all keys
+            //   nrg <  4: p2 = 1, 2 or 4 row slots; waves share a row group's keys
+            const int p2 = nrg >= 4 ? 4 : (nrg == 1 ? 1 : (nrg == 2 ? 2 : 4));
+            const int kt_step = kAttnWaves / p2;
+            const int kt_first = wave / p2;
+            int own_rg[OWNX];
+            int n_own = 0;
 #pragma unroll
-        for (int j = 0; j < OWN; ++j) {
-            const int rl = (nrg >= 4) ? wave + kAttnWaves * j : (j == 0 ? wave % p2 : nrg);
-            own_rg[j] = rl;
-            n_own += rl < nrg ? 1 : 0;
-        }
-        const bool split_mode = nrg < 4;
+            for (int j = 0; j < OWNX; ++j) {
+                const int rl = (nrg >= 4) ? wave + kAttnWaves * j : (j == 0 ? wave % p2 : nrg);
+                own_rg[j] = rl;
+                n_own += rl < nrg ? 1 : 0;
+            }
+            const bool split_mode = nrg < 4;
 
-        // queries of the owned row groups (B operand layout); rows past the
-        // tree read row 0 of the group and are never published
-        RowState<D> st[OWN];
-        bf16x8 qf[OWN][D / 32];
+            // queries of the owned row groups (B operand layout); rows past the
+            // tree read row 0 of the group and are never published
+            RowState<D> st[OWNX];
+            bf16x8 qf[OWNX][D / 32];
 #pragma unroll
-        for (int j = 0; j < OWN; ++j) {
-            st[j].init();
-            if (rb0 + own_rg[j] == 0) {  // already loaded
+            for (int j = 0; j < OWNX; ++j) {
+                st[j].init();
+                if (rb0 + own_rg[j] == 0) {  // already loaded
 #pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks) qf[j][ks] = q0[ks];
-                continue;
+                    for (int ks = 0; ks < D / 32; ++ks) qf[j][ks] = q0[ks];
+                    continue;
+                }
+                if (j >= n_own) {  // no row group: never read
+#pragma unroll
+                    for (int ks = 0; ks < D / 32; ++ks) qf[j][ks] = bf16x8{};
+                    continue;
+                }
+                const int r = (rb0 + own_rg[j]) * kRowsPerGroup + col;
+                const bool ok = j < n_own && r < rows_b;
+                const int qi = ok ? r / group : 0;
+                const int qh = g * group + (ok ? r % group : 0);
+                const uint16_t *qrow = qb + (static_cast<int64_t>(qi) * hq + qh) * D;
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks)
+                    qf[j][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 32 * ks + 8 * h4));
             }
-            if (j >= n_own) {  // no row group: never read
-#pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks) qf[j][ks] = bf16x8{};
-                continue;
-            }
-            const int r = (rb0 + own_rg[j]) * kRowsPerGroup + col;
-            const bool ok = j < n_own && r < rows_b;
-            const int qi = ok ? r / group : 0;
-            const int qh = g * group + (ok ? r % group : 0);
-            const uint16_t *qrow = qb + (static_cast<int64_t>(qi) * hq + qh) * D;
-#pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks)
-                qf[j][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 32 * ks + 8 * h4));
-        }
 
 #define TD_COMPUTE(buf, sc)                                                                    \
-    {                                                                                          \
-        const int valid = TD_SUB_VALID(sc);                                                    \
-        const int ntiles = (valid + kKeyTile - 1) / kKeyTile;                                  \
-        for (int kt = split_mode ? kt_first : 0; kt < ntiles; kt += split_mode ? kt_step : 1) \
-            tile_dma<D, OWN>(buf, buf + kVOff, qf, n_own, kt, valid, scale2, lane, st);        \
-    }
-        // sub-chunk sc sits in buffer sc % 2; the next one streams meanwhile
-        for (int sc = 0; sc < n_sub; sc += 2) {
-            __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of sub-chunk sc have landed
-            __syncthreads();                // everyone's have; buffer 1 is free
-            if (sc + 1 < n_sub) TD_ISSUE(sc + 1, sbuf1);
-            TD_COMPUTE(sbuf0, sc);
-            if (sc + 1 >= n_sub) break;
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (sc + 2 < n_sub) TD_ISSUE(sc + 2, sbuf0);
-            TD_COMPUTE(sbuf1, sc + 1);
+        {                                                                                          \
+            const int valid = TD_SUB_VALID(sc);                                                    \
+            const int ntiles = (valid + kKeyTile - 1) / kKeyTile;                                  \
+            for (int kt = split_mode ? kt_first : 0; kt < ntiles; kt += split_mode ? kt_step : 1) \
+                tile_dma<D, OWNX>(buf, buf + kVOff, qf, n_own, kt, valid, scale2, lane, st);        \
         }
+            // sub-chunk sc sits in buffer sc % 2; the next one streams meanwhile
+            for (int sc = 0; sc < n_sub; sc += 2) {
+                __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of sub-chunk sc have landed
+                __syncthreads();                // everyone's have; buffer 1 is free
+                if (sc + 1 < n_sub) TD_ISSUE(sc + 1, sbuf1);
+                TD_COMPUTE(sbuf0, sc);
+                if (sc + 1 >= n_sub) break;
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (sc + 2 < n_sub) TD_ISSUE(sc + 2, sbuf0);
+                TD_COMPUTE(sbuf1, sc + 1);
+            }
 #undef TD_COMPUTE
-        __syncthreads();  // every wave is done with both buffers
+            __syncthreads();  // every wave is done with both buffers
 
-        // row sums over the four lane groups
+            // row sums over the four lane groups
 #pragma unroll
-        for (int j = 0; j < OWN; ++j) {
-            st[j].l += xchg_f<4>(st[j].l);
-            st[j].l += xchg_f<5>(st[j].l);
-        }
+            for (int j = 0; j < OWNX; ++j) {
+                st[j].l += xchg_f<4>(st[j].l);
+                st[j].l += xchg_f<5>(st[j].l);
+            }
 
-        float *wm = ws;
-        float *wl = ws + prow_total;
-        float *wo = ws + 2 * prow_total;
-        if (!split_mode || kt_step == 1) {
-            // each owned row group is complete in this wave: store its rows
+            float *wm = ws;
+            float *wl = ws + prow_total;
+            float *wo = ws + 2 * prow_total;
+            if (!split_mode || kt_step == 1) {
+                // each owned row group is complete in this wave: store its rows
 #pragma unroll
-            for (int j = 0; j < OWN; ++j) {
-                if (j >= n_own) break;
-                const int rg = rb0 + own_rg[j];
-                if (rg * kRowsPerGroup + col >= rows_b) continue;
-                const int64_t pr = prow_index(c, g, rg, col, hkv, n_rg);
-                if (h4 == 0) {
-                    wm[pr] = st[j].m;
-                    wl[pr] = st[j].l;
+                for (int j = 0; j < OWNX; ++j) {
+                    if (j >= n_own) break;
+                    const int rg = rb0 + own_rg[j];
+                    if (rg * kRowsPerGroup + col >= rows_b) continue;
+                    const int64_t pr = prow_index(c, g, rg, col, hkv, n_rg);
+                    if (h4 == 0) {
+                        wm[pr] = st[j].m;
+                        wl[pr] = st[j].l;
+                    }
+#pragma unroll
+                    for (int dt = 0; dt < D / 16; ++dt)
+                        *reinterpret_cast<f32x4 *>(&wo[pr * D + 16 * dt + 4 * h4]) = st[j].o[dt];
                 }
+            } else {
+                // split mode: kt_step waves per row group merge through LDS
+                constexpr int kMP = D + 4;
+                static_assert((2 * kAttnWaves * kRowsPerGroup + kAttnWaves * kRowsPerGroup * kMP) * 4 <=
+                                  kSubB * 2 * D * 2,
+                              "the merge area fits one sub-chunk buffer");
+                float *mw = reinterpret_cast<float *>(sbuf0);      // [4][16]
+                float *lw = mw + kAttnWaves * kRowsPerGroup;       // [4][16]
+                float *ow = lw + kAttnWaves * kRowsPerGroup;       // [4][16][kMP]
+                // rows padded by 4 floats: the 16 rows of one 16-byte store land
+                // in distinct banks
+                if (n_own > 0) {
+                    if (h4 == 0) {
+                        mw[wave * kRowsPerGroup + col] = st[0].m;
+                        lw[wave * kRowsPerGroup + col] = st[0].l;
+                    }
 #pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt)
-                    *reinterpret_cast<f32x4 *>(&wo[pr * D + 16 * dt + 4 * h4]) = st[j].o[dt];
+                    for (int dt = 0; dt < D / 16; ++dt)
+                        *reinterpret_cast<f32x4 *>(&ow[(wave * kRowsPerGroup + col) * kMP + 16 * dt + 4 * h4]) =
+                            st[0].o[dt];
+                }
+                __syncthreads();
+                // 16 threads per (row slot, row), each a D/16 slice; slot s merges
+                // waves s, s + p2, ...
+                constexpr int kPer = D / 16;
+                for (int idx = tid; idx < p2 * kRowsPerGroup * 16; idx += kAttnThreads) {
+                    const int sl = idx / (kRowsPerGroup * 16);
+                    const int r = (idx / 16) % kRowsPerGroup;
+                    if (sl >= nrg || (rb0 + sl) * kRowsPerGroup + r >= rows_b) continue;
+                    const int ds = (idx % 16) * kPer;
+                    float M = -INFINITY;
+                    for (int v = sl; v < kAttnWaves; v += p2) M = fmaxf(M, mw[v * kRowsPerGroup + r]);
+                    float Ls = 0.f;
+                    float acc[kPer];
+#pragma unroll
+                    for (int k = 0; k < kPer; ++k) acc[k] = 0.f;
+                    for (int v = sl; v < kAttnWaves; v += p2) {
+                        const float mv = mw[v * kRowsPerGroup + r];
+                        const float f = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+                        Ls += f * lw[v * kRowsPerGroup + r];
+#pragma unroll
+                        for (int k = 0; k < kPer; ++k) acc[k] += f * ow[(v * kRowsPerGroup + r) * kMP + ds + k];
+                    }
+                    const int64_t pr = prow_index(c, g, rb0 + sl, r, hkv, n_rg);
+                    if ((idx % 16) == 0) {
+                        wm[pr] = M;
+                        wl[pr] = Ls;
+                    }
+#pragma unroll
+                    for (int k = 0; k < kPer; k += 4)
+                        *reinterpret_cast<f32x4 *>(&wo[pr * D + ds + k]) =
+                            f32x4{acc[k], acc[k + 1], acc[k + 2], acc[k + 3]};
+                }
+                __syncthreads();  // LDS is reused by the next row block
             }
-        } else {
-            // split mode: kt_step waves per row group merge through LDS
-            constexpr int kMP = D + 4;
-            static_assert((2 * kAttnWaves * kRowsPerGroup + kAttnWaves * kRowsPerGroup * kMP) * 4 <=
-                              kSubB * 2 * D * 2,
-                          "the merge area fits one sub-chunk buffer");
-            float *mw = reinterpret_cast<float *>(sbuf0);      // [4][16]
-            float *lw = mw + kAttnWaves * kRowsPerGroup;       // [4][16]
-            float *ow = lw + kAttnWaves * kRowsPerGroup;       // [4][16][kMP]
-            // rows padded by 4 floats: the 16 rows of one 16-byte store land
-            // in distinct banks
-            if (n_own > 0) {
-                if (h4 == 0) {
-                    mw[wave * kRowsPerGroup + col] = st[0].m;
-                    lw[wave * kRowsPerGroup + col] = st[0].l;
-                }
-#pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt)
-                    *reinterpret_cast<f32x4 *>(&ow[(wave * kRowsPerGroup + col) * kMP + 16 * dt + 4 * h4]) =
-                        st[0].o[dt];
-            }
-            __syncthreads();
-            // 16 threads per (row slot, row), each a D/16 slice; slot s merges
-            // waves s, s + p2, ...
-            constexpr int kPer = D / 16;
-            for (int idx = tid; idx < p2 * kRowsPerGroup * 16; idx += kAttnThreads) {
-                const int sl = idx / (kRowsPerGroup * 16);
-                const int r = (idx / 16) % kRowsPerGroup;
-                if (sl >= nrg || (rb0 + sl) * kRowsPerGroup + r >= rows_b) continue;
-                const int ds = (idx % 16) * kPer;
-                float M = -INFINITY;
-                for (int v = sl; v < kAttnWaves; v += p2) M = fmaxf(M, mw[v * kRowsPerGroup + r]);
-                float Ls = 0.f;
-                float acc[kPer];
-#pragma unroll
-                for (int k = 0; k < kPer; ++k) acc[k] = 0.f;
-                for (int v = sl; v < kAttnWaves; v += p2) {
-                    const float mv = mw[v * kRowsPerGroup + r];
-                    const float f = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
-                    Ls += f * lw[v * kRowsPerGroup + r];
-#pragma unroll
-                    for (int k = 0; k < kPer; ++k) acc[k] += f * ow[(v * kRowsPerGroup + r) * kMP + ds + k];
-                }
-                const int64_t pr = prow_index(c, g, rb0 + sl, r, hkv, n_rg);
-                if ((idx % 16) == 0) {
-                    wm[pr] = M;
-                    wl[pr] = Ls;
-                }
-#pragma unroll
-                for (int k = 0; k < kPer; k += 4)
-                    *reinterpret_cast<f32x4 *>(&wo[pr * D + ds + k]) =
-                        f32x4{acc[k], acc[k + 1], acc[k + 2], acc[k + 3]};
-            }
-            __syncthreads();  // LDS is reused by the next row block
         }
-    }
+    };
+    if (OWN2 > OWN && n_rg_b > kAttnWaves * OWN)
+        row_blocks(std::integral_constant<int, OWN2>{});
+    else
+        row_blocks(std::integral_constant<int, OWN>{});
 #undef TD_ISSUE
 #undef TD_SUB_VALID
 }
@@ -1098,8 +1109,8 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
                        static_cast<const float *>(k_ctx), static_cast<const float *>(v_ctx), off, n_nodes, \
                        batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,             \
                        static_cast<float *>(ws), prow_total)
-#define TD_SPLIT_BF(OWN)                                                                       \
-    hipLaunchKernelGGL((attn_split_bf16<D, OWN>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)), \
+#define TD_SPLIT_BF(...)                                                                       \
+    hipLaunchKernelGGL((attn_split_bf16<D, __VA_ARGS__>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)), \
                        dim3(kAttnThreads), 0, st, static_cast<const uint16_t *>(q),             \
                        static_cast<const uint16_t *>(k_ctx), static_cast<const uint16_t *>(v_ctx), \
                        off, n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2, \
@@ -1117,7 +1128,12 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
         switch (own) {
         case 1: TD_SPLIT_BF(1); break;
         case 2: TD_SPLIT_BF(2); break;
-        default: TD_SPLIT_BF(3); break;
+        default:
+            // trees of more than 12 row groups take 5 per wave (one pass over
+            // the keys up to 20 row groups), smaller ones 3
+            if (pl.own > 3) TD_SPLIT_BF(3, 5);
+            else TD_SPLIT_BF(3);
+            break;
         }
     } else {
         if (own <= 1) TD_SPLIT(1);

@@ -126,6 +126,13 @@ CONFIGS["qwen3_8b_masksens"] = CONFIGS["qwen3_8b"].replace(
     spike_lo=14.0, spike_hi=20.0)
 CONFIGS["tiny_masksens"] = CONFIGS["tiny_fixed"].replace(
     name="tiny_masksens", index=10, attn_law="mask_sensitive")
+# Few rows cut into one slice per compute unit, as at the Qwen3-8B shape, but
+# two sequences of 8 positions with K = 4 (16 slices per row), and four
+# sequences of 16 positions with fewer slices per row (4) than K = 8.
+CONFIGS["two_seq_k4"] = CONFIGS["tiny_fixed"].replace(name="two_seq_k4", index=13, batch=2)
+CONFIGS["few_slices"] = CONFIGS["tiny_fixed"].replace(
+    name="few_slices", index=14, batch=4, block=16, vocab=65000, logit_dtype="bf16", topk=8,
+    spike_lo=0.0, spike_hi=12.0)
 
 
 def _rng(cfg: Config, tensor: int, seq: int = 0) -> np.random.Generator:

@@ -885,7 +885,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
 // butterfly levels 0..2 (within 8 lanes).  Tree keys: each lane dots its 16
 // dims, levels 3..5 sum the 8 dim slices.
 // ---------------------------------------------------------------------------
-constexpr int kCombineRows = kAttnThreads / kWave;  // rows per workgroup
+constexpr int kCombineRows = kAttnThreads / kWave;  // waves per workgroup
+// When the combine's grid is larger than the chip keeps resident (about 3
+// waves per SIMD at its register use), each wave takes two output rows, r
+// and r + half, of one (sequence, KV head): rows beyond the tree then cost
+// half the waves.  Host and device agree on the split.
+constexpr int64_t kCombineResident = 256 * 4 * 3;
+inline bool combine_two_rows(int64_t waves) { return waves > 2 * kCombineResident; }
+__host__ __device__ inline int combine_half(int rows_per_bg, int two) {
+    return two ? (rows_per_bg + 1) / 2 : rows_per_bg;
+}
+__host__ __device__ inline int combine_blocks(int rows_per_bg, int two) {
+    return (combine_half(rows_per_bg, two) + kCombineRows - 1) / kCombineRows;
+}
 
 // N consecutive elements (16-byte aligned) widened to float.
 template <typename T, int N>
@@ -922,7 +934,7 @@ __device__ __forceinline__ int wave_sum_i(int v) {
 
 // ACC: the grid carries one more workgroup per sequence, whose wave 0 runs
 // the acceptance walk (the verify step's last kernel).
-template <typename T, int D, bool ACC>
+template <typename T, int D, bool ACC, bool TWO>
 __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     const T *__restrict__ q, const int64_t *__restrict__ ctx_offsets, const T *__restrict__ k_tree,
     const T *__restrict__ v_tree, const uint64_t *__restrict__ mask,
@@ -931,7 +943,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     AcceptArgs accept) {
     constexpr int kSlice = D / 8;  // dims per lane group
     const int rows_per_bg = group * nq_max;
-    const int blocks_per_bg = (rows_per_bg + kCombineRows - 1) / kCombineRows;
+    const int half = combine_half(rows_per_bg, TWO);
+    const int blocks_per_bg = combine_blocks(rows_per_bg, TWO);
     if constexpr (ACC) {
         const int64_t first_acc = static_cast<int64_t>(batch) * hkv * blocks_per_bg;
         if (blockIdx.x >= first_acc) {
@@ -948,151 +961,174 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     const int b = blockIdx.x / (blocks_per_bg * hkv);
     const int lane = threadIdx.x & 63;
     const int r = blk * kCombineRows + (threadIdx.x >> 6);
-    if (r >= rows_per_bg) return;
-    const int i = r / group;
-    const int h = g * group + r % group;
+    if (r >= half) return;
     const int slice = lane >> 3;
     const int cg = lane & 7;
-    T *orow = out + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + slice * kSlice;
     const int n = min(n_nodes[b], nq_max - 1);
-    if (i > n) {  // a row beyond the tree: zeros
+    auto out_row = [&](int rr) {
+        const int i = rr / group;
+        const int h = g * group + rr % group;
+        return out + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + slice * kSlice;
+    };
+    auto zero_row = [&](int rr) {
         if (cg == 0) {
+            T *orow = out_row(rr);
 #pragma unroll
             for (int k = 0; k < kSlice; ++k) orow[k] = from_f32<T>(0.f);
         }
+    };
+    auto combine_row = [&](int r) __attribute__((always_inline)) {
+        const int i = r / group;
+        const int h = g * group + r % group;
+        T *orow = out_row(r);
+        // Everything this row needs that does not depend on other loads goes out
+        // first: the query slice, the mask row and the root's key and value
+        // (the root is on every row's path).
+        const T *qrow = q + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + slice * kSlice;
+        const int64_t kv0 = (static_cast<int64_t>(b) * nq_max * hkv + g) * D + slice * kSlice;
+        float qv[kSlice], k0v[kSlice], v0v[kSlice];
+        load_slice<T, kSlice>(qrow, qv);
+        load_slice<T, kSlice>(k_tree + kv0, k0v);
+        load_slice<T, kSlice>(v_tree + kv0, v0v);
+        const int words = (nq_max + 63) / 64;
+        const uint64_t *mrow = mask + (static_cast<int64_t>(b) * nq_max + i) * words;
+        uint64_t mw[4];
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) mw[wd] = wd < words ? mrow[wd] : 0;
+
+        // chunk base of sequence b: the lanes count the chunks of sequences < b
+        int cbl = 0;
+        for (int s2 = lane; s2 < b; s2 += kWave)
+            cbl += static_cast<int>(chunks_of(ctx_offsets[s2 + 1] - ctx_offsets[s2], chunk));
+        const int64_t cb = wave_sum_i(cbl);
+        const int nch = static_cast<int>(chunks_of(ctx_offsets[b + 1] - ctx_offsets[b], chunk));
+        const int rg = r / kRowsPerGroup;
+        const int rr = r % kRowsPerGroup;
+        const float *wm = ws;
+        const float *wl = ws + prow_total;
+        const float *wo = ws + 2 * prow_total;
+
+        // context partials: lane group cg takes chunks cg, cg + 8, ...; up to
+        // kCB of them per trip with all their loads in flight, merged online
+        constexpr int kCB = 4;
+        float M = -INFINITY;
+        float Lsum = 0.f;
+        float acc[kSlice];
+#pragma unroll
+        for (int k = 0; k < kSlice; ++k) acc[k] = 0.f;
+        for (int c0 = 0; c0 < nch; c0 += 8 * kCB) {
+            float mv[kCB], lv[kCB];
+            f32x4 ov[kCB][kSlice / 4];
+#pragma unroll
+            for (int u = 0; u < kCB; ++u) {
+                const int cc = min(c0 + cg + 8 * u, nch - 1);  // in range; repeats are dropped below
+                const int64_t pr = prow_index(cb + cc, g, rg, rr, hkv, n_rg);
+                mv[u] = wm[pr];
+                lv[u] = wl[pr];
+                const f32x4 *op = reinterpret_cast<const f32x4 *>(&wo[pr * D + slice * kSlice]);
+#pragma unroll
+                for (int k4 = 0; k4 < kSlice / 4; ++k4) ov[u][k4] = op[k4];
+            }
+            // Branch-free on purpose: every loaded value is used, so the
+            // compiler keeps all of a trip's loads in flight together instead of
+            // sinking the O loads behind the m loads.  Repeated and empty chunks
+            // get weight 0 (every partial read here was written, so finite).
+            float mb = M;
+#pragma unroll
+            for (int u = 0; u < kCB; ++u) mb = fmaxf(mb, c0 + cg + 8 * u < nch ? mv[u] : -INFINITY);
+            const float base = mb == -INFINITY ? 0.f : mb;
+            const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - base);
+            Lsum *= fo;
+#pragma unroll
+            for (int k = 0; k < kSlice; ++k) acc[k] *= fo;
+#pragma unroll
+            for (int u = 0; u < kCB; ++u) {
+                const bool use = c0 + cg + 8 * u < nch && mv[u] != -INFINITY;
+                const float f = use ? __builtin_amdgcn_exp2f(mv[u] - base) : 0.f;
+                Lsum += f * lv[u];
+#pragma unroll
+                for (int k4 = 0; k4 < kSlice / 4; ++k4)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[4 * k4 + e] += f * ov[u][k4][e];
+            }
+            M = mb;
+        }
+        // merge the 8 chunk groups (levels 0..2 of the lane exchanges)
+        {
+            float Mg = M;
+            Mg = fmaxf(Mg, xchg_f<0>(Mg));
+            Mg = fmaxf(Mg, xchg_f<1>(Mg));
+            Mg = fmaxf(Mg, xchg_f<2>(Mg));
+            const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mg);
+            Lsum *= f;
+            Lsum += xchg_f<0>(Lsum);
+            Lsum += xchg_f<1>(Lsum);
+            Lsum += xchg_f<2>(Lsum);
+#pragma unroll
+            for (int k = 0; k < kSlice; ++k) {
+                acc[k] *= f;
+                acc[k] += xchg_f<0>(acc[k]);
+                acc[k] += xchg_f<1>(acc[k]);
+                acc[k] += xchg_f<2>(acc[k]);
+            }
+            M = Mg;
+        }
+
+        // tree keys on the root path of i (mask row), one dot product per bit;
+        // the root's key and value are already in registers
+        auto add_key = [&](const float (&kk)[kSlice], const float (&vv)[kSlice]) {
+            float dot = 0.f;
+#pragma unroll
+            for (int k = 0; k < kSlice; ++k) dot += qv[k] * kk[k];
+            dot += xchg_f<3>(dot);
+            dot += xchg_f<4>(dot);
+            dot += xchg_f<5>(dot);
+            const float sc = dot * scale2;
+            const float Mn = fmaxf(M, sc);
+            const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+            const float fn = __builtin_amdgcn_exp2f(sc - Mn);
+            Lsum = Lsum * fo + fn;
+#pragma unroll
+            for (int k = 0; k < kSlice; ++k) acc[k] = acc[k] * fo + vv[k] * fn;
+            M = Mn;
+        };
+        if (mw[0] & 1ull) add_key(k0v, v0v);
+        mw[0] &= ~1ull;
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+            uint64_t bits = mw[wd];
+            while (bits) {
+                const int j = wd * 64 + __ffsll(static_cast<long long>(bits)) - 1;
+                bits &= bits - 1;
+                if (j >= nq_max) break;  // bits beyond the tree rows are ignored
+                const int64_t kv = ((static_cast<int64_t>(b) * nq_max + j) * hkv + g) * D + slice * kSlice;
+                float kk[kSlice], vv[kSlice];
+                load_slice<T, kSlice>(k_tree + kv, kk);
+                load_slice<T, kSlice>(v_tree + kv, vv);
+                add_key(kk, vv);
+            }
+        }
+        if (cg == 0) {
+            const float inv = 1.f / Lsum;
+#pragma unroll
+            for (int k = 0; k < kSlice; ++k) orow[k] = from_f32<T>(acc[k] * inv);
+        }
+    };
+    // the wave's second row, r + half, lies beyond a tree that fills at most
+    // half the rows (zeros), so only a larger tree makes the wave merge two
+    // rows.  The zeros go out last: stores count against the same counter
+    // as the loads, and would hold up the first row's waits.
+    const int r2 = r + half;
+    const bool has2 = TWO && r2 < rows_per_bg;
+    if (r / group > n) {  // beyond the tree, and so is r2
+        zero_row(r);
+        if (has2) zero_row(r2);
         return;
     }
-    // Everything this row needs that does not depend on other loads goes out
-    // first: the query slice, the mask row and the root's key and value
-    // (the root is on every row's path).
-    const T *qrow = q + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + slice * kSlice;
-    const int64_t kv0 = (static_cast<int64_t>(b) * nq_max * hkv + g) * D + slice * kSlice;
-    float qv[kSlice], k0v[kSlice], v0v[kSlice];
-    load_slice<T, kSlice>(qrow, qv);
-    load_slice<T, kSlice>(k_tree + kv0, k0v);
-    load_slice<T, kSlice>(v_tree + kv0, v0v);
-    const int words = (nq_max + 63) / 64;
-    const uint64_t *mrow = mask + (static_cast<int64_t>(b) * nq_max + i) * words;
-    uint64_t mw[4];
-#pragma unroll
-    for (int wd = 0; wd < 4; ++wd) mw[wd] = wd < words ? mrow[wd] : 0;
-
-    // chunk base of sequence b: the lanes count the chunks of sequences < b
-    int cbl = 0;
-    for (int s2 = lane; s2 < b; s2 += kWave)
-        cbl += static_cast<int>(chunks_of(ctx_offsets[s2 + 1] - ctx_offsets[s2], chunk));
-    const int64_t cb = wave_sum_i(cbl);
-    const int nch = static_cast<int>(chunks_of(ctx_offsets[b + 1] - ctx_offsets[b], chunk));
-    const int rg = r / kRowsPerGroup;
-    const int rr = r % kRowsPerGroup;
-    const float *wm = ws;
-    const float *wl = ws + prow_total;
-    const float *wo = ws + 2 * prow_total;
-
-    // context partials: lane group cg takes chunks cg, cg + 8, ...; up to
-    // kCB of them per trip with all their loads in flight, merged online
-    constexpr int kCB = 4;
-    float M = -INFINITY;
-    float Lsum = 0.f;
-    float acc[kSlice];
-#pragma unroll
-    for (int k = 0; k < kSlice; ++k) acc[k] = 0.f;
-    for (int c0 = 0; c0 < nch; c0 += 8 * kCB) {
-        float mv[kCB], lv[kCB];
-        f32x4 ov[kCB][kSlice / 4];
-#pragma unroll
-        for (int u = 0; u < kCB; ++u) {
-            const int cc = min(c0 + cg + 8 * u, nch - 1);  // in range; repeats are dropped below
-            const int64_t pr = prow_index(cb + cc, g, rg, rr, hkv, n_rg);
-            mv[u] = wm[pr];
-            lv[u] = wl[pr];
-            const f32x4 *op = reinterpret_cast<const f32x4 *>(&wo[pr * D + slice * kSlice]);
-#pragma unroll
-            for (int k4 = 0; k4 < kSlice / 4; ++k4) ov[u][k4] = op[k4];
-        }
-        // Branch-free on purpose: every loaded value is used, so the
-        // compiler keeps all of a trip's loads in flight together instead of
-        // sinking the O loads behind the m loads.  Repeated and empty chunks
-        // get weight 0 (every partial read here was written, so finite).
-        float mb = M;
-#pragma unroll
-        for (int u = 0; u < kCB; ++u) mb = fmaxf(mb, c0 + cg + 8 * u < nch ? mv[u] : -INFINITY);
-        const float base = mb == -INFINITY ? 0.f : mb;
-        const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - base);
-        Lsum *= fo;
-#pragma unroll
-        for (int k = 0; k < kSlice; ++k) acc[k] *= fo;
-#pragma unroll
-        for (int u = 0; u < kCB; ++u) {
-            const bool use = c0 + cg + 8 * u < nch && mv[u] != -INFINITY;
-            const float f = use ? __builtin_amdgcn_exp2f(mv[u] - base) : 0.f;
-            Lsum += f * lv[u];
-#pragma unroll
-            for (int k4 = 0; k4 < kSlice / 4; ++k4)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[4 * k4 + e] += f * ov[u][k4][e];
-        }
-        M = mb;
-    }
-    // merge the 8 chunk groups (levels 0..2 of the lane exchanges)
-    {
-        float Mg = M;
-        Mg = fmaxf(Mg, xchg_f<0>(Mg));
-        Mg = fmaxf(Mg, xchg_f<1>(Mg));
-        Mg = fmaxf(Mg, xchg_f<2>(Mg));
-        const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mg);
-        Lsum *= f;
-        Lsum += xchg_f<0>(Lsum);
-        Lsum += xchg_f<1>(Lsum);
-        Lsum += xchg_f<2>(Lsum);
-#pragma unroll
-        for (int k = 0; k < kSlice; ++k) {
-            acc[k] *= f;
-            acc[k] += xchg_f<0>(acc[k]);
-            acc[k] += xchg_f<1>(acc[k]);
-            acc[k] += xchg_f<2>(acc[k]);
-        }
-        M = Mg;
-    }
-
-    // tree keys on the root path of i (mask row), one dot product per bit;
-    // the root's key and value are already in registers
-    auto add_key = [&](const float (&kk)[kSlice], const float (&vv)[kSlice]) {
-        float dot = 0.f;
-#pragma unroll
-        for (int k = 0; k < kSlice; ++k) dot += qv[k] * kk[k];
-        dot += xchg_f<3>(dot);
-        dot += xchg_f<4>(dot);
-        dot += xchg_f<5>(dot);
-        const float sc = dot * scale2;
-        const float Mn = fmaxf(M, sc);
-        const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-        const float fn = __builtin_amdgcn_exp2f(sc - Mn);
-        Lsum = Lsum * fo + fn;
-#pragma unroll
-        for (int k = 0; k < kSlice; ++k) acc[k] = acc[k] * fo + vv[k] * fn;
-        M = Mn;
-    };
-    if (mw[0] & 1ull) add_key(k0v, v0v);
-    mw[0] &= ~1ull;
-#pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-        uint64_t bits = mw[wd];
-        while (bits) {
-            const int j = wd * 64 + __ffsll(static_cast<long long>(bits)) - 1;
-            bits &= bits - 1;
-            if (j >= nq_max) break;  // bits beyond the tree rows are ignored
-            const int64_t kv = ((static_cast<int64_t>(b) * nq_max + j) * hkv + g) * D + slice * kSlice;
-            float kk[kSlice], vv[kSlice];
-            load_slice<T, kSlice>(k_tree + kv, kk);
-            load_slice<T, kSlice>(v_tree + kv, vv);
-            add_key(kk, vv);
-        }
-    }
-    if (cg == 0) {
-        const float inv = 1.f / Lsum;
-#pragma unroll
-        for (int k = 0; k < kSlice; ++k) orow[k] = from_f32<T>(acc[k] * inv);
+    combine_row(r);
+    if (has2) {
+        if (r2 / group <= n) combine_row(r2);
+        else zero_row(r2);
     }
 }
 
@@ -1141,21 +1177,20 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
     }
 #undef TD_SPLIT
 #undef TD_SPLIT_BF
-    const int blocks_per_bg = (pl.group * nq_max + kCombineRows - 1) / kCombineRows;
+    const bool two = combine_two_rows(static_cast<int64_t>(batch) * hkv * pl.group * nq_max);
+    const int blocks_per_bg = combine_blocks(pl.group * nq_max, two);
     const int64_t blocks = static_cast<int64_t>(batch) * hkv * blocks_per_bg;
-    if (acc)
-        hipLaunchKernelGGL((attn_tree_combine<T, D, true>), dim3(static_cast<unsigned>(blocks + batch)),
-                           dim3(kAttnThreads), 0, st, static_cast<const T *>(q), off,
-                           static_cast<const T *>(k_tree), static_cast<const T *>(v_tree), mask,
-                           n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,
-                           static_cast<const float *>(ws), prow_total, static_cast<T *>(out), *acc);
-    else
-        hipLaunchKernelGGL((attn_tree_combine<T, D, false>), dim3(static_cast<unsigned>(blocks)),
-                           dim3(kAttnThreads), 0, st, static_cast<const T *>(q), off,
-                           static_cast<const T *>(k_tree), static_cast<const T *>(v_tree), mask,
-                           n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,
-                           static_cast<const float *>(ws), prow_total, static_cast<T *>(out),
-                           AcceptArgs{});
+#define TD_COMBINE(ACC, TWO, NB, ARGS)                                                           \
+    hipLaunchKernelGGL((attn_tree_combine<T, D, ACC, TWO>), dim3(static_cast<unsigned>(NB)),      \
+                       dim3(kAttnThreads), 0, st, static_cast<const T *>(q), off,                 \
+                       static_cast<const T *>(k_tree), static_cast<const T *>(v_tree), mask,      \
+                       n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,      \
+                       static_cast<const float *>(ws), prow_total, static_cast<T *>(out), ARGS)
+    if (acc && two) TD_COMBINE(true, true, blocks + batch, *acc);
+    else if (acc) TD_COMBINE(true, false, blocks + batch, *acc);
+    else if (two) TD_COMBINE(false, true, blocks, AcceptArgs{});
+    else TD_COMBINE(false, false, blocks, AcceptArgs{});
+#undef TD_COMBINE
 }
 
 inline int sub_chunk(td_dtype dt) { return dt == TD_BF16 ? Sub<uint16_t>::CH : Sub<float>::CH; }

@@ -134,11 +134,6 @@ __device__ __forceinline__ bool find_chunk(const int64_t *__restrict__ off, int 
     return false;
 }
 
-template <typename T> __device__ __forceinline__ float to_f32(T x);
-template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) {
-    return __uint_as_float(static_cast<uint32_t>(x) << 16);
-}
-template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) { return f32_to_bf16(x); }
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
@@ -518,6 +513,48 @@ __device__ __forceinline__ void issue_rows(const uint16_t *gbase, int ks32, int 
     }
 }
 
+// K fragments of one 32-key tile (the A operand of S^T = K Q^T: lane l
+// reads key 16 hf + l % 16 of the tile, dims 8 (l / 16) + 32 ks ..), all
+// reads in flight before one wait.  Issued from assembly: the compiler's
+// schedule of the plain loads waits for each read before issuing the next.
+template <int D>
+__device__ __forceinline__ void read_k(const uint16_t *sK, int kt, int lane, bf16x8 (&fk)[2][D / 32]) {
+    constexpr int RK = rk_pieces<D>();
+    const int col = lane & 15;
+    const int h4 = lane >> 4;
+    const uint32_t a0 = lds_addr(sK + (kt * kKeyTile + col) * RK * 8 + 8 * h4);
+    const uint32_t a1 = lds_addr(sK + (kt * kKeyTile + 16 + col) * RK * 8 + 8 * h4);
+    u32x4 t[2 * (D / 32)];
+    if constexpr (D == 128) {
+        asm volatile(
+            "ds_read_b128 %0, %8\n"
+            "ds_read_b128 %1, %8 offset:64\n"
+            "ds_read_b128 %2, %8 offset:128\n"
+            "ds_read_b128 %3, %8 offset:192\n"
+            "ds_read_b128 %4, %9\n"
+            "ds_read_b128 %5, %9 offset:64\n"
+            "ds_read_b128 %6, %9 offset:128\n"
+            "ds_read_b128 %7, %9 offset:192\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]),
+              "=&v"(t[6]), "=&v"(t[7])
+            : "v"(a0), "v"(a1));
+    } else {
+        asm volatile(
+            "ds_read_b128 %0, %4\n"
+            "ds_read_b128 %1, %4 offset:64\n"
+            "ds_read_b128 %2, %5\n"
+            "ds_read_b128 %3, %5 offset:64\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+            : "v"(a0), "v"(a1));
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) fk[hf][ks] = __builtin_bit_cast(bf16x8, t[hf * (D / 32) + ks]);
+}
+
 // V^T fragments of one 32-key tile, all reads in flight before one wait.
 // The LDS reads are issued from assembly: the compiler's own transposing-read
 // builtin makes it wait for the other buffer's loads first.
@@ -581,20 +618,12 @@ template <int D, int OWN>
 __device__ __forceinline__ void tile_dma(const uint16_t *sK, const uint16_t *sV,
                                          const bf16x8 (&qf)[OWN][D / 32], int n_own, int kt,
                                          int valid, float scale2, int lane, RowState<D> (&st)[OWN]) {
-    constexpr int RK = rk_pieces<D>();
-    const int col = lane & 15;
     const int h4 = lane >> 4;
     bf16x8 pf[OWN];
     float alpha[OWN];
     {
         bf16x8 fk[2][D / 32];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const uint16_t *krow = sK + (kt * kKeyTile + 16 * hf + col) * RK * 8 + 8 * h4;
-#pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks)
-                fk[hf][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(krow + 32 * ks));
-        }
+        read_k<D>(sK, kt, lane, fk);
         const bool ragged = kt * kKeyTile + kKeyTile > valid;
 #pragma unroll
         for (int j = 0; j < OWN; ++j) {
@@ -607,7 +636,7 @@ __device__ __forceinline__ void tile_dma(const uint16_t *sK, const uint16_t *sV,
                 for (int ks = 0; ks < D / 32; ++ks)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk[hf][ks], qf[j][ks], acc, 0, 0, 0);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) sc[4 * hf + t] = acc[t] * scale2;
+                for (int t = 0; t < 4; ++t) sc[4 * hf + t] = acc[t];
             }
             if (ragged) {
 #pragma unroll
@@ -619,12 +648,12 @@ __device__ __forceinline__ void tile_dma(const uint16_t *sK, const uint16_t *sV,
             for (int t = 1; t < 8; ++t) tmax = fmaxf(tmax, sc[t]);
             tmax = fmaxf(tmax, xchg_f<4>(tmax));
             tmax = fmaxf(tmax, xchg_f<5>(tmax));
-            const float m_new = fmaxf(st[j].m, tmax);
+            const float m_new = fmaxf(st[j].m, tmax * scale2);
             alpha[j] = __builtin_amdgcn_exp2f(st[j].m - m_new);
             float ps = 0.f;
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const float p = __builtin_amdgcn_exp2f(sc[t] - m_new);
+                const float p = __builtin_amdgcn_exp2f(fmaf(sc[t], scale2, -m_new));
                 ps += p;
                 pf[j][t] = static_cast<__bf16>(p);  // round to nearest even
             }

@@ -625,18 +625,38 @@ __device__ __forceinline__ void tile_dma(const uint16_t *sK, const uint16_t *sV,
         bf16x8 fk[2][D / 32];
         read_k<D>(sK, kt, lane, fk);
         const bool ragged = kt * kKeyTile + kKeyTile > valid;
+        auto scores = [&](int j, f32x4 (&a)[2]) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                a[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks)
+                    a[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk[hf][ks], qf[j][ks], a[hf], 0, 0, 0);
+            }
+        };
+        // With many row groups, row group j + 1's score MFMAs are issued
+        // before row group j's softmax, so the matrix core works while the
+        // vector unit does (with few, the extra live registers cost more
+        // than the overlap gains).
+        constexpr bool kAhead = OWN >= 4;
+        f32x4 cur[2], nxt[2] = {};
+        if (kAhead && n_own > 0) scores(0, cur);
 #pragma unroll
         for (int j = 0; j < OWN; ++j) {
             if (j >= n_own) break;
+            if constexpr (kAhead) {
+                if (j + 1 < OWN && j + 1 < n_own) scores(j + 1 < OWN ? j + 1 : j, nxt);
+            } else {
+                scores(j, cur);
+            }
             float sc[8];
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk[hf][ks], qf[j][ks], acc, 0, 0, 0);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) sc[4 * hf + t] = acc[t];
+                for (int t = 0; t < 4; ++t) sc[4 * hf + t] = cur[hf][t];
+            if constexpr (kAhead) {
+                cur[0] = nxt[0];
+                cur[1] = nxt[1];
             }
             if (ragged) {
 #pragma unroll

@@ -54,6 +54,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kAttnThreads = 256;
+constexpr int kAttnCUs = 256;  // compute units of the gfx950 parts
 constexpr int kAttnWaves = 4;
 constexpr int kRowsPerGroup = 16;
 constexpr int kKeyTile = 32;
@@ -1214,9 +1215,11 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
         case 1: TD_SPLIT_BF(1); break;
         case 2: TD_SPLIT_BF(2); break;
         default:
-            // trees of more than 12 row groups take 5 per wave (one pass over
-            // the keys up to 20 row groups), smaller ones 3
-            if (pl.own > 3) TD_SPLIT_BF(3, 5);
+            // when the chip has several work items per compute unit, trees of
+            // more than 12 row groups take 5 per wave (one pass over the keys
+            // up to 20 row groups) and smaller ones 3; with about one item per
+            // unit (a latency-bound step) the lighter 3-group kernel alone
+            if (pl.own > 3 && pl.items > 2 * kAttnCUs) TD_SPLIT_BF(3, 5);
             else TD_SPLIT_BF(3);
             break;
         }

@@ -17,17 +17,21 @@
 //                   chunk's first loads are issued before the tree size and
 //                   the queries arrive, and each next sub-chunk's loads fly
 //                   during the compute.  A wave owns up to OWN row groups
-//                   (queries and O^T accumulators in registers) and shares
-//                   each K and V fragment it reads from LDS among them; row
+//                   (queries and O^T accumulators in registers; bf16 at
+//                   D = 128 takes 5 instead of 3 for a large tree when the
+//                   grid is throughput-bound) and shares each K and V
+//                   fragment it reads from LDS among them; row
 //                   blocks of 4 OWN row groups are processed in turn; a block
 //                   of fewer than 4 row groups splits the keys of each
 //                   sub-chunk over the waves, which merge through LDS.
 //                   Softmax is online in base 2.  One (m, l, O) partial per
 //                   tree row and chunk is stored.
-//  attn_tree_combine one wave per output row: merges the chunk partials
-//                   (every load in flight at once), adds the ancestor-masked
-//                   tree keys (sparse: one dot product per set mask bit) and
-//                   writes the normalised row; rows beyond the tree get zeros.
+//  attn_tree_combine one wave per output row (two rows r, r + half for grids
+//                   larger than the chip keeps resident): merges the chunk
+//                   partials (every load in flight at once), adds the
+//                   ancestor-masked tree keys (sparse: one dot product per
+//                   set mask bit) and writes the normalised row; rows beyond
+//                   the tree get zeros.
 //
 // MFMA 16x16x32 bf16 operand layout (wave64): A (16 x 32): lane l holds row
 // l % 16, k = 8 (l / 16) .. +7; B (32 x 16): lane l holds column l % 16, the

@@ -976,6 +976,30 @@ __device__ __forceinline__ void load_slice(const T *p, float (&x)[N]) {
     }
 }
 
+// The same slice as raw 16-byte words (loads in flight, no use yet), and
+// their widening to float.
+template <typename T, int N> constexpr int raw_words() { return N * static_cast<int>(sizeof(T)) / 16; }
+template <typename T, int N>
+__device__ __forceinline__ void load_raw(const T *p, u32x4 (&w)[raw_words<T, N>()]) {
+#pragma unroll
+    for (int k = 0; k < raw_words<T, N>(); ++k) w[k] = reinterpret_cast<const u32x4 *>(p)[k];
+}
+template <typename T, int N>
+__device__ __forceinline__ void widen(const u32x4 (&w)[raw_words<T, N>()], float (&x)[N]) {
+#pragma unroll
+    for (int k = 0; k < raw_words<T, N>(); ++k) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (sizeof(T) == 2) {
+                x[8 * k + 2 * e] = bf16_lo(w[k][e]);
+                x[8 * k + 2 * e + 1] = bf16_hi(w[k][e]);
+            } else {
+                x[4 * k + e] = __uint_as_float(w[k][e]);
+            }
+        }
+    }
+}
+
 __device__ __forceinline__ int wave_sum_i(int v) {
     v += xchg_i<0>(v);
     v += xchg_i<1>(v);
@@ -1148,18 +1172,37 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
         };
         if (mw[0] & 1ull) add_key(k0v, v0v);
         mw[0] &= ~1ull;
+        // the other keys kTB at a time, all their loads in flight before the
+        // first is used (bits in increasing order, as a one-by-one walk)
+        constexpr int kTB = sizeof(T) == 2 ? 4 : 2;
+        constexpr int kRW = raw_words<T, kSlice>();
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd) {
             uint64_t bits = mw[wd];
             while (bits) {
-                const int j = wd * 64 + __ffsll(static_cast<long long>(bits)) - 1;
-                bits &= bits - 1;
-                if (j >= nq_max) break;  // bits beyond the tree rows are ignored
-                const int64_t kv = ((static_cast<int64_t>(b) * nq_max + j) * hkv + g) * D + slice * kSlice;
-                float kk[kSlice], vv[kSlice];
-                load_slice<T, kSlice>(k_tree + kv, kk);
-                load_slice<T, kSlice>(v_tree + kv, vv);
-                add_key(kk, vv);
+                bool have[kTB];
+                u32x4 kr[kTB][kRW], vr[kTB][kRW];
+#pragma unroll
+                for (int u = 0; u < kTB; ++u) {
+                    const int j = wd * 64 + __ffsll(static_cast<long long>(bits)) - 1;
+                    have[u] = bits != 0 && j < nq_max;  // bits beyond the tree rows are ignored
+                    bits &= bits - 1;
+                    if (have[u]) {
+                        const int64_t kv =
+                            ((static_cast<int64_t>(b) * nq_max + j) * hkv + g) * D + slice * kSlice;
+                        load_raw<T, kSlice>(k_tree + kv, kr[u]);
+                        load_raw<T, kSlice>(v_tree + kv, vr[u]);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kTB; ++u) {
+                    if (have[u]) {
+                        float kk[kSlice], vv[kSlice];
+                        widen<T, kSlice>(kr[u], kk);
+                        widen<T, kSlice>(vr[u], vv);
+                        add_key(kk, vv);
+                    }
+                }
             }
         }
         if (cg == 0) {

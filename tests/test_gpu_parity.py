@@ -312,7 +312,8 @@ def gpu_pipeline(td, cfg, x, inp):
 
 @pytest.mark.parametrize("name,sample", [("tiny", None), ("tiny_fixed", None), ("qwen3_8b", None),
                                          ("qwen3_8b_stress", None), ("llama31_8b", [0, 3]),
-                                         ("batched", [0, 9]), ("long", [5, 40])])
+                                         ("batched", [0, 9]), ("long", [5, 40]),
+                                         ("two_seq_k4", None), ("few_slices", None)])
 def test_pipeline(td, name, sample):
     cfg = wl.CONFIGS[name]
     say("pipeline", name, sample)

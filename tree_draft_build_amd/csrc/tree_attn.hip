@@ -18,8 +18,9 @@
 //                   the queries arrive, and each next sub-chunk's loads fly
 //                   during the compute.  A wave owns up to OWN row groups
 //                   (queries and O^T accumulators in registers; bf16 at
-//                   D = 128 takes 5 instead of 3 for a large tree when the
-//                   grid is throughput-bound) and shares each K and V
+//                   D = 128 runs one-group code for trees of up to 4 row
+//                   groups, and 3 or, when the grid is throughput-bound, 5
+//                   for larger ones) and shares each K and V
 //                   fragment it reads from LDS among them; row
 //                   blocks of 4 OWN row groups are processed in turn; a block
 //                   of fewer than 4 row groups splits the keys of each
@@ -1262,12 +1263,12 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
         case 1: TD_SPLIT_BF(1); break;
         case 2: TD_SPLIT_BF(2); break;
         default:
-            // when the chip has several work items per compute unit, trees of
-            // more than 12 row groups take 5 per wave (one pass over the keys
-            // up to 20 row groups) and smaller ones 3; with about one item per
-            // unit (a latency-bound step) the lighter 3-group kernel alone
-            if (pl.own > 3 && pl.items > 2 * kAttnCUs) TD_SPLIT_BF(3, 5);
-            else TD_SPLIT_BF(3);
+            // trees of up to 4 row groups take the one-group code; larger
+            // ones 5 per wave when the chip has several work items per
+            // compute unit (one pass over the keys up to 20 row groups),
+            // else 3 (a latency-bound step: the lighter code)
+            if (pl.own > 3 && pl.items > 2 * kAttnCUs) TD_SPLIT_BF(1, 5);
+            else TD_SPLIT_BF(1, 3);
             break;
         }
     } else {

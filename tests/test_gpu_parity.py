@@ -291,6 +291,30 @@ def test_attention_mask_sensitive(td, name):
     assert int(tree["n_nodes"][0]) == cfg.n_max
 
 
+@pytest.mark.parametrize("law", ["normal", "mask_sensitive"])
+def test_attention_row_group_paths(td, law):
+    """Every tree row of sequences whose trees take each of the split kernel's
+    row-group paths, in a grid of more than two work items per compute unit
+    (8 sequences x 4096 keys x 8 KV heads: 1088 work items), where trees of
+    more than 4 row groups of 16 rows take 5 row groups per wave (the early
+    score MFMAs of the next row group and their hand-over are used from the
+    second row group on): 17, 11, 5, 8 and 4 row groups (n_nodes 64, 40, 16,
+    30, 12), then 13 and 16 (50, 63); one sequence has no tree beyond the
+    root."""
+    say("attn row-group paths", law)
+    cfg = wl.CONFIGS["qwen3_8b"].replace(name="rg5", index=52, batch=8, n_max=64, use_stop=False,
+                                         ctx_law="fixed", ctx_p0=4096, attn_law=law)
+    inp = wl.make_attn_inputs(cfg)
+    n_nodes = np.array([64, 40, 16, 30, 12, 50, 63, 0], np.int32)
+    par = random_parents(np.random.default_rng(52), n_nodes, cfg.nq_max)
+    got, mask = run_attn(td, cfg, inp, par, n_nodes)
+    for b0, b1 in ((0, 5), (5, 8)):
+        want = oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
+                                inp["k_tree"], inp["v_tree"], mask, n_nodes, cfg.hq, cfg.hkv,
+                                cfg.head_dim, wl.attn_scale(cfg), seqs=(b0, b1))
+        attn_close(got[b0:b1], want, "bf16", f"row-group paths {law} seqs {b0}..{b1 - 1}")
+
+
 # ---------------------------------------------------------------------------
 # end to end: the whole path on the GPU vs the whole path in the oracle
 # ---------------------------------------------------------------------------
@@ -329,18 +353,12 @@ def test_pipeline(td, name, sample):
     # mask of the GPU tree, checked against the oracle's mask of the same tree
     np.testing.assert_array_equal(g["mask"][seqs],
                                   oracle.tree_mask(sub_tree["node_parent"], sub_tree["n_nodes"]))
-    # attention of the GPU tree (sampled sequences; rows limited for long contexts)
-    row_limit = 3 if name == "long" else -1
+    # attention of the GPU tree on every row of the sampled sequences
     for b in seqs:
         want = oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
                                 inp["k_tree"], inp["v_tree"], g["mask"], g["tree"]["n_nodes"],
-                                cfg.hq, cfg.hkv, cfg.head_dim, wl.attn_scale(cfg), seqs=(b, b + 1),
-                                row_limit=row_limit)
-        got = g["out"][b:b + 1]
-        if row_limit >= 0:
-            got = got.copy()
-            got[:, row_limit + 1:] = 0
-        attn_close(got, want, cfg.attn_dtype, f"{name} seq {b}")
+                                cfg.hq, cfg.hkv, cfg.head_dim, wl.attn_scale(cfg), seqs=(b, b + 1))
+        attn_close(g["out"][b:b + 1], want, cfg.attn_dtype, f"{name} seq {b}")
     # acceptance on the GPU tree with the synthetic target
     lf = wl.logits_as_f64(x, cfg.logit_dtype)
     tg = targets_by_path(cfg, lf, g["tree"])

@@ -18,8 +18,10 @@
  * Conventions shared by every call
  *  - Every array pointer is DEVICE memory owned by the caller, unless a
  *    comment says otherwise.  The library allocates nothing and keeps no
- *    state besides a thread-local error string and a per-device property
- *    cache.
+ *    state besides a thread-local error string.
+ *  - Launch plans (slices per logit row, key chunks per context) are sized
+ *    for the 256 compute units of the MI355X (gfx950); they stay correct on
+ *    a part with another count, only less well balanced.
  *  - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t;
  *    NULL = the default stream).  TD_OK means "validated and enqueued".
  *    Tree sizes (n_nodes) stay on the device: no call waits for the host.
@@ -54,7 +56,8 @@ typedef enum {
     TD_EINVAL = 1,        /* null pointer, bad size, misaligned buffer, too small workspace */
     TD_ECAPACITY = 2,     /* a size above the compiled capacities */
     TD_EUNSUPPORTED = 3,  /* dtype / head_dim combination not built */
-    TD_EHIP = 4           /* the HIP runtime reported an error at launch */
+    TD_EHIP = 4,          /* the HIP runtime reported an error */
+    TD_ESYNC = 5          /* td_workspace_status: a cross-workgroup hand-off gave up */
 } td_status;
 
 typedef enum { TD_F32 = 0, TD_BF16 = 1 } td_dtype;
@@ -84,13 +87,36 @@ const char *td_last_error(void);
  *   first use and again whenever batch, block, vocab or K change (it holds
  *   the workgroups' call epochs, which tag the partial results they hand
  *   over); every call leaves it ready for the next call of the same shape.
- *   Calls that overlap in time must not share a workspace.
+ *   Calls that overlap in time must not share a workspace.  A broken
+ *   hand-off is reported by td_workspace_status (lse of the row is NaN).
  */
 size_t td_draft_topk_workspace(int32_t batch, int32_t block, int32_t vocab, int32_t K);
 td_status td_draft_topk(const void *logits, td_dtype dtype, int32_t batch, int32_t block,
                         int32_t vocab, int64_t pos_stride, int32_t K, int32_t *topk_id,
                         double *topk_logq, double *lse, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * td_workspace_status -- did a call that used this workspace give up waiting?
+ * The top-K kernel and the verify step's first kernel hand partial results
+ * from workgroup to workgroup through the workspace (epoch-tagged words).  A
+ * waiter polls a bounded number of times; if the words never arrive (the
+ * workspace was not zero-filled after a shape change, two overlapping calls
+ * shared it, or the GPU started the waiting workgroups before the ones they
+ * wait for and those could not run) it gives up instead of hanging:
+ *   - a row merger writes lse = NaN for its row (its ids and log q are then
+ *     meaningless), and
+ *   - a tree builder writes n_nodes = -1 for its sequence (its tree entries
+ *     are then meaningless; the verify step's attention then writes zero
+ *     rows and its acceptance reports A = 0 with the root's target token),
+ * and each sets a bit in a status word at the start of the workspace.
+ * This call waits for `stream`, reads that word and clears it: TD_OK if no
+ * call gave up since the last check, TD_ESYNC otherwise (td_last_error()
+ * names the failed hand-offs).  It synchronises the stream; a serving loop
+ * calls it when it reads results back.  workspace: a workspace of
+ * td_draft_topk or td_verify_step (not of td_tree_verify_attn).
+ */
+td_status td_workspace_status(void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * td_build_tree -- stage (b).
@@ -110,7 +136,9 @@ td_status td_draft_topk(const void *logits, td_dtype dtype, int32_t batch, int32
  * min(n_max, available candidates) nodes are inserted.  log rho, A_hat and S
  * are accumulated in float64.
  * Inputs:  topk_id [batch][block][K], topk_logq [batch][block][K] as written
- *          by td_draft_topk; root_token [batch] or NULL (then -1 is stored).
+ *          by td_draft_topk (ids in [0, TD_MAX_VOCAB); the kernel uses the
+ *          low 18 bits of each id); root_token [batch] or NULL (then -1 is
+ *          stored).
  * Outputs (index 0 = root; nodes in insertion order, parent index < child):
  *   n_nodes     [batch]           number of draft nodes N (root excluded)
  *   node_token  [batch][n_max+1]  token id (-1 beyond N)
@@ -130,9 +158,14 @@ td_status td_build_tree(const int32_t *topk_id, const double *topk_logq, int32_t
 
 /* ------------------------------------------------------------------------
  * td_tree_mask -- stage (b').
- * Bit-packed ancestor-or-self mask of every tree row: bit j of row i is set
- * iff node j lies on the root path of node i (i included), so that a tree
- * query sees only its own prefix.  Row i = row(parent(i)) | (1 << i).
+ * The draft tree is prefix-closed (Methodik §1, marginal independence: the
+ * per-position candidates combine freely into a prefix tree), and the target
+ * verifies all its nodes in one parallel pass (Problemstellung), so each
+ * node's query may see exactly the tokens of its own prefix: the context and
+ * the tree nodes on its root path.  This call writes that set as a bit-packed
+ * ancestor-or-self mask of every tree row: bit j of row i is set iff node j
+ * lies on the root path of node i (i included).  Row i = row(parent(i)) |
+ * (1 << i).
  * Inputs:  node_parent [batch][nq_max], n_nodes [batch] (nq_max = n_max+1).
  * Output:  mask [batch][nq_max][words], words = (nq_max + 63) / 64; bit j of
  *          a row is bit (j % 64) of word j / 64.  Rows beyond n_nodes are 0.
@@ -205,7 +238,8 @@ td_status td_accept(const int32_t *node_token, const int32_t *node_parent, const
  * ZERO-FILLED before its first use and again whenever the shape fields
  * (batch, block, vocab, topk, n_max, hq, hkv, head_dim, total_ctx) change;
  * every call leaves it ready for the next call of the same shape.  Calls
- * that overlap in time must not share a workspace.
+ * that overlap in time must not share a workspace.  A broken hand-off is
+ * reported by td_workspace_status (see there for the sentinels).
  * stages selects the kernels a call enqueues: TD_STEP_DRAFT (kernel 1: top-K,
  * tree, mask), TD_STEP_VERIFY (kernels 2 and 3: attention and acceptance),
  * or 0 for both.  A serving loop builds the tree with TD_STEP_DRAFT, runs the

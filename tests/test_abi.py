@@ -25,7 +25,7 @@ def b():
 
 def test_every_declared_symbol_is_exported(b):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(b.lib, n), n
     assert sorted(b.EXPORTED) == names
@@ -33,6 +33,13 @@ def test_every_declared_symbol_is_exported(b):
 
 def test_abi_version(b):
     assert b.lib.td_abi_version() == 1
+
+
+def test_workspace_status_validation(b):
+    assert b.lib.td_workspace_status(None, 1 << 20, None) == 1
+    assert b.lib.td_workspace_status(P(4097), 1 << 20, None) == 1
+    assert b.lib.td_workspace_status(P(4096), 8, None) == 1
+    assert "status" in b.last_error()
 
 
 def test_workspace_queries(b):

@@ -204,3 +204,68 @@ def test_step_in_two_calls(td, name):
         s.run(stages=td.TD_STEP_VERIFY)
         torch.cuda.synchronize()
         assert_same(ref, step_outputs(s), f"{name} two calls {rep}")
+
+
+def _scramble_epochs(ws, nbytes):
+    """Every 8-byte word of the first nbytes (past the 16-byte status header)
+    set to its own index: the workgroups' epoch words then all differ, so no
+    waiter ever sees the tag it polls for, and every bounded wait gives up.
+    Only the library's own polls read these words; no kernel indexes with
+    them."""
+    n8 = nbytes // 8
+    pat = torch.arange(n8, dtype=torch.int64, device=ws.device)
+    pat[:2] = 0                                     # the status header stays clear
+    ws[:n8 * 8].view(torch.int64).copy_(pat)
+
+
+def test_handoff_give_up_is_reported(td):
+    """A workspace that was not zero-filled (its epoch words disagree) makes
+    the kernels' bounded waits give up: the row mergers write lse = NaN and
+    the tree builders n_nodes = -1, td_workspace_status reports TD_ESYNC once
+    and clears the word, and after re-zeroing the results are right again."""
+    print("[case] hand-off give-up", flush=True)
+    # stand-alone top-K: 2 rows of 64 slices each
+    x = wl.f32_to_bf16_bits(np.random.default_rng(5).standard_normal((1, 2, 65536)).astype(np.float32))
+    lg = dev(x)
+    ws = td.draft_topk_alloc_workspace(1, 2, 65536, 8, DEV)
+    ids0, lq0, lse0 = [t.clone() for t in td.draft_topk(lg, 8, workspace=ws)]
+    assert td.workspace_status(ws) == td.TD_OK
+    _scramble_epochs(ws, td.draft_topk_workspace(1, 2, 65536, 8))
+    _, _, lse = td.draft_topk(lg, 8, workspace=ws)
+    assert td.workspace_status(ws) == td.TD_ESYNC
+    assert "row merge" in td.last_error()
+    assert torch.isnan(lse).all()
+    assert td.workspace_status(ws) == td.TD_OK      # the check cleared the word
+    ws.zero_()
+    ids, lq, lse = td.draft_topk(lg, 8, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids0) and torch.equal(lq, lq0) and torch.equal(lse, lse0)
+    assert td.workspace_status(ws) == td.TD_OK
+
+    # the fused step at the Qwen3-8B stress shape
+    cfg = wl.CONFIGS["qwen3_8b_stress"]
+    xs, inp, d = inputs(cfg)
+    ref = modular(td, cfg, d, None)
+    tree_np = {k: ref[k].numpy() for k in ("node_token", "node_parent", "n_nodes")}
+    tg = dev(targets_by_path(cfg, wl.logits_as_f64(xs, cfg.logit_dtype), tree_np))
+    ref = modular(td, cfg, d, tg)
+    s = make_step(td, cfg, d)
+    s.set_inputs(d["logits"], d["q"], d["k_ctx"], d["v_ctx"], d["off"], d["k_tree"], d["v_tree"], tg)
+    s.run()
+    assert s.status() == td.TD_OK
+    assert_same(ref, step_outputs(s), "before scrambling")
+    _scramble_epochs(s.workspace, td.draft_topk_workspace(cfg.batch, cfg.block, cfg.vocab, cfg.topk))
+    s.run()
+    assert s.status() == td.TD_ESYNC
+    err = td.last_error()
+    assert "row merge" in err and "tree build" in err
+    got = step_outputs(s)
+    assert int(got["n_nodes"][0]) == -1
+    assert torch.isnan(got["lse"]).all()
+    assert int(got["accept_len"][0]) == 0
+    assert int(got["bonus_token"][0]) == int(tg[0, 0])
+    assert not got["out"].view(torch.int16).any()    # zero rows: there is no tree
+    s.workspace.zero_()
+    s.run()
+    assert s.status() == td.TD_OK
+    assert_same(ref, step_outputs(s), "after re-zeroing")

@@ -18,16 +18,17 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # TREEDRAFT_LIB selects another build of the library (e.g. for A/B timing).
 LIB_PATH = os.environ.get("TREEDRAFT_LIB") or os.path.join(_HERE, "libtreedraft.so")
 
-TD_OK, TD_EINVAL, TD_ECAPACITY, TD_EUNSUPPORTED, TD_EHIP = range(5)
+TD_OK, TD_EINVAL, TD_ECAPACITY, TD_EUNSUPPORTED, TD_EHIP, TD_ESYNC = range(6)
 TD_F32, TD_BF16 = 0, 1
 TD_STEP_DRAFT, TD_STEP_VERIFY = 1, 2
-STATUS_NAMES = {0: "TD_OK", 1: "TD_EINVAL", 2: "TD_ECAPACITY", 3: "TD_EUNSUPPORTED", 4: "TD_EHIP"}
+STATUS_NAMES = {0: "TD_OK", 1: "TD_EINVAL", 2: "TD_ECAPACITY", 3: "TD_EUNSUPPORTED", 4: "TD_EHIP",
+                5: "TD_ESYNC"}
 
 # every symbol declared in include/treedraft.h
 EXPORTED = ["td_abi_version", "td_last_error", "td_draft_topk_workspace", "td_draft_topk",
             "td_build_tree", "td_tree_mask", "td_tree_verify_attn_workspace",
             "td_tree_verify_attn", "td_accept", "td_step_args_bytes", "td_verify_step_workspace",
-            "td_verify_step"]
+            "td_verify_step", "td_workspace_status"]
 
 
 class StepArgs(ctypes.Structure):
@@ -83,8 +84,9 @@ def _load():
     lib.td_verify_step_workspace.argtypes = [ctypes.POINTER(StepArgs)]
     lib.td_verify_step_workspace.restype = c_size_t
     lib.td_verify_step.argtypes = [ctypes.POINTER(StepArgs), P, c_size_t, P]
+    lib.td_workspace_status.argtypes = [P, c_size_t, P]
     for name in ("td_draft_topk", "td_build_tree", "td_tree_mask", "td_tree_verify_attn",
-                 "td_accept", "td_verify_step"):
+                 "td_accept", "td_verify_step", "td_workspace_status"):
         getattr(lib, name).restype = c_int
     if lib.td_step_args_bytes() != ctypes.sizeof(StepArgs):
         raise ImportError("td_step_args layout differs between the library and this binding")
@@ -162,6 +164,18 @@ def draft_topk(logits, K, out=None, workspace=None, stream=None):
     _check(lib.td_draft_topk(_ptr(logits), _dt(logits), b, B, V, V, K, _ptr(ids), _ptr(lq),
                              _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
     return ids, lq, lse
+
+
+def workspace_status(workspace, stream=None):
+    """Wait for the stream, then read and clear the status word of a top-K or
+    verify-step workspace.  Returns TD_OK, or TD_ESYNC when a cross-workgroup
+    hand-off gave up since the last check (last_error() says which)."""
+    _dev(workspace, "workspace")
+    st = lib.td_workspace_status(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream))
+    if st not in (TD_OK, TD_ESYNC):
+        _check(st)
+    return st
 
 
 def alloc_tree(batch, n_max, device):
@@ -312,6 +326,11 @@ class VerifyStep:
         a.target_token = target_token.data_ptr()
         a.root_token = None if root_token is None else root_token.data_ptr()
         self._keep = (logits, q, k_ctx, v_ctx, ctx_offsets, k_tree, v_tree, target_token, root_token)
+
+    def status(self, stream=None):
+        """TD_OK, or TD_ESYNC if a hand-off of an earlier call gave up
+        (waits for the stream; clears the status word)."""
+        return workspace_status(self.workspace, stream)
 
     def run(self, stream=None, stages=0):
         """Enqueue the step (stages: TD_STEP_DRAFT | TD_STEP_VERIFY, 0 = both)."""

@@ -3,6 +3,7 @@
 #include <cstdarg>
 #include <cstdio>
 
+#include "step_launch.h"
 #include "td_internal.h"
 
 namespace td {
@@ -34,3 +35,35 @@ td_status check_launch(const char *what) {
 extern "C" int td_abi_version(void) { return TD_ABI_VERSION; }
 
 extern "C" const char *td_last_error(void) { return td::g_err; }
+
+using namespace td;
+
+extern "C" td_status td_workspace_status(void *workspace, size_t workspace_bytes, void *stream) {
+    clear_error();
+    if (!workspace || !aligned16(workspace))
+        return fail(TD_EINVAL, "td_workspace_status: null or misaligned workspace");
+    if (workspace_bytes < kStatusBytes)
+        return fail(TD_EINVAL, "td_workspace_status: workspace smaller than its status header");
+    hipStream_t s = as_stream(stream);
+    uint32_t word = 0;
+    hipError_t e = hipMemcpyAsync(&word, workspace, sizeof word, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        set_error("td_workspace_status: reading the status word failed: %s", hipGetErrorString(e));
+        return TD_EHIP;
+    }
+    if (word == 0) return TD_OK;
+    const uint32_t zero = 0;
+    e = hipMemcpyAsync(workspace, &zero, sizeof zero, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        set_error("td_workspace_status: clearing the status word failed: %s", hipGetErrorString(e));
+        return TD_EHIP;
+    }
+    set_error("a cross-workgroup hand-off gave up waiting (%s%s%s); the workspace was not "
+              "zero-filled after a shape change, or was shared by overlapping calls",
+              (word & kStatusMerge) ? "row merge: lse NaN" : "",
+              (word & kStatusMerge) && (word & kStatusTree) ? ", " : "",
+              (word & kStatusTree) ? "tree build: n_nodes -1" : "");
+    return TD_ESYNC;
+}

@@ -19,7 +19,7 @@ __global__ __launch_bounds__(kWave) void build_tree_kernel(const int32_t *__rest
     const int root_tok = P.root_token ? P.root_token[b] : -1;
     const int BK = P.block * P.K;
     for (int e = lane; e < BK; e += kWave) {
-        t.ids[e] = topk_id[static_cast<int64_t>(b) * BK + e];
+        t.ids[e] = static_cast<int>(static_cast<uint32_t>(topk_id[static_cast<int64_t>(b) * BK + e]) & kTokenMask);
         t.lq[e] = topk_logq[static_cast<int64_t>(b) * BK + e];
     }
     wave_lds_sync();

@@ -146,6 +146,9 @@ __device__ __forceinline__ void wave_select(KeyList<KW> &l, int K, uint64_t (&wi
 
 // Workspace layout for R rows of `splits` partials each (zero-filled once,
 // and again whenever the problem's shape changes):
+//   uint32 status[4]                bit kStatusMerge / kStatusTree is set when
+//          a row merger / tree builder gave up waiting for a hand-off (read
+//          and cleared by td_workspace_status)
 //   uint64 part[R][splits][2K + 4]  per workgroup: its epoch (word 0), then
 //          the tagged words of its partial: key j low/high halves (1 + 2j,
 //          2 + 2j), log2 max (2K + 1), float64 sum (2K + 2, 2K + 3)
@@ -157,6 +160,7 @@ __device__ __forceinline__ void wave_select(KeyList<KW> &l, int K, uint64_t (&wi
 // written and read as one 8-byte atomic, so a reader takes a word only once
 // the word of this call has landed.
 struct TopkWs {
+    uint32_t *status;
     uint64_t *part;
     uint64_t *rowrec;
 };
@@ -165,12 +169,14 @@ __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~size_t(
 __host__ __device__ inline int part_words(int K) { return 2 * K + 3; }  // data words
 
 inline size_t topk_ws_bytes(int64_t rows, int64_t parts, int K) {
-    return align16(parts * (part_words(K) + 1) * 8) + align16(rows * 3 * K * 8);
+    return kStatusBytes + align16(parts * (part_words(K) + 1) * 8) + align16(rows * 3 * K * 8);
 }
 
 __host__ __device__ inline TopkWs topk_ws(void *base, int64_t rows, int64_t parts, int K) {
     char *p = static_cast<char *>(base);
     TopkWs w;
+    w.status = reinterpret_cast<uint32_t *>(p);
+    p += kStatusBytes;
     w.part = reinterpret_cast<uint64_t *>(p);
     p += align16(parts * (part_words(K) + 1) * 8);
     w.rowrec = reinterpret_cast<uint64_t *>(p);
@@ -194,10 +200,17 @@ __device__ __forceinline__ void put_word(uint64_t *p, uint32_t data, uint32_t ta
 
 // Polls of words whose writers have not landed them yet, per get_words call.
 // Every awaited word comes from a workgroup of lower index in the same
-// launch, which the dispatcher has started before the waiting one, so the
-// wait is a few microseconds; the bound only guards against a broken
-// protocol (the outputs then carry NaN or -1).
+// launch, which the dispatcher normally starts before the waiting one, so
+// the wait is a few microseconds.  The bound guards against a broken
+// protocol (a workspace not re-zeroed after a shape change, or workgroups
+// started out of index order while the waiting ones fill the chip): the
+// waiter then gives up, its outputs carry the documented sentinels (lse NaN,
+// n_nodes -1) and it sets its bit in the workspace status word.
 constexpr int kSpinLimit = 1 << 16;
+
+__device__ __forceinline__ void raise_status(uint32_t *status, uint32_t bit) {
+    __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Reads n <= NW tagged words p[idx[u]] (all loads in flight at once) into
 // out[u]; returns false if some word never carried the tag.  Every poll
@@ -662,6 +675,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
         if (lane == 0) {
             sm_lse = lse;
             lse_out[row] = lse;
+            if (sm_fail) raise_status(W.status, kStatusMerge);
         }
     }
 
@@ -790,7 +804,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
             for (int u = 0; u < 2; ++u) {
                 const int e = e0 + u * kWave;
                 if (e < BK) {
-                    tl.ids[e] = static_cast<int>(v[3 * u]);
+                    // ids are < 2^18 (TD_MAX_VOCAB); the mask keeps a word that
+                    // never arrived from steering the builder's table indexing
+                    tl.ids[e] = static_cast<int>(v[3 * u] & kTokenMask);
                     tl.lq[e] = __longlong_as_double(static_cast<long long>(
                         static_cast<uint64_t>(v[3 * u + 1]) | (static_cast<uint64_t>(v[3 * u + 2]) << 32)));
                 }
@@ -798,7 +814,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
         }
         wave_lds_sync();
         build_tree_wave<SLOTS, true>(tl, tp, to, b, lane, root_tok);
-        if (lane == 0 && !ok) to.n_nodes[b] = -1;
+        if (lane == 0 && !ok) {
+            to.n_nodes[b] = -1;
+            raise_status(W.status, kStatusTree);
+        }
     }
 }
 

@@ -12,7 +12,14 @@ namespace td {
 struct TreeParams;
 struct TreeOut;
 
-// top-K workspace bytes (per-workgroup epoch-tagged partials + row records)
+// The top-K and verify-step workspaces start with a 16-byte status header:
+// word 0 collects kStatus* bits, set by a waiter that gave up on a hand-off.
+constexpr size_t kStatusBytes = 16;
+constexpr uint32_t kStatusMerge = 1u;  // a row merger gave up (lse NaN)
+constexpr uint32_t kStatusTree = 2u;   // a tree builder gave up (n_nodes -1)
+
+// top-K workspace bytes (status header, per-workgroup epoch-tagged partials,
+// row records)
 size_t topk_workspace_bytes(int batch, int block, int vocab, int K);
 
 // The verify step's first kernel: top-K of every position, then each

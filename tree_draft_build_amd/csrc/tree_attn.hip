@@ -767,6 +767,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
     TD_ISSUE(0, sbuf0);
     const int rows_b = group * min(nn_b + 1, nq_max);
     const int n_rg_b = (rows_b + kRowsPerGroup - 1) / kRowsPerGroup;
+    if (n_rg_b <= 0) {  // no row at all (a tree build that gave up): drain the loads above
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
 
     auto row_blocks = [&](auto own_tag) __attribute__((always_inline)) {
         constexpr int OWNX = decltype(own_tag)::value;

@@ -26,6 +26,9 @@
 namespace td {
 
 constexpr uint32_t kEmptyKey = 0xffffffffu;
+// Token ids fit in 18 bits (TD_MAX_VOCAB = 2^18); the frontier key packs them
+// so, and the builders mask the ids they load with this before packing.
+constexpr uint32_t kTokenMask = 0x3ffffu;
 
 // LDS ordering inside one wavefront: LDS operations of a wave complete in
 // issue order; this keeps the compiler from moving them and waits for them.

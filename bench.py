@@ -8,9 +8,14 @@ Cache cannot serve a step from the previous one.
 
 Prints one JSON line (rank 0, one GPU):
   value        verify steps per second over the K timed steps
-  roofline     the dominant kernel's algorithmic bytes / its average launch
-               time measured with HIP events on the launch stream
-  cpu_baseline the CPU oracle timed on a bounded sample of the same workload
+  roofline     the dominant kernel's algorithmic bytes (or flops) / its
+               average duration, measured with HIP events attached to the
+               kernel's own dispatch (td_verify_step_events) over K launches
+  tree_row     the same shape with the tree fixed at N = 64 (65 query rows):
+               the attention kernels' HBM and MFMA fractions at a full tree
+  streaming    64 independent sequences of the headline shape per step
+  cpu_baseline the CPU oracle timed on a bounded sample of the same workload,
+               on all host cores (and on one thread)
 """
 from __future__ import annotations
 
@@ -40,11 +45,15 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly")
     ap.add_argument("--graph-steps", type=int, default=8, help="steps captured per HIP graph")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain copies of MIB MiB (profiler byte-counter reference)")
     ap.add_argument("--no-streaming", dest="streaming", action="store_false",
                     help="skip the 64-sequence streaming measurement")
+    ap.add_argument("--no-tree-row", dest="tree_row", action="store_false",
+                    help="skip the full-tree (N = 64 fixed) measurement")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the all-core oracle baseline (0: every core available)")
     return ap.parse_args()
 
 
@@ -65,6 +74,15 @@ def main():
         return
     cfg = wl.CONFIGS[args.config]
     result, x, inp = measure(cfg, args, args.steps, args.warmup)
+    if args.tree_row and cfg.name == "qwen3_8b":
+        # the same shape with a full tree (N = 64 fixed, 65 query rows)
+        tcfg = wl.CONFIGS["qwen3_8b_tree"]
+        tres, _, _ = measure(tcfg, args, max(10, args.steps // 2), max(2, args.warmup // 2))
+        result["tree_row"] = {
+            "workload": tcfg.name, "n_nodes": tres["config"]["n_nodes"][:1],
+            "value": tres["value"], "unit": "verify steps/s", "ms_per_step": tres["ms_per_step"],
+            "steps": tres["steps"], "kernels_us": tres["kernels_us"],
+            "kernel_roofline": tres["kernel_roofline"]}
     if args.streaming and cfg.name == "qwen3_8b":
         # the same per-sequence work, 64 independent sequences per step
         scfg = wl.CONFIGS["qwen3_8b_x64"]
@@ -77,7 +95,7 @@ def main():
             "kernels_us": sres["kernels_us"], "roofline": sres["roofline"],
             "stage_roofline": sres["stage_roofline"]}
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(cfg, x, inp, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(cfg, x, inp, args.cpu_seconds, args.cpu_threads)
     print(json.dumps(result), flush=True)
 
 
@@ -242,10 +260,31 @@ def measure(cfg, args, steps, warmup):
 
     # ---------------- the step's kernels, timed apart ----------------
     # Kernel 1 (top-K + tree + mask) alone, and kernels 2-3 (attention +
-    # acceptance) alone, each over the same number of launches with HIP events
-    # on the launch stream; the average launch time is the loop time / count.
-    k1_ms = timed(make_runner(td.TD_STEP_DRAFT), steps)
-    k23_ms = timed(make_runner(td.TD_STEP_VERIFY), steps)
+    # acceptance) alone, each over the same number of launches.  Two figures:
+    #  - duration: HIP events attached to the kernels' own dispatch
+    #    (td_verify_step_events), one pair per launch, averaged: the
+    #    kernels' execution time as a kernel-trace profiler reports it;
+    #  - loop: graph replays of back-to-back launches between two events on
+    #    the launch stream, divided by the count (includes the launch gaps).
+    def kernel_ms(stages, count):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(count)]
+        for a, b_ in evs:            # create the HIP events behind them
+            a.record(stream)
+            b_.record(stream)
+        for i in range(warmup):
+            fused(i, stages)
+        torch.cuda.synchronize()
+        for i, (a, b_) in enumerate(evs):
+            vs.args = args_per_set[(warmup + i) % n_sets]
+            vs.run_timed(a, b_, stages=stages)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b_) for a, b_ in evs]))
+
+    k1_ms = kernel_ms(td.TD_STEP_DRAFT, steps)
+    k23_ms = kernel_ms(td.TD_STEP_VERIFY, steps)
+    k1_loop_ms = timed(make_runner(td.TD_STEP_DRAFT), steps)
+    k23_loop_ms = timed(make_runner(td.TD_STEP_VERIFY), steps)
 
     # ---------------- per-stage calls (HIP events, eager) ----------------
     names = ["draft_topk", "build_tree+tree_mask", "tree_verify_attn", "accept"]
@@ -284,21 +323,25 @@ def measure(cfg, args, steps, warmup):
     flops_c = int(4 * cfg.hq * cfg.head_dim * (rows * L).sum() + 4 * cfg.hq * cfg.head_dim * anc)
     ridge = MFMA_BF16_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
-    def roofline(kernel, ms, nbytes, nflops):
+    def roofline(kernel, ms, loop_ms, nbytes, nflops):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        tfs = nflops / (ms * 1e-3) / 1e12
         if nflops / nbytes > ridge:
-            ach = nflops / (ms * 1e-3) / 1e12
-            r = dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_TFLOPS,
-                     unit="TFLOP/s", frac=round(ach / MFMA_BF16_TFLOPS, 4), traffic=None)
+            r = dict(bound="mfma", achieved=round(tfs, 2), peak=MFMA_BF16_TFLOPS,
+                     unit="TFLOP/s", frac=round(tfs / MFMA_BF16_TFLOPS, 4), traffic=None)
         else:
-            ach = nbytes / (ms * 1e-3) / 1e9
-            r = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                     frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
+            r = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                     frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None)
         r.update(kernel=kernel, bytes_per_launch=int(nbytes), flops_per_launch=int(nflops),
-                 avg_launch_us=round(ms * 1e3, 2))
+                 avg_launch_us=round(ms * 1e3, 2), timing="HIP events on the kernels' dispatch",
+                 hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                 mfma_frac=round(tfs / MFMA_BF16_TFLOPS, 5) if nflops else None,
+                 loop_us_per_launch=round(loop_ms * 1e3, 2))
         return r
 
-    k1 = roofline("topk_tree (kernel 1: top-K + tree + mask)", k1_ms, bytes_a + bytes_b, 0)
-    k23 = roofline("attention + acceptance (kernels 2-3)", k23_ms, bytes_c, flops_c)
+    k1 = roofline("topk_tree (kernel 1: top-K + tree + mask)", k1_ms, k1_loop_ms,
+                  bytes_a + bytes_b, 0)
+    k23 = roofline("attention + acceptance (kernels 2-3)", k23_ms, k23_loop_ms, bytes_c, flops_c)
     measured = hbm_traffic(cfg.name)
     if measured:
         k1["traffic"] = measured.get("topk_tree")
@@ -406,9 +449,40 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_mib": int(mib), "copies": 5}), flush=True)
 
 
-def cpu_baseline(cfg, x, inp, budget_s):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, x, inp, budget_s, threads=0):
     """The CPU oracle, as it stands, on whole verify steps of the same
-    workload: as many full steps as fit in about budget_s seconds."""
+    workload: as many full steps as fit in about budget_s seconds, first on
+    every core available to this process (the oracle spreads independent
+    outputs over OpenMP threads), then on one thread."""
+    import oracle
+    avail = len(os.sched_getaffinity(0))
+    n = threads if threads > 0 else avail
+    before = oracle.set_threads(0)
+    try:
+        used = oracle.set_threads(n)
+        multi = cpu_steps(cfg, x, inp, budget_s)
+        oracle.set_threads(1)
+        single = cpu_steps(cfg, x, inp, budget_s)
+    finally:
+        oracle.set_threads(before)
+    return {"value": multi["value"], "unit": "verify steps/s", "cores": used, "kind": "oracle",
+            "sample": multi["sample"] + f", {used} OpenMP threads",
+            "cpu_model": cpu_model(), "cores_available": avail,
+            "single_thread": {"value": single["value"], "cores": 1, "sample": single["sample"]}}
+
+
+def cpu_steps(cfg, x, inp, budget_s):
     import oracle
     from tree_draft_build_amd import workload as wl
 
@@ -433,8 +507,8 @@ def cpu_baseline(cfg, x, inp, budget_s):
         el = time.perf_counter() - t0
         if el >= budget_s or steps >= 1000:
             break
-    return {"value": round(steps / el, 3), "unit": "verify steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} whole verify steps of {cfg.name} in {el:.1f} s, single thread"}
+    return {"value": round(steps / el, 3),
+            "sample": f"{steps} whole verify steps of {cfg.name} in {el:.1f} s"}
 
 
 if __name__ == "__main__":

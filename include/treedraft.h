@@ -234,7 +234,8 @@ td_status td_accept(const int32_t *node_token, const int32_t *node_parent, const
  * output arrays (the fields below use their names, layouts and rules).
  * nq_max = n_max + 1.  target_token [batch][n_max+1] is an input: the
  * target's greedy token at every node of the tree this step builds.
- * Workspace: td_verify_step_workspace(args) bytes, 16-byte aligned,
+ * Workspace: td_verify_step_workspace(args) bytes (a function of the shape
+ * fields and attn_dtype), 16-byte aligned,
  * ZERO-FILLED before its first use and again whenever the shape fields
  * (batch, block, vocab, topk, n_max, hq, hkv, head_dim, total_ctx) change;
  * every call leaves it ready for the next call of the same shape.  Calls
@@ -289,6 +290,22 @@ size_t td_step_args_bytes(void);
 size_t td_verify_step_workspace(const td_step_args *args);
 td_status td_verify_step(const td_step_args *args, void *workspace, size_t workspace_bytes,
                          void *stream);
+
+/* ------------------------------------------------------------------------
+ * td_verify_step_events -- td_verify_step with timing events attached to its
+ * kernels (a measurement aid): start_event (a hipEvent_t, or NULL) is
+ * recorded when the call's first kernel begins executing and stop_event
+ * (hipEvent_t or NULL) when its last kernel has finished, from the kernels'
+ * own dispatch timestamps, so hipEventElapsedTime(start, stop) is the
+ * execution time of the call's kernels (for one kernel, its duration as a
+ * kernel-trace profiler reports it; for several, from the first one's start
+ * to the last one's end) without the launch gaps before them.  The events
+ * must have been created by the caller (with timing enabled) on the
+ * stream's device.  Not for use under stream capture.  Same arguments,
+ * results and statuses as td_verify_step otherwise.
+ */
+td_status td_verify_step_events(const td_step_args *args, void *workspace, size_t workspace_bytes,
+                                void *stream, void *start_event, void *stop_event);
 
 #ifdef __cplusplus
 }

@@ -39,6 +39,8 @@ def _load(path=None):
         lib.or_tree_attn.argtypes = [P, P, P, P, P, P, P, P, c_int, c_int, c_int, c_int, c_int,
                                      c_double, c_int, P, c_int32, c_int32, c_int32]
         lib.or_accept.argtypes = [P, P, P, P, c_int, c_int, c_int, P, P, P]
+        lib.or_set_threads.argtypes = [c_int]
+        lib.or_set_threads.restype = c_int
         for f in (lib.or_draft_topk, lib.or_build_tree, lib.or_tree_mask, lib.or_tree_attn,
                   lib.or_accept):
             f.restype = c_int
@@ -53,6 +55,13 @@ def use_library(path=None):
     _lib = None
     if path is not None:
         _load(path)
+
+
+def set_threads(n: int = 0) -> int:
+    """Threads the oracle spreads independent outputs over (n <= 0: keep the
+    current setting); returns the count in effect.  Results do not depend on
+    it: every output is computed by one thread in the same order."""
+    return int(_load().or_set_threads(int(n)))
 
 
 def _p(a):

@@ -11,7 +11,10 @@
  *
  * Arithmetic is float64 throughout; inputs in bfloat16 or float32 are widened
  * exactly.  Loops run in the order the definitions read; no blocking, no
- * reordering, no fast-math.
+ * reordering, no fast-math.  Independent outputs (one logit row, one
+ * sequence's tree, one attention row of one head) may be computed by
+ * different OpenMP threads; each output's own arithmetic runs in the same
+ * order whatever the thread count, so results do not depend on it.
  *
  * Readings of points the pages leave open (listed again in the design notes):
  *  - the branching universe at depth d+1 is the top-K of q_{d+1} (K is a
@@ -29,6 +32,22 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads used by the functions below (1 without OpenMP); returns the count
+ * in effect. */
+int or_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
 
 enum { OR_OK = 0, OR_EINVAL = 1, OR_EDISAGREE = 5 };
 
@@ -71,10 +90,19 @@ int or_draft_topk(const void *logits, int dtype, int batch, int block, int vocab
     if (!logits || batch < 0 || block <= 0 || vocab <= 0 || K <= 0 || K > vocab ||
         pos_stride < vocab || (dtype != 0 && dtype != 1))
         return OR_EINVAL;
+    int status = OR_OK;
+#pragma omp parallel
+    {
     or_cand *all = (or_cand *)malloc(sizeof(or_cand) * (size_t)vocab);
-    if (!all) return OR_EINVAL;
-    for (int b = 0; b < batch; ++b) {
-        for (int k = 0; k < block; ++k) {
+    if (!all) {
+#pragma omp atomic write
+        status = OR_EINVAL;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < (int64_t)batch * block; ++r) {
+        if (!all) continue;
+        int b = (int)(r / block), k = (int)(r % block);
+        {
             int64_t row = ((int64_t)b * block + k) * pos_stride;
             /* max, then the sum of exp(l - max) in token order */
             double m = -INFINITY;
@@ -101,7 +129,8 @@ int or_draft_topk(const void *logits, int dtype, int batch, int block, int vocab
         }
     }
     free(all);
-    return OR_OK;
+    }
+    return status;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -145,10 +174,18 @@ int or_build_tree(const int32_t *topk_id, const double *topk_logq, int batch, in
     if (!topk_id || !topk_logq || batch < 0 || block <= 0 || K <= 0 || n_max < 0)
         return OR_EINVAL;
     int cap = K * (n_max + 1) + 1;
-    or_node *front = (or_node *)malloc(sizeof(or_node) * (size_t)cap);
-    if (!front) return OR_EINVAL;
     int W = n_max + 1;
+    int status = OR_OK;
+#pragma omp parallel
+    {
+    or_node *front = (or_node *)malloc(sizeof(or_node) * (size_t)cap);
+    if (!front) {
+#pragma omp atomic write
+        status = OR_EINVAL;
+    }
+#pragma omp for schedule(dynamic, 1)
     for (int b = 0; b < batch; ++b) {
+        if (!front) continue;
         int32_t *tok = node_token + (int64_t)b * W;
         int32_t *par = node_parent + (int64_t)b * W;
         int32_t *dep = node_depth + (int64_t)b * W;
@@ -209,7 +246,8 @@ int or_build_tree(const int32_t *topk_id, const double *topk_logq, int batch, in
         if (speedup_out) speedup_out[b] = s_now;
     }
     free(front);
-    return OR_OK;
+    }
+    return status;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -273,13 +311,25 @@ int or_tree_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
     int64_t maxlen = 0;
     for (int b = b_begin; b < b_end; ++b)
         if (ctx_offsets[b + 1] - ctx_offsets[b] > maxlen) maxlen = ctx_offsets[b + 1] - ctx_offsets[b];
+    int status = OR_OK;
+#pragma omp parallel
+    {
     double *sc = (double *)malloc(sizeof(double) * (size_t)(maxlen + nq_max));
-    if (!sc) return OR_EINVAL;
-    for (int b = b_begin; b < b_end; ++b) {
+    if (!sc) {
+#pragma omp atomic write
+        status = OR_EINVAL;
+    }
+    /* one (sequence, row, head) output per iteration */
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < (int64_t)(b_end - b_begin) * nq_max * hq; ++t) {
+        if (!sc) continue;
+        int b = b_begin + (int)(t / ((int64_t)nq_max * hq));
+        int i = (int)((t / hq) % nq_max);
+        int h = (int)(t % hq);
         int64_t c0 = ctx_offsets[b], L = ctx_offsets[b + 1] - ctx_offsets[b];
         int rows = n_nodes[b] + 1;
-        for (int i = 0; i < nq_max; ++i)
-            for (int h = 0; h < hq; ++h) {
+        {
+            {
                 double *o = out + (((int64_t)(b - b_begin) * nq_max + i) * hq + h) * d;
                 for (int e = 0; e < d; ++e) o[e] = 0.0;
                 if (i >= rows || (row_limit >= 0 && i > row_limit)) continue;
@@ -323,9 +373,11 @@ int or_tree_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
                     for (int e = 0; e < d; ++e) o[e] += p * widen(v_tree, dtype, voff + e);
                 }
             }
+        }
     }
     free(sc);
-    return OR_OK;
+    }
+    return status;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -25,7 +25,7 @@ def b():
 
 def test_every_declared_symbol_is_exported(b):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(b.lib, n), n
     assert sorted(b.EXPORTED) == names
@@ -144,3 +144,4 @@ def test_step_args_layout_and_validation(b):
     a.hkv = 8
     a.stages = b.TD_STEP_DRAFT
     assert b.lib.td_verify_step(ctypes.byref(a), FAKE, 1 << 30, None) == 2
+

@@ -172,3 +172,29 @@ def test_one_wrong_mask_bit_is_visible():
     diff = np.abs(flipped - base).max(axis=-1)
     assert diff[0, 9].min() > 0.1                 # far beyond the bf16 tolerance 2e-2
     assert np.all(diff[0, :9] == 0) and np.all(diff[0, 10:] == 0)
+
+
+def test_thread_count_does_not_change_results():
+    """The oracle's outputs are the same, bit for bit, on one thread and on
+    several (each output is computed by one thread in a fixed order)."""
+    import oracle as orc
+    from tree_draft_build_amd import workload as wl
+    cfg = wl.CONFIGS["tiny_fixed"].replace(batch=3, n_max=12)
+    x = wl.make_logits(cfg)
+    inp = wl.make_attn_inputs(cfg)
+    res = []
+    before = orc.set_threads(0)
+    try:
+        for n in (1, 4):
+            orc.set_threads(n)
+            ids, lq, lse = orc.draft_topk(x, cfg.topk)
+            tr = orc.build_tree(ids, lq, cfg.n_max, False)
+            m = orc.tree_mask(tr["node_parent"], tr["n_nodes"])
+            o = orc.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
+                              inp["k_tree"], inp["v_tree"], m, tr["n_nodes"], cfg.hq, cfg.hkv,
+                              cfg.head_dim, wl.attn_scale(cfg))
+            res.append((ids, lq, lse, tr["node_token"], tr["node_logrho"], o))
+    finally:
+        orc.set_threads(before)
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)

@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "TD_OK", 1: "TD_EINVAL", 2: "TD_ECAPACITY", 3: "TD_EUNSUPPORT
 EXPORTED = ["td_abi_version", "td_last_error", "td_draft_topk_workspace", "td_draft_topk",
             "td_build_tree", "td_tree_mask", "td_tree_verify_attn_workspace",
             "td_tree_verify_attn", "td_accept", "td_step_args_bytes", "td_verify_step_workspace",
-            "td_verify_step", "td_workspace_status"]
+            "td_verify_step", "td_workspace_status", "td_verify_step_events"]
 
 
 class StepArgs(ctypes.Structure):
@@ -85,8 +85,9 @@ def _load():
     lib.td_verify_step_workspace.restype = c_size_t
     lib.td_verify_step.argtypes = [ctypes.POINTER(StepArgs), P, c_size_t, P]
     lib.td_workspace_status.argtypes = [P, c_size_t, P]
+    lib.td_verify_step_events.argtypes = [ctypes.POINTER(StepArgs), P, c_size_t, P, P, P]
     for name in ("td_draft_topk", "td_build_tree", "td_tree_mask", "td_tree_verify_attn",
-                 "td_accept", "td_verify_step", "td_workspace_status"):
+                 "td_accept", "td_verify_step", "td_workspace_status", "td_verify_step_events"):
         getattr(lib, name).restype = c_int
     if lib.td_step_args_bytes() != ctypes.sizeof(StepArgs):
         raise ImportError("td_step_args layout differs between the library and this binding")
@@ -331,6 +332,16 @@ class VerifyStep:
         """TD_OK, or TD_ESYNC if a hand-off of an earlier call gave up
         (waits for the stream; clears the status word)."""
         return workspace_status(self.workspace, stream)
+
+    def run_timed(self, start, stop, stream=None, stages=0):
+        """Enqueue the step with torch timing events attached to its kernels:
+        start.elapsed_time(stop) is then the execution time of the selected
+        stages' kernels, first start to last end (both events must have been
+        recorded once before, so that their HIP events exist)."""
+        self.args.stages = stages
+        _check(lib.td_verify_step_events(ctypes.byref(self.args), _ptr(self.workspace),
+                                         self.workspace.numel(), _stream(stream),
+                                         c_void_p(start.cuda_event), c_void_p(stop.cuda_event)))
 
     def run(self, stream=None, stages=0):
         """Enqueue the step (stages: TD_STEP_DRAFT | TD_STEP_VERIFY, 0 = both)."""

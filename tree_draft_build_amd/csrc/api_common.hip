@@ -12,6 +12,8 @@ namespace {
 thread_local char g_err[512] = {0};
 }
 
+thread_local LaunchEvents t_launch_events = {nullptr, nullptr};
+
 void set_error(const char *fmt, ...) {
     va_list ap;
     va_start(ap, fmt);

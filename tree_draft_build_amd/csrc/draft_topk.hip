@@ -859,7 +859,7 @@ template <typename T, int KM, bool FUSE, int SLOTS>
 void launch_topk(const void *logits, int rows, int vocab, int64_t pos_stride, int K,
                  const TopkPlan &pl, void *ws, int32_t *topk_id, double *topk_logq, double *lse,
                  const TreeParams &tp, const TreeOut &to, hipStream_t st) {
-    hipLaunchKernelGGL((topk_kernel<T, KM, FUSE, SLOTS>), dim3(pl.splits, rows), dim3(kTopkThreads),
+    TD_LAUNCH((topk_kernel<T, KM, FUSE, SLOTS>), dim3(pl.splits, rows), dim3(kTopkThreads),
                        0, st, static_cast<const T *>(logits), vocab, pos_stride, pl.slice, pl.splits,
                        K, ws, topk_id, topk_logq, lse, tp, to);
 }

@@ -1,6 +1,7 @@
 // Internal helpers of libtreedraft (gfx950, wave64).  Not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,6 +35,28 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Events attached to the calling thread's next kernel launches (set by
+// td_verify_step_events for the duration of one call): the first launch
+// records `start` when it begins executing, every launch records `stop` when
+// it ends, so the last launch's end stands.  Both null: plain launches.
+struct LaunchEvents {
+    hipEvent_t start, stop;
+};
+extern thread_local LaunchEvents t_launch_events;
+
+// hipLaunchKernelGGL, with the thread's launch events attached when set.
+#define TD_LAUNCH(KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                      \
+    do {                                                                                       \
+        if (::td::t_launch_events.start || ::td::t_launch_events.stop) {                       \
+            hipEvent_t td_start_ = ::td::t_launch_events.start;                               \
+            ::td::t_launch_events.start = nullptr;                                             \
+            hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, td_start_,               \
+                                  ::td::t_launch_events.stop, 0, __VA_ARGS__);                 \
+        } else {                                                                               \
+            hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);               \
+        }                                                                                      \
+    } while (0)
 
 // ---------------------------------------------------------------------------
 // device side

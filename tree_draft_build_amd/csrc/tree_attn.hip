@@ -1242,13 +1242,13 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
     const float scale2 = scale * kLog2e;
     const int64_t prow_total = pl.n_chunks * hkv * pl.n_rg * kRowsPerGroup;
 #define TD_SPLIT(OWN)                                                                          \
-    hipLaunchKernelGGL((attn_split_f32<D, OWN>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)), \
+    TD_LAUNCH((attn_split_f32<D, OWN>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)), \
                        dim3(kAttnThreads), 0, st, static_cast<const float *>(q),                \
                        static_cast<const float *>(k_ctx), static_cast<const float *>(v_ctx), off, n_nodes, \
                        batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,             \
                        static_cast<float *>(ws), prow_total)
 #define TD_SPLIT_BF(...)                                                                       \
-    hipLaunchKernelGGL((attn_split_bf16<D, __VA_ARGS__>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)), \
+    TD_LAUNCH((attn_split_bf16<D, __VA_ARGS__>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)), \
                        dim3(kAttnThreads), 0, st, static_cast<const uint16_t *>(q),             \
                        static_cast<const uint16_t *>(k_ctx), static_cast<const uint16_t *>(v_ctx), \
                        off, n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2, \
@@ -1285,7 +1285,7 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
     const int blocks_per_bg = combine_blocks(pl.group * nq_max, two);
     const int64_t blocks = static_cast<int64_t>(batch) * hkv * blocks_per_bg;
 #define TD_COMBINE(ACC, TWO, NB, ARGS)                                                           \
-    hipLaunchKernelGGL((attn_tree_combine<T, D, ACC, TWO>), dim3(static_cast<unsigned>(NB)),      \
+    TD_LAUNCH((attn_tree_combine<T, D, ACC, TWO>), dim3(static_cast<unsigned>(NB)),      \
                        dim3(kAttnThreads), 0, st, static_cast<const T *>(q), off,                 \
                        static_cast<const T *>(k_tree), static_cast<const T *>(v_tree), mask,      \
                        n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,      \

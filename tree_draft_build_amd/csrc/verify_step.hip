@@ -34,15 +34,23 @@ extern "C" size_t td_verify_step_workspace(const td_step_args *a) {
         a->hq <= 0 || a->hkv <= 0 || a->hq % a->hkv || a->total_ctx < 0)
         return 0;
     const int nq_max = a->n_max + 1;
-    const size_t attn = std::max(
-        attn_workspace_bytes(a->batch, nq_max, a->hq, a->hkv, a->head_dim, a->total_ctx, TD_BF16),
-        attn_workspace_bytes(a->batch, nq_max, a->hq, a->hkv, a->head_dim, a->total_ctx, TD_F32));
+    // the attention partials of the step's own dtype (either's, should the
+    // field hold neither: validation then rejects the call anyway)
+    const bool known = a->attn_dtype == TD_BF16 || a->attn_dtype == TD_F32;
+    const size_t attn = known ? attn_workspace_bytes(a->batch, nq_max, a->hq, a->hkv, a->head_dim,
+                                                     a->total_ctx, a->attn_dtype)
+                              : std::max(attn_workspace_bytes(a->batch, nq_max, a->hq, a->hkv,
+                                                              a->head_dim, a->total_ctx, TD_BF16),
+                                         attn_workspace_bytes(a->batch, nq_max, a->hq, a->hkv,
+                                                              a->head_dim, a->total_ctx, TD_F32));
     return topk_part(a) + attn;
 }
 
-extern "C" td_status td_verify_step(const td_step_args *a, void *workspace, size_t workspace_bytes,
-                                    void *stream) {
-    clear_error();
+namespace {
+
+// Validation of the argument block (no workspace): records the message and
+// returns the status; enqueues nothing.
+td_status check_step(const td_step_args *a) {
     if (!a) return fail(TD_EINVAL, "td_verify_step: null args");
     const int stages = a->stages == 0 ? (TD_STEP_DRAFT | TD_STEP_VERIFY) : a->stages;
     if (stages & ~(TD_STEP_DRAFT | TD_STEP_VERIFY))
@@ -73,11 +81,15 @@ extern "C" td_status td_verify_step(const td_step_args *a, void *workspace, size
         if (st != TD_OK) return st;
     }
     if (!a->mask || !aligned8(a->mask)) return fail(TD_EINVAL, "td_verify_step: mask must be set");
-    if (!workspace || !aligned16(workspace))
-        return fail(TD_EINVAL, "td_verify_step: null or misaligned workspace");
-    if (workspace_bytes < td_verify_step_workspace(a))
-        return fail(TD_EINVAL, "td_verify_step: workspace too small");
+    return TD_OK;
+}
 
+// Enqueue the selected stages (arguments already checked).
+td_status launch_step(const td_step_args *a, void *workspace, void *stream) {
+    const int stages = a->stages == 0 ? (TD_STEP_DRAFT | TD_STEP_VERIFY) : a->stages;
+    const bool draft = stages & TD_STEP_DRAFT;
+    const bool verify = stages & TD_STEP_VERIFY;
+    const int nq_max = a->n_max + 1;
     hipStream_t s = as_stream(stream);
     char *ws = static_cast<char *>(workspace);
     if (draft) {
@@ -96,4 +108,30 @@ extern "C" td_status td_verify_step(const td_step_args *a, void *workspace, size
                          a->head_dim, a->scale, a->attn_dtype, ws + topk_part(a), a->out, &acc, s);
     }
     return check_launch("td_verify_step");
+}
+
+}  // namespace
+
+extern "C" td_status td_verify_step(const td_step_args *a, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+    clear_error();
+    const td_status st = check_step(a);
+    if (st != TD_OK) return st;
+    if (!workspace || !aligned16(workspace))
+        return fail(TD_EINVAL, "td_verify_step: null or misaligned workspace");
+    const size_t need = td_verify_step_workspace(a);
+    if (need == 0)
+        return fail(TD_EINVAL, "td_verify_step: invalid shape fields (batch, block, vocab, topk, "
+                               "n_max, hq, hkv, total_ctx)");
+    if (workspace_bytes < need) return fail(TD_EINVAL, "td_verify_step: workspace too small");
+    return launch_step(a, workspace, stream);
+}
+
+extern "C" td_status td_verify_step_events(const td_step_args *a, void *workspace,
+                                           size_t workspace_bytes, void *stream, void *start_event,
+                                           void *stop_event) {
+    t_launch_events = {static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+    const td_status st = td_verify_step(a, workspace, workspace_bytes, stream);
+    t_launch_events = {nullptr, nullptr};
+    return st;
 }

@@ -116,6 +116,12 @@ CONFIGS: dict[str, Config] = {
 # rate of the same per-sequence work (one cold batch-1 step is latency-bound).
 CONFIGS["qwen3_8b_x64"] = CONFIGS["qwen3_8b"].replace(name="qwen3_8b_x64", index=5, batch=64)
 
+# The Qwen3-8B shape with the tree fixed at its budget (N = 64, 65 query
+# rows): the tree-attention roofline at a full tree (the S(N) stop picks
+# small trees under this logit law).
+CONFIGS["qwen3_8b_tree"] = CONFIGS["qwen3_8b"].replace(name="qwen3_8b_tree", index=6,
+                                                        use_stop=False)
+
 # Variants used only as parity cases.
 CONFIGS["tiny_fixed"] = CONFIGS["tiny"].replace(name="tiny_fixed", use_stop=False)
 # Peaked marginals: S-stop trees reach the budget cap and the full block depth.

@@ -307,6 +307,29 @@ td_status td_verify_step(const td_step_args *args, void *workspace, size_t works
 td_status td_verify_step_events(const td_step_args *args, void *workspace, size_t workspace_bytes,
                                 void *stream, void *start_event, void *stop_event);
 
+/* ------------------------------------------------------------------------
+ * td_verify_step_noalloc -- td_verify_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the same kernels and results, with the workspace
+ * in a static device array of the library (64 MiB per GPU, held by each GPU
+ * the library runs on until the process ends) instead of a caller buffer.
+ * The caller still passes every input and output through args.  The call
+ * allocates nothing; on its first call on a device it looks up that
+ * device's copy of the array.  Each call clears the array's hand-off words
+ * itself (one small fill kernel ahead of the step's kernels, when the draft
+ * stage is selected), so shape changes between calls need no caller action.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other threads) race and give wrong results; a
+ * draft-only call and its verify-only call may be split as in
+ * td_verify_step.  Hand-off failures show only as the sentinels described
+ * at td_workspace_status (lse NaN, n_nodes -1).
+ * Returns TD_ECAPACITY when td_verify_step_workspace(args) exceeds 64 MiB
+ * (one sequence of 4096 context tokens with a 64-node budget at 32/8 heads
+ * of 128 needs 36 MiB; 64 sequences of 8k-token contexts need more: use
+ * td_verify_step there), otherwise the statuses of td_verify_step.
+ */
+td_status td_verify_step_noalloc(const td_step_args *args, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ def b():
 
 def test_every_declared_symbol_is_exported(b):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(b.lib, n), n
     assert sorted(b.EXPORTED) == names
@@ -144,4 +144,11 @@ def test_step_args_layout_and_validation(b):
     a.hkv = 8
     a.stages = b.TD_STEP_DRAFT
     assert b.lib.td_verify_step(ctypes.byref(a), FAKE, 1 << 30, None) == 2
-
+    # the allocation-free variant validates the same way before anything else
+    assert b.lib.td_verify_step_noalloc(ctypes.byref(a), None) == 2
+    assert b.lib.td_verify_step_noalloc(None, None) == 1
+    a.topk = 8
+    a.stages = 0
+    a.batch, a.total_ctx, a.max_ctx = 64, 64 * 32768, 32768
+    assert b.lib.td_verify_step_noalloc(ctypes.byref(a), None) == 2
+    assert "64 MiB" in b.last_error()

@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "TD_OK", 1: "TD_EINVAL", 2: "TD_ECAPACITY", 3: "TD_EUNSUPPORT
 EXPORTED = ["td_abi_version", "td_last_error", "td_draft_topk_workspace", "td_draft_topk",
             "td_build_tree", "td_tree_mask", "td_tree_verify_attn_workspace",
             "td_tree_verify_attn", "td_accept", "td_step_args_bytes", "td_verify_step_workspace",
-            "td_verify_step", "td_workspace_status", "td_verify_step_events"]
+            "td_verify_step", "td_workspace_status", "td_verify_step_noalloc",
+            "td_verify_step_events"]
 
 
 class StepArgs(ctypes.Structure):
@@ -85,9 +86,11 @@ def _load():
     lib.td_verify_step_workspace.restype = c_size_t
     lib.td_verify_step.argtypes = [ctypes.POINTER(StepArgs), P, c_size_t, P]
     lib.td_workspace_status.argtypes = [P, c_size_t, P]
+    lib.td_verify_step_noalloc.argtypes = [ctypes.POINTER(StepArgs), P]
     lib.td_verify_step_events.argtypes = [ctypes.POINTER(StepArgs), P, c_size_t, P, P, P]
     for name in ("td_draft_topk", "td_build_tree", "td_tree_mask", "td_tree_verify_attn",
-                 "td_accept", "td_verify_step", "td_workspace_status", "td_verify_step_events"):
+                 "td_accept", "td_verify_step", "td_workspace_status", "td_verify_step_noalloc",
+                 "td_verify_step_events"):
         getattr(lib, name).restype = c_int
     if lib.td_step_args_bytes() != ctypes.sizeof(StepArgs):
         raise ImportError("td_step_args layout differs between the library and this binding")

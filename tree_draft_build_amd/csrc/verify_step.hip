@@ -10,6 +10,7 @@
 // The device code is the stage calls' own.
 
 #include <algorithm>
+#include <mutex>
 
 #include "step_launch.h"
 #include "td_internal.h"
@@ -134,4 +135,80 @@ extern "C" td_status td_verify_step_events(const td_step_args *a, void *workspac
     const td_status st = td_verify_step(a, workspace, workspace_bytes, stream);
     t_launch_events = {nullptr, nullptr};
     return st;
+}
+
+// ---------------------------------------------------------------------------
+// td_verify_step_noalloc: the same kernels with the workspace in a static
+// device array instead of a caller buffer, for callers that cannot allocate.
+// Each GPU the library runs on holds its own copy of the array until the
+// process ends; host code reaches it only through the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device on its first call.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = size_t(64) << 20;  // 64 MiB per GPU
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address of the current device (looked up once per device).
+td_status scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        set_error("td_verify_step_noalloc: hipGetDevice failed: %s", hipGetErrorString(e));
+        return TD_EHIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(TD_ECAPACITY, "td_verify_step_noalloc: device index above 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            set_error("td_verify_step_noalloc: hipGetSymbolAddress failed: %s", hipGetErrorString(e));
+            return TD_EHIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return TD_OK;
+}
+
+// Zero n bytes (a multiple of 16, 16-byte aligned) with ordinary vector
+// stores: the top-K hand-off words of the previous call must not be seen.
+__global__ __launch_bounds__(256) void zero_fill(uint4 *__restrict__ p, int64_t n16) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+        p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+}  // namespace
+
+extern "C" td_status td_verify_step_noalloc(const td_step_args *a, void *stream) {
+    clear_error();
+    td_status st = check_step(a);
+    if (st != TD_OK) return st;
+    const size_t need = td_verify_step_workspace(a);
+    if (need == 0) return fail(TD_EINVAL, "td_verify_step_noalloc: invalid shape fields");
+    if (need > kScratchBytes)
+        return fail(TD_ECAPACITY, "td_verify_step_noalloc: the problem needs more than the 64 MiB "
+                                  "scratch; use td_verify_step with a workspace");
+    void *ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != TD_OK) return st;
+    const int stages = a->stages == 0 ? (TD_STEP_DRAFT | TD_STEP_VERIFY) : a->stages;
+    if (stages & TD_STEP_DRAFT) {
+        // every call starts from cleared hand-off words (the array keeps the
+        // last call's contents, possibly of another shape); the attention
+        // partials need no clearing
+        const int64_t n16 = static_cast<int64_t>(topk_part(a) / 16);
+        const unsigned blocks = static_cast<unsigned>(std::min<int64_t>(1024, (n16 + 255) / 256));
+        hipLaunchKernelGGL(zero_fill, dim3(blocks), dim3(256), 0, as_stream(stream),
+                           static_cast<uint4 *>(ws), n16);
+    }
+    return launch_step(a, ws, stream);
 }

@@ -36,13 +36,15 @@ def _load(path=None):
         lib.or_build_tree.argtypes = [P, P, c_int, c_int, c_int, c_int, c_int, c_double, c_double,
                                       c_double, c_int, c_double, c_double, P, P, P, P, P, P, P, P, P]
         lib.or_tree_mask.argtypes = [P, P, c_int, c_int, P]
-        lib.or_tree_attn.argtypes = [P, P, P, P, P, P, P, P, c_int, c_int, c_int, c_int, c_int,
+        lib.or_tree_attn.argtypes = [P, P, P, P, P, P, P, P, P, c_int, c_int, c_int, c_int, c_int,
                                      c_double, c_int, P, c_int32, c_int32, c_int32]
+        lib.or_kv_commit.argtypes = [P, P, P, P, P, c_int, c_int, c_int, c_int, c_int, c_int, P, P,
+                                     P, P, P]
         lib.or_accept.argtypes = [P, P, P, P, c_int, c_int, c_int, P, P, P]
         lib.or_set_threads.argtypes = [c_int]
         lib.or_set_threads.restype = c_int
         for f in (lib.or_draft_topk, lib.or_build_tree, lib.or_tree_mask, lib.or_tree_attn,
-                  lib.or_accept):
+                  lib.or_accept, lib.or_kv_commit):
             f.restype = c_int
         _lib = lib
     return _lib
@@ -140,8 +142,10 @@ def tree_mask(node_parent, n_nodes, nq_max=None):
 
 
 def tree_attn(q, k_ctx, v_ctx, ctx_offsets, k_tree, v_tree, mask, n_nodes, hq, hkv, d, scale,
-              seqs=None, row_limit=-1):
-    """float64 output [len(seqs)][nq_max][hq][d]; seqs = contiguous range (b0, b1)."""
+              seqs=None, row_limit=-1, ctx_lengths=None):
+    """float64 output [len(seqs)][nq_max][hq][d]; seqs = contiguous range (b0, b1).
+    ctx_lengths [batch] (optional): sequence b's context is the first
+    ctx_lengths[b] rows of its region (None: the whole region)."""
     arrs = [np.ascontiguousarray(x) for x in (q, k_ctx, v_ctx, k_tree, v_tree)]
     q, k_ctx, v_ctx, k_tree, v_tree = arrs
     dt = _dtype_code(q)
@@ -153,7 +157,8 @@ def tree_attn(q, k_ctx, v_ctx, ctx_offsets, k_tree, v_tree, mask, n_nodes, hq, h
     batch, nq_max = q.shape[0], q.shape[1]
     b0, b1 = (0, batch) if seqs is None else seqs
     out = np.empty((b1 - b0, nq_max, hq, d), np.float64)
-    _check(_load().or_tree_attn(_p(q), _p(k_ctx), _p(v_ctx), _p(ctx_offsets), _p(k_tree),
+    lens = None if ctx_lengths is None else _c(ctx_lengths, np.int64)
+    _check(_load().or_tree_attn(_p(q), _p(k_ctx), _p(v_ctx), _p(ctx_offsets), _p(lens), _p(k_tree),
                                 _p(v_tree), _p(mask), _p(n_nodes), batch, nq_max, hq, hkv, d,
                                 float(scale), dt, _p(out), b0, b1, int(row_limit)), "or_tree_attn")
     return out
@@ -171,3 +176,27 @@ def accept(node_token, node_parent, n_nodes, target_token, block):
     _check(_load().or_accept(_p(node_token), _p(node_parent), _p(n_nodes), _p(target_token), b,
                              W - 1, block, _p(alen), _p(path), _p(bonus)), "or_accept")
     return alen, path, bonus
+
+
+def kv_commit(k_tree, v_tree, accept_len, accept_path, bonus_token, k_cache, v_cache, ctx_offsets,
+              ctx_lengths, hkv, d):
+    """Append each sequence's accepted path (root first) from the tree K/V to
+    its context region.  k_cache / v_cache [total][hkv][d] and ctx_lengths
+    [batch] are updated IN PLACE; returns next_root [batch] (the bonus)."""
+    k_tree = np.ascontiguousarray(k_tree)
+    v_tree = np.ascontiguousarray(v_tree)
+    dt = _dtype_code(k_tree)
+    for x in (v_tree, k_cache, v_cache):
+        assert x.dtype == k_tree.dtype and x.flags.c_contiguous
+    assert ctx_lengths.dtype == np.int64 and ctx_lengths.flags.c_contiguous
+    accept_len = _c(accept_len, np.int32)
+    accept_path = _c(accept_path, np.int32)
+    bonus = _c(bonus_token, np.int32)
+    ctx_offsets = _c(ctx_offsets, np.int64)
+    batch, nq_max = k_tree.shape[0], k_tree.shape[1]
+    block = accept_path.shape[1] - 1
+    nxt = np.empty(batch, np.int32)
+    _check(_load().or_kv_commit(_p(k_tree), _p(v_tree), _p(accept_len), _p(accept_path), _p(bonus),
+                                batch, nq_max, block, hkv, d, dt, _p(k_cache), _p(v_cache),
+                                _p(ctx_offsets), _p(ctx_lengths), _p(nxt)), "or_kv_commit")
+    return nxt

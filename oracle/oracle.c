@@ -296,10 +296,21 @@ int or_tree_mask(const int32_t *node_parent, const int32_t *n_nodes, int batch, 
 /* values.  KV head of query head h is h / (hq / hkv).                       */
 /* ------------------------------------------------------------------------ */
 
+/* ctx_lengths (optional): sequence b's context is the first ctx_lengths[b]
+ * rows of its region ctx_offsets[b] .. ctx_offsets[b+1]-1 (the rest of the
+ * region is room for later tokens); NULL: the whole region. */
+static int64_t ctx_len(const int64_t *ctx_offsets, const int64_t *ctx_lengths, int b)
+{
+    int64_t region = ctx_offsets[b + 1] - ctx_offsets[b];
+    if (!ctx_lengths) return region;
+    return ctx_lengths[b] < region ? ctx_lengths[b] : region;
+}
+
 int or_tree_attn(const void *q, const void *k_ctx, const void *v_ctx, const int64_t *ctx_offsets,
-                 const void *k_tree, const void *v_tree, const uint64_t *mask,
-                 const int32_t *n_nodes, int batch, int nq_max, int hq, int hkv, int d,
-                 double scale, int dtype, double *out, int32_t b_begin, int32_t b_end,
+                 const int64_t *ctx_lengths, const void *k_tree, const void *v_tree,
+                 const uint64_t *mask, const int32_t *n_nodes, int batch, int nq_max, int hq,
+                 int hkv, int d, double scale, int dtype, double *out, int32_t b_begin,
+                 int32_t b_end,
                  int32_t row_limit /* rows > row_limit are skipped (left zero); <0: all */)
 {
     if (!q || !k_ctx || !v_ctx || !ctx_offsets || !k_tree || !v_tree || !mask || !n_nodes ||
@@ -310,7 +321,7 @@ int or_tree_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
     int group = hq / hkv;
     int64_t maxlen = 0;
     for (int b = b_begin; b < b_end; ++b)
-        if (ctx_offsets[b + 1] - ctx_offsets[b] > maxlen) maxlen = ctx_offsets[b + 1] - ctx_offsets[b];
+        if (ctx_len(ctx_offsets, ctx_lengths, b) > maxlen) maxlen = ctx_len(ctx_offsets, ctx_lengths, b);
     int status = OR_OK;
 #pragma omp parallel
     {
@@ -326,7 +337,7 @@ int or_tree_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
         int b = b_begin + (int)(t / ((int64_t)nq_max * hq));
         int i = (int)((t / hq) % nq_max);
         int h = (int)(t % hq);
-        int64_t c0 = ctx_offsets[b], L = ctx_offsets[b + 1] - ctx_offsets[b];
+        int64_t c0 = ctx_offsets[b], L = ctx_len(ctx_offsets, ctx_lengths, b);
         int rows = n_nodes[b] + 1;
         {
             {
@@ -438,4 +449,51 @@ int or_accept(const int32_t *node_token, const int32_t *node_parent, const int32
     free(acc);
     free(depth);
     return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* After verification: the accepted path becomes context.  The target has  */
+/* verified the tree in one pass and decoding continues from the accepted   */
+/* prefix ("Problemstellung"); its keys and values, computed in that pass,  */
+/* are kept (the KV cache of the verification is reused, as the FlexDraft   */
+/* page's decoupled execution does).  For sequence b with accepted length A  */
+/* and path p_0 = root, p_1 .. p_A: tree rows p_0 .. p_A are appended, in    */
+/* that order, after the L_b context rows of b's region; L_b grows by A+1;  */
+/* the bonus token is the next step's root.  Rows that would not fit in the */
+/* region are not written and L_b stops at the region's end.               */
+/* ------------------------------------------------------------------------ */
+
+int or_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accept_len,
+                 const int32_t *accept_path, const int32_t *bonus_token, int batch, int nq_max,
+                 int block, int hkv, int d, int dtype, void *k_cache, void *v_cache,
+                 const int64_t *ctx_offsets, int64_t *ctx_lengths, int32_t *next_root)
+{
+    if (!k_tree || !v_tree || !accept_len || !accept_path || !k_cache || !v_cache ||
+        !ctx_offsets || !ctx_lengths || batch < 0 || nq_max <= 0 || block <= 0 || hkv <= 0 ||
+        d <= 0 || (dtype != 0 && dtype != 1))
+        return OR_EINVAL;
+    size_t esz = dtype == 0 ? 4 : 2;
+    size_t row_bytes = (size_t)hkv * (size_t)d * esz; /* one token: every KV head */
+    for (int b = 0; b < batch; ++b) {
+        int A = accept_len[b];
+        if (A < 0 || A > block) return OR_EINVAL;
+        int64_t region = ctx_offsets[b + 1] - ctx_offsets[b];
+        int64_t L = ctx_lengths[b];
+        if (L < 0 || L > region) return OR_EINVAL;
+        for (int j = 0; j <= A; ++j) {
+            int node = accept_path[(int64_t)b * (block + 1) + j];
+            if (node < 0 || node >= nq_max) return OR_EINVAL;
+            if (L >= region) break; /* the region is full */
+            int64_t dst = ctx_offsets[b] + L;
+            int64_t src = (int64_t)b * nq_max + node;
+            memcpy((char *)k_cache + (size_t)dst * row_bytes,
+                   (const char *)k_tree + (size_t)src * row_bytes, row_bytes);
+            memcpy((char *)v_cache + (size_t)dst * row_bytes,
+                   (const char *)v_tree + (size_t)src * row_bytes, row_bytes);
+            L = L + 1;
+        }
+        ctx_lengths[b] = L;
+        if (next_root) next_root[b] = bonus_token ? bonus_token[b] : -1;
+    }
+    return OR_OK;
 }

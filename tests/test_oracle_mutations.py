@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import test_oracle_accept as tac
+import test_oracle_commit as tcm
 import test_oracle_mask_attn as tma
 import test_oracle_topk as tto
 import test_oracle_tree as ttr
@@ -61,6 +62,17 @@ MUTATIONS = [
     ("bonus from the parent of the last accepted", "bonus_token[b] = tgt[u];",
      "bonus_token[b] = tgt[u > 0 ? par[u] : 0];",
      lambda: tac.test_hand_built([5, 9, 0, 2, 0, 4, -1], 3, [0, 1, 3, 5], 4)),
+    ("commit skips the root", "for (int j = 0; j <= A; ++j) {\n            int node",
+     "for (int j = 1; j <= A; ++j) {\n            int node",
+     lambda: tcm.test_commit_follows_greedy_chain()),
+    ("commit takes the path's parent rows",
+     "int node = accept_path[(int64_t)b * (block + 1) + j];",
+     "int node = accept_path[(int64_t)b * (block + 1) + (j > 0 ? j - 1 : 0)];",
+     lambda: tcm.test_committed_prefix_reproduces_tree_attention()),
+    ("commit ignores the region end", "if (L >= region) break;", "(void)region;",
+     lambda: tcm.test_commit_stops_at_the_region_end()),
+    ("attention ignores context lengths", "if (!ctx_lengths) return region;", "return region;",
+     lambda: tcm.test_attention_over_context_lengths_equals_compacted()),
 ]
 
 

@@ -52,6 +52,8 @@ def parse():
                     help="skip the 64-sequence streaming measurement")
     ap.add_argument("--no-tree-row", dest="tree_row", action="store_false",
                     help="skip the full-tree (N = 64 fixed) measurement")
+    ap.add_argument("--no-decode", dest="decode", action="store_false",
+                    help="skip the multi-step decode loop with KV commit")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="threads of the all-core oracle baseline (0: every core available)")
     return ap.parse_args()
@@ -83,6 +85,11 @@ def main():
             "value": tres["value"], "unit": "verify steps/s", "ms_per_step": tres["ms_per_step"],
             "steps": tres["steps"], "kernels_us": tres["kernels_us"],
             "kernel_roofline": tres["kernel_roofline"]}
+    if args.decode and cfg.name == "qwen3_8b":
+        # the step in a decode loop: the accepted path's K/V committed into
+        # the context after each step, the bonus token as the next root
+        result["decode"] = decode_row(wl.CONFIGS["qwen3_8b_stress"], args,
+                                      max(16, args.steps // 2), max(8, args.warmup))
     if args.streaming and cfg.name == "qwen3_8b":
         # the same per-sequence work, 64 independent sequences per step
         scfg = wl.CONFIGS["qwen3_8b_x64"]
@@ -379,6 +386,114 @@ def measure(cfg, args, steps, warmup):
                                  "TFLOP/s": round(flops_c / (stage_ms[2] * 1e-3) / 1e12, 3)}},
     }
     return result, x, inp
+
+
+def decode_row(cfg, args, steps, warmup):
+    """The verify step in a synthetic decode loop: each step runs kernels 1-3
+    with the commit fused into kernel 3, so the accepted path's keys and
+    values are appended to the context (which grows in place inside a region
+    of room steps * (block + 1) rows) and the bonus token becomes the next
+    root; per-step inputs (logits, tree queries and K/V) rotate over 8 sets.
+    The synthetic target depends on the tree's token paths only, so one
+    target array per input set, made before the loop, serves every step."""
+    import torch
+
+    from tree_draft_build_amd import binding as td
+    from tree_draft_build_amd import workload as wl
+
+    dev = torch.device("cuda:0")
+    n_sets = 8
+    total = 2 * n_sets + warmup + steps          # every step the loop below can run
+    inp0 = wl.make_attn_inputs(cfg)
+    L0 = inp0["ctx_len"].astype(np.int64)
+    region = L0 + total * (cfg.block + 1)
+    off = np.zeros(cfg.batch + 1, np.int64)
+    off[1:] = np.cumsum(region)
+    tdt = torch.bfloat16 if cfg.attn_dtype == "bf16" else torch.float32
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    kc = torch.zeros((int(off[-1]), cfg.hkv, cfg.head_dim), dtype=tdt, device=dev)
+    vc = torch.zeros_like(kc)
+    for b in range(cfg.batch):
+        o = int(inp0["ctx_offsets"][b])
+        kc[int(off[b]):int(off[b]) + int(L0[b])] = up(inp0["k_ctx"][o:o + int(L0[b])])
+        vc[int(off[b]):int(off[b]) + int(L0[b])] = up(inp0["v_ctx"][o:o + int(L0[b])])
+    goff = torch.from_numpy(off).to(dev)
+    lens = torch.from_numpy(L0.copy()).to(dev)
+    # kernel 1 reads the root as it starts, kernel 3 of the same step writes
+    # the bonus into the same array afterwards: the next step's root
+    root = torch.zeros(cfg.batch, dtype=torch.int32, device=dev)
+    vs = td.VerifyStep(batch=cfg.batch, block=cfg.block, vocab=cfg.vocab, topk=cfg.topk,
+                       n_max=cfg.n_max, use_stop=cfg.use_stop,
+                       cost=(cfg.cost_a, cfg.cost_b, cfg.cost_c, cfg.cost_knee), l_ar=cfg.l_ar,
+                       ahat0=cfg.ahat0, hq=cfg.hq, hkv=cfg.hkv, head_dim=cfg.head_dim,
+                       scale=wl.attn_scale(cfg),
+                       logits_dtype=td.TD_BF16 if cfg.logit_dtype == "bf16" else td.TD_F32,
+                       attn_dtype=td.TD_BF16 if cfg.attn_dtype == "bf16" else td.TD_F32,
+                       total_ctx=int(off[-1]), max_ctx=int(region.max()), device=dev)
+    sets, accepted_per_set = [], []
+    for k in range(n_sets):
+        scfg = cfg.replace(index=cfg.index + 100 + k)
+        x = wl.make_logits(scfg)
+        inp = wl.make_attn_inputs(scfg)
+        d = dict(logits=up(x), q=up(inp["q"]), k_tree=up(inp["k_tree"]), v_tree=up(inp["v_tree"]))
+        tg = torch.full((cfg.batch, cfg.nq_max), -1, dtype=torch.int32, device=dev)
+        vs.set_inputs(d["logits"], d["q"], kc, vc, goff, d["k_tree"], d["v_tree"], tg,
+                      root_token=root, ctx_lengths=lens)
+        vs.run(stages=td.TD_STEP_DRAFT)
+        torch.cuda.synchronize()
+        tree = {k_: v.cpu().numpy() for k_, v in vs.tree.items()}
+        tg.copy_(torch.from_numpy(wl.target_tokens(scfg, wl.logits_as_f64(x, scfg.logit_dtype),
+                                                   tree["node_token"], tree["node_parent"],
+                                                   tree["n_nodes"])))
+        vs.set_inputs(d["logits"], d["q"], kc, vc, goff, d["k_tree"], d["v_tree"], tg,
+                      root_token=root, ctx_lengths=lens, commit=True, next_root=root)
+        sets.append((td.StepArgs.from_buffer_copy(vs.args), d, tg))
+
+    def one(i):
+        vs.args = sets[i % n_sets][0]
+        vs.run()
+
+    G = n_sets
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    for i in range(G):           # warm the kernels before capture (no commit state lost:
+        one(i)                   # these steps are part of the loop)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for i in range(G):
+            one(i)
+    stream = torch.cuda.current_stream()
+    done = G
+    while done < warmup:
+        graph.replay()
+        done += G
+    torch.cuda.synchronize()
+    len0 = lens.cpu().numpy().copy()
+    reps = max(1, steps // G)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / (reps * G)
+    grown = lens.cpu().numpy() - len0
+    tokens = float(grown.sum()) / (reps * G)            # committed tokens per step, all sequences
+    assert td.workspace_status(vs.workspace) == td.TD_OK
+    return {"workload": cfg.name + " decode loop", "batch": cfg.batch, "steps": reps * G,
+            "value": round(1e3 / ms, 1), "unit": "decode steps/s", "ms_per_step": round(ms, 5),
+            "tokens_per_step": round(tokens, 3),
+            "tokens_per_s": round(tokens * 1e3 / ms, 1),
+            "context_growth": [int(v) for v in grown[:4]],
+            "note": "kernels 1-3 per step, the KV commit fused into kernel 3, which also "
+                    "writes the bonus as the next step's root"}
 
 
 def _code_tokens(text):

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define TD_ABI_VERSION 1
+#define TD_ABI_VERSION 2
 
 /* Compiled capacities. */
 #define TD_MAX_TOPK 32        /* K */
@@ -183,10 +183,14 @@ td_status td_tree_mask(const int32_t *node_parent, const int32_t *n_nodes, int32
  * Rows i > n_nodes[b] are written as zeros.
  * Inputs:
  *   q        [batch][nq_max][hq][head_dim]
- *   k_ctx, v_ctx [total_ctx][hkv][head_dim]; sequence b owns context rows
- *            ctx_offsets[b] .. ctx_offsets[b+1]-1 (ctx_offsets int64
+ *   k_ctx, v_ctx [total_ctx][hkv][head_dim]; sequence b owns the region of
+ *            rows ctx_offsets[b] .. ctx_offsets[b+1]-1 (ctx_offsets int64
  *            [batch+1], device, non-decreasing, ctx_offsets[0] = 0,
- *            ctx_offsets[batch] = total_ctx).  max_ctx >= every length.
+ *            ctx_offsets[batch] = total_ctx).  Its context is the whole
+ *            region when ctx_lengths is NULL, else the region's first
+ *            ctx_lengths[b] rows (int64 [batch], device; values are clamped
+ *            to [0, region size]); the rest of a region is room for tokens
+ *            that td_kv_commit appends.  max_ctx is not used.
  *   k_tree, v_tree [batch][nq_max][hkv][head_dim]
  *   mask     as written by td_tree_mask; n_nodes [batch].
  *   dtype TD_BF16 or TD_F32 (all of q/k/v/out); head_dim 64 or 128.
@@ -198,7 +202,8 @@ td_status td_tree_mask(const int32_t *node_parent, const int32_t *n_nodes, int32
 size_t td_tree_verify_attn_workspace(int32_t batch, int32_t nq_max, int32_t hq, int32_t hkv,
                                      int32_t head_dim, int64_t total_ctx, int64_t max_ctx);
 td_status td_tree_verify_attn(const void *q, const void *k_ctx, const void *v_ctx,
-                              const int64_t *ctx_offsets, int64_t total_ctx, int64_t max_ctx,
+                              const int64_t *ctx_offsets, const int64_t *ctx_lengths,
+                              int64_t total_ctx, int64_t max_ctx,
                               const void *k_tree, const void *v_tree, const uint64_t *mask,
                               const int32_t *n_nodes, int32_t batch, int32_t nq_max, int32_t hq,
                               int32_t hkv, int32_t head_dim, float scale, td_dtype dtype,
@@ -225,6 +230,37 @@ td_status td_accept(const int32_t *node_token, const int32_t *node_parent, const
                     void *stream);
 
 /* ------------------------------------------------------------------------
+ * td_kv_commit -- after stage (d): the accepted prefix becomes context.
+ * The target verified every tree node in one pass and decoding continues
+ * from the accepted prefix (Problemstellung); the keys and values that pass
+ * computed for the prefix's tokens are kept rather than recomputed (the
+ * FlexDraft page, Methodik §3, decoupled execution: the verification's KV
+ * cache is reused).  For sequence b with accepted length A = accept_len[b]
+ * and path p_0 = 0 (the root), p_1 .. p_A = accept_path[b][0..A]: the tree
+ * rows p_0 .. p_A of k_tree / v_tree (every KV head) are copied, in that
+ * order, to rows ctx_offsets[b] + L_b, ... of k_cache / v_cache, where
+ * L_b = ctx_lengths[b]; then ctx_lengths[b] += A + 1 and next_root[b] =
+ * bonus_token[b] (the bonus token is the next step's root).  Rows that
+ * would pass the end of b's region (ctx_offsets[b+1]) are not written and
+ * ctx_lengths[b] stops at the region's size; a region with room for
+ * block + 1 more rows never overflows.
+ * Inputs:  k_tree, v_tree [batch][nq_max][hkv][head_dim] (the tree rows
+ *          given to td_tree_verify_attn); accept_len [batch], accept_path
+ *          [batch][block+1], bonus_token [batch] as written by td_accept
+ *          (path entries outside [0, nq_max) end the copy).
+ * In/out:  k_cache, v_cache [total][hkv][head_dim] (the context arrays of
+ *          td_tree_verify_attn; same dtype as the tree rows); ctx_lengths
+ *          [batch] int64.  ctx_offsets [batch+1] as for the attention.
+ * Output:  next_root [batch] (may be NULL).
+ * dtype TD_BF16 or TD_F32; head_dim 64 or 128; 16-byte aligned arrays.
+ */
+td_status td_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accept_len,
+                       const int32_t *accept_path, const int32_t *bonus_token, int32_t batch,
+                       int32_t nq_max, int32_t block, int32_t hkv, int32_t head_dim,
+                       td_dtype dtype, void *k_cache, void *v_cache, const int64_t *ctx_offsets,
+                       int64_t *ctx_lengths, int32_t *next_root, void *stream);
+
+/* ------------------------------------------------------------------------
  * td_verify_step -- the whole verify step, stages (a) to (d), in three
  * kernels instead of the five calls' seven: (1) top-K of every position,
  * then, by the last position of each sequence to finish, that sequence's
@@ -241,6 +277,9 @@ td_status td_accept(const int32_t *node_token, const int32_t *node_parent, const
  * every call leaves it ready for the next call of the same shape.  Calls
  * that overlap in time must not share a workspace.  A broken hand-off is
  * reported by td_workspace_status (see there for the sentinels).
+ * With commit != 0 the step also performs td_kv_commit (inside kernel 3,
+ * after each sequence's acceptance walk): ctx_lengths must then be set, and
+ * k_ctx / v_ctx are written (rows past each context) as k_cache / v_cache.
  * stages selects the kernels a call enqueues: TD_STEP_DRAFT (kernel 1: top-K,
  * tree, mask), TD_STEP_VERIFY (kernels 2 and 3: attention and acceptance),
  * or 0 for both.  A serving loop builds the tree with TD_STEP_DRAFT, runs the
@@ -267,6 +306,7 @@ typedef struct {
     /* stage (c) */
     const void *q, *k_ctx, *v_ctx;
     const int64_t *ctx_offsets;
+    int64_t *ctx_lengths; /* [batch] or NULL (NULL: whole regions, no commit) */
     int64_t total_ctx, max_ctx;
     const void *k_tree, *v_tree;
     int32_t hq, hkv, head_dim;
@@ -274,6 +314,9 @@ typedef struct {
     td_dtype attn_dtype;
     /* stage (d) */
     const int32_t *target_token;
+    /* after (d): KV commit of the accepted path (td_kv_commit) */
+    int32_t commit;       /* nonzero: commit; needs ctx_lengths */
+    int32_t *next_root;   /* [batch] or NULL: the bonus tokens, as next roots */
     /* outputs */
     int32_t *topk_id;
     double *topk_logq, *lse;

@@ -25,14 +25,14 @@ def b():
 
 def test_every_declared_symbol_is_exported(b):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(b.lib, n), n
     assert sorted(b.EXPORTED) == names
 
 
 def test_abi_version(b):
-    assert b.lib.td_abi_version() == 1
+    assert b.lib.td_abi_version() == 2
 
 
 def test_workspace_status_validation(b):
@@ -93,18 +93,32 @@ def test_mask_accept_validation(b):
 
 def test_attention_validation(b):
     ws = b.tree_verify_attn_workspace(1, 65, 32, 8, 128, 4096, 4096)
-    base = [FAKE, FAKE, FAKE, FAKE, 4096, 4096, FAKE, FAKE, FAKE, FAKE, 1, 65, 32, 8, 128,
+    base = [FAKE, FAKE, FAKE, FAKE, None, 4096, 4096, FAKE, FAKE, FAKE, FAKE, 1, 65, 32, 8, 128,
             0.088, 1, FAKE, FAKE, ws, None]
-    bad = list(base); bad[13] = 7
+    bad = list(base); bad[14] = 7
     assert b.lib.td_tree_verify_attn(*bad) == 1 and "multiple" in b.last_error()
-    bad = list(base); bad[14] = 96
+    bad = list(base); bad[15] = 96
     assert b.lib.td_tree_verify_attn(*bad) == 3
-    bad = list(base); bad[19] = ws - 1
+    bad = list(base); bad[20] = ws - 1
     assert b.lib.td_tree_verify_attn(*bad) == 1 and "workspace" in b.last_error()
     bad = list(base); bad[0] = FAKE8
     assert b.lib.td_tree_verify_attn(*bad) == 1
-    bad = list(base); bad[11] = 257
+    bad = list(base); bad[12] = 257
     assert b.lib.td_tree_verify_attn(*bad) == 2
+    bad = list(base); bad[4] = P(4096 + 4)          # misaligned context lengths
+    assert b.lib.td_tree_verify_attn(*bad) == 1
+
+
+def test_kv_commit_validation(b):
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 65, 16, 8, 128, 1, FAKE, FAKE, FAKE, FAKE, None, None]
+    bad = list(base); bad[0] = None
+    assert b.lib.td_kv_commit(*bad) == 1 and "null" in b.last_error()
+    bad = list(base); bad[9] = 96
+    assert b.lib.td_kv_commit(*bad) == 3
+    bad = list(base); bad[7] = 33
+    assert b.lib.td_kv_commit(*bad) == 2
+    bad = list(base); bad[11] = FAKE8
+    assert b.lib.td_kv_commit(*bad) == 1 and "misaligned" in b.last_error()
 
 
 def test_step_args_layout_and_validation(b):

@@ -29,7 +29,7 @@ EXPORTED = ["td_abi_version", "td_last_error", "td_draft_topk_workspace", "td_dr
             "td_build_tree", "td_tree_mask", "td_tree_verify_attn_workspace",
             "td_tree_verify_attn", "td_accept", "td_step_args_bytes", "td_verify_step_workspace",
             "td_verify_step", "td_workspace_status", "td_verify_step_noalloc",
-            "td_verify_step_events"]
+            "td_verify_step_events", "td_kv_commit"]
 
 
 class StepArgs(ctypes.Structure):
@@ -41,10 +41,11 @@ class StepArgs(ctypes.Structure):
         ("cost_c", c_double), ("cost_knee", c_int32), ("l_ar", c_double), ("ahat0", c_double),
         ("root_token", c_void_p),
         ("q", c_void_p), ("k_ctx", c_void_p), ("v_ctx", c_void_p), ("ctx_offsets", c_void_p),
-        ("total_ctx", c_int64), ("max_ctx", c_int64), ("k_tree", c_void_p), ("v_tree", c_void_p),
+        ("ctx_lengths", c_void_p), ("total_ctx", c_int64), ("max_ctx", c_int64), ("k_tree", c_void_p), ("v_tree", c_void_p),
         ("hq", c_int32), ("hkv", c_int32), ("head_dim", c_int32), ("scale", c_float),
         ("attn_dtype", c_int),
         ("target_token", c_void_p),
+        ("commit", c_int32), ("next_root", c_void_p),
         ("topk_id", c_void_p), ("topk_logq", c_void_p), ("lse", c_void_p),
         ("n_nodes", c_void_p), ("node_token", c_void_p), ("node_parent", c_void_p),
         ("node_depth", c_void_p), ("node_logrho", c_void_p), ("ahat", c_void_p),
@@ -78,8 +79,10 @@ def _load():
     lib.td_tree_mask.argtypes = [P, P, c_int32, c_int32, P, P]
     lib.td_tree_verify_attn_workspace.argtypes = [c_int32] * 5 + [c_int64, c_int64]
     lib.td_tree_verify_attn_workspace.restype = c_size_t
-    lib.td_tree_verify_attn.argtypes = [P, P, P, P, c_int64, c_int64, P, P, P, P, c_int32, c_int32,
+    lib.td_tree_verify_attn.argtypes = [P, P, P, P, P, c_int64, c_int64, P, P, P, P, c_int32, c_int32,
                                         c_int32, c_int32, c_int32, c_float, c_int, P, P, c_size_t, P]
+    lib.td_kv_commit.argtypes = [P, P, P, P, P, c_int32, c_int32, c_int32, c_int32, c_int32, c_int,
+                                 P, P, P, P, P, P]
     lib.td_accept.argtypes = [P, P, P, P, c_int32, c_int32, c_int32, P, P, P, P]
     lib.td_step_args_bytes.restype = c_size_t
     lib.td_verify_step_workspace.argtypes = [ctypes.POINTER(StepArgs)]
@@ -90,7 +93,7 @@ def _load():
     lib.td_verify_step_events.argtypes = [ctypes.POINTER(StepArgs), P, c_size_t, P, P, P]
     for name in ("td_draft_topk", "td_build_tree", "td_tree_mask", "td_tree_verify_attn",
                  "td_accept", "td_verify_step", "td_workspace_status", "td_verify_step_noalloc",
-                 "td_verify_step_events"):
+                 "td_verify_step_events", "td_kv_commit"):
         getattr(lib, name).restype = c_int
     if lib.td_step_args_bytes() != ctypes.sizeof(StepArgs):
         raise ImportError("td_step_args layout differs between the library and this binding")
@@ -235,8 +238,10 @@ def tree_verify_attn_alloc_workspace(batch, nq_max, hq, hkv, head_dim, total_ctx
 
 
 def tree_verify_attn(q, k_ctx, v_ctx, ctx_offsets, total_ctx, max_ctx, k_tree, v_tree, mask,
-                     n_nodes, scale, out=None, workspace=None, stream=None):
-    """q [b][nq][hq][d]; k_ctx/v_ctx [total][hkv][d]; k_tree/v_tree [b][nq][hkv][d]."""
+                     n_nodes, scale, out=None, workspace=None, stream=None, ctx_lengths=None):
+    """q [b][nq][hq][d]; k_ctx/v_ctx [total][hkv][d]; k_tree/v_tree [b][nq][hkv][d];
+    ctx_lengths int64 [b] or None (the context is the first ctx_lengths[b]
+    rows of sequence b's region; None: the whole region)."""
     _dev(q, "q")
     b, nq, hq, d = q.shape
     hkv = k_tree.shape[2]
@@ -244,6 +249,8 @@ def tree_verify_attn(q, k_ctx, v_ctx, ctx_offsets, total_ctx, max_ctx, k_tree, v
                          ("k_ctx", k_ctx, (total_ctx, hkv, d)), ("v_ctx", v_ctx, (total_ctx, hkv, d))):
         _dev(t, name, q.dtype, shp)
     _dev(ctx_offsets, "ctx_offsets", torch.int64, (b + 1,))
+    if ctx_lengths is not None:
+        _dev(ctx_lengths, "ctx_lengths", torch.int64, (b,))
     _dev(mask, "mask", torch.int64, (b, nq, (nq + 63) // 64))
     _dev(n_nodes, "n_nodes", torch.int32, (b,))
     if out is None:
@@ -251,7 +258,8 @@ def tree_verify_attn(q, k_ctx, v_ctx, ctx_offsets, total_ctx, max_ctx, k_tree, v
     if workspace is None:
         workspace = tree_verify_attn_alloc_workspace(b, nq, hq, hkv, d, total_ctx, max_ctx,
                                                      q.device)
-    _check(lib.td_tree_verify_attn(_ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_offsets), total_ctx,
+    _check(lib.td_tree_verify_attn(_ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_offsets),
+                                   _ptr(ctx_lengths), total_ctx,
                                    max_ctx, _ptr(k_tree), _ptr(v_tree), _ptr(mask), _ptr(n_nodes), b,
                                    nq, hq, hkv, d, float(scale), _dt(q), _ptr(out), _ptr(workspace),
                                    workspace.numel(), _stream(stream)))
@@ -273,6 +281,30 @@ def accept(node_token, node_parent, n_nodes, target_token, block, out=None, stre
     _check(lib.td_accept(_ptr(node_token), _ptr(node_parent), _ptr(n_nodes), _ptr(target_token), b,
                          W - 1, block, _ptr(alen), _ptr(path), _ptr(bonus), _stream(stream)))
     return alen, path, bonus
+
+
+def kv_commit(k_tree, v_tree, accept_len, accept_path, bonus_token, k_cache, v_cache, ctx_offsets,
+              ctx_lengths, next_root=None, stream=None):
+    """Append each sequence's accepted path (root first) from the tree K/V to
+    its context region of k_cache / v_cache; ctx_lengths advances in place.
+    next_root (int32 [b], optional) receives the bonus tokens."""
+    _dev(k_tree, "k_tree")
+    b, nq, hkv, d = k_tree.shape
+    _dev(v_tree, "v_tree", k_tree.dtype, k_tree.shape)
+    _dev(accept_len, "accept_len", torch.int32, (b,))
+    _dev(accept_path, "accept_path", torch.int32)
+    block = accept_path.shape[1] - 1
+    _dev(bonus_token, "bonus_token", torch.int32, (b,))
+    _dev(k_cache, "k_cache", k_tree.dtype)
+    _dev(v_cache, "v_cache", k_tree.dtype, k_cache.shape)
+    _dev(ctx_offsets, "ctx_offsets", torch.int64, (b + 1,))
+    _dev(ctx_lengths, "ctx_lengths", torch.int64, (b,))
+    if next_root is not None:
+        _dev(next_root, "next_root", torch.int32, (b,))
+    _check(lib.td_kv_commit(_ptr(k_tree), _ptr(v_tree), _ptr(accept_len), _ptr(accept_path),
+                            _ptr(bonus_token), b, nq, block, hkv, d, _dt(k_tree), _ptr(k_cache),
+                            _ptr(v_cache), _ptr(ctx_offsets), _ptr(ctx_lengths), _ptr(next_root),
+                            _stream(stream)))
 
 
 # ---------------------------------------------------------------------------
@@ -321,15 +353,24 @@ class VerifyStep:
                                      dtype=torch.uint8, device=dev)
 
     def set_inputs(self, logits, q, k_ctx, v_ctx, ctx_offsets, k_tree, v_tree, target_token,
-                   root_token=None):
+                   root_token=None, ctx_lengths=None, commit=False, next_root=None):
+        """commit: after acceptance, append the accepted path's K/V to the
+        contexts (k_ctx / v_ctx rows after ctx_lengths[b], which advances);
+        next_root receives the bonus tokens."""
+        if commit and ctx_lengths is None:
+            raise ValueError("commit needs ctx_lengths")
         a = self.args
         a.logits = logits.data_ptr()
         a.q, a.k_ctx, a.v_ctx = q.data_ptr(), k_ctx.data_ptr(), v_ctx.data_ptr()
         a.ctx_offsets = ctx_offsets.data_ptr()
+        a.ctx_lengths = None if ctx_lengths is None else ctx_lengths.data_ptr()
+        a.commit = int(bool(commit))
+        a.next_root = None if next_root is None else next_root.data_ptr()
         a.k_tree, a.v_tree = k_tree.data_ptr(), v_tree.data_ptr()
         a.target_token = target_token.data_ptr()
         a.root_token = None if root_token is None else root_token.data_ptr()
-        self._keep = (logits, q, k_ctx, v_ctx, ctx_offsets, k_tree, v_tree, target_token, root_token)
+        self._keep = (logits, q, k_ctx, v_ctx, ctx_offsets, k_tree, v_tree, target_token, root_token,
+                      ctx_lengths, next_root)
 
     def status(self, stream=None):
         """TD_OK, or TD_ESYNC if a hand-off of an earlier call gave up

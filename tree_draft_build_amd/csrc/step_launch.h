@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "tree_core.h"
 #include "treedraft.h"
 
 namespace td {
@@ -30,15 +31,19 @@ void launch_topk_tree(const void *logits, td_dtype dtype, int batch, int block, 
 
 // Tree attention; with accept_* set, the combine kernel also runs the
 // acceptance walk of every sequence.
+// With commit set, the acceptance workgroup of each sequence then appends the
+// accepted path's K/V to the context (cm).
 struct AcceptArgs {
     const int32_t *node_token, *node_parent, *target_token;
     int n_max, block;
     int32_t *accept_len, *accept_path, *bonus_token;
+    int commit;
+    CommitArgs cm;
 };
 size_t attn_workspace_bytes(int batch, int nq_max, int hq, int hkv, int head_dim,
                             int64_t total_ctx, td_dtype dtype);
 void launch_attention(const void *q, const void *k_ctx, const void *v_ctx, const int64_t *off,
-                      int64_t total_ctx, const void *k_tree, const void *v_tree,
+                      const int64_t *lens, int64_t total_ctx, const void *k_tree, const void *v_tree,
                       const uint64_t *mask, const int32_t *n_nodes, int batch, int nq_max, int hq,
                       int hkv, int head_dim, float scale, td_dtype dtype, void *ws, void *out,
                       const AcceptArgs *acc, hipStream_t st);

@@ -106,7 +106,10 @@ inline AttnPlan attn_plan(int batch, int nq_max, int hq, int hkv, int64_t total_
 }
 
 // Workspace: partial rows [n_chunks][hkv][n_rg][16]: m (float32), then l,
-// then O[D]; row r of a (chunk, KV head) lives at prow_index(...).
+// then O[D]; row r of a (chunk, KV head) lives at prow_index(...); then one
+// record per sequence (its first chunk index and chunk count), written by
+// the split kernel and read by the combine kernel, which so never reads the
+// context lengths (a fused KV commit may advance them in the same kernel).
 __device__ __forceinline__ int64_t prow_index(int64_t c, int g, int rg, int row, int hkv, int n_rg) {
     return ((c * hkv + g) * n_rg + rg) * kRowsPerGroup + row;
 }
@@ -118,14 +121,23 @@ __device__ __forceinline__ int64_t chunks_of(int64_t L, int chunk) {
     return L > 0 ? (L + chunk - 1) / chunk : 1;
 }
 
-// Locate chunk c of the ragged concatenation: sequence b, its key range, its
-// first chunk index and its chunk count.
-__device__ __forceinline__ bool find_chunk(const int64_t *__restrict__ off, int batch, int chunk,
+// Context length of sequence s: its region off[s] .. off[s+1]-1, or the
+// first lens[s] rows of it when lengths are given (clamped to the region).
+__device__ __forceinline__ int64_t seq_len(const int64_t *__restrict__ off,
+                                           const int64_t *__restrict__ lens, int s) {
+    const int64_t region = off[s + 1] - off[s];
+    return lens ? std::max<int64_t>(0, std::min<int64_t>(lens[s], region)) : region;
+}
+
+// Locate chunk c of the contexts: sequence b, its key range, its first chunk
+// index and its chunk count.
+__device__ __forceinline__ bool find_chunk(const int64_t *__restrict__ off,
+                                           const int64_t *__restrict__ lens, int batch, int chunk,
                                            int64_t c, int &b, int64_t &k0, int64_t &k1,
                                            int64_t &cbase, int &nch) {
     int64_t acc = 0;
     for (int s = 0; s < batch; ++s) {
-        const int64_t L = off[s + 1] - off[s];
+        const int64_t L = seq_len(off, lens, s);
         const int64_t n = chunks_of(L, chunk);
         if (c < acc + n) {
             b = s;
@@ -270,9 +282,9 @@ template <int D> struct Stage<float, D> {
 template <int D, int OWN>
 __global__ __launch_bounds__(kAttnThreads) void attn_split_f32(
     const float *__restrict__ q, const float *__restrict__ k_ctx, const float *__restrict__ v_ctx,
-    const int64_t *__restrict__ ctx_offsets, const int32_t *__restrict__ n_nodes, int batch,
-    int nq_max, int hq, int hkv, int group, int n_rg, int chunk, float scale2, float *__restrict__ ws,
-    int64_t prow_total) {
+    const int64_t *__restrict__ ctx_offsets, const int64_t *__restrict__ ctx_lengths,
+    const int32_t *__restrict__ n_nodes, int batch, int nq_max, int hq, int hkv, int group, int n_rg,
+    int chunk, float scale2, float *__restrict__ ws, int64_t prow_total, int2 *__restrict__ seqinfo) {
     using T = float;
     using L = Lds<T, D>;
     constexpr int CH = L::CH;
@@ -284,7 +296,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_f32(
     const int g = static_cast<int>(blockIdx.x % hkv);
     int b, nch;
     int64_t k0, k1, cbase;
-    if (!find_chunk(ctx_offsets, batch, chunk, c, b, k0, k1, cbase, nch)) return;
+    if (!find_chunk(ctx_offsets, ctx_lengths, batch, chunk, c, b, k0, k1, cbase, nch)) return;
+    if (k0 == 0 && g == 0 && threadIdx.x == 0)
+        seqinfo[b] = int2{static_cast<int>(cbase), nch};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -710,8 +724,9 @@ template <int D, int OWN, int OWN2 = OWN>
 __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_ctx,
     const uint16_t *__restrict__ v_ctx, const int64_t *__restrict__ ctx_offsets,
-    const int32_t *__restrict__ n_nodes, int batch, int nq_max, int hq, int hkv, int group, int n_rg,
-    int chunk, float scale2, float *__restrict__ ws, int64_t prow_total) {
+    const int64_t *__restrict__ ctx_lengths, const int32_t *__restrict__ n_nodes, int batch,
+    int nq_max, int hq, int hkv, int group, int n_rg, int chunk, float scale2,
+    float *__restrict__ ws, int64_t prow_total, int2 *__restrict__ seqinfo) {
     // two buffers, each K then V of one sub-chunk; the merge scratch of
     // split mode reuses them once no load is in flight
     __shared__ __attribute__((aligned(16))) uint16_t sbuf0[sub_elems<D>()];
@@ -723,7 +738,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
     const int g = static_cast<int>(blockIdx.x % hkv);
     int b, nch;
     int64_t k0, k1, cbase;
-    if (!find_chunk(ctx_offsets, batch, chunk, c, b, k0, k1, cbase, nch)) return;
+    if (!find_chunk(ctx_offsets, ctx_lengths, batch, chunk, c, b, k0, k1, cbase, nch)) return;
+    if (k0 == 0 && g == 0 && threadIdx.x == 0)
+        seqinfo[b] = int2{static_cast<int>(cbase), nch};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1005,21 +1022,11 @@ __device__ __forceinline__ void widen(const u32x4 (&w)[raw_words<T, N>()], float
     }
 }
 
-__device__ __forceinline__ int wave_sum_i(int v) {
-    v += xchg_i<0>(v);
-    v += xchg_i<1>(v);
-    v += xchg_i<2>(v);
-    v += xchg_i<3>(v);
-    v += xchg_i<4>(v);
-    v += xchg_i<5>(v);
-    return v;
-}
-
 // ACC: the grid carries one more workgroup per sequence, whose wave 0 runs
 // the acceptance walk (the verify step's last kernel).
 template <typename T, int D, bool ACC, bool TWO>
 __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
-    const T *__restrict__ q, const int64_t *__restrict__ ctx_offsets, const T *__restrict__ k_tree,
+    const T *__restrict__ q, const int2 *__restrict__ seqinfo, const T *__restrict__ k_tree,
     const T *__restrict__ v_tree, const uint64_t *__restrict__ mask,
     const int32_t *__restrict__ n_nodes, int batch, int nq_max, int hq, int hkv, int group, int n_rg,
     int chunk, float scale2, const float *__restrict__ ws, int64_t prow_total, T *__restrict__ out,
@@ -1031,11 +1038,20 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     if constexpr (ACC) {
         const int64_t first_acc = static_cast<int64_t>(batch) * hkv * blocks_per_bg;
         if (blockIdx.x >= first_acc) {
+            const int bs = static_cast<int>(blockIdx.x - first_acc);
+            __shared__ int s_path[TD_MAX_BLOCK + 1];
+            __shared__ int s_acc[2];  // accepted length, bonus token
             if (threadIdx.x < kWave)
                 accept_wave(accept.node_token, accept.node_parent, n_nodes, accept.target_token,
                             accept.n_max, accept.block, accept.accept_len, accept.accept_path,
-                            accept.bonus_token,
-                            static_cast<int>(blockIdx.x - first_acc), threadIdx.x);
+                            accept.bonus_token, bs, threadIdx.x, s_path, s_acc);
+            if (accept.commit) {  // the accepted path becomes context (uniform branch)
+                __shared__ int64_t s_len;
+                if (threadIdx.x == 0) s_len = commit_length(accept.cm, bs);
+                __syncthreads();
+                commit_seq(accept.cm, bs, s_path, s_acc[0], s_acc[1], s_len, threadIdx.x,
+                           kAttnThreads);
+            }
             return;
         }
     }
@@ -1079,12 +1095,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd) mw[wd] = wd < words ? mrow[wd] : 0;
 
-        // chunk base of sequence b: the lanes count the chunks of sequences < b
-        int cbl = 0;
-        for (int s2 = lane; s2 < b; s2 += kWave)
-            cbl += static_cast<int>(chunks_of(ctx_offsets[s2 + 1] - ctx_offsets[s2], chunk));
-        const int64_t cb = wave_sum_i(cbl);
-        const int nch = static_cast<int>(chunks_of(ctx_offsets[b + 1] - ctx_offsets[b], chunk));
+        // first chunk and chunk count of sequence b (left by the split kernel)
+        const int2 si = seqinfo[b];
+        const int64_t cb = si.x;
+        const int nch = si.y;
         const int rg = r / kRowsPerGroup;
         const int rr = r % kRowsPerGroup;
         const float *wm = ws;
@@ -1236,23 +1250,24 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
 
 template <typename T, int D>
 void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int64_t *off,
-                 const void *k_tree, const void *v_tree, const uint64_t *mask,
+                 const int64_t *lens, const void *k_tree, const void *v_tree, const uint64_t *mask,
                  const int32_t *n_nodes, int batch, int nq_max, int hq, int hkv, float scale,
                  const AttnPlan &pl, void *ws, void *out, const AcceptArgs *acc, hipStream_t st) {
     const float scale2 = scale * kLog2e;
     const int64_t prow_total = pl.n_chunks * hkv * pl.n_rg * kRowsPerGroup;
+    int2 *seqinfo = reinterpret_cast<int2 *>(static_cast<float *>(ws) + prow_total * (2 + D));
 #define TD_SPLIT(OWN)                                                                          \
     TD_LAUNCH((attn_split_f32<D, OWN>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)), \
                        dim3(kAttnThreads), 0, st, static_cast<const float *>(q),                \
-                       static_cast<const float *>(k_ctx), static_cast<const float *>(v_ctx), off, n_nodes, \
-                       batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,             \
-                       static_cast<float *>(ws), prow_total)
+                       static_cast<const float *>(k_ctx), static_cast<const float *>(v_ctx), off, lens, \
+                       n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,    \
+                       static_cast<float *>(ws), prow_total, seqinfo)
 #define TD_SPLIT_BF(...)                                                                       \
     TD_LAUNCH((attn_split_bf16<D, __VA_ARGS__>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)), \
                        dim3(kAttnThreads), 0, st, static_cast<const uint16_t *>(q),             \
                        static_cast<const uint16_t *>(k_ctx), static_cast<const uint16_t *>(v_ctx), \
-                       off, n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2, \
-                       static_cast<float *>(ws), prow_total)
+                       off, lens, n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk,   \
+                       scale2, static_cast<float *>(ws), prow_total, seqinfo)
     const int own = std::min(pl.own, max_own<T, D>());
     if constexpr (max_own<T, D>() == 5) {
         switch (own) {
@@ -1286,7 +1301,7 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
     const int64_t blocks = static_cast<int64_t>(batch) * hkv * blocks_per_bg;
 #define TD_COMBINE(ACC, TWO, NB, ARGS)                                                           \
     TD_LAUNCH((attn_tree_combine<T, D, ACC, TWO>), dim3(static_cast<unsigned>(NB)),      \
-                       dim3(kAttnThreads), 0, st, static_cast<const T *>(q), off,                 \
+                       dim3(kAttnThreads), 0, st, static_cast<const T *>(q), seqinfo,             \
                        static_cast<const T *>(k_tree), static_cast<const T *>(v_tree), mask,      \
                        n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,      \
                        static_cast<const float *>(ws), prow_total, static_cast<T *>(out), ARGS)
@@ -1300,9 +1315,8 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
 inline int sub_chunk(td_dtype dt) { return dt == TD_BF16 ? Sub<uint16_t>::CH : Sub<float>::CH; }
 
 inline size_t attn_ws_size(const AttnPlan &pl, int batch, int hkv, int D) {
-    (void)batch;
     const int64_t prow_total = pl.n_chunks * hkv * pl.n_rg * kRowsPerGroup;
-    return static_cast<size_t>(prow_total) * (2 + D) * sizeof(float);
+    return static_cast<size_t>(prow_total) * (2 + D) * sizeof(float) + static_cast<size_t>(batch) * 8;
 }
 
 }  // namespace
@@ -1314,14 +1328,14 @@ size_t attn_workspace_bytes(int batch, int nq_max, int hq, int hkv, int head_dim
 }
 
 void launch_attention(const void *q, const void *k_ctx, const void *v_ctx, const int64_t *off,
-                      int64_t total_ctx, const void *k_tree, const void *v_tree,
+                      const int64_t *lens, int64_t total_ctx, const void *k_tree, const void *v_tree,
                       const uint64_t *mask, const int32_t *n_nodes, int batch, int nq_max, int hq,
                       int hkv, int head_dim, float scale, td_dtype dtype, void *ws, void *out,
                       const AcceptArgs *acc, hipStream_t st) {
     const AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, sub_chunk(dtype));
     const bool bf = dtype == TD_BF16;
 #define TD_ATTN(T, DD)                                                                          \
-    launch_attn<T, DD>(q, k_ctx, v_ctx, off, k_tree, v_tree, mask, n_nodes, batch, nq_max, hq,  \
+    launch_attn<T, DD>(q, k_ctx, v_ctx, off, lens, k_tree, v_tree, mask, n_nodes, batch, nq_max, hq, \
                        hkv, scale, pl, ws, out, acc, st)
     if (bf && head_dim == 128)
         TD_ATTN(uint16_t, 128);
@@ -1379,7 +1393,8 @@ td_status td::check_attn_args(const void *q, const void *k_ctx, const void *v_ct
 }
 
 extern "C" td_status td_tree_verify_attn(const void *q, const void *k_ctx, const void *v_ctx,
-                                         const int64_t *ctx_offsets, int64_t total_ctx,
+                                         const int64_t *ctx_offsets, const int64_t *ctx_lengths,
+                                         int64_t total_ctx,
                                          int64_t max_ctx, const void *k_tree, const void *v_tree,
                                          const uint64_t *mask, const int32_t *n_nodes,
                                          int32_t batch, int32_t nq_max, int32_t hq, int32_t hkv,
@@ -1390,12 +1405,14 @@ extern "C" td_status td_tree_verify_attn(const void *q, const void *k_ctx, const
                                           v_tree, mask, n_nodes, batch, nq_max, hq, hkv, head_dim,
                                           dtype, out);
     if (chk != TD_OK) return chk;
+    if (ctx_lengths && !aligned8(ctx_lengths))
+        return fail(TD_EINVAL, "td_tree_verify_attn: misaligned ctx_lengths");
     if (!workspace || !aligned16(workspace))
         return fail(TD_EINVAL, "td_tree_verify_attn: null or misaligned workspace");
     if (workspace_bytes <
         td_tree_verify_attn_workspace(batch, nq_max, hq, hkv, head_dim, total_ctx, max_ctx))
         return fail(TD_EINVAL, "td_tree_verify_attn: workspace too small");
-    launch_attention(q, k_ctx, v_ctx, ctx_offsets, total_ctx, k_tree, v_tree, mask, n_nodes, batch,
+    launch_attention(q, k_ctx, v_ctx, ctx_offsets, ctx_lengths, total_ctx, k_tree, v_tree, mask, n_nodes, batch,
                      nq_max, hq, hkv, head_dim, scale, dtype, workspace, out, nullptr,
                      as_stream(stream));
     return check_launch("td_tree_verify_attn");

@@ -286,14 +286,17 @@ __device__ __forceinline__ void prefill_tree_outputs(const TreeParams &P, const 
 }
 
 // Greedy acceptance of sequence b with one wavefront: from the root, step to
-// the child carrying the target's greedy token while one exists.
+// the child carrying the target's greedy token while one exists.  With
+// lds_path / lds_acc set, the path (root first) and (A, bonus) are also left
+// in LDS for the workgroup.
 __device__ __forceinline__ void accept_wave(const int32_t *__restrict__ node_token,
                                             const int32_t *__restrict__ node_parent,
                                             const int32_t *__restrict__ n_nodes,
                                             const int32_t *__restrict__ target_token, int n_max,
                                             int block, int32_t *__restrict__ accept_len,
                                             int32_t *__restrict__ accept_path,
-                                            int32_t *__restrict__ bonus_token, int b, int lane) {
+                                            int32_t *__restrict__ bonus_token, int b, int lane,
+                                            int *lds_path = nullptr, int *lds_acc = nullptr) {
     const int W = n_max + 1;
     const int64_t base = static_cast<int64_t>(b) * W;
     const int n = min(n_nodes[b], n_max);
@@ -317,11 +320,64 @@ __device__ __forceinline__ void accept_wave(const int32_t *__restrict__ node_tok
         if (next == 0x7fffffff) break;
         u = next;
         ++A;
-        if (lane == 0) path[A] = u;
+        if (lane == 0) {
+            path[A] = u;
+            if (lds_path) lds_path[A] = u;
+        }
     }
     if (lane == 0) {
+        const int bonus = target_token[base + u];
         accept_len[b] = A;
-        bonus_token[b] = target_token[base + u];
+        bonus_token[b] = bonus;
+        if (lds_path) lds_path[0] = 0;
+        if (lds_acc) {
+            lds_acc[0] = A;
+            lds_acc[1] = bonus;
+        }
+    }
+}
+
+// KV commit of the accepted path (the verified prefix becomes context; the
+// verification's keys and values are kept): for sequence b, tree rows
+// path[0..A] (root first) are copied, every KV head at once, after the L
+// context rows of b's region ctx_offsets[b] .. ctx_offsets[b+1]-1; rows that
+// would pass the region's end are dropped.  One token's keys of every KV
+// head are row16 16-byte vectors.
+struct CommitArgs {
+    const uint4 *k_tree, *v_tree;  // [batch][nq_max][row16]
+    uint4 *k_cache, *v_cache;      // [total][row16]
+    const int64_t *ctx_offsets;    // [batch + 1]
+    int64_t *ctx_lengths;          // [batch], advanced by the rows written
+    int32_t *next_root;            // [batch] or null: the bonus token
+    int nq_max, row16;
+};
+
+// The context length of b, clamped to its region (read before any thread
+// of the committing workgroup may advance it).
+__device__ __forceinline__ int64_t commit_length(const CommitArgs &c, int b) {
+    const int64_t region = c.ctx_offsets[b + 1] - c.ctx_offsets[b];
+    const int64_t L = c.ctx_lengths[b];
+    return L < 0 ? 0 : (L > region ? region : L);
+}
+
+// Threads t, t + nthreads, ... of one workgroup copy the rows; path[0..A]
+// are valid tree rows (< nq_max); L from commit_length.
+__device__ __forceinline__ void commit_seq(const CommitArgs &c, int b, const int *path, int A,
+                                           int bonus, int64_t L, int t, int nthreads) {
+    const int64_t base = c.ctx_offsets[b];
+    const int64_t room = c.ctx_offsets[b + 1] - base - L;
+    const int rows = static_cast<int>(A + 1 < room ? A + 1 : room);
+    for (int e = t; e < rows * c.row16; e += nthreads) {
+        const int j = e / c.row16;
+        const int v = e - j * c.row16;
+        const int64_t src = (static_cast<int64_t>(b) * c.nq_max + path[j]) * c.row16 + v;
+        const int64_t dst = (base + L + j) * c.row16 + v;
+        c.k_cache[dst] = c.k_tree[src];
+        c.v_cache[dst] = c.v_tree[src];
+    }
+    if (t == 0) {
+        c.ctx_lengths[b] = L + (rows > 0 ? rows : 0);
+        if (c.next_root) c.next_root[b] = bonus;
     }
 }
 

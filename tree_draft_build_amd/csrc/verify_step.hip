@@ -82,6 +82,14 @@ td_status check_step(const td_step_args *a) {
         if (st != TD_OK) return st;
     }
     if (!a->mask || !aligned8(a->mask)) return fail(TD_EINVAL, "td_verify_step: mask must be set");
+    if (a->ctx_lengths && !aligned8(a->ctx_lengths))
+        return fail(TD_EINVAL, "td_verify_step: misaligned ctx_lengths");
+    if (verify && a->commit) {
+        if (!a->ctx_lengths)
+            return fail(TD_EINVAL, "td_verify_step: commit needs ctx_lengths");
+        if (!a->k_ctx || !a->v_ctx)
+            return fail(TD_EINVAL, "td_verify_step: commit needs the context arrays");
+    }
     return TD_OK;
 }
 
@@ -102,9 +110,18 @@ td_status launch_step(const td_step_args *a, void *workspace, void *stream) {
                          a->topk, ws, a->topk_id, a->topk_logq, a->lse, tp, to, s);
     }
     if (verify) {
-        const AcceptArgs acc{a->node_token, a->node_parent, a->target_token, a->n_max, a->block,
-                             a->accept_len, a->accept_path, a->bonus_token};
-        launch_attention(a->q, a->k_ctx, a->v_ctx, a->ctx_offsets, a->total_ctx, a->k_tree,
+        AcceptArgs acc{a->node_token, a->node_parent, a->target_token, a->n_max, a->block,
+                       a->accept_len, a->accept_path, a->bonus_token, a->commit != 0, CommitArgs{}};
+        if (a->commit) {
+            const int esz = a->attn_dtype == TD_F32 ? 4 : 2;
+            acc.cm = CommitArgs{static_cast<const uint4 *>(a->k_tree),
+                                static_cast<const uint4 *>(a->v_tree),
+                                static_cast<uint4 *>(const_cast<void *>(a->k_ctx)),
+                                static_cast<uint4 *>(const_cast<void *>(a->v_ctx)),
+                                a->ctx_offsets, a->ctx_lengths, a->next_root, nq_max,
+                                a->hkv * a->head_dim * esz / 16};
+        }
+        launch_attention(a->q, a->k_ctx, a->v_ctx, a->ctx_offsets, a->ctx_lengths, a->total_ctx, a->k_tree,
                          a->v_tree, a->mask, a->n_nodes, a->batch, nq_max, a->hq, a->hkv,
                          a->head_dim, a->scale, a->attn_dtype, ws + topk_part(a), a->out, &acc, s);
     }

@@ -14,6 +14,7 @@ Parity unpinned: none of these functions; every one has a pin in
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from ctypes import POINTER, c_double, c_int, c_int32, c_int64, c_void_p
 
@@ -34,7 +35,10 @@ def _load(path=None):
         P = c_void_p
         lib.or_draft_topk.argtypes = [P, c_int, c_int, c_int, c_int, c_int64, c_int, P, P, P]
         lib.or_build_tree.argtypes = [P, P, c_int, c_int, c_int, c_int, c_int, c_double, c_double,
-                                      c_double, c_int, c_double, c_double, P, P, P, P, P, P, P, P, P]
+                                      c_double, c_int, c_double, c_double, P, P, P, P, P, P, P, P, P,
+                                      c_int, c_double]
+        lib.or_flex_budget.argtypes = [c_int, c_int, c_int, c_int, c_int, P, P]
+        lib.or_flex_budget.restype = None
         lib.or_tree_mask.argtypes = [P, P, c_int, c_int, P]
         lib.or_tree_attn.argtypes = [P, P, P, P, P, P, P, P, P, c_int, c_int, c_int, c_int, c_int,
                                      c_double, c_int, P, c_int32, c_int32, c_int32]
@@ -105,9 +109,10 @@ def draft_topk(logits: np.ndarray, K: int):
 
 
 def build_tree(topk_id, topk_logq, n_max, use_stop, cost=(1.0, 0.0, 0.0, 0), l_ar=1.0,
-               ahat0=1.0, root_token=None, want_curve=False):
+               ahat0=1.0, root_token=None, want_curve=False, branch=0, min_logrho=-math.inf):
     """Best-first tree.  Returns dict of node arrays [b][n_max+1] (index 0 = root),
-    n_nodes[b] (draft nodes), ahat[b], speedup[b] and optionally s_curve."""
+    n_nodes[b] (draft nodes), ahat[b], speedup[b] and optionally s_curve.
+    branch: children per node (0: K); min_logrho: no node below this log rho."""
     topk_id = _c(topk_id, np.int32)
     topk_logq = _c(topk_logq, np.float64)
     b, B, K = topk_id.shape
@@ -123,10 +128,20 @@ def build_tree(topk_id, topk_logq, n_max, use_stop, cost=(1.0, 0.0, 0.0, 0), l_a
                                  ca, cb, cc, int(knee), l_ar, ahat0, _p(rt), _p(out["n_nodes"]),
                                  _p(out["node_token"]), _p(out["node_parent"]),
                                  _p(out["node_depth"]), _p(out["node_logrho"]), _p(out["ahat"]),
-                                 _p(out["speedup"]), _p(curve)), "or_build_tree")
+                                 _p(out["speedup"]), _p(curve), int(branch), float(min_logrho)),
+           "or_build_tree")
     if want_curve:
         out["s_curve"] = curve
     return out
+
+
+def flex_budget(batch, switch_batch, K, n_max, block):
+    """(branch, n_max) of a step of `batch` sequences under the batch-size
+    switch (single branch at or above switch_batch)."""
+    br, nm = ctypes.c_int(0), ctypes.c_int(0)
+    _load().or_flex_budget(int(batch), int(switch_batch), int(K), int(n_max), int(block),
+                           ctypes.byref(br), ctypes.byref(nm))
+    return br.value, nm.value
 
 
 def tree_mask(node_parent, n_nodes, nq_max=None):

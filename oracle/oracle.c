@@ -169,10 +169,19 @@ int or_build_tree(const int32_t *topk_id, const double *topk_logq, int batch, in
                   double l_ar, double ahat0, const int32_t *root_token, int32_t *n_nodes,
                   int32_t *node_token, int32_t *node_parent, int32_t *node_depth,
                   double *node_logrho, double *ahat_out, double *speedup_out,
-                  double *s_curve /* optional [batch][n_max+1]: S(n) of T_n, NAN beyond */)
+                  double *s_curve /* optional [batch][n_max+1]: S(n) of T_n, NAN beyond */,
+                  int branch /* children per node: ranks 0..branch-1 (<= 0 or > K: K) */,
+                  double min_logrho /* selective verification: no node below this log rho */)
 {
     if (!topk_id || !topk_logq || batch < 0 || block <= 0 || K <= 0 || n_max < 0)
         return OR_EINVAL;
+    /* Selective verification (FlexDraft page, "Methodik" 3, Flex-Decoding): a
+     * candidate's cumulative draft confidence is its path score rho; branches
+     * below the threshold are pruned, and since every remaining candidate
+     * scores at most the best one, growth stops at the first best candidate
+     * below it.  Dynamic switching runs large batches on a single branch:
+     * branch = 1 keeps only each position's top-1 token. */
+    int nb = (branch <= 0 || branch > K) ? K : branch;
     int cap = K * (n_max + 1) + 1;
     int W = n_max + 1;
     int status = OR_OK;
@@ -201,7 +210,7 @@ int or_build_tree(const int32_t *topk_id, const double *topk_logq, int batch, in
         const double *lq = topk_logq + (int64_t)b * block * K;
 
         int nf = 0;
-        for (int j = 0; j < K; ++j) { /* children of the root use q_1 */
+        for (int j = 0; j < nb; ++j) { /* children of the root use q_1 */
             front[nf].logrho = lq[j];
             front[nf].depth = 1;
             front[nf].token = ids[j];
@@ -216,26 +225,28 @@ int or_build_tree(const int32_t *topk_id, const double *topk_logq, int batch, in
             int best = 0;
             for (int f = 1; f < nf; ++f)
                 if (better(&front[f], &front[best])) best = f;
-            or_node nb = front[best];
-            double ahat_next = ahat + exp(nb.logrho);
+            or_node nd = front[best];
+            if (nd.logrho < min_logrho)
+                break; /* the best candidate is below the confidence threshold */
+            double ahat_next = ahat + exp(nd.logrho);
             double s_next = ahat_next * l_ar / cost_model(n + 1, ca, cb, cc, knee);
             if (use_stop && !(s_next > s_now))
                 break; /* S would not rise: the tree is T_n */
             ++n;
-            tok[n] = nb.token;
-            par[n] = nb.parent;
-            dep[n] = nb.depth;
-            lr[n] = nb.logrho;
+            tok[n] = nd.token;
+            par[n] = nd.parent;
+            dep[n] = nd.depth;
+            lr[n] = nd.logrho;
             ahat = ahat_next;
             s_now = s_next;
             if (s_curve) s_curve[(int64_t)b * W + n] = s_now;
             front[best] = front[nf - 1];
             --nf;
-            if (nb.depth < block) { /* children at depth d+1 use q_{d+1} */
-                for (int j = 0; j < K; ++j) {
-                    front[nf].logrho = nb.logrho + lq[(int64_t)nb.depth * K + j];
-                    front[nf].depth = nb.depth + 1;
-                    front[nf].token = ids[(int64_t)nb.depth * K + j];
+            if (nd.depth < block) { /* children at depth d+1 use q_{d+1} */
+                for (int j = 0; j < nb; ++j) {
+                    front[nf].logrho = nd.logrho + lq[(int64_t)nd.depth * K + j];
+                    front[nf].depth = nd.depth + 1;
+                    front[nf].token = ids[(int64_t)nd.depth * K + j];
                     front[nf].parent = n;
                     ++nf;
                 }
@@ -496,4 +507,22 @@ int or_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accept_l
         if (next_root) next_root[b] = bonus_token ? bonus_token[b] : -1;
     }
     return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dynamic switching by batch size (FlexDraft page, "Methodik" 3): below    */
+/* switch_batch sequences a step verifies the full tree (branch K, budget   */
+/* n_max); at or above it, a single branch (branch 1, at most block nodes). */
+/* switch_batch <= 0 never switches.                                        */
+/* ------------------------------------------------------------------------ */
+void or_flex_budget(int batch, int switch_batch, int K, int n_max, int block, int *branch_out,
+                    int *n_max_out)
+{
+    if (switch_batch > 0 && batch >= switch_batch) {
+        *branch_out = 1;
+        *n_max_out = n_max < block ? n_max : block;
+    } else {
+        *branch_out = K;
+        *n_max_out = n_max;
+    }
 }

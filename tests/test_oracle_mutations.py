@@ -14,6 +14,7 @@ import oracle
 import test_oracle_accept as tac
 import test_oracle_commit as tcm
 import test_oracle_mask_attn as tma
+import test_oracle_selective as tse
 import test_oracle_topk as tto
 import test_oracle_tree as ttr
 
@@ -28,8 +29,8 @@ MUTATIONS = [
      "return (a->id < b->id) - (a->id > b->id);",
      lambda: tto.test_topk_matches_bruteforce_with_ties("bf16", 8)),
     ("children use q_d instead of q_{d+1}",
-     "front[nf].logrho = nb.logrho + lq[(int64_t)nb.depth * K + j];",
-     "front[nf].logrho = nb.logrho + lq[(int64_t)(nb.depth - 1) * K + j];",
+     "front[nf].logrho = nd.logrho + lq[(int64_t)nd.depth * K + j];",
+     "front[nf].logrho = nd.logrho + lq[(int64_t)(nd.depth - 1) * K + j];",
      lambda: ttr.test_best_first_order_is_global_sort(3, 3, 4, False)),
     ("depth tie-break reversed", "if (a->depth != b->depth) return a->depth < b->depth;",
      "if (a->depth != b->depth) return a->depth > b->depth;",
@@ -71,6 +72,12 @@ MUTATIONS = [
      lambda: tcm.test_committed_prefix_reproduces_tree_attention()),
     ("commit ignores the region end", "if (L >= region) break;", "(void)region;",
      lambda: tcm.test_commit_stops_at_the_region_end()),
+    ("threshold drops a node exactly at it", "if (nd.logrho < min_logrho)",
+     "if (nd.logrho <= min_logrho)",
+     lambda: tse.test_threshold_is_a_prefix_of_the_global_order(0, 40)),
+    ("branch cap ignored at the root", "for (int j = 0; j < nb; ++j) { /* children of the root",
+     "for (int j = 0; j < K; ++j) { /* children of the root",
+     lambda: tse.test_branch_cap_is_the_order_over_low_ranks(1)),
     ("attention ignores context lengths", "if (!ctx_lengths) return region;", "return region;",
      lambda: tcm.test_attention_over_context_lengths_equals_compacted()),
 ]

@@ -135,6 +135,16 @@ td_status td_workspace_status(void *workspace, size_t workspace_bytes, void *str
  * stopping before node n+1 when S(n+1) <= S(n).  Otherwise exactly
  * min(n_max, available candidates) nodes are inserted.  log rho, A_hat and S
  * are accumulated in float64.
+ * Selective verification (the FlexDraft page, Methodik §3, Flex-Decoding:
+ * branches of low cumulative draft confidence are pruned; a node's
+ * cumulative confidence is its path score rho): when min_logrho < 0 no
+ * node with log rho < min_logrho is inserted (0, positive or -INFINITY:
+ * no threshold, so a zero-filled argument block prunes nothing); since the
+ * best candidate bounds
+ * all others, growth stops at the first best candidate below it.  branch
+ * (1..K; other values mean K) caps the children per node at the ranks
+ * 0..branch-1 of the next position; branch = 1 drafts the single top-1
+ * branch of the sequential mode (see td_flex_budget).
  * Inputs:  topk_id [batch][block][K], topk_logq [batch][block][K] as written
  *          by td_draft_topk (ids in [0, TD_MAX_VOCAB); the kernel uses the
  *          low 18 bits of each id); root_token [batch] or NULL (then -1 is
@@ -152,9 +162,22 @@ td_status td_workspace_status(void *workspace, size_t workspace_bytes, void *str
 td_status td_build_tree(const int32_t *topk_id, const double *topk_logq, int32_t batch,
                         int32_t block, int32_t K, int32_t n_max, int32_t use_stop, double cost_a,
                         double cost_b, double cost_c, int32_t cost_knee, double l_ar,
-                        double ahat0, const int32_t *root_token, int32_t *n_nodes,
+                        double ahat0, int32_t branch, double min_logrho,
+                        const int32_t *root_token, int32_t *n_nodes,
                         int32_t *node_token, int32_t *node_parent, int32_t *node_depth,
                         double *node_logrho, double *ahat, double *speedup, void *stream);
+
+/* ------------------------------------------------------------------------
+ * td_flex_budget -- the batch-size switch of the FlexDraft page (Methodik §3,
+ * Flex-Decoding, dynamic switching): small batches verify the whole tree,
+ * large ones a single branch drafted from the verified prefix.  Host
+ * function (no GPU work): for a step of `batch` sequences, writes *branch =
+ * K and *n_max_out = n_max when switch_batch <= 0 or batch < switch_batch,
+ * else *branch = 1 and *n_max_out = min(n_max, block).  Pass both to
+ * td_build_tree / td_step_args.  Either pointer may be NULL.
+ */
+void td_flex_budget(int32_t batch, int32_t switch_batch, int32_t K, int32_t n_max, int32_t block,
+                    int32_t *branch, int32_t *n_max_out);
 
 /* ------------------------------------------------------------------------
  * td_tree_mask -- stage (b').
@@ -303,6 +326,8 @@ typedef struct {
     int32_t cost_knee;
     double l_ar, ahat0;
     const int32_t *root_token; /* may be NULL */
+    int32_t branch;            /* children per node (1..topk; other values: topk) */
+    double min_logrho;         /* selective verification threshold if < 0 (0: off) */
     /* stage (c) */
     const void *q, *k_ctx, *v_ctx;
     const int64_t *ctx_offsets;

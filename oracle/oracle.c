@@ -171,7 +171,8 @@ int or_build_tree(const int32_t *topk_id, const double *topk_logq, int batch, in
                   double *node_logrho, double *ahat_out, double *speedup_out,
                   double *s_curve /* optional [batch][n_max+1]: S(n) of T_n, NAN beyond */,
                   int branch /* children per node: ranks 0..branch-1 (<= 0 or > K: K) */,
-                  double min_logrho /* selective verification: no node below this log rho */)
+                  double min_logrho /* selective verification: no node below this log rho
+                                       (a threshold when < 0; 0 or more: none) */)
 {
     if (!topk_id || !topk_logq || batch < 0 || block <= 0 || K <= 0 || n_max < 0)
         return OR_EINVAL;
@@ -226,7 +227,7 @@ int or_build_tree(const int32_t *topk_id, const double *topk_logq, int batch, in
             for (int f = 1; f < nf; ++f)
                 if (better(&front[f], &front[best])) best = f;
             or_node nd = front[best];
-            if (nd.logrho < min_logrho)
+            if (min_logrho < 0.0 && nd.logrho < min_logrho)
                 break; /* the best candidate is below the confidence threshold */
             double ahat_next = ahat + exp(nd.logrho);
             double s_next = ahat_next * l_ar / cost_model(n + 1, ca, cb, cc, knee);

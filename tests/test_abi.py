@@ -25,7 +25,7 @@ def b():
 
 def test_every_declared_symbol_is_exported(b):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(b.lib, n), n
     assert sorted(b.EXPORTED) == names
@@ -74,14 +74,23 @@ def test_draft_topk_validation(b, args, status, needle):
 
 
 def test_build_tree_validation(b):
-    base = [FAKE, FAKE, 1, 16, 8, 64, 1, 1.0, 0.005, 0.03, 32, 1.0, 1.0, None, FAKE, FAKE, FAKE,
-            FAKE, FAKE, None, None, None]
+    base = [FAKE, FAKE, 1, 16, 8, 64, 1, 1.0, 0.005, 0.03, 32, 1.0, 1.0, 0, -1e300, None, FAKE, FAKE,
+            FAKE, FAKE, FAKE, None, None, None]
     bad = list(base); bad[5] = 256
     assert b.lib.td_build_tree(*bad) == 2 and "capacity" in b.last_error()
     bad = list(base); bad[0] = None
     assert b.lib.td_build_tree(*bad) == 1
     bad = list(base); bad[5] = -1
     assert b.lib.td_build_tree(*bad) == 1
+
+
+def test_flex_budget_matches_oracle(b):
+    import oracle
+    for batch in (1, 7, 8, 64):
+        for switch in (0, 8, 16):
+            for n_max in (4, 64):
+                assert b.flex_budget(batch, switch, 8, n_max, 16) == \
+                    oracle.flex_budget(batch, switch, 8, n_max, 16)
 
 
 def test_mask_accept_validation(b):

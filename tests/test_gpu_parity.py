@@ -371,3 +371,33 @@ def test_pipeline(td, name, sample):
     np.testing.assert_array_equal(path.cpu().numpy(), p_o)
     np.testing.assert_array_equal(bonus.cpu().numpy(), b_o)
     assert np.all(a_o <= np.maximum(0, g["tree"]["node_depth"].max(axis=1)))
+
+
+@pytest.mark.parametrize("name", ["tiny_fixed", "qwen3_8b_stress", "batched", "llama31_8b"])
+@pytest.mark.parametrize("branch,cut", [(0, 9), (1, None), (3, 20), (2, None)])
+def test_build_tree_selective(td, name, branch, cut):
+    """Selective verification (threshold on log rho between the oracle's
+    cut-th and next node) and the branch cap, same inputs, GPU vs oracle."""
+    cfg = wl.CONFIGS[name]
+    say("build_tree selective", name, branch, cut)
+    x = wl.make_logits(cfg, list(range(min(cfg.batch, 4))))
+    ids, lq, _ = oracle.draft_topk(x, cfg.topk)
+    tau = float("-inf")
+    if cut is not None:
+        ref = oracle.build_tree(ids, lq, cfg.n_max, False, branch=branch)
+        lr = ref["node_logrho"][0, 1:]
+        tau = float((lr[cut - 1] + lr[cut]) / 2) if cut < int(ref["n_nodes"][0]) else -1e300
+    kw = dict(branch=branch, min_logrho=tau)
+    orc = dict(ids=ids, lq=lq,
+               tree=oracle.build_tree(ids, lq, cfg.n_max, cfg.use_stop, cost_of(cfg), cfg.l_ar,
+                                      cfg.ahat0, **kw),
+               full=oracle.build_tree(ids, lq, cfg.n_max, False, cost_of(cfg), cfg.l_ar, cfg.ahat0,
+                                      want_curve=True, **kw))
+    t = np_tree(td.build_tree(torch.from_numpy(ids).to(DEV), torch.from_numpy(lq).to(DEV),
+                              cfg.n_max, cfg.use_stop, cost_of(cfg), cfg.l_ar, cfg.ahat0, **kw))
+    for b in range(x.shape[0]):
+        compare_tree(b, t, orc, cfg.use_stop)
+        n = int(t["n_nodes"][b])
+        assert np.all(t["node_logrho"][b, 1:n + 1] >= tau)
+        if branch == 1:
+            assert n <= cfg.block

@@ -31,9 +31,9 @@ def dev(x):
     return torch.from_numpy(x).to(DEV)
 
 
-def modular(td, cfg, d, tg):
+def modular(td, cfg, d, tg, **kw):
     ids, lq, lse = td.draft_topk(d["logits"], cfg.topk)
-    t = td.build_tree(ids, lq, cfg.n_max, cfg.use_stop, cost_of(cfg), cfg.l_ar, cfg.ahat0)
+    t = td.build_tree(ids, lq, cfg.n_max, cfg.use_stop, cost_of(cfg), cfg.l_ar, cfg.ahat0, **kw)
     mask = td.tree_mask(t["node_parent"], t["n_nodes"])
     out = td.tree_verify_attn(d["q"], d["k_ctx"], d["v_ctx"], d["off"], d["total"], d["maxc"],
                               d["k_tree"], d["v_tree"], mask, t["n_nodes"], wl.attn_scale(cfg))
@@ -45,14 +45,14 @@ def modular(td, cfg, d, tg):
     return {k: v.cpu() for k, v in res.items()}
 
 
-def make_step(td, cfg, d):
+def make_step(td, cfg, d, **kw):
     s = td.VerifyStep(batch=cfg.batch, block=cfg.block, vocab=cfg.vocab, topk=cfg.topk,
                       n_max=cfg.n_max, use_stop=cfg.use_stop, cost=cost_of(cfg), l_ar=cfg.l_ar,
                       ahat0=cfg.ahat0, hq=cfg.hq, hkv=cfg.hkv, head_dim=cfg.head_dim,
                       scale=wl.attn_scale(cfg),
                       logits_dtype=td.TD_BF16 if cfg.logit_dtype == "bf16" else td.TD_F32,
                       attn_dtype=td.TD_BF16 if cfg.attn_dtype == "bf16" else td.TD_F32,
-                      total_ctx=d["total"], max_ctx=d["maxc"], device=DEV)
+                      total_ctx=d["total"], max_ctx=d["maxc"], device=DEV, **kw)
     return s
 
 
@@ -269,3 +269,23 @@ def test_handoff_give_up_is_reported(td):
     s.run()
     assert s.status() == td.TD_OK
     assert_same(ref, step_outputs(s), "after re-zeroing")
+
+
+@pytest.mark.parametrize("name,kw", [("qwen3_8b_stress", dict(branch=3, min_logrho=-6.0)),
+                                     ("batched", dict(branch=1)),
+                                     ("long", dict(min_logrho=-40.0))])
+def test_step_selective_equals_stage_calls(td, name, kw):
+    """The fused step with a branch cap and a confidence threshold gives the
+    stage calls' results with the same settings."""
+    cfg = wl.CONFIGS[name]
+    print("[case] step selective", name, kw, flush=True)
+    x, inp, d = inputs(cfg)
+    ref = modular(td, cfg, d, None, **kw)
+    tree_np = {k: ref[k].numpy() for k in ("node_token", "node_parent", "n_nodes")}
+    tg = dev(targets_by_path(cfg, wl.logits_as_f64(x, cfg.logit_dtype), tree_np))
+    ref = modular(td, cfg, d, tg, **kw)
+    s = make_step(td, cfg, d, **kw)
+    s.set_inputs(d["logits"], d["q"], d["k_ctx"], d["v_ctx"], d["off"], d["k_tree"], d["v_tree"], tg)
+    s.run()
+    torch.cuda.synchronize()
+    assert_same(ref, step_outputs(s), f"{name} selective")

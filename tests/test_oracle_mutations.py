@@ -72,8 +72,8 @@ MUTATIONS = [
      lambda: tcm.test_committed_prefix_reproduces_tree_attention()),
     ("commit ignores the region end", "if (L >= region) break;", "(void)region;",
      lambda: tcm.test_commit_stops_at_the_region_end()),
-    ("threshold drops a node exactly at it", "if (nd.logrho < min_logrho)",
-     "if (nd.logrho <= min_logrho)",
+    ("threshold drops a node exactly at it", "if (min_logrho < 0.0 && nd.logrho < min_logrho)",
+     "if (min_logrho < 0.0 && nd.logrho <= min_logrho)",
      lambda: tse.test_threshold_is_a_prefix_of_the_global_order(0, 40)),
     ("branch cap ignored at the root", "for (int j = 0; j < nb; ++j) { /* children of the root",
      "for (int j = 0; j < K; ++j) { /* children of the root",

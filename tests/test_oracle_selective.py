@@ -42,7 +42,8 @@ def test_threshold_is_a_prefix_of_the_global_order(seed, n_max):
     K, B = 3, 4
     order = global_order(universe(ids[0], lq[0], B, K))
     scores = [v["lr"] for _, v in order]
-    for tau in (scores[0] + 1.0, scores[2], (scores[6] + scores[7]) / 2, scores[-1] - 1.0):
+    for tau in (scores[0] + 0.5, scores[2], (scores[6] + scores[7]) / 2, scores[-1] - 1.0):
+        assert tau < 0
         tree = oracle.build_tree(ids[:, :, :K], lq[:, :, :K], n_max, False, min_logrho=tau)
         want_n = min(n_max, sum(1 for x in scores if x >= tau))
         assert int(tree["n_nodes"][0]) == want_n
@@ -82,6 +83,15 @@ def test_threshold_with_the_budget_stop():
         n_tau = int(np.sum(lr >= tau))
         assert int(t["n_nodes"][0]) == min(n_stop, n_tau)
         assert oracle_paths(t) == oracle_paths(full)[:min(n_stop, n_tau)]
+
+
+def test_nonnegative_threshold_is_off():
+    ids, lq = tables(5)
+    a = oracle.build_tree(ids, lq, 12, False)
+    for tau in (0.0, 3.0):
+        b = oracle.build_tree(ids, lq, 12, False, min_logrho=tau)
+        for k in ("n_nodes", "node_token", "node_parent"):
+            np.testing.assert_array_equal(a[k], b[k])
 
 
 @pytest.mark.parametrize("batch,switch,want", [(1, 8, (8, 64)), (7, 8, (8, 64)), (8, 8, (1, 16)),

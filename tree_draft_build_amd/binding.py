@@ -29,7 +29,7 @@ EXPORTED = ["td_abi_version", "td_last_error", "td_draft_topk_workspace", "td_dr
             "td_build_tree", "td_tree_mask", "td_tree_verify_attn_workspace",
             "td_tree_verify_attn", "td_accept", "td_step_args_bytes", "td_verify_step_workspace",
             "td_verify_step", "td_workspace_status", "td_verify_step_noalloc",
-            "td_verify_step_events", "td_kv_commit"]
+            "td_verify_step_events", "td_kv_commit", "td_flex_budget"]
 
 
 class StepArgs(ctypes.Structure):
@@ -39,7 +39,7 @@ class StepArgs(ctypes.Structure):
         ("vocab", c_int32), ("pos_stride", c_int64), ("topk", c_int32),
         ("n_max", c_int32), ("use_stop", c_int32), ("cost_a", c_double), ("cost_b", c_double),
         ("cost_c", c_double), ("cost_knee", c_int32), ("l_ar", c_double), ("ahat0", c_double),
-        ("root_token", c_void_p),
+        ("root_token", c_void_p), ("branch", c_int32), ("min_logrho", c_double),
         ("q", c_void_p), ("k_ctx", c_void_p), ("v_ctx", c_void_p), ("ctx_offsets", c_void_p),
         ("ctx_lengths", c_void_p), ("total_ctx", c_int64), ("max_ctx", c_int64), ("k_tree", c_void_p), ("v_tree", c_void_p),
         ("hq", c_int32), ("hkv", c_int32), ("head_dim", c_int32), ("scale", c_float),
@@ -74,8 +74,10 @@ def _load():
     lib.td_draft_topk.argtypes = [P, c_int, c_int32, c_int32, c_int32, c_int64, c_int32, P, P, P, P,
                                   c_size_t, P]
     lib.td_build_tree.argtypes = [P, P, c_int32, c_int32, c_int32, c_int32, c_int32, c_double,
-                                  c_double, c_double, c_int32, c_double, c_double, P, P, P, P, P, P,
-                                  P, P, P]
+                                  c_double, c_double, c_int32, c_double, c_double, c_int32,
+                                  c_double, P, P, P, P, P, P, P, P, P]
+    lib.td_flex_budget.argtypes = [c_int32] * 5 + [P, P]
+    lib.td_flex_budget.restype = None
     lib.td_tree_mask.argtypes = [P, P, c_int32, c_int32, P, P]
     lib.td_tree_verify_attn_workspace.argtypes = [c_int32] * 5 + [c_int64, c_int64]
     lib.td_tree_verify_attn_workspace.restype = c_size_t
@@ -197,7 +199,9 @@ def alloc_tree(batch, n_max, device):
 
 
 def build_tree(topk_id, topk_logq, n_max, use_stop, cost=(1.0, 0.0, 0.0, 0), l_ar=1.0, ahat0=1.0,
-               root_token=None, out=None, stream=None):
+               root_token=None, out=None, stream=None, branch=0, min_logrho=float("-inf")):
+    """branch: children per node (0: K); min_logrho: selective verification
+    threshold on log rho (-inf: off)."""
     _dev(topk_id, "topk_id", torch.int32)
     b, B, K = topk_id.shape
     _dev(topk_logq, "topk_logq", torch.float64, (b, B, K))
@@ -207,10 +211,19 @@ def build_tree(topk_id, topk_logq, n_max, use_stop, cost=(1.0, 0.0, 0.0, 0), l_a
     ca, cb, cc, knee = cost
     _check(lib.td_build_tree(_ptr(topk_id), _ptr(topk_logq), b, B, K, n_max, int(bool(use_stop)),
                              float(ca), float(cb), float(cc), int(knee), float(l_ar), float(ahat0),
-                             _ptr(root_token), _ptr(t["n_nodes"]), _ptr(t["node_token"]),
+                             int(branch), float(min_logrho), _ptr(root_token), _ptr(t["n_nodes"]), _ptr(t["node_token"]),
                              _ptr(t["node_parent"]), _ptr(t["node_depth"]), _ptr(t["node_logrho"]),
                              _ptr(t["ahat"]), _ptr(t["speedup"]), _stream(stream)))
     return t
+
+
+def flex_budget(batch, switch_batch, K, n_max, block):
+    """(branch, n_max) for a step of `batch` sequences under the batch-size
+    switch (td_flex_budget)."""
+    br, nm = ctypes.c_int32(0), ctypes.c_int32(0)
+    lib.td_flex_budget(int(batch), int(switch_batch), int(K), int(n_max), int(block),
+                       ctypes.byref(br), ctypes.byref(nm))
+    return br.value, nm.value
 
 
 def tree_mask(node_parent, n_nodes, out=None, stream=None):
@@ -318,7 +331,8 @@ class VerifyStep:
     captured in a HIP graph."""
 
     def __init__(self, *, batch, block, vocab, topk, n_max, use_stop, cost, l_ar, ahat0, hq, hkv,
-                 head_dim, scale, logits_dtype, attn_dtype, total_ctx, max_ctx, device):
+                 head_dim, scale, logits_dtype, attn_dtype, total_ctx, max_ctx, device, branch=0,
+                 min_logrho=float("-inf")):
         dev = device
         W = n_max + 1
         self.topk_id = torch.empty((batch, block, topk), dtype=torch.int32, device=dev)
@@ -337,6 +351,7 @@ class VerifyStep:
         a.n_max, a.use_stop = n_max, int(bool(use_stop))
         a.cost_a, a.cost_b, a.cost_c, a.cost_knee = float(cost[0]), float(cost[1]), float(cost[2]), int(cost[3])
         a.l_ar, a.ahat0 = float(l_ar), float(ahat0)
+        a.branch, a.min_logrho = int(branch), float(min_logrho)
         a.total_ctx, a.max_ctx = int(total_ctx), int(max_ctx)
         a.hq, a.hkv, a.head_dim, a.scale, a.attn_dtype = hq, hkv, head_dim, float(scale), attn_dtype
         t = self.tree

@@ -92,7 +92,8 @@ td_status td::check_tree_args(const int32_t *topk_id, const double *topk_logq, i
 extern "C" td_status td_build_tree(const int32_t *topk_id, const double *topk_logq, int32_t batch,
                                    int32_t block, int32_t K, int32_t n_max, int32_t use_stop,
                                    double cost_a, double cost_b, double cost_c, int32_t cost_knee,
-                                   double l_ar, double ahat0, const int32_t *root_token,
+                                   double l_ar, double ahat0, int32_t branch, double min_logrho,
+                                   const int32_t *root_token,
                                    int32_t *n_nodes, int32_t *node_token, int32_t *node_parent,
                                    int32_t *node_depth, double *node_logrho, double *ahat,
                                    double *speedup, void *stream) {
@@ -101,7 +102,7 @@ extern "C" td_status td_build_tree(const int32_t *topk_id, const double *topk_lo
                                           node_token, node_parent, node_depth, node_logrho);
     if (chk != TD_OK) return chk;
     TreeParams P{block, K, n_max, use_stop, cost_a, cost_b, cost_c, cost_knee, l_ar, ahat0,
-                 root_token};
+                 root_token, tree_branch(branch, K), min_logrho};
     TreeOut o{n_nodes, node_token, node_parent, node_depth, node_logrho, ahat, speedup, nullptr};
     hipStream_t st = as_stream(stream);
     switch (tree_slots(n_max)) {  // frontier: 1 + 2 n_max entries over 64 lanes
@@ -153,4 +154,11 @@ extern "C" td_status td_accept(const int32_t *node_token, const int32_t *node_pa
                        node_parent, n_nodes, target_token, n_max, block, accept_len, accept_path,
                        bonus_token);
     return check_launch("td_accept");
+}
+
+extern "C" void td_flex_budget(int32_t batch, int32_t switch_batch, int32_t K, int32_t n_max,
+                               int32_t block, int32_t *branch, int32_t *n_max_out) {
+    const bool single = switch_batch > 0 && batch >= switch_batch;
+    if (branch) *branch = single ? 1 : K;
+    if (n_max_out) *n_max_out = single ? (n_max < block ? n_max : block) : n_max;
 }

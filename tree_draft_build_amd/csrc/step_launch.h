@@ -19,6 +19,9 @@ constexpr size_t kStatusBytes = 16;
 constexpr uint32_t kStatusMerge = 1u;  // a row merger gave up (lse NaN)
 constexpr uint32_t kStatusTree = 2u;   // a tree builder gave up (n_nodes -1)
 
+// children per node of the tree builders: branch in 1..K, else K
+inline int tree_branch(int branch, int K) { return branch >= 1 && branch <= K ? branch : K; }
+
 // top-K workspace bytes (status header, per-workgroup epoch-tagged partials,
 // row records)
 size_t topk_workspace_bytes(int batch, int block, int vocab, int K);

@@ -60,6 +60,8 @@ struct TreeParams {
     int knee;
     double l_ar, ahat0;
     const int32_t *root_token;  // may be null
+    int branch;                 // children per node, 1..K (ranks 0..branch-1)
+    double min_logrho;          // selective verification: no node below this (< 0; else off)
 };
 
 struct TreeOut {
@@ -161,6 +163,9 @@ __device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &
 #undef TD_TREE_LEVEL
         }
         if (wk == kEmptyKey) break;  // no valid candidate left
+        // selective verification: every remaining candidate scores at most
+        // the best one, so the first one below the threshold ends the tree
+        if (P.min_logrho < 0.0 && wl < P.min_logrho) break;
 
         const double ahat_next = ahat + exp(wl);
         const double s_next = ahat_next * P.l_ar / cost_model(n + 1, P.ca, P.cb, P.cc, P.knee);
@@ -195,7 +200,7 @@ __device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &
         s_now = s_next;
 
         // lazy pushes: next sibling, then first child
-        if (rank + 1 < K) {
+        if (rank + 1 < P.branch) {
             const int e = count++;
             const int j = (depth - 1) * K + rank + 1;
             const double plr = parent == 0 ? 0.0 : t.lr[parent];

@@ -103,7 +103,8 @@ td_status launch_step(const td_step_args *a, void *workspace, void *stream) {
     char *ws = static_cast<char *>(workspace);
     if (draft) {
         const TreeParams tp{a->block, a->topk, a->n_max, a->use_stop, a->cost_a, a->cost_b,
-                            a->cost_c, a->cost_knee, a->l_ar, a->ahat0, a->root_token};
+                            a->cost_c, a->cost_knee, a->l_ar, a->ahat0, a->root_token,
+                            tree_branch(a->branch, a->topk), a->min_logrho};
         const TreeOut to{a->n_nodes, a->node_token, a->node_parent, a->node_depth,
                          a->node_logrho, a->ahat, a->speedup, a->mask};
         launch_topk_tree(a->logits, a->logits_dtype, a->batch, a->block, a->vocab, a->pos_stride,

@@ -39,6 +39,11 @@ def _load(path=None):
                                       c_int, c_double]
         lib.or_flex_budget.argtypes = [c_int, c_int, c_int, c_int, c_int, P, P]
         lib.or_flex_budget.restype = None
+        lib.or_tree_qkv.argtypes = [P, P, P, P, P, P, P, c_int, c_int, c_int, c_int, c_int, c_int,
+                                    c_int, c_double, P, P, P]
+        lib.or_lm_head_argmax.argtypes = [P, P, P, c_int, c_int, c_int, c_int, P, P, P]
+        lib.or_tree_qkv.restype = c_int
+        lib.or_lm_head_argmax.restype = c_int
         lib.or_tree_mask.argtypes = [P, P, c_int, c_int, P]
         lib.or_tree_attn.argtypes = [P, P, P, P, P, P, P, P, P, c_int, c_int, c_int, c_int, c_int,
                                      c_double, c_int, P, c_int32, c_int32, c_int32]
@@ -215,3 +220,46 @@ def kv_commit(k_tree, v_tree, accept_len, accept_path, bonus_token, k_cache, v_c
                                 batch, nq_max, block, hkv, d, dt, _p(k_cache), _p(v_cache),
                                 _p(ctx_offsets), _p(ctx_lengths), _p(nxt)), "or_kv_commit")
     return nxt
+
+
+def tree_qkv(embed, w_qkv, node_token, node_depth, n_nodes, ctx_offsets, hq, hkv, d, rope_base,
+             ctx_lengths=None):
+    """Projection of the tree tokens' embeddings with rotary positions.
+    embed [vocab][hidden], w_qkv [(hq + 2 hkv) d][hidden] bf16 bits (uint16).
+    Returns float64 q [b][nq][hq][d], k, v [b][nq][hkv][d] (zero beyond the tree)."""
+    embed = np.ascontiguousarray(embed, dtype=np.uint16)
+    w_qkv = np.ascontiguousarray(w_qkv, dtype=np.uint16)
+    node_token = _c(node_token, np.int32)
+    node_depth = _c(node_depth, np.int32)
+    n_nodes = _c(n_nodes, np.int32)
+    ctx_offsets = _c(ctx_offsets, np.int64)
+    lens = None if ctx_lengths is None else _c(ctx_lengths, np.int64)
+    b, nq = node_token.shape
+    vocab, hidden = embed.shape
+    assert w_qkv.shape == ((hq + 2 * hkv) * d, hidden)
+    q = np.empty((b, nq, hq, d))
+    k = np.empty((b, nq, hkv, d))
+    v = np.empty((b, nq, hkv, d))
+    _check(_load().or_tree_qkv(_p(embed), _p(w_qkv), _p(node_token), _p(node_depth), _p(n_nodes),
+                               _p(ctx_offsets), _p(lens), b, nq, hidden, vocab, hq, hkv, d,
+                               float(rope_base), _p(q), _p(k), _p(v)), "or_tree_qkv")
+    return q, k, v
+
+
+def lm_head_argmax(rows, w_lm, n_nodes):
+    """Greedy token of every tree row: argmax over the vocabulary of
+    rows [b][nq][hidden] (bf16 bits) times w_lm [vocab][hidden] (bf16 bits),
+    ties to the smaller id; -1 beyond the tree.  Returns (target, best,
+    second): the two largest float64 logits of each row."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint16)
+    w_lm = np.ascontiguousarray(w_lm, dtype=np.uint16)
+    n_nodes = _c(n_nodes, np.int32)
+    b, nq, hidden = rows.shape
+    vocab = w_lm.shape[0]
+    assert w_lm.shape[1] == hidden
+    tgt = np.empty((b, nq), np.int32)
+    best = np.empty((b, nq))
+    second = np.empty((b, nq))
+    _check(_load().or_lm_head_argmax(_p(rows), _p(w_lm), _p(n_nodes), b, nq, hidden, vocab,
+                                     _p(tgt), _p(best), _p(second)), "or_lm_head_argmax")
+    return tgt, best, second

@@ -527,3 +527,113 @@ void or_flex_budget(int batch, int switch_batch, int K, int n_max, int block, in
         *n_max_out = n_max;
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* A one-layer stand-in for the target's verification pass over the tree   */
+/* (the target scores every tree node in one parallel pass, "Problem-       */
+/* stellung"; its greedy token at each node is what acceptance compares,    */
+/* "Experimentelle Ergebnisse": temperature 0).  The pages fix no model; the */
+/* readings here: a node's input is the embedding row of its token; Q, K, V */
+/* are linear projections of it; rotary position embedding (rotate-half,    */
+/* inverse frequencies base^(-2j/D)) at the node's sequence position, which */
+/* is the context length plus its depth (tree siblings share a position);   */
+/* the attention output row (all query heads, hq * D = hidden) is the final */
+/* hidden state, and the target's greedy token is the argmax over the       */
+/* vocabulary of its product with the LM head (ties: smaller id).           */
+/* ------------------------------------------------------------------------ */
+
+/* element k of bf16 row r of a [rows][cols] table */
+static double bf(const void *t, int64_t cols, int64_t r, int64_t k)
+{
+    return widen(t, 1, r * cols + k);
+}
+
+int or_tree_qkv(const void *embed, const void *w_qkv, const int32_t *node_token,
+                const int32_t *node_depth, const int32_t *n_nodes, const int64_t *ctx_offsets,
+                const int64_t *ctx_lengths, int batch, int nq_max, int hidden, int vocab, int hq,
+                int hkv, int d, double rope_base, double *q, double *k, double *v)
+{
+    if (!embed || !w_qkv || !node_token || !node_depth || !n_nodes || !ctx_offsets || !q || !k ||
+        !v || batch < 0 || nq_max <= 0 || hidden <= 0 || vocab <= 0 || hq <= 0 || hkv <= 0 ||
+        d <= 0 || d % 2)
+        return OR_EINVAL;
+    int nout = (hq + 2 * hkv) * d;
+#pragma omp parallel
+    {
+    double *y = (double *)malloc(sizeof(double) * (size_t)nout);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < (int64_t)batch * nq_max; ++t) {
+        int b = (int)(t / nq_max), i = (int)(t % nq_max);
+        double *qo = q + t * hq * d, *ko = k + t * hkv * d, *vo = v + t * hkv * d;
+        for (int e = 0; e < hq * d; ++e) qo[e] = 0.0;
+        for (int e = 0; e < hkv * d; ++e) { ko[e] = 0.0; vo[e] = 0.0; }
+        if (!y || i > n_nodes[b]) continue;
+        int tok = node_token[t];
+        if (tok < 0 || tok >= vocab) tok = 0; /* no token: row 0 of the table */
+        /* projection: y[n] = sum_k x[k] w[n][k], in k order */
+        for (int n = 0; n < nout; ++n) {
+            double acc = 0.0;
+            for (int kk = 0; kk < hidden; ++kk)
+                acc += bf(embed, hidden, tok, kk) * bf(w_qkv, hidden, n, kk);
+            y[n] = acc;
+        }
+        /* rotary position embedding of the query and key heads */
+        int64_t len = ctx_offsets[b + 1] - ctx_offsets[b];
+        if (ctx_lengths && ctx_lengths[b] < len) len = ctx_lengths[b] < 0 ? 0 : ctx_lengths[b];
+        int depth = node_depth[t] < 0 ? 0 : node_depth[t];
+        double pos = (double)(len + depth);
+        for (int h = 0; h < hq + hkv; ++h) {
+            double *x = y + (int64_t)h * d;
+            for (int j = 0; j < d / 2; ++j) {
+                double ang = pos * pow(rope_base, -2.0 * j / d);
+                double c = cos(ang), s = sin(ang);
+                double x1 = x[j], x2 = x[j + d / 2];
+                x[j] = x1 * c - x2 * s;
+                x[j + d / 2] = x2 * c + x1 * s;
+            }
+        }
+        for (int e = 0; e < hq * d; ++e) qo[e] = y[e];
+        for (int e = 0; e < hkv * d; ++e) {
+            ko[e] = y[hq * d + e];
+            vo[e] = y[(hq + hkv) * d + e];
+        }
+    }
+    free(y);
+    }
+    return OR_OK;
+}
+
+int or_lm_head_argmax(const void *rows, const void *w_lm, const int32_t *n_nodes, int batch,
+                      int nq_max, int hidden, int vocab, int32_t *target, double *best,
+                      double *second)
+{
+    if (!rows || !w_lm || !n_nodes || !target || batch < 0 || nq_max <= 0 || hidden <= 0 ||
+        vocab <= 0)
+        return OR_EINVAL;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < (int64_t)batch * nq_max; ++t) {
+        int b = (int)(t / nq_max), i = (int)(t % nq_max);
+        target[t] = -1;
+        if (best) best[t] = NAN;
+        if (second) second[t] = NAN;
+        if (i > n_nodes[b]) continue;
+        double m1 = -INFINITY, m2 = -INFINITY;
+        int arg = -1;
+        for (int n = 0; n < vocab; ++n) {
+            double acc = 0.0;
+            for (int kk = 0; kk < hidden; ++kk)
+                acc += bf(rows, hidden, t, kk) * bf(w_lm, hidden, n, kk);
+            if (acc > m1) { /* strictly larger: the smaller id keeps a tie */
+                m2 = m1;
+                m1 = acc;
+                arg = n;
+            } else if (acc > m2) {
+                m2 = acc;
+            }
+        }
+        target[t] = arg;
+        if (best) best[t] = m1;
+        if (second) second[t] = m2;
+    }
+    return OR_OK;
+}

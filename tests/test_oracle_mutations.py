@@ -13,6 +13,7 @@ import pytest
 import oracle
 import test_oracle_accept as tac
 import test_oracle_commit as tcm
+import test_oracle_layer as tly
 import test_oracle_mask_attn as tma
 import test_oracle_selective as tse
 import test_oracle_topk as tto
@@ -78,6 +79,16 @@ MUTATIONS = [
     ("branch cap ignored at the root", "for (int j = 0; j < nb; ++j) { /* children of the root",
      "for (int j = 0; j < K; ++j) { /* children of the root",
      lambda: tse.test_branch_cap_is_the_order_over_low_ranks(1)),
+    ("rotation sign flipped", "x[j + d / 2] = x2 * c + x1 * s;", "x[j + d / 2] = x2 * c - x1 * s;",
+     lambda: tly.test_rotation_is_complex_multiplication()),
+    ("rotary frequencies halved", "double ang = pos * pow(rope_base, -2.0 * j / d);",
+     "double ang = pos * pow(rope_base, -1.0 * j / d);",
+     lambda: tly.test_rotation_is_complex_multiplication()),
+    ("position ignores depth", "double pos = (double)(len + depth);", "double pos = (double)len;",
+     lambda: tly.test_rotation_is_complex_multiplication()),
+    ("argmax tie to the larger id", "if (acc > m1) { /* strictly larger",
+     "if (acc >= m1) { /* strictly larger",
+     lambda: tly.test_argmax_matches_library_product_with_ties()),
     ("attention ignores context lengths", "if (!ctx_lengths) return region;", "return region;",
      lambda: tcm.test_attention_over_context_lengths_equals_compacted()),
 ]

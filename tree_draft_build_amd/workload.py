@@ -34,6 +34,7 @@ import numpy as np
 # Stream ids of the seeded generators.  Each (config, tensor, sequence) gets its
 # own PCG64 stream so that any one sequence can be regenerated on its own.
 T_LOGITS, T_SPIKE_IDX, T_SPIKE_MAG, T_SPIKE_ON, T_CTX_LEN, T_Q, T_KCTX, T_VCTX, T_KTREE, T_VTREE = range(10)
+T_EMBED, T_WQKV, T_WLM, T_ROWS = range(10, 14)
 
 
 @dataclass(frozen=True)
@@ -364,3 +365,62 @@ def target_tokens(cfg: Config, logits_f64: np.ndarray, node_token, node_parent, 
         out[i] = tm.tree_targets(i, node_token[i], node_parent[i], int(n_nodes[i]),
                                  node_token.shape[1] - 1)
     return out
+
+
+# ----------------------------------------------------------------------------
+# Weights of the one-layer verification stand-in (random, seeded)
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class LayerShape:
+    """Shape of the verification stand-in: Qwen3-8B's hidden size, heads and
+    vocabulary by default (the attention output of all query heads, hq * d,
+    is the hidden state the LM head reads)."""
+    vocab: int = 151936
+    hq: int = 32
+    hkv: int = 8
+    head_dim: int = 128
+    rope_base: float = 1e6
+
+    @property
+    def hidden(self) -> int:
+        return self.hq * self.head_dim
+
+    @property
+    def qkv_out(self) -> int:
+        return (self.hq + 2 * self.hkv) * self.head_dim
+
+
+def layer_shape(cfg: Config) -> LayerShape:
+    return LayerShape(vocab=cfg.vocab, hq=cfg.hq, hkv=cfg.hkv, head_dim=cfg.head_dim)
+
+
+def _normal_lut(scale: float) -> np.ndarray:
+    """256 bf16 bit patterns: the N(0, scale^2) quantiles at (i + 0.5) / 256."""
+    from statistics import NormalDist
+    nd = NormalDist()
+    v = np.array([nd.inv_cdf((i + 0.5) / 256) * scale for i in range(256)], np.float32)
+    return f32_to_bf16_bits(v)
+
+
+def _table(cfg: Config, tensor: int, rows: int, cols: int, scale: float) -> np.ndarray:
+    """[rows][cols] bf16 bits: each element one of 256 normal quantiles of
+    standard deviation `scale`, drawn uniformly (one random byte each)."""
+    codes = _rng(cfg, tensor).integers(0, 256, size=(rows, cols), dtype=np.uint8)
+    return _normal_lut(scale)[codes]
+
+
+def layer_weights(cfg: Config, shape: LayerShape | None = None) -> dict:
+    """Embedding table embed [vocab][hidden] (std 1), projection w_qkv
+    [(hq + 2 hkv) d][hidden] and LM head w_lm [vocab][hidden] (std
+    1/sqrt(hidden), so projections and logits are of order 1); bf16 bits."""
+    sh = layer_shape(cfg) if shape is None else shape
+    H = sh.hidden
+    return dict(embed=_table(cfg, T_EMBED, sh.vocab, H, 1.0),
+                w_qkv=_table(cfg, T_WQKV, sh.qkv_out, H, 1.0 / math.sqrt(H)),
+                w_lm=_table(cfg, T_WLM, sh.vocab, H, 1.0 / math.sqrt(H)))
+
+
+def hidden_rows(cfg: Config, rows: int, hidden: int) -> np.ndarray:
+    """[batch][rows][hidden] bf16 bits, std 1: stand-in final hidden states."""
+    return _table(cfg, T_ROWS, cfg.batch * rows, hidden, 1.0).reshape(cfg.batch, rows, hidden)

@@ -284,6 +284,61 @@ td_status td_kv_commit(const void *k_tree, const void *v_tree, const int32_t *ac
                        int64_t *ctx_lengths, int32_t *next_root, void *stream);
 
 /* ------------------------------------------------------------------------
+ * The verification pass, one layer (a stand-in for the target model; the
+ * pages fix no model).  The target scores every tree node in one parallel
+ * pass (Problemstellung) and acceptance compares its greedy token at each
+ * node (Experimentelle Ergebnisse: temperature 0).  These two calls give a
+ * one-layer target over the tree, with weights the caller provides:
+ *   td_tree_qkv        inputs of td_tree_verify_attn from the tree tokens;
+ *   td_lm_head_argmax  target_token of td_accept from the attention output.
+ * Readings: node i's input is the embedding row of its token; Q, K, V are
+ * linear projections of it; the query and key heads get rotary position
+ * embedding (rotate-half: dims j and j + D/2 of a head turn by the angle
+ * pos * rope_base^(-2j/D)) at position pos = L_b + depth(i), L_b the
+ * context length (tree siblings share a position); the attention output of
+ * all query heads (hidden = hq * head_dim) is the final hidden state; the
+ * greedy token is its argmax over the LM head (ties: smaller id).
+ * All matrices are bf16, rows contiguous, 16-byte aligned; products
+ * accumulate in float32; hidden must be a multiple of 128.  The workspace
+ * (td_verify_layer_workspace bytes, 16-byte aligned) holds partial sums
+ * only and needs no initialisation; one buffer serves both calls.
+ */
+size_t td_verify_layer_workspace(int32_t batch, int32_t nq_max, int32_t hq, int32_t hkv,
+                                 int32_t head_dim, int32_t vocab);
+
+/* td_tree_qkv
+ * Inputs:  embed [vocab][hidden]; w_qkv [(hq + 2 hkv) head_dim][hidden]
+ *          (output rows: the hq query heads, then hkv key heads, then hkv
+ *          value heads, head_dim each); node_token, node_depth
+ *          [batch][nq_max] and n_nodes [batch] as written by td_build_tree
+ *          (the root's token must be set: pass root_token there; a token
+ *          outside [0, vocab) reads embedding row 0); ctx_offsets /
+ *          ctx_lengths as for td_tree_verify_attn (they give L_b).
+ * Outputs: q [batch][nq_max][hq][head_dim], k_tree, v_tree
+ *          [batch][nq_max][hkv][head_dim] (bf16); rows past n_nodes[b] are
+ *          zero.  rope_base > 1 (Qwen3: 1e6).
+ */
+td_status td_tree_qkv(const void *embed, const void *w_qkv, const int32_t *node_token,
+                      const int32_t *node_depth, const int32_t *n_nodes,
+                      const int64_t *ctx_offsets, const int64_t *ctx_lengths, int32_t batch,
+                      int32_t nq_max, int32_t vocab, int32_t hq, int32_t hkv, int32_t head_dim,
+                      double rope_base, void *q, void *k_tree, void *v_tree, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* td_lm_head_argmax
+ * Inputs:  hidden_rows [batch][nq_max][hq * head_dim] (the attention
+ *          output: td_tree_verify_attn's out); w_lm [vocab][hq * head_dim];
+ *          n_nodes [batch].
+ * Output:  target_token [batch][nq_max]: the argmax over the vocabulary of
+ *          the row's logits (float32 accumulation; equal values go to the
+ *          smaller id), -1 past n_nodes[b].  The logits never reach memory.
+ */
+td_status td_lm_head_argmax(const void *hidden_rows, const void *w_lm, const int32_t *n_nodes,
+                            int32_t batch, int32_t nq_max, int32_t hq, int32_t head_dim,
+                            int32_t vocab, int32_t *target_token, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * td_verify_step -- the whole verify step, stages (a) to (d), in three
  * kernels instead of the five calls' seven: (1) top-K of every position,
  * then, by the last position of each sequence to finish, that sequence's

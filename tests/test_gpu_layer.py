@@ -1,0 +1,213 @@
+"""GPU: the one-layer verification stand-in (td_tree_qkv, td_lm_head_argmax)
+against the oracle, at a small shape on every row and at the Qwen3-8B shape
+(hidden 4096, vocabulary 151936) on a 65-row tree.
+
+Bars: q / k / v (bf16 outputs, float32 accumulation) within half a bf16 ulp
+of the float64 value plus 1e-3; target tokens exact wherever the oracle's
+best logit leads its runner-up by more than the float32 accumulation bound
+delta = 2 K 2^-24 sum_k |a_k| max |w|, and elsewhere a token whose oracle
+logit is within delta of the best (several answers are then correct)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import cost_of
+from tree_draft_build_amd import workload as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def td():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tree_draft_build_amd import binding
+    return binding
+
+
+def dev(x):
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(x).to(DEV)
+
+
+def f64(bits):
+    return wl.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def host_bf16(t):
+    return f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def qkv_close(got, want, what):
+    err = np.abs(got - want)
+    bound = 2.0 ** -8 * np.abs(want) + 1e-3
+    worst = (err / bound).max()
+    assert worst <= 1.0, f"{what}: error {err.max():.3g} exceeds the bound (ratio {worst:.3g})"
+
+
+def check_targets(got, rows_bits, w_bits, want, best, second, n_nodes, what):
+    a = f64(rows_bits)
+    wmax = np.abs(f64(w_bits)).max()
+    K = a.shape[-1]
+    for b in range(got.shape[0]):
+        for i in range(got.shape[1]):
+            if i > n_nodes[b]:
+                assert got[b, i] == -1, f"{what}: row {b},{i} past the tree"
+                continue
+            delta = 2 * K * 2.0 ** -24 * np.abs(a[b, i]).sum() * wmax
+            if best[b, i] - second[b, i] > delta:
+                assert got[b, i] == want[b, i], f"{what}: row {b},{i}: {got[b, i]} vs {want[b, i]}"
+            else:
+                lg = a[b, i] @ f64(w_bits[got[b, i]])
+                assert lg >= best[b, i] - delta, f"{what}: row {b},{i} near tie, invalid token"
+
+
+def tree_of(cfg, x):
+    ids, lq, _ = oracle.draft_topk(x, cfg.topk)
+    return oracle.build_tree(ids, lq, cfg.n_max, cfg.use_stop, cost_of(cfg), cfg.l_ar, cfg.ahat0,
+                             root_token=np.arange(cfg.batch, dtype=np.int32) + 7)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(2, 1, 64), (2, 2, 128), (4, 1, 64)])
+def test_tree_qkv_small(td, hq, hkv, d):
+    print("[case] tree_qkv small", hq, hkv, d, flush=True)
+    cfg = wl.CONFIGS["tiny_fixed"].replace(name="lqs", index=91, batch=3, vocab=300, hq=hq,
+                                           hkv=hkv, head_dim=d, ctx_law="uniform", ctx_p0=0,
+                                           ctx_p1=900, spike_lo=8.0, spike_hi=12.0)
+    sh = wl.LayerShape(vocab=cfg.vocab, hq=hq, hkv=hkv, head_dim=d, rope_base=1e4)
+    w = wl.layer_weights(cfg, sh)
+    tr = tree_of(cfg, wl.make_logits(cfg))
+    off = wl.ctx_offsets(cfg)
+    lens = np.array([0, 5, 10 ** 6], np.int64)          # empty, short, whole region
+    want = oracle.tree_qkv(w["embed"], w["w_qkv"], tr["node_token"], tr["node_depth"],
+                           tr["n_nodes"], off, hq, hkv, d, sh.rope_base, ctx_lengths=lens)
+    got = td.tree_qkv(dev(w["embed"]), dev(w["w_qkv"]), dev(tr["node_token"]),
+                      dev(tr["node_depth"]), dev(tr["n_nodes"]), dev(off), hq, hkv, d,
+                      sh.rope_base, ctx_lengths=dev(lens))
+    torch.cuda.synchronize()
+    for name, g, o in zip("qkv", got, want):
+        qkv_close(host_bf16(g), o, f"{name} {hq}/{hkv}x{d}")
+
+
+def test_lm_head_argmax_small(td):
+    print("[case] lm head small", flush=True)
+    cfg = wl.CONFIGS["tiny_fixed"].replace(name="lms", index=92, batch=3, n_max=40)
+    sh = wl.LayerShape(vocab=1000, hq=2, hkv=1, head_dim=128)
+    w = wl.layer_weights(cfg, sh)
+    rows = wl.hidden_rows(cfg, cfg.nq_max, sh.hidden)
+    w_lm = w["w_lm"].copy()
+    # exact ties: every row's winner copied into a smaller id
+    lg = f64(rows) @ f64(w_lm).T
+    for t in set(int(v) for v in lg.argmax(-1)[:, :4].ravel()):
+        if t > 0:
+            w_lm[t - 1] = w_lm[t]
+    n_nodes = np.array([40, 0, 17], np.int32)
+    want, best, second = oracle.lm_head_argmax(rows, w_lm, n_nodes)
+    got = td.lm_head_argmax(dev(rows), dev(w_lm), dev(n_nodes))
+    torch.cuda.synchronize()
+    check_targets(got.cpu().numpy(), rows, w_lm, want, best, second, n_nodes, "small")
+
+
+@pytest.fixture(scope="module")
+def qwen_layer():
+    cfg = wl.CONFIGS["qwen3_8b_stress"].replace(use_stop=False)
+    return cfg, wl.layer_shape(cfg), wl.layer_weights(cfg)
+
+
+def test_tree_qkv_qwen_shape(td, qwen_layer):
+    cfg, sh, w = qwen_layer
+    print("[case] tree_qkv qwen shape", flush=True)
+    x = wl.make_logits(cfg)
+    tr = tree_of(cfg, x)
+    assert int(tr["n_nodes"][0]) == 64
+    off = wl.ctx_offsets(cfg)
+    got = td.tree_qkv(dev(w["embed"]), dev(w["w_qkv"]), dev(tr["node_token"]),
+                      dev(tr["node_depth"]), dev(tr["n_nodes"]), dev(off), sh.hq, sh.hkv,
+                      sh.head_dim, sh.rope_base)
+    torch.cuda.synchronize()
+    want = oracle.tree_qkv(w["embed"], w["w_qkv"], tr["node_token"], tr["node_depth"],
+                           tr["n_nodes"], off, sh.hq, sh.hkv, sh.head_dim, sh.rope_base)
+    for name, g, o in zip("qkv", got, want):
+        qkv_close(host_bf16(g), o, f"{name} qwen shape")
+
+
+def test_lm_head_argmax_qwen_shape(td, qwen_layer):
+    cfg, sh, w = qwen_layer
+    print("[case] lm head qwen shape", flush=True)
+    rows = wl.hidden_rows(cfg.replace(batch=1), 65, sh.hidden)
+    n_nodes = np.array([64], np.int32)
+    got = td.lm_head_argmax(dev(rows), dev(w["w_lm"]), dev(n_nodes)).cpu().numpy()
+    torch.cuda.synchronize()
+    sample = [0, 1, 31, 64]                              # rows the oracle recomputes
+    sub = np.ascontiguousarray(rows[:, sample])
+    want, best, second = oracle.lm_head_argmax(sub, w["w_lm"], np.array([len(sample) - 1], np.int32))
+    check_targets(got[:, sample], sub, w["w_lm"], want, best, second,
+                  np.array([len(sample) - 1]), "qwen shape")
+
+
+def test_verify_layer_pipeline(td):
+    """Tree -> Q/K/V -> tree attention -> LM-head targets -> acceptance, all
+    on the GPU, against the oracle's own float64 pipeline on the same tree
+    (its q / k / v and attention output rounded to bf16 where the GPU's
+    stages hand bf16 on).  Attention within the bf16 bar; targets exact where
+    the oracle's best logit leads by more than the perturbation that the
+    attention bar allows (2e-2 per element times sum |w|), else a token
+    within that margin; acceptance bit-exact given the targets."""
+    print("[case] verify layer pipeline", flush=True)
+    cfg = wl.CONFIGS["tiny_fixed"].replace(name="lpipe", index=93, batch=2, vocab=512, hq=4,
+                                           hkv=2, head_dim=64, ctx_law="uniform", ctx_p0=30,
+                                           ctx_p1=90, spike_lo=8.0, spike_hi=12.0,
+                                           attn_dtype="bf16")
+    sh = wl.LayerShape(vocab=cfg.vocab, hq=cfg.hq, hkv=cfg.hkv, head_dim=cfg.head_dim,
+                       rope_base=1e4)
+    w = wl.layer_weights(cfg, sh)
+    x = wl.make_logits(cfg)
+    tr = tree_of(cfg, x)
+    inp = wl.make_attn_inputs(cfg)                       # context K/V
+    off = inp["ctx_offsets"]
+    g = {k: dev(v) for k, v in tr.items() if isinstance(v, np.ndarray)}
+    q, kt, vt = td.tree_qkv(dev(w["embed"]), dev(w["w_qkv"]), g["node_token"], g["node_depth"],
+                            g["n_nodes"], dev(off), sh.hq, sh.hkv, sh.head_dim, sh.rope_base)
+    mask = td.tree_mask(g["node_parent"], g["n_nodes"])
+    out = td.tree_verify_attn(q, dev(inp["k_ctx"]), dev(inp["v_ctx"]), dev(off), int(off[-1]),
+                              int(inp["ctx_len"].max()), kt, vt, mask, g["n_nodes"],
+                              wl.attn_scale(cfg))
+    tgt = td.lm_head_argmax(out, dev(w["w_lm"]), g["n_nodes"])
+    alen, path, bonus = td.accept(g["node_token"], g["node_parent"], g["n_nodes"], tgt, cfg.block)
+    torch.cuda.synchronize()
+    # the oracle's pipeline
+    oq, ok_, ov = oracle.tree_qkv(w["embed"], w["w_qkv"], tr["node_token"], tr["node_depth"],
+                                  tr["n_nodes"], off, sh.hq, sh.hkv, sh.head_dim, sh.rope_base)
+    for name, gg, o in (("q", q, oq), ("k", kt, ok_), ("v", vt, ov)):
+        qkv_close(host_bf16(gg), o, f"pipeline {name}")
+    bits = lambda a: wl.f32_to_bf16_bits(a.astype(np.float32))
+    m_o = oracle.tree_mask(tr["node_parent"], tr["n_nodes"])
+    oa = oracle.tree_attn(bits(oq), inp["k_ctx"], inp["v_ctx"], off, bits(ok_), bits(ov), m_o,
+                          tr["n_nodes"], sh.hq, sh.hkv, sh.head_dim, wl.attn_scale(cfg))
+    oa_g = host_bf16(out)
+    assert np.abs(oa_g - oa).max() < 2e-2
+    rows = bits(oa).reshape(cfg.batch, cfg.nq_max, -1)
+    want, best, second = oracle.lm_head_argmax(rows, w["w_lm"], tr["n_nodes"])
+    got_t = tgt.cpu().numpy()
+    wl_f = f64(w["w_lm"])
+    decisive = 0
+    for b in range(cfg.batch):
+        for i in range(cfg.nq_max):
+            if i > tr["n_nodes"][b]:
+                assert got_t[b, i] == -1
+                continue
+            margin = 2e-2 * np.abs(wl_f).sum(-1).max()
+            if best[b, i] - second[b, i] > 2 * margin:
+                assert got_t[b, i] == want[b, i]
+                decisive += 1
+            else:
+                assert f64(rows[b, i]) @ wl_f[got_t[b, i]] >= best[b, i] - 2 * margin
+    a_o, p_o, b_o = oracle.accept(tr["node_token"], tr["node_parent"], tr["n_nodes"], got_t,
+                                  cfg.block)
+    np.testing.assert_array_equal(alen.cpu().numpy(), a_o)
+    np.testing.assert_array_equal(path.cpu().numpy(), p_o)
+    np.testing.assert_array_equal(bonus.cpu().numpy(), b_o)

@@ -29,7 +29,8 @@ EXPORTED = ["td_abi_version", "td_last_error", "td_draft_topk_workspace", "td_dr
             "td_build_tree", "td_tree_mask", "td_tree_verify_attn_workspace",
             "td_tree_verify_attn", "td_accept", "td_step_args_bytes", "td_verify_step_workspace",
             "td_verify_step", "td_workspace_status", "td_verify_step_noalloc",
-            "td_verify_step_events", "td_kv_commit", "td_flex_budget"]
+            "td_verify_step_events", "td_kv_commit", "td_flex_budget",
+            "td_verify_layer_workspace", "td_tree_qkv", "td_lm_head_argmax"]
 
 
 class StepArgs(ctypes.Structure):
@@ -78,6 +79,12 @@ def _load():
                                   c_double, P, P, P, P, P, P, P, P, P]
     lib.td_flex_budget.argtypes = [c_int32] * 5 + [P, P]
     lib.td_flex_budget.restype = None
+    lib.td_verify_layer_workspace.argtypes = [c_int32] * 6
+    lib.td_verify_layer_workspace.restype = c_size_t
+    lib.td_tree_qkv.argtypes = [P, P, P, P, P, P, P, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                c_int32, c_double, P, P, P, P, c_size_t, P]
+    lib.td_lm_head_argmax.argtypes = [P, P, P, c_int32, c_int32, c_int32, c_int32, c_int32, P, P,
+                                      c_size_t, P]
     lib.td_tree_mask.argtypes = [P, P, c_int32, c_int32, P, P]
     lib.td_tree_verify_attn_workspace.argtypes = [c_int32] * 5 + [c_int64, c_int64]
     lib.td_tree_verify_attn_workspace.restype = c_size_t
@@ -95,7 +102,8 @@ def _load():
     lib.td_verify_step_events.argtypes = [ctypes.POINTER(StepArgs), P, c_size_t, P, P, P]
     for name in ("td_draft_topk", "td_build_tree", "td_tree_mask", "td_tree_verify_attn",
                  "td_accept", "td_verify_step", "td_workspace_status", "td_verify_step_noalloc",
-                 "td_verify_step_events", "td_kv_commit"):
+                 "td_verify_step_events", "td_kv_commit", "td_tree_qkv",
+                 "td_lm_head_argmax"):
         getattr(lib, name).restype = c_int
     if lib.td_step_args_bytes() != ctypes.sizeof(StepArgs):
         raise ImportError("td_step_args layout differs between the library and this binding")
@@ -318,6 +326,65 @@ def kv_commit(k_tree, v_tree, accept_len, accept_path, bonus_token, k_cache, v_c
                             _ptr(bonus_token), b, nq, block, hkv, d, _dt(k_tree), _ptr(k_cache),
                             _ptr(v_cache), _ptr(ctx_offsets), _ptr(ctx_lengths), _ptr(next_root),
                             _stream(stream)))
+
+
+def verify_layer_workspace(batch, nq_max, hq, hkv, head_dim, vocab, device):
+    n = int(lib.td_verify_layer_workspace(batch, nq_max, hq, hkv, head_dim, vocab))
+    if n == 0:
+        raise TreedraftError(TD_EINVAL, "invalid verify-layer shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def tree_qkv(embed, w_qkv, node_token, node_depth, n_nodes, ctx_offsets, hq, hkv, head_dim,
+             rope_base, ctx_lengths=None, out=None, workspace=None, stream=None):
+    """Q / K / V of the tree tokens with rotary positions (bf16).  Returns
+    (q [b][nq][hq][d], k_tree [b][nq][hkv][d], v_tree)."""
+    _dev(embed, "embed", torch.bfloat16)
+    vocab, hidden = embed.shape
+    _dev(w_qkv, "w_qkv", torch.bfloat16, ((hq + 2 * hkv) * head_dim, hidden))
+    _dev(node_token, "node_token", torch.int32)
+    b, nq = node_token.shape
+    _dev(node_depth, "node_depth", torch.int32, (b, nq))
+    _dev(n_nodes, "n_nodes", torch.int32, (b,))
+    _dev(ctx_offsets, "ctx_offsets", torch.int64, (b + 1,))
+    if ctx_lengths is not None:
+        _dev(ctx_lengths, "ctx_lengths", torch.int64, (b,))
+    dev = embed.device
+    if out is None:
+        out = (torch.empty((b, nq, hq, head_dim), dtype=torch.bfloat16, device=dev),
+               torch.empty((b, nq, hkv, head_dim), dtype=torch.bfloat16, device=dev),
+               torch.empty((b, nq, hkv, head_dim), dtype=torch.bfloat16, device=dev))
+    q, k, v = out
+    if workspace is None:
+        workspace = verify_layer_workspace(b, nq, hq, hkv, head_dim, vocab, dev)
+    _check(lib.td_tree_qkv(_ptr(embed), _ptr(w_qkv), _ptr(node_token), _ptr(node_depth),
+                           _ptr(n_nodes), _ptr(ctx_offsets), _ptr(ctx_lengths), b, nq, vocab, hq,
+                           hkv, head_dim, float(rope_base), _ptr(q), _ptr(k), _ptr(v),
+                           _ptr(workspace), workspace.numel(), _stream(stream)))
+    return q, k, v
+
+
+def lm_head_argmax(hidden_rows, w_lm, n_nodes, out=None, workspace=None, stream=None):
+    """Greedy target token of every tree row: argmax over the vocabulary of
+    hidden_rows [b][nq][hq][d] (or [b][nq][hidden]) times w_lm [vocab][hidden]."""
+    _dev(hidden_rows, "hidden_rows", torch.bfloat16)
+    b, nq = hidden_rows.shape[:2]
+    hidden = hidden_rows[0, 0].numel()
+    _dev(w_lm, "w_lm", torch.bfloat16)
+    vocab = w_lm.shape[0]
+    if w_lm.shape[1] != hidden:
+        raise ValueError("w_lm must have shape [vocab][hidden]")
+    _dev(n_nodes, "n_nodes", torch.int32, (b,))
+    head_dim = 128 if hidden % 128 == 0 else 64
+    hq = hidden // head_dim
+    if out is None:
+        out = torch.empty((b, nq), dtype=torch.int32, device=w_lm.device)
+    if workspace is None:
+        workspace = verify_layer_workspace(b, nq, hq, hq, head_dim, vocab, w_lm.device)
+    _check(lib.td_lm_head_argmax(_ptr(hidden_rows), _ptr(w_lm), _ptr(n_nodes), b, nq, hq, head_dim,
+                                 vocab, _ptr(out), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)))
+    return out
 
 
 # ---------------------------------------------------------------------------

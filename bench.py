@@ -54,6 +54,8 @@ def parse():
                     help="skip the full-tree (N = 64 fixed) measurement")
     ap.add_argument("--no-decode", dest="decode", action="store_false",
                     help="skip the multi-step decode loop with KV commit")
+    ap.add_argument("--no-layer", dest="layer", action="store_false",
+                    help="skip the one-layer verification pass and the tachometer")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="threads of the all-core oracle baseline (0: every core available)")
     return ap.parse_args()
@@ -85,6 +87,10 @@ def main():
             "value": tres["value"], "unit": "verify steps/s", "ms_per_step": tres["ms_per_step"],
             "steps": tres["steps"], "kernels_us": tres["kernels_us"],
             "kernel_roofline": tres["kernel_roofline"]}
+    if args.layer and cfg.name == "qwen3_8b":
+        # the one-layer verification pass (Q/K/V + RoPE, attention, LM-head
+        # argmax) at the Qwen3-8B shape, and the tachometer fitted to it
+        result.update(layer_rows(args))
     if args.decode and cfg.name == "qwen3_8b":
         # the step in a decode loop: the accepted path's K/V committed into
         # the context after each step, the bonus token as the next root
@@ -386,6 +392,148 @@ def measure(cfg, args, steps, warmup):
                                  "TFLOP/s": round(flops_c / (stage_ms[2] * 1e-3) / 1e12, 3)}},
     }
     return result, x, inp
+
+
+def layer_rows(args):
+    """The one-layer verification pass at the Qwen3-8B shape (hidden 4096,
+    32/8 heads of 128, vocabulary 151936, random bf16 weights) on a 64-node
+    tree over a 4096-token context:
+      verify_layer  per call: td_tree_qkv (the 6144 x 4096 projection streams
+                    50 MB of weights) and td_lm_head_argmax (151936 x 4096:
+                    1.24 GB), each against the HBM roofline, and the whole
+                    step (draft kernel, Q/K/V, attention, LM head, acceptance)
+                    in a graph;
+      tachometer    the pass timed over tree sizes 0 .. 255 and the fit of
+                    C(N) = a + b N + c max(0, N - knee); with the fitted cost
+                    the S(N) stop picks N* on the headline logits."""
+    import torch
+
+    from tree_draft_build_amd import binding as td
+    from tree_draft_build_amd import tachometer as tach
+    from tree_draft_build_amd import workload as wl
+
+    dev = torch.device("cuda:0")
+    cfg = wl.CONFIGS["qwen3_8b_tree"]
+    sh = wl.layer_shape(cfg)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    w = {k: up(v) for k, v in wl.layer_weights(cfg, sh).items()}
+    x = wl.make_logits(cfg)
+    inp = wl.make_attn_inputs(cfg)
+    kc, vc, off = up(inp["k_ctx"]), up(inp["v_ctx"]), up(inp["ctx_offsets"])
+    ids, lq, _ = td.draft_topk(up(x), cfg.topk)
+    stream = torch.cuda.current_stream()
+    pass_kw = dict(batch=cfg.batch, hq=sh.hq, hkv=sh.hkv, head_dim=sh.head_dim, vocab=sh.vocab,
+                   weights=w, k_ctx=kc, v_ctx=vc, ctx_offsets=off, scale=wl.attn_scale(cfg),
+                   rope_base=sh.rope_base, device=dev)
+
+    # ---- per call, at N = 64 ----
+    tree = td.build_tree(ids, lq, cfg.n_max, False)
+    vp = tach.VerifyPass(nq_max=cfg.nq_max, **pass_kw)
+    reps = max(20, args.steps // 4)
+
+    def loop_us(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(reps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / reps
+
+    rows = cfg.batch * cfg.nq_max
+    qkv_us = loop_us(lambda: td.tree_qkv(w["embed"], w["w_qkv"], tree["node_token"],
+                                          tree["node_depth"], tree["n_nodes"], off, sh.hq, sh.hkv,
+                                          sh.head_dim, sh.rope_base, out=(vp.q, vp.kt, vp.vt),
+                                          workspace=vp.ws_layer))
+    lm_us = loop_us(lambda: td.lm_head_argmax(vp.out, w["w_lm"], tree["n_nodes"], out=vp.target,
+                                               workspace=vp.ws_layer))
+    qkv_bytes = sh.qkv_out * sh.hidden * 2 + rows * sh.hidden * 2 + rows * sh.qkv_out * 2
+    lm_bytes = sh.vocab * sh.hidden * 2 + rows * sh.hidden * 2 + rows * 4
+
+    def roof(name, us, nbytes, flops):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"kernel": name, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "avg_launch_us": round(us, 2),
+                "bytes_per_launch": int(nbytes), "flops_per_launch": int(flops),
+                "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_TFLOPS, 5),
+                "timing": "HIP events around back-to-back calls"}
+
+    # ---- the whole step with the layer, graph-captured ----
+    vs = td.VerifyStep(batch=cfg.batch, block=cfg.block, vocab=cfg.vocab, topk=cfg.topk,
+                       n_max=cfg.n_max, use_stop=False,
+                       cost=(cfg.cost_a, cfg.cost_b, cfg.cost_c, cfg.cost_knee), l_ar=cfg.l_ar,
+                       ahat0=cfg.ahat0, hq=cfg.hq, hkv=cfg.hkv, head_dim=cfg.head_dim,
+                       scale=wl.attn_scale(cfg), logits_dtype=td.TD_BF16, attn_dtype=td.TD_BF16,
+                       total_ctx=int(inp["ctx_offsets"][-1]), max_ctx=int(inp["ctx_len"].max()),
+                       device=dev)
+    root = torch.zeros(cfg.batch, dtype=torch.int32, device=dev)
+    lg = up(x)
+    vs.set_inputs(lg, vp.q, kc, vc, off, vp.kt, vp.vt, vp.target, root_token=root)
+    acc = (torch.empty(cfg.batch, dtype=torch.int32, device=dev),
+           torch.empty((cfg.batch, cfg.block + 1), dtype=torch.int32, device=dev),
+           torch.empty(cfg.batch, dtype=torch.int32, device=dev))
+
+    def full_step():
+        vs.run(stages=td.TD_STEP_DRAFT)              # top-K, tree, mask
+        t = vs.tree
+        td.tree_qkv(w["embed"], w["w_qkv"], t["node_token"], t["node_depth"], t["n_nodes"], off,
+                    sh.hq, sh.hkv, sh.head_dim, sh.rope_base, out=(vp.q, vp.kt, vp.vt),
+                    workspace=vp.ws_layer)
+        td.tree_verify_attn(vp.q, kc, vc, off, vp.total_ctx, vp.total_ctx, vp.kt, vp.vt, vs.mask,
+                            t["n_nodes"], wl.attn_scale(cfg), out=vp.out, workspace=vp.ws_attn)
+        td.lm_head_argmax(vp.out, w["w_lm"], t["n_nodes"], out=vp.target, workspace=vp.ws_layer)
+        td.accept(t["node_token"], t["node_parent"], t["n_nodes"], vp.target, cfg.block, out=acc)
+
+    full_step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        full_step()
+    step_us = loop_us(g.replay)
+
+    # ---- tachometer ----
+    points = tach.measure(ids, lq, reps=10, warmup=2, **pass_kw)
+    fit = tach.fit(points)
+    # the fitted cost model drives the S(N) stop on the headline logits
+    hcfg = wl.CONFIGS["qwen3_8b"]
+    hids, hlq, _ = td.draft_topk(up(wl.make_logits(hcfg)), hcfg.topk)
+    picked = {}
+    for name, cost, lar in (("configured", (hcfg.cost_a, hcfg.cost_b, hcfg.cost_c, hcfg.cost_knee),
+                             hcfg.l_ar), ("fitted", fit["cost"], fit["l_ar"])):
+        t_ = td.build_tree(hids, hlq, hcfg.n_max, True, cost, lar, hcfg.ahat0)
+        picked[name] = {"n_nodes": int(t_["n_nodes"][0]), "ahat": round(float(t_["ahat"][0]), 4),
+                        "speedup_estimate": round(float(t_["speedup"][0]), 4)}
+    return {
+        "verify_layer": {
+            "workload": "qwen3_8b_tree one-layer verification (hidden 4096, vocab 151936)",
+            "rows": rows,
+            "step_value": round(1e6 / step_us, 1), "step_unit": "verify steps/s",
+            "step_us": round(step_us, 2),
+            "step": "kernel 1 (top-K, tree, mask), Q/K/V + RoPE (2 kernels), attention "
+                    "(2 kernels), LM-head argmax (2 kernels), acceptance; one graph",
+            "kernel_roofline": {
+                "tree_qkv": roof("tree_qkv (projection + RoPE)", qkv_us, qkv_bytes,
+                                 2 * rows * sh.hidden * sh.qkv_out),
+                "lm_head_argmax": roof("lm_head_argmax", lm_us, lm_bytes,
+                                       2 * rows * sh.hidden * sh.vocab)}},
+        "tachometer": {
+            "what": "the one-layer verification pass (Q/K/V, tree attention, LM-head argmax) "
+                    "timed at tree sizes N, fitted to C(N) = a + b N + c max(0, N - knee)",
+            "points_us": [[p[1], round(p[2], 2)] for p in points],
+            "fit_us": {"a": round(fit["a_us"], 3), "b": round(fit["b_us"], 5),
+                       "c": round(fit["c_us"], 5), "knee": fit["knee"], "r2": round(fit["r2"], 5)},
+            "cost_normalised": [round(v, 6) for v in fit["cost"][:3]] + [fit["cost"][3]],
+            "stop_on_headline_logits": picked}}
 
 
 def decode_row(cfg, args, steps, warmup):

@@ -180,6 +180,23 @@ void td_flex_budget(int32_t batch, int32_t switch_batch, int32_t K, int32_t n_ma
                     int32_t *branch, int32_t *n_max_out);
 
 /* ------------------------------------------------------------------------
+ * td_fit_cost -- the tachometer's fit (Methodik §3, latency modelling: a
+ * roofline model of the verification latency, calibrated on observed
+ * runtimes).  Host function; every pointer is HOST memory.  Fits
+ *   C(N) = a + b N + c max(0, N - knee)
+ * to count >= 3 measured pairs (n[i] draft nodes, t[i] verification time)
+ * by least squares: every integer knee in [knee_min, knee_max] is tried and
+ * the smallest residual sum of squares wins (equal sums: the smaller knee;
+ * a knee at or past every n[i] fits c = 0).  Writes a, b, c, knee and, if
+ * rss is not NULL, the residual sum.  For td_build_tree's stop, pass the
+ * coefficients as they are with l_ar = a (the one-token step), or divided
+ * by a with l_ar = 1.
+ */
+td_status td_fit_cost(const double *n, const double *t, int32_t count, int32_t knee_min,
+                      int32_t knee_max, double *a, double *b, double *c, int32_t *knee,
+                      double *rss);
+
+/* ------------------------------------------------------------------------
  * td_tree_mask -- stage (b').
  * The draft tree is prefix-closed (Methodik §1, marginal independence: the
  * per-position candidates combine freely into a prefix tree), and the target

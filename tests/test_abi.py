@@ -25,7 +25,7 @@ def b():
 
 def test_every_declared_symbol_is_exported(b):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(b.lib, n), n
     assert sorted(b.EXPORTED) == names
@@ -175,3 +175,30 @@ def test_step_args_layout_and_validation(b):
     a.batch, a.total_ctx, a.max_ctx = 64, 64 * 32768, 32768
     assert b.lib.td_verify_step_noalloc(ctypes.byref(a), None) == 2
     assert "64 MiB" in b.last_error()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fit_cost_matches_oracle(b, seed):
+    """The library's fit (normal equations) against the oracle's (library
+    least squares per knee) on noisy piecewise-linear measurements."""
+    import numpy as np
+    from oracle.fit import fit_cost
+    rng = np.random.default_rng(seed)
+    n = np.repeat(np.array([0, 1, 2, 4, 8, 16, 24, 32, 48, 64, 80, 96, 128], float), 3)
+    knee = int(rng.integers(8, 100))
+    t = 50 + rng.uniform(0, 0.2) * n + rng.uniform(0.5, 3) * np.maximum(0, n - knee)
+    t = t + rng.normal(0, 0.05, len(t))
+    got = b.fit_cost(n, t, 0, 128)
+    want = fit_cost(n, t, 0, 128)
+    assert got[3] == want[3]
+    for g, w in zip(got[:3], want[:3]):
+        assert g == pytest.approx(w, rel=1e-7, abs=1e-9)
+    assert got[4] == pytest.approx(want[4], rel=1e-7)
+
+
+def test_fit_cost_validation(b):
+    import numpy as np
+    with pytest.raises(b.TreedraftError):
+        b.fit_cost(np.array([1.0, 2.0]), np.array([1.0, 2.0]), 0, 4)
+    with pytest.raises(b.TreedraftError):
+        b.fit_cost(np.array([1.0, 2.0, 3.0]), np.array([1.0, 2.0, 3.0]), 5, 4)

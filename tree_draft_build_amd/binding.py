@@ -30,7 +30,7 @@ EXPORTED = ["td_abi_version", "td_last_error", "td_draft_topk_workspace", "td_dr
             "td_tree_verify_attn", "td_accept", "td_step_args_bytes", "td_verify_step_workspace",
             "td_verify_step", "td_workspace_status", "td_verify_step_noalloc",
             "td_verify_step_events", "td_kv_commit", "td_flex_budget",
-            "td_verify_layer_workspace", "td_tree_qkv", "td_lm_head_argmax"]
+            "td_verify_layer_workspace", "td_tree_qkv", "td_lm_head_argmax", "td_fit_cost"]
 
 
 class StepArgs(ctypes.Structure):
@@ -79,6 +79,8 @@ def _load():
                                   c_double, P, P, P, P, P, P, P, P, P]
     lib.td_flex_budget.argtypes = [c_int32] * 5 + [P, P]
     lib.td_flex_budget.restype = None
+    lib.td_fit_cost.argtypes = [P, P, c_int32, c_int32, c_int32, P, P, P, P, P]
+    lib.td_fit_cost.restype = c_int
     lib.td_verify_layer_workspace.argtypes = [c_int32] * 6
     lib.td_verify_layer_workspace.restype = c_size_t
     lib.td_tree_qkv.argtypes = [P, P, P, P, P, P, P, c_int32, c_int32, c_int32, c_int32, c_int32,
@@ -232,6 +234,22 @@ def flex_budget(batch, switch_batch, K, n_max, block):
     lib.td_flex_budget(int(batch), int(switch_batch), int(K), int(n_max), int(block),
                        ctypes.byref(br), ctypes.byref(nm))
     return br.value, nm.value
+
+
+def fit_cost(n, t, knee_min, knee_max):
+    """Least-squares fit of C(N) = a + b N + c max(0, N - knee) to measured
+    (n, t) pairs (host arrays).  Returns (a, b, c, knee, rss)."""
+    import numpy as np
+    n = np.ascontiguousarray(n, dtype=np.float64)
+    t = np.ascontiguousarray(t, dtype=np.float64)
+    if n.shape != t.shape:
+        raise ValueError("n and t differ in length")
+    a, b, c, r = c_double(), c_double(), c_double(), c_double()
+    k = c_int32()
+    _check(lib.td_fit_cost(n.ctypes.data_as(c_void_p), t.ctypes.data_as(c_void_p), len(n),
+                           int(knee_min), int(knee_max), ctypes.byref(a), ctypes.byref(b),
+                           ctypes.byref(c), ctypes.byref(k), ctypes.byref(r)))
+    return a.value, b.value, c.value, k.value, r.value
 
 
 def tree_mask(node_parent, n_nodes, out=None, stream=None):

@@ -107,8 +107,8 @@ td_status td_draft_topk(const void *logits, td_dtype dtype, int32_t batch, int32
  *   - a row merger writes lse = NaN for its row (its ids and log q are then
  *     meaningless), and
  *   - a tree builder writes n_nodes = -1 for its sequence (its tree entries
- *     are then meaningless; the verify step's attention then writes zero
- *     rows and its acceptance reports A = 0 with the root's target token),
+ *     are then meaningless; the verify step's attention then writes no
+ *     row and its acceptance reports A = 0 with the root's target token),
  * and each sets a bit in a status word at the start of the workspace.
  * This call waits for `stream`, reads that word and clears it: TD_OK if no
  * call gave up since the last check, TD_ESYNC otherwise (td_last_error()
@@ -220,7 +220,8 @@ td_status td_tree_mask(const int32_t *node_parent, const int32_t *n_nodes, int32
  *   out[b][i][h] = sum_j softmax_j(scale * q[b][i][h] . k_j) v_j
  * over the admitted keys j: all context keys of b, plus the tree keys whose
  * bit is set in mask row (b, i).  KV head of query head h is h / (hq/hkv).
- * Rows i > n_nodes[b] are written as zeros.
+ * Rows i > n_nodes[b] of out are not written (their contents are left as
+ * they were): only the tree's rows are verified.
  * Inputs:
  *   q        [batch][nq_max][hq][head_dim]
  *   k_ctx, v_ctx [total_ctx][hkv][head_dim]; sequence b owns the region of

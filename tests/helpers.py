@@ -106,9 +106,21 @@ def targets_by_path(cfg, logits_f64, gpu_tree, seqs=None):
                             gpu_tree["n_nodes"], seqs=seqs)
 
 
-def attn_close(got, want, dtype, what=""):
-    """Attention parity: absolute bound (2e-2 bf16, 1e-4 f32) and, as extra
-    evidence, a relative Frobenius bound per (row, head) block."""
+def tree_rows(a, n_nodes):
+    """Copy of a [b][nq][...] array with the rows past each tree (i >
+    n_nodes[b]) set to zero: the attention leaves those rows unwritten."""
+    a = np.array(a, copy=True)
+    for b, n in enumerate(np.asarray(n_nodes).reshape(-1)):
+        a[b, int(n) + 1:] = 0
+    return a
+
+
+def attn_close(got, want, dtype, what, n_nodes):
+    """Attention parity on the tree rows (rows past n_nodes[b] are not
+    written and not compared): absolute bound (2e-2 bf16, 1e-4 f32) and, as
+    extra evidence, a relative Frobenius bound per (row, head) block."""
+    got = tree_rows(got, n_nodes)
+    want = tree_rows(want, n_nodes)
     atol = 2e-2 if dtype == "bf16" else 1e-4
     rel = 1e-2 if dtype == "bf16" else 1e-5
     err = np.abs(got - want)
@@ -118,4 +130,4 @@ def attn_close(got, want, dtype, what=""):
     ok = den > 0
     worst = (num[ok] / den[ok]).max() if ok.any() else 0.0
     assert worst <= rel, f"{what}: relative Frobenius error {worst:.3g} > {rel}"
-    assert np.all(got[~ok] == 0), f"{what}: rows that must be zero are not"
+    assert np.all(got[~ok] == 0), f"{what}: tree rows that must be zero are not"

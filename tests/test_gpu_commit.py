@@ -81,7 +81,7 @@ def test_attention_over_context_lengths(td):
     want = oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"], inp["k_tree"],
                             inp["v_tree"], mask, n_nodes, cfg.hq, cfg.hkv, cfg.head_dim,
                             wl.attn_scale(cfg), ctx_lengths=lens)
-    attn_close(got, want, "bf16", "context lengths")
+    attn_close(got, want, "bf16", "context lengths", n_nodes)
 
 
 @pytest.mark.parametrize("name,steps", [("qwen3_8b_stress", 4), ("tiny_masksens", 3)])
@@ -150,7 +150,7 @@ def test_multi_step_decode(td, name, steps):
             got = wl.bf16_bits_to_f32(host(vs.out)).astype(np.float64)
         else:
             got = host(vs.out).astype(np.float64)
-        attn_close(got, want, cfg.attn_dtype, f"{name} step {step}")
+        attn_close(got, want, cfg.attn_dtype, f"{name} step {step}", tree["n_nodes"])
         a_o, p_o, b_o = oracle.accept(tree["node_token"], tree["node_parent"], tree["n_nodes"], tg,
                                       cfg.block)
         np.testing.assert_array_equal(vs.accept_len.cpu().numpy(), a_o)

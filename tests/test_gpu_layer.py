@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import cost_of
+from helpers import cost_of, tree_rows
 from tree_draft_build_amd import workload as wl
 
 pytestmark = pytest.mark.gpu
@@ -188,8 +188,8 @@ def test_verify_layer_pipeline(td):
     m_o = oracle.tree_mask(tr["node_parent"], tr["n_nodes"])
     oa = oracle.tree_attn(bits(oq), inp["k_ctx"], inp["v_ctx"], off, bits(ok_), bits(ov), m_o,
                           tr["n_nodes"], sh.hq, sh.hkv, sh.head_dim, wl.attn_scale(cfg))
-    oa_g = host_bf16(out)
-    assert np.abs(oa_g - oa).max() < 2e-2
+    oa_g = tree_rows(host_bf16(out), tr["n_nodes"])
+    assert np.abs(oa_g - tree_rows(oa, tr["n_nodes"])).max() < 2e-2
     rows = bits(oa).reshape(cfg.batch, cfg.nq_max, -1)
     want, best, second = oracle.lm_head_argmax(rows, w["w_lm"], tr["n_nodes"])
     got_t = tgt.cpu().numpy()

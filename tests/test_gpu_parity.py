@@ -256,7 +256,7 @@ def test_attention_small_ragged(td, dtype, d, hq, hkv):
     want = oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
                             inp["k_tree"], inp["v_tree"], mask, n_nodes, hq, hkv, d,
                             wl.attn_scale(cfg))
-    attn_close(got, want, dtype, f"attn {dtype} d{d} {hq}/{hkv}")
+    attn_close(got, want, dtype, f"attn {dtype} d{d} {hq}/{hkv}", n_nodes)
 
 
 def test_attention_empty_context(td):
@@ -270,7 +270,7 @@ def test_attention_empty_context(td):
     want = oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
                             inp["k_tree"], inp["v_tree"], mask, n_nodes, cfg.hq, cfg.hkv,
                             cfg.head_dim, wl.attn_scale(cfg))
-    attn_close(got, want, "bf16", "empty context")
+    attn_close(got, want, "bf16", "empty context", n_nodes)
 
 
 @pytest.mark.parametrize("name", ["tiny_masksens", "qwen3_8b_masksens"])
@@ -287,7 +287,7 @@ def test_attention_mask_sensitive(td, name):
     want = oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
                             inp["k_tree"], inp["v_tree"], mask, tree["n_nodes"], cfg.hq, cfg.hkv,
                             cfg.head_dim, wl.attn_scale(cfg))
-    attn_close(got, want, cfg.attn_dtype, name)
+    attn_close(got, want, cfg.attn_dtype, name, tree["n_nodes"])
     assert int(tree["n_nodes"][0]) == cfg.n_max
 
 
@@ -312,7 +312,8 @@ def test_attention_row_group_paths(td, law):
         want = oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
                                 inp["k_tree"], inp["v_tree"], mask, n_nodes, cfg.hq, cfg.hkv,
                                 cfg.head_dim, wl.attn_scale(cfg), seqs=(b0, b1))
-        attn_close(got[b0:b1], want, "bf16", f"row-group paths {law} seqs {b0}..{b1 - 1}")
+        attn_close(got[b0:b1], want, "bf16", f"row-group paths {law} seqs {b0}..{b1 - 1}",
+                   n_nodes[b0:b1])
 
 
 # ---------------------------------------------------------------------------
@@ -358,7 +359,8 @@ def test_pipeline(td, name, sample):
         want = oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
                                 inp["k_tree"], inp["v_tree"], g["mask"], g["tree"]["n_nodes"],
                                 cfg.hq, cfg.hkv, cfg.head_dim, wl.attn_scale(cfg), seqs=(b, b + 1))
-        attn_close(g["out"][b:b + 1], want, cfg.attn_dtype, f"{name} seq {b}")
+        attn_close(g["out"][b:b + 1], want, cfg.attn_dtype, f"{name} seq {b}",
+                   g["tree"]["n_nodes"][b:b + 1])
     # acceptance on the GPU tree with the synthetic target
     lf = wl.logits_as_f64(x, cfg.logit_dtype)
     tg = targets_by_path(cfg, lf, g["tree"])

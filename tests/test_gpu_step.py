@@ -42,7 +42,7 @@ def modular(td, cfg, d, tg, **kw):
         a, p, bo = td.accept(t["node_token"], t["node_parent"], t["n_nodes"], tg, cfg.block)
         res.update(accept_len=a, accept_path=p, bonus_token=bo)
     torch.cuda.synchronize()
-    return {k: v.cpu() for k, v in res.items()}
+    return only_tree_rows({k: v.cpu() for k, v in res.items()})
 
 
 def make_step(td, cfg, d, **kw):
@@ -60,7 +60,17 @@ def step_outputs(s):
     res = dict(topk_id=s.topk_id, topk_logq=s.topk_logq, lse=s.lse, mask=s.mask, out=s.out,
                accept_len=s.accept_len, accept_path=s.accept_path, bonus_token=s.bonus_token,
                **s.tree)
-    return {k: v.cpu() for k, v in res.items()}
+    return only_tree_rows({k: v.cpu() for k, v in res.items()})
+
+
+def only_tree_rows(res):
+    """The attention output's rows past each tree are not written: zero
+    them in the host copy so two runs compare on the tree rows only."""
+    out = res["out"].clone()
+    for b, n in enumerate(res["n_nodes"].tolist()):
+        out[b, max(n, -1) + 1:] = 0
+    res["out"] = out
+    return res
 
 
 def inputs(cfg):
@@ -171,7 +181,7 @@ def test_step_against_oracle(td):
                             inp["v_tree"], m, tr["n_nodes"], cfg.hq, cfg.hkv, cfg.head_dim,
                             wl.attn_scale(cfg))
     got = wl.bf16_bits_to_f32(out["out"].view(torch.int16).numpy().view(np.uint16)).astype(np.float64)
-    attn_close(got, want, "bf16", "step attention")
+    attn_close(got, want, "bf16", "step attention", tr["n_nodes"])
     a_o, p_o, b_o = oracle.accept(tr["node_token"], tr["node_parent"], tr["n_nodes"], tg_np, cfg.block)
     np.testing.assert_array_equal(out["accept_len"].numpy(), a_o)
     np.testing.assert_array_equal(out["accept_path"].numpy(), p_o)
@@ -264,7 +274,7 @@ def test_handoff_give_up_is_reported(td):
     assert torch.isnan(got["lse"]).all()
     assert int(got["accept_len"][0]) == 0
     assert int(got["bonus_token"][0]) == int(tg[0, 0])
-    assert not got["out"].view(torch.int16).any()    # zero rows: there is no tree
+    # n_nodes -1: no row is a tree row, so the attention wrote none
     s.workspace.zero_()
     s.run()
     assert s.status() == td.TD_OK

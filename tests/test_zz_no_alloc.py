@@ -43,7 +43,12 @@ def _outputs(s):
     res = dict(topk_id=s.topk_id, topk_logq=s.topk_logq, lse=s.lse, mask=s.mask, out=s.out,
                accept_len=s.accept_len, accept_path=s.accept_path, bonus_token=s.bonus_token,
                **s.tree)
-    return {k: v.cpu() for k, v in res.items()}
+    res = {k: v.cpu() for k, v in res.items()}
+    out = res["out"].clone()                       # rows past a tree are not written
+    for b, n in enumerate(res["n_nodes"].tolist()):
+        out[b, n + 1:] = 0
+    res["out"] = out
+    return res
 
 
 @pytest.mark.parametrize("first,second", [("qwen3_8b_stress", "tiny"), ("batched", "two_seq_k4")])

@@ -27,12 +27,13 @@
 //                   sub-chunk over the waves, which merge through LDS.
 //                   Softmax is online in base 2.  One (m, l, O) partial per
 //                   tree row and chunk is stored.
-//  attn_tree_combine one wave per output row (two rows r, r + half for grids
-//                   larger than the chip keeps resident): merges the chunk
-//                   partials (every load in flight at once), adds the
-//                   ancestor-masked tree keys (sparse: one dot product per
-//                   set mask bit) and writes the normalised row; rows beyond
-//                   the tree get zeros.
+//  attn_tree_combine one wave per output row of the trees (the rows of all
+//                   trees are numbered through a prefix sum of the tree
+//                   sizes, and the waves take them in turn):
+//                   merges the chunk partials (every load in flight at
+//                   once), adds the ancestor-masked tree keys (sparse: one
+//                   dot product per set mask bit) and writes the normalised
+//                   row; rows past a tree are not written.
 //
 // MFMA 16x16x32 bf16 operand layout (wave64): A (16 x 32): lane l holds row
 // l % 16, k = 8 (l / 16) .. +7; B (32 x 16): lane l holds column l % 16, the
@@ -466,10 +467,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_f32(
 }
 
 // ---------------------------------------------------------------------------
-// attn_split_bf16: the bf16 split kernel.  Sub-chunks of kSubB keys stream
-// straight from HBM into one of two LDS buffers (global_load_lds, 16 bytes
-// per lane) while the other buffer is computed on, so no register holds
-// staged data.  K and V sit key-major in LDS, each key row padded:
+// attn_split_bf16: the bf16 split kernel.  Sub-chunks of SUB keys stream
+// straight from HBM into a ring of LDS buffers (global_load_lds, 16 bytes per
+// lane) while one buffer is computed on, and no register holds staged data:
+// two buffers of 128 keys (chunks of up to 512 keys: fewer, larger steps), or
+// four of 64 keys (longer chunks: three sub-chunks in flight during the
+// compute, 96 KB per compute unit instead of 64).  K and V sit key-major in
+// LDS, each key row padded:
 //   K rows of D/8 + 1 16-byte pieces: S^T = K Q^T reads 16 consecutive key
 //     rows at one piece (A operand), and those fall in distinct banks;
 //   V rows of D/8 + 2 pieces: O^T += V^T P^T needs V transposed, which
@@ -482,7 +486,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_f32(
 // The pad pieces of a row load a copy of its last piece (same instruction,
 // no extra HBM traffic).
 // ---------------------------------------------------------------------------
-constexpr int kSubB = 128;  // keys per LDS sub-chunk (bf16): 4 tiles, one per wave in split mode
+// buffers of the ring for a sub-chunk of SUB keys (the LDS holds 256 keys)
+template <int SUB> constexpr int ring_of() { return SUB == 64 ? 4 : 2; }
+constexpr int kRingChunk = 1024;  // chunks of at least this many keys take 64-key sub-chunks
 
 template <int D> constexpr int rk_pieces() { return D / 8 + 1; }
 template <int D> constexpr int rv_pieces() { return D / 8 + 2; }
@@ -490,11 +496,25 @@ template <int D> constexpr int rv_pieces() { return D / 8 + 2; }
 // workgroup, so every wave issues the same, compile-time number of direct
 // loads (the compiler can then wait for an earlier load without waiting for
 // them); the slots past the rows take copies of the last row.
-template <int R> constexpr int region_slots() {
-    return (kSubB * R + kAttnThreads - 1) / kAttnThreads * kAttnThreads;
+template <int SUB, int R> constexpr int region_slots() {
+    return (SUB * R + kAttnThreads - 1) / kAttnThreads * kAttnThreads;
 }
-template <int D> constexpr int sub_k_elems() { return region_slots<rk_pieces<D>()>() * 8; }
-template <int D> constexpr int sub_elems() { return (region_slots<rk_pieces<D>()>() + region_slots<rv_pieces<D>()>()) * 8; }
+template <int SUB, int D> constexpr int sub_k_elems() { return region_slots<SUB, rk_pieces<D>()>() * 8; }
+template <int SUB, int D> constexpr int sub_elems() {
+    return (region_slots<SUB, rk_pieces<D>()>() + region_slots<SUB, rv_pieces<D>()>()) * 8;
+}
+// direct-load instructions each wave issues per sub-chunk (K and V)
+template <int SUB, int D> constexpr int sub_loads() {
+    return (region_slots<SUB, rk_pieces<D>()>() + region_slots<SUB, rv_pieces<D>()>()) / kAttnThreads;
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (the N most recent); LDS and export counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef unsigned u2_t __attribute__((ext_vector_type(2)));
@@ -511,11 +531,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 
 // Enqueue the direct loads of one sub-chunk's K or V rows (LDS rows of R
 // pieces; rows at or past `valid` repeat key valid - 1 and are masked later).
-template <int D, int R>
+template <int SUB, int D, int R>
 __device__ __forceinline__ void issue_rows(const uint16_t *gbase, int ks32, int valid, uint16_t *lds,
                                            int wave, int lane) {
     constexpr int P = D / 8;
-    constexpr int kRounds = region_slots<R>() / kAttnThreads;
+    constexpr int kRounds = region_slots<SUB, R>() / kAttnThreads;
     // slot of this lane in round r: (r 4 + wave) 64 + lane; its (row, piece)
     // advance by (256 / R, 256 % R) per round
     int row = (wave * kWave + lane) / R;
@@ -720,19 +740,24 @@ __device__ __forceinline__ void tile_dma(const uint16_t *sK, const uint16_t *sV,
 // OWN2 > OWN: a tree of more than 4 OWN row groups is processed with OWN2
 // per wave instead (one pass over the keys where OWN would need several);
 // smaller trees keep the lighter OWN code.
-template <int D, int OWN, int OWN2 = OWN>
+template <int D, int OWN, int OWN2, int SUB>
 __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_ctx,
     const uint16_t *__restrict__ v_ctx, const int64_t *__restrict__ ctx_offsets,
     const int64_t *__restrict__ ctx_lengths, const int32_t *__restrict__ n_nodes, int batch,
     int nq_max, int hq, int hkv, int group, int n_rg, int chunk, float scale2,
     float *__restrict__ ws, int64_t prow_total, int2 *__restrict__ seqinfo) {
-    // two buffers, each K then V of one sub-chunk; the merge scratch of
-    // split mode reuses them once no load is in flight
-    __shared__ __attribute__((aligned(16))) uint16_t sbuf0[sub_elems<D>()];
-    __shared__ __attribute__((aligned(16))) uint16_t sbuf1[sub_elems<D>()];
-    static_assert(sub_elems<D>() * 2 * 2 >= kAttnWaves * kRowsPerGroup * (D + 2) * 4, "merge scratch");
-    constexpr int kVOff = sub_k_elems<D>();  // the V region follows the K region
+    // kRing buffers, each K then V of one sub-chunk; the merge scratch of
+    // split mode reuses buffer 0 once no load is in flight
+    constexpr int kSubB = SUB;
+    constexpr int kRing = ring_of<SUB>();
+    constexpr int kSubElems = sub_elems<SUB, D>();
+    __shared__ __attribute__((aligned(16))) uint16_t sring[kRing * kSubElems];
+    uint16_t *const sbuf0 = sring;
+    constexpr int kVOff = sub_k_elems<SUB, D>();  // the V region follows the K region
+    constexpr int kLoads = sub_loads<SUB, D>();
+    static_assert(2 * kLoads < 64, "two sub-chunks' loads fit the wait counter");
+    auto ring = [&](int sc) { return sring + (sc & (kRing - 1)) * kSubElems; };
 
     const int64_t c = blockIdx.x / hkv;
     const int g = static_cast<int>(blockIdx.x % hkv);
@@ -764,9 +789,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
     {                                                                                          \
         const int64_t s0_ = (k0 + static_cast<int64_t>(sc) * kSubB) * kstride;               \
         const int v_ = TD_SUB_VALID(sc);                                                       \
-        issue_rows<D, rk_pieces<D>()>(v_ > 0 ? kbase + s0_ : q, static_cast<int>(kstride),     \
+        issue_rows<SUB, D, rk_pieces<D>()>(v_ > 0 ? kbase + s0_ : q, static_cast<int>(kstride), \
                                       v_ > 0 ? v_ : 1, buf, wave, lane);                       \
-        issue_rows<D, rv_pieces<D>()>(v_ > 0 ? vbase + s0_ : q, static_cast<int>(kstride),     \
+        issue_rows<SUB, D, rv_pieces<D>()>(v_ > 0 ? vbase + s0_ : q, static_cast<int>(kstride), \
                                       v_ > 0 ? v_ : 1, buf + kVOff, wave, lane);               \
     }
     const int nn_b = n_nodes[b];  // in flight while the first loads are issued
@@ -781,7 +806,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
         for (int ks = 0; ks < D / 32; ++ks)
             q0[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 32 * ks + 8 * h4));
     }
-    TD_ISSUE(0, sbuf0);
+    // the ring's first kRing - 1 sub-chunks (sub-chunk 0 even without keys)
+    TD_ISSUE(0, ring(0));
+#pragma unroll
+    for (int p = 1; p + 1 < kRing; ++p)
+        if (n_sub > p) TD_ISSUE(p, ring(p));
     const int rows_b = group * min(nn_b + 1, nq_max);
     const int n_rg_b = (rows_b + kRowsPerGroup - 1) / kRowsPerGroup;
     if (n_rg_b <= 0) {  // no row at all (a tree build that gave up): drain the loads above
@@ -796,7 +825,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
         const int n_blk = (n_rg_b + kBlock - 1) / kBlock;
         const int per_blk = n_blk > 0 ? (n_rg_b + n_blk - 1) / n_blk : 1;
         for (int rb0 = 0; rb0 < n_rg_b; rb0 += per_blk) {
-            if (rb0 > 0 && n_sub > 0) TD_ISSUE(0, sbuf0);  // another row block: stream the chunk again
+            if (rb0 > 0 && n_sub > 0) {  // another row block: stream the chunk again
+#pragma unroll
+                for (int p = 0; p + 1 < kRing; ++p)
+                    if (n_sub > p) TD_ISSUE(p, ring(p));
+            }
             const int nrg = min(per_blk, n_rg_b - rb0);
             // wave -> (row groups, key tiles) assignment
             //   nrg >= 4: wave w owns row groups w, w + 4, ... of the block, all keys
@@ -840,6 +873,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
                 for (int ks = 0; ks < D / 32; ++ks)
                     qf[j][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 32 * ks + 8 * h4));
             }
+            // The queries arrive behind the ring's first direct loads; waiting
+            // for all of them here (they land together) settles the queries
+            // once, so no wait inside the loop below is held up by them.
+            __builtin_amdgcn_s_waitcnt(0);
 
 #define TD_COMPUTE(buf, sc)                                                                    \
         {                                                                                          \
@@ -848,20 +885,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
             for (int kt = split_mode ? kt_first : 0; kt < ntiles; kt += split_mode ? kt_step : 1) \
                 tile_dma<D, OWNX>(buf, buf + kVOff, qf, n_own, kt, valid, scale2, lane, st);        \
         }
-            // sub-chunk sc sits in buffer sc % 2; the next one streams meanwhile
-            for (int sc = 0; sc < n_sub; sc += 2) {
-                __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of sub-chunk sc have landed
-                __syncthreads();                // everyone's have; buffer 1 is free
-                if (sc + 1 < n_sub) TD_ISSUE(sc + 1, sbuf1);
-                TD_COMPUTE(sbuf0, sc);
-                if (sc + 1 >= n_sub) break;
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();
-                if (sc + 2 < n_sub) TD_ISSUE(sc + 2, sbuf0);
-                TD_COMPUTE(sbuf1, sc + 1);
+            // sub-chunk sc sits in buffer sc % kRing; the kRing - 2 after it
+            // stay in flight while it is waited for, and sub-chunk
+            // sc + kRing - 1 goes into the buffer sub-chunk sc - 1 used
+            for (int sc = 0; sc < n_sub; ++sc) {
+                const int ahead = min(kRing - 2, n_sub - 1 - sc);  // sub-chunks issued after sc
+                if (ahead >= 2) wait_vm<2 * kLoads>();
+                else if (ahead == 1) wait_vm<kLoads>();
+                else wait_vm<0>();
+                __syncthreads();  // everyone's loads of sc have landed; buffer sc - 1 is free
+                if (sc + kRing - 1 < n_sub) TD_ISSUE(sc + kRing - 1, ring(sc + kRing - 1));
+                uint16_t *const cur = ring(sc);
+                TD_COMPUTE(cur, sc);
             }
 #undef TD_COMPUTE
-            __syncthreads();  // every wave is done with both buffers
+            __builtin_amdgcn_s_waitcnt(0);  // also a sub-chunk 0 without keys
+            __syncthreads();  // every wave is done with every buffer
 
             // row sums over the four lane groups
 #pragma unroll
@@ -893,7 +932,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
                 // split mode: kt_step waves per row group merge through LDS
                 constexpr int kMP = D + 4;
                 static_assert((2 * kAttnWaves * kRowsPerGroup + kAttnWaves * kRowsPerGroup * kMP) * 4 <=
-                                  kSubB * 2 * D * 2,
+                                  kSubElems * 2,
                               "the merge area fits one sub-chunk buffer");
                 float *mw = reinterpret_cast<float *>(sbuf0);      // [4][16]
                 float *lw = mw + kAttnWaves * kRowsPerGroup;       // [4][16]
@@ -962,17 +1001,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
 // dims, levels 3..5 sum the 8 dim slices.
 // ---------------------------------------------------------------------------
 constexpr int kCombineRows = kAttnThreads / kWave;  // waves per workgroup
-// When the combine's grid is larger than the chip keeps resident (about 3
-// waves per SIMD at its register use), each wave takes two output rows, r
-// and r + half, of one (sequence, KV head): rows beyond the tree then cost
-// half the waves.  Host and device agree on the split.
-constexpr int64_t kCombineResident = 256 * 4 * 3;
-inline bool combine_two_rows(int64_t waves) { return waves > 2 * kCombineResident; }
-__host__ __device__ inline int combine_half(int rows_per_bg, int two) {
-    return two ? (rows_per_bg + 1) / 2 : rows_per_bg;
-}
-__host__ __device__ inline int combine_blocks(int rows_per_bg, int two) {
-    return (combine_half(rows_per_bg, two) + kCombineRows - 1) / kCombineRows;
+// The rows of the trees, (sequence b, KV head g, row r = tree row i * G +
+// head) with r < G (n_b + 1), are numbered b-major through the prefix sums
+// of hq (n_b + 1) (each workgroup computes them in LDS from the tree sizes),
+// and wave w takes rows w, w + W, ... of the W waves in the grid.  The grid
+// has one wave per row slot of the capacity, at most about twice the waves
+// the chip holds at the combine's register use (3 per SIMD).
+constexpr int64_t kCombineWaves = 256 * 4 * 3 * 2;
+inline int combine_blocks(int64_t slots) {
+    return static_cast<int>(std::max<int64_t>(
+        1, std::min<int64_t>((slots + kCombineRows - 1) / kCombineRows, kCombineWaves / kCombineRows)));
 }
 
 // N consecutive elements (16-byte aligned) widened to float.
@@ -1024,21 +1062,18 @@ __device__ __forceinline__ void widen(const u32x4 (&w)[raw_words<T, N>()], float
 
 // ACC: the grid carries one more workgroup per sequence, whose wave 0 runs
 // the acceptance walk (the verify step's last kernel).
-template <typename T, int D, bool ACC, bool TWO>
+template <typename T, int D, bool ACC>
 __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     const T *__restrict__ q, const int2 *__restrict__ seqinfo, const T *__restrict__ k_tree,
     const T *__restrict__ v_tree, const uint64_t *__restrict__ mask,
     const int32_t *__restrict__ n_nodes, int batch, int nq_max, int hq, int hkv, int group, int n_rg,
     int chunk, float scale2, const float *__restrict__ ws, int64_t prow_total, T *__restrict__ out,
-    AcceptArgs accept) {
+    int n_blocks, AcceptArgs accept) {
     constexpr int kSlice = D / 8;  // dims per lane group
     const int rows_per_bg = group * nq_max;
-    const int half = combine_half(rows_per_bg, TWO);
-    const int blocks_per_bg = combine_blocks(rows_per_bg, TWO);
     if constexpr (ACC) {
-        const int64_t first_acc = static_cast<int64_t>(batch) * hkv * blocks_per_bg;
-        if (blockIdx.x >= first_acc) {
-            const int bs = static_cast<int>(blockIdx.x - first_acc);
+        if (static_cast<int>(blockIdx.x) >= n_blocks) {
+            const int bs = static_cast<int>(blockIdx.x) - n_blocks;
             __shared__ int s_path[TD_MAX_BLOCK + 1];
             __shared__ int s_acc[2];  // accepted length, bonus token
             if (threadIdx.x < kWave)
@@ -1055,31 +1090,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
             return;
         }
     }
-    const int blk = blockIdx.x % blocks_per_bg;
-    const int g = (blockIdx.x / blocks_per_bg) % hkv;
-    const int b = blockIdx.x / (blocks_per_bg * hkv);
     const int lane = threadIdx.x & 63;
-    const int r = blk * kCombineRows + (threadIdx.x >> 6);
-    if (r >= half) return;
     const int slice = lane >> 3;
     const int cg = lane & 7;
-    const int n = min(n_nodes[b], nq_max - 1);
-    auto out_row = [&](int rr) {
-        const int i = rr / group;
-        const int h = g * group + rr % group;
-        return out + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + slice * kSlice;
-    };
-    auto zero_row = [&](int rr) {
-        if (cg == 0) {
-            T *orow = out_row(rr);
-#pragma unroll
-            for (int k = 0; k < kSlice; ++k) orow[k] = from_f32<T>(0.f);
-        }
-    };
-    auto combine_row = [&](int r) __attribute__((always_inline)) {
+    auto combine_row = [&](int b, int g, int r) __attribute__((always_inline)) {
         const int i = r / group;
         const int h = g * group + r % group;
-        T *orow = out_row(r);
+        T *orow = out + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + slice * kSlice;
         // Everything this row needs that does not depend on other loads goes out
         // first: the query slice, the mask row and the root's key and value
         // (the root is on every row's path).
@@ -1230,21 +1247,72 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
             for (int k = 0; k < kSlice; ++k) orow[k] = from_f32<T>(acc[k] * inv);
         }
     };
-    // the wave's second row, r + half, lies beyond a tree that fills at most
-    // half the rows (zeros), so only a larger tree makes the wave merge two
-    // rows.  The zeros go out last: stores count against the same counter
-    // as the loads, and would hold up the first row's waits.
-    const int r2 = r + half;
-    const bool has2 = TWO && r2 < rows_per_bg;
-    if (r / group > n) {  // beyond the tree, and so is r2
-        zero_row(r);
-        if (has2) zero_row(r2);
+    // prefix sums of the rows of the trees, per sequence: pre[b] = rows of
+    // sequences < b (each thread sums a run of sequences, then the runs are
+    // scanned in LDS)
+    __shared__ uint32_t pre[TD_MAX_BATCH + 1];
+    __shared__ uint32_t runs[kAttnThreads];
+    if (batch == 1) {  // one sequence: no sums to share
+        const uint32_t total = static_cast<uint32_t>(hq) * (min(n_nodes[0], nq_max - 1) + 1);
+        const uint32_t rows_g = static_cast<uint32_t>(group) * (min(n_nodes[0], nq_max - 1) + 1);
+        const uint32_t waves = static_cast<uint32_t>(n_blocks) * kCombineRows;
+        for (uint32_t t = blockIdx.x * kCombineRows + (threadIdx.x >> 6); t < total; t += waves) {
+            const uint32_t g = t / rows_g;
+            combine_row(0, static_cast<int>(g), static_cast<int>(t - g * rows_g));
+        }
         return;
     }
-    combine_row(r);
-    if (has2) {
-        if (r2 / group <= n) combine_row(r2);
-        else zero_row(r2);
+    {
+        const int per = (batch + kAttnThreads - 1) / kAttnThreads;
+        const int b0 = threadIdx.x * per;
+        const int b1 = min(batch, b0 + per);
+        uint32_t sum = 0;
+        for (int b = b0; b < b1; ++b) {
+            const int n = min(n_nodes[b], nq_max - 1);
+            pre[b] = sum;
+            sum += n >= 0 ? static_cast<uint32_t>(hq) * (n + 1) : 0u;
+        }
+        runs[threadIdx.x] = sum;
+        __syncthreads();
+        if (threadIdx.x < kWave) {  // exclusive scan of the 256 runs: 4 per lane, then the lanes
+            static_assert(kAttnThreads == 4 * kWave, "four runs per lane");
+            const int l = threadIdx.x;
+            const uint32_t r0 = runs[4 * l], r1 = runs[4 * l + 1], r2 = runs[4 * l + 2],
+                           r3 = runs[4 * l + 3];
+            const uint32_t own = r0 + r1 + r2 + r3;
+            uint32_t inc = own;
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const uint32_t o = __shfl_up(inc, d, kWave);
+                inc += l >= d ? o : 0u;
+            }
+            const uint32_t ex = inc - own;
+            runs[4 * l] = ex;
+            runs[4 * l + 1] = ex + r0;
+            runs[4 * l + 2] = ex + r0 + r1;
+            runs[4 * l + 3] = ex + r0 + r1 + r2;
+            if (l == kWave - 1) pre[batch] = inc;
+        }
+        __syncthreads();
+        const uint32_t add = runs[threadIdx.x];
+        for (int b = b0; b < b1; ++b) pre[b] += add;
+        __syncthreads();
+    }
+    const uint32_t total = pre[batch];
+    const uint32_t waves = static_cast<uint32_t>(n_blocks) * kCombineRows;
+    for (uint32_t t = blockIdx.x * kCombineRows + (threadIdx.x >> 6); t < total; t += waves) {
+        // the sequence of row t: the last b with pre[b] <= t (binary search)
+        int lo = 0, hi = batch - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        const int b = lo;
+        const uint32_t rest = t - pre[b];
+        const uint32_t rows_g = static_cast<uint32_t>(group) * (min(n_nodes[b], nq_max - 1) + 1);
+        const uint32_t g = rest / rows_g;
+        combine_row(b, static_cast<int>(g), static_cast<int>(rest - g * rows_g));
     }
 }
 
@@ -1262,12 +1330,19 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
                        static_cast<const float *>(k_ctx), static_cast<const float *>(v_ctx), off, lens, \
                        n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,    \
                        static_cast<float *>(ws), prow_total, seqinfo)
-#define TD_SPLIT_BF(...)                                                                       \
-    TD_LAUNCH((attn_split_bf16<D, __VA_ARGS__>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)), \
+#define TD_SPLIT_BF2(SUB, OWN, OWN2)                                                           \
+    TD_LAUNCH((attn_split_bf16<D, OWN, OWN2, SUB>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)), \
                        dim3(kAttnThreads), 0, st, static_cast<const uint16_t *>(q),             \
                        static_cast<const uint16_t *>(k_ctx), static_cast<const uint16_t *>(v_ctx), \
                        off, lens, n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk,   \
                        scale2, static_cast<float *>(ws), prow_total, seqinfo)
+    const bool ring4 = pl.chunk >= kRingChunk;
+#define TD_SPLIT_BF_2(OWN, OWN2)                                                               \
+    do {                                                                                       \
+        if (ring4) TD_SPLIT_BF2(64, OWN, OWN2);                                                \
+        else TD_SPLIT_BF2(128, OWN, OWN2);                                                     \
+    } while (0)
+#define TD_SPLIT_BF(OWN) TD_SPLIT_BF_2(OWN, OWN)
     const int own = std::min(pl.own, max_own<T, D>());
     if constexpr (max_own<T, D>() == 5) {
         switch (own) {
@@ -1286,8 +1361,8 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
             // ones 5 per wave when the chip has several work items per
             // compute unit (one pass over the keys up to 20 row groups),
             // else 3 (a latency-bound step: the lighter code)
-            if (pl.own > 3 && pl.items > 2 * kAttnCUs) TD_SPLIT_BF(1, 5);
-            else TD_SPLIT_BF(1, 3);
+            if (pl.own > 3 && pl.items > 2 * kAttnCUs) TD_SPLIT_BF_2(1, 5);
+            else TD_SPLIT_BF_2(1, 3);
             break;
         }
     } else {
@@ -1296,19 +1371,18 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
     }
 #undef TD_SPLIT
 #undef TD_SPLIT_BF
-    const bool two = combine_two_rows(static_cast<int64_t>(batch) * hkv * pl.group * nq_max);
-    const int blocks_per_bg = combine_blocks(pl.group * nq_max, two);
-    const int64_t blocks = static_cast<int64_t>(batch) * hkv * blocks_per_bg;
-#define TD_COMBINE(ACC, TWO, NB, ARGS)                                                           \
-    TD_LAUNCH((attn_tree_combine<T, D, ACC, TWO>), dim3(static_cast<unsigned>(NB)),      \
+#undef TD_SPLIT_BF_2
+#undef TD_SPLIT_BF2
+    const int blocks = combine_blocks(static_cast<int64_t>(batch) * hkv * pl.group * nq_max);
+#define TD_COMBINE(ACC, NB, ARGS)                                                                \
+    TD_LAUNCH((attn_tree_combine<T, D, ACC>), dim3(static_cast<unsigned>(NB)),                    \
                        dim3(kAttnThreads), 0, st, static_cast<const T *>(q), seqinfo,             \
                        static_cast<const T *>(k_tree), static_cast<const T *>(v_tree), mask,      \
                        n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,      \
-                       static_cast<const float *>(ws), prow_total, static_cast<T *>(out), ARGS)
-    if (acc && two) TD_COMBINE(true, true, blocks + batch, *acc);
-    else if (acc) TD_COMBINE(true, false, blocks + batch, *acc);
-    else if (two) TD_COMBINE(false, true, blocks, AcceptArgs{});
-    else TD_COMBINE(false, false, blocks, AcceptArgs{});
+                       static_cast<const float *>(ws), prow_total, static_cast<T *>(out), blocks, \
+                       ARGS)
+    if (acc) TD_COMBINE(true, blocks + batch, *acc);
+    else TD_COMBINE(false, blocks, AcceptArgs{});
 #undef TD_COMBINE
 }
 

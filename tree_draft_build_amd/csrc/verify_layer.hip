@@ -113,15 +113,33 @@ __device__ __forceinline__ void read_a(uint32_t addr, bf16x8 (&af)[RM]) {
     for (int r = 0; r < RM; ++r) af[r] = __builtin_bit_cast(bf16x8, t[r]);
 }
 
-// MODE 0: float32 partial sums of k slice blockIdx.z into
+// MODE 0: float32 partial sums of k slice z = blockIdx.y into
 //         part[(z * M + m) * N + n];
 // MODE 1: per row m, the best (value, column) of this workgroup's columns
-//         into best[m * gridDim.x + blockIdx.x] (value bits, column).
+//         into best[m * col_tiles + column tile] (value bits, column).
 // Requires K_slice a multiple of kKC and 16-byte aligned rows.
+// Workgroup order: the chip hands consecutive workgroups to its 8 XCDs in
+// turn, each XCD with its own L2.  The row tiles of one column tile read the
+// same weight columns, so they are given ids that differ by multiples of 8
+// (one XCD, one L2): ids run over (group of 8 column tiles, row tile, column
+// tile within the group).
+constexpr int kXcds = 8;
+struct TileId {
+    int col, row;
+};
+__device__ __forceinline__ TileId tile_of(int id, int row_tiles, int col_tiles) {
+    const int per_group = kXcds * row_tiles;
+    const int g = id / per_group;
+    const int rest = id - g * per_group;
+    const int first = g * kXcds;
+    const int width = min(kXcds, col_tiles - first);  // the last group may be narrower
+    return {first + rest % width, rest / width};
+}
+
 template <int RM, int MODE>
 __global__ __launch_bounds__(kGT) void gemm_rows(RowsA a, const uint16_t *__restrict__ w, int M,
-                                                 int N, int K, int k_slice,
-                                                 float *__restrict__ part,
+                                                 int N, int K, int k_slice, int row_tiles,
+                                                 int col_tiles, float *__restrict__ part,
                                                  int2 *__restrict__ best) {
     constexpr int BM = 16 * RM;
     constexpr int R = a_rounds<RM>();
@@ -130,8 +148,9 @@ __global__ __launch_bounds__(kGT) void gemm_rows(RowsA a, const uint16_t *__rest
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int m0 = blockIdx.y * BM;
-    const int k0 = blockIdx.z * k_slice;
+    const TileId tl = tile_of(blockIdx.x, row_tiles, col_tiles);
+    const int m0 = tl.row * BM;
+    const int k0 = blockIdx.y * k_slice;
     const int n_chunks = k_slice / kKC;
 
     // direct loads of the A rows: slot s = r 256 + tid holds (row s / kPc,
@@ -150,7 +169,7 @@ __global__ __launch_bounds__(kGT) void gemm_rows(RowsA a, const uint16_t *__rest
     };
 
     // this wave's W columns (clamped; columns past N are dropped later)
-    const int col0 = blockIdx.x * kBN + wave * (kCB * 16) + (lane & 15);
+    const int col0 = tl.col * kBN + wave * (kCB * 16) + (lane & 15);
     const uint16_t *wrow[kCB];
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb)
@@ -160,8 +179,7 @@ __global__ __launch_bounds__(kGT) void gemm_rows(RowsA a, const uint16_t *__rest
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int cb = 0; cb < kCB; ++cb)
-                dst[ks][cb] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4 *>(wrow[cb] + c * kKC + ks * 32));
+                dst[ks][cb] = *reinterpret_cast<const u32x4 *>(wrow[cb] + c * kKC + ks * 32);
     };
 
     f32x4 acc[RM][kCB];
@@ -218,7 +236,7 @@ __global__ __launch_bounds__(kGT) void gemm_rows(RowsA a, const uint16_t *__rest
                 for (int i = 0; i < 4; ++i) {
                     const int m = m0 + 16 * r + 4 * (lane >> 4) + i;
                     if (m < M && n < N)
-                        part[(static_cast<int64_t>(blockIdx.z) * M + m) * N + n] = acc[r][cb][i];
+                        part[(static_cast<int64_t>(blockIdx.y) * M + m) * N + n] = acc[r][cb][i];
                 }
             }
     } else {
@@ -271,8 +289,7 @@ __global__ __launch_bounds__(kGT) void gemm_rows(RowsA a, const uint16_t *__rest
                     col = s_col[q][tid];
                 }
             }
-            best[static_cast<int64_t>(m0 + tid) * gridDim.x + blockIdx.x] =
-                int2{__float_as_int(v), col};
+            best[static_cast<int64_t>(m0 + tid) * col_tiles + tl.col] = int2{__float_as_int(v), col};
         }
     }
 }
@@ -285,7 +302,9 @@ __device__ __forceinline__ int64_t ctx_len_of(const int64_t *off, const int64_t 
     return L < 0 ? 0 : (L > region ? region : L);
 }
 
-// One workgroup per problem row m = b nq + i: the k slices summed in order,
+// Workgroup (m, y): problem row m = b nq + i, pairs 256 y .. 256 y + 255 of
+// it, one per thread (all of a thread's loads in flight at once): the k
+// slices summed in order,
 // rotary embedding of the query and key heads at position L_b + depth(i)
 // (rotate-half pairs (j, j + D/2), frequency base^(-2j/D), angle and its
 // sine and cosine in float64), rounded to bf16; rows past the tree: zeros.
@@ -301,13 +320,23 @@ __global__ __launch_bounds__(256) void qkv_finish(const float *__restrict__ part
     const int m = blockIdx.x;
     const int b = m / nq;
     const int i = m - b * nq;
+    const int e = blockIdx.y * blockDim.x + threadIdx.x;
     const bool in_tree = i <= n_nodes[b];
     const int dep = depth[m] < 0 ? 0 : depth[m];
     const double pos = static_cast<double>(ctx_len_of(off, lens, b) + dep);
     const int half = D / 2;
     const int pairs = (hq + 2 * hkv) * half;
-    const double lb = log2(rope_base);
-    for (int e = threadIdx.x; e < pairs; e += blockDim.x) {
+    // the rotation of pair j is the same for every head of the row
+    __shared__ float s_cos[64], s_sin[64];
+    if (threadIdx.x < half) {
+        const double ang = pos * exp2(-2.0 * threadIdx.x / D * log2(rope_base));
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        s_cos[threadIdx.x] = static_cast<float>(cs);
+        s_sin[threadIdx.x] = static_cast<float>(sn);
+    }
+    __syncthreads();
+    if (e < pairs) {
         const int h = e / half;
         const int j = e - h * half;
         const int n1 = h * D + j;
@@ -319,10 +348,7 @@ __global__ __launch_bounds__(256) void qkv_finish(const float *__restrict__ part
         }
         float y1 = x1, y2 = x2;
         if (h < hq + hkv) {
-            const double ang = pos * exp2(-2.0 * j / D * lb);
-            double s, c;
-            sincos(ang, &s, &c);
-            const float cf = static_cast<float>(c), sf = static_cast<float>(s);
+            const float cf = s_cos[j], sf = s_sin[j];
             y1 = x1 * cf - x2 * sf;
             y2 = x2 * cf + x1 * sf;
         }
@@ -398,15 +424,19 @@ inline int qkv_splits(int M, int N, int K) {
 template <int MODE>
 void launch_gemm(const RowsA &a, const uint16_t *w, int M, int N, int K, int splits, float *part,
                  int2 *best, hipStream_t st) {
-    const dim3 grid(col_tiles(N), row_tiles(M), splits);
+    const int rt = row_tiles(M), ct = col_tiles(N);
+    const dim3 grid(rt * ct, splits);
     const int k_slice = K / splits;
+#define TD_GEMM(RM) \
+    TD_LAUNCH((gemm_rows<RM, MODE>), grid, dim3(kGT), 0, st, a, w, M, N, K, k_slice, rt, ct, part, best)
     switch (rows_rm(M)) {
-    case 1: TD_LAUNCH((gemm_rows<1, MODE>), grid, dim3(kGT), 0, st, a, w, M, N, K, k_slice, part, best); break;
-    case 2: TD_LAUNCH((gemm_rows<2, MODE>), grid, dim3(kGT), 0, st, a, w, M, N, K, k_slice, part, best); break;
-    case 3: TD_LAUNCH((gemm_rows<3, MODE>), grid, dim3(kGT), 0, st, a, w, M, N, K, k_slice, part, best); break;
-    case 4: TD_LAUNCH((gemm_rows<4, MODE>), grid, dim3(kGT), 0, st, a, w, M, N, K, k_slice, part, best); break;
-    default: TD_LAUNCH((gemm_rows<5, MODE>), grid, dim3(kGT), 0, st, a, w, M, N, K, k_slice, part, best); break;
+    case 1: TD_GEMM(1); break;
+    case 2: TD_GEMM(2); break;
+    case 3: TD_GEMM(3); break;
+    case 4: TD_GEMM(4); break;
+    default: TD_GEMM(5); break;
     }
+#undef TD_GEMM
 }
 
 size_t qkv_ws(int M, int N, int K) {
@@ -482,7 +512,8 @@ extern "C" td_status td_tree_qkv(const void *embed, const void *w_qkv, const int
     float *part = static_cast<float *>(workspace);
     const RowsA a{static_cast<const uint16_t *>(embed), H, node_token, vocab};
     launch_gemm<0>(a, static_cast<const uint16_t *>(w_qkv), M, N, H, splits, part, nullptr, s);
-    TD_LAUNCH(qkv_finish, dim3(M), dim3(256), 0, s, part, splits, M, N, node_depth, n_nodes,
+    const int pairs = (hq + 2 * hkv) * head_dim / 2;
+    TD_LAUNCH(qkv_finish, dim3(M, (pairs + 255) / 256), dim3(256), 0, s, part, splits, M, N, node_depth, n_nodes,
               ctx_offsets, ctx_lengths, nq_max, hq, hkv, head_dim, rope_base,
               static_cast<uint16_t *>(q), static_cast<uint16_t *>(k_tree),
               static_cast<uint16_t *>(v_tree));

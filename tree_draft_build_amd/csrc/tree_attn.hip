@@ -650,74 +650,68 @@ __device__ __forceinline__ void read_vt(const uint16_t *sV, int kt, int lane, bf
         fv[dt] = __builtin_bit_cast(bf16x8, u32x4{t[2 * dt].x, t[2 * dt].y, t[2 * dt + 1].x, t[2 * dt + 1].y});
 }
 
-// One 32-key tile for the n_own row groups a wave owns: S^T = K Q^T (K rows
-// read from LDS once for all of them), online softmax in base 2, then
-// O^T += V^T P^T (V^T fragments read once).  valid: keys of the sub-chunk
-// (keys at or past it are masked).
+// Headroom of the lazy running maximum (base 2): a row's reference maximum
+// moves only when one of its scores passes it by more than this, so every
+// probability stays below 2^kLazyMax (exact in float32 and bf16) and the
+// accumulators are rescaled on few tiles.  Any reference value gives the
+// same softmax; the partials carry theirs to the combine.
+constexpr float kLazyMax = 8.f;
+
+// One 32-key tile for the OWN row groups a wave owns (all of them computed:
+// a row group past the tree has zero queries and is never stored): S^T =
+// K Q^T (K rows read from LDS once for all), then, in one straight block,
+// P = exp2(S scale2 - m) and O^T += V^T P^T (V^T fragments read once), so
+// the matrix core works on one row group while the vector unit makes the
+// next one's probabilities.  Keys at or past `valid` are masked.
 template <int D, int OWN>
 __device__ __forceinline__ void tile_dma(const uint16_t *sK, const uint16_t *sV,
-                                         const bf16x8 (&qf)[OWN][D / 32], int n_own, int kt,
-                                         int valid, float scale2, int lane, RowState<D> (&st)[OWN]) {
+                                         const bf16x8 (&qf)[OWN][D / 32], int kt, int valid,
+                                         float scale2, int lane, RowState<D> (&st)[OWN]) {
     const int h4 = lane >> 4;
-    bf16x8 pf[OWN];
-    float alpha[OWN];
+    float sc[OWN][8];
     {
         bf16x8 fk[2][D / 32];
         read_k<D>(sK, kt, lane, fk);
-        const bool ragged = kt * kKeyTile + kKeyTile > valid;
-        auto scores = [&](int j, f32x4 (&a)[2]) {
+#pragma unroll
+        for (int j = 0; j < OWN; ++j)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                a[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < D / 32; ++ks)
-                    a[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk[hf][ks], qf[j][ks], a[hf], 0, 0, 0);
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk[hf][ks], qf[j][ks], a, 0, 0, 0);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) sc[j][4 * hf + t] = a[t];
             }
-        };
-        // With many row groups, row group j + 1's score MFMAs are issued
-        // before row group j's softmax, so the matrix core works while the
-        // vector unit does (with few, the extra live registers cost more
-        // than the overlap gains).
-        constexpr bool kAhead = OWN >= 4;
-        f32x4 cur[2], nxt[2] = {};
-        if (kAhead && n_own > 0) scores(0, cur);
+    }
+    if (kt * kKeyTile + kKeyTile > valid) {
+#pragma unroll
+        for (int j = 0; j < OWN; ++j)
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                sc[j][t] = kt * kKeyTile + slot_key(h4, t) < valid ? sc[j][t] : -INFINITY;
+    }
+    // does any score of this lane pass its row's reference by the headroom?
+    float lmax[OWN];
+    bool over = false;
+#pragma unroll
+    for (int j = 0; j < OWN; ++j) {
+        float x = sc[j][0];
+#pragma unroll
+        for (int t = 1; t < 8; ++t) x = fmaxf(x, sc[j][t]);
+        lmax[j] = x;
+        over = over || x * scale2 > st[j].m + kLazyMax;
+    }
+    if (__builtin_amdgcn_ballot_w64(over)) {  // the first tile, then rarely
 #pragma unroll
         for (int j = 0; j < OWN; ++j) {
-            if (j >= n_own) break;
-            if constexpr (kAhead) {
-                if (j + 1 < OWN && j + 1 < n_own) scores(j + 1 < OWN ? j + 1 : j, nxt);
-            } else {
-                scores(j, cur);
-            }
-            float sc[8];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) sc[4 * hf + t] = cur[hf][t];
-            if constexpr (kAhead) {
-                cur[0] = nxt[0];
-                cur[1] = nxt[1];
-            }
-            if (ragged) {
-#pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    sc[t] = kt * kKeyTile + slot_key(h4, t) < valid ? sc[t] : -INFINITY;
-            }
-            float tmax = sc[0];
-#pragma unroll
-            for (int t = 1; t < 8; ++t) tmax = fmaxf(tmax, sc[t]);
-            tmax = fmaxf(tmax, xchg_f<4>(tmax));
+            float tmax = fmaxf(lmax[j], xchg_f<4>(lmax[j]));
             tmax = fmaxf(tmax, xchg_f<5>(tmax));
             const float m_new = fmaxf(st[j].m, tmax * scale2);
-            alpha[j] = __builtin_amdgcn_exp2f(st[j].m - m_new);
-            float ps = 0.f;
+            const float alpha = __builtin_amdgcn_exp2f(st[j].m - m_new);
+            st[j].l *= alpha;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sc[t], scale2, -m_new));
-                ps += p;
-                pf[j][t] = static_cast<__bf16>(p);  // round to nearest even
-            }
-            st[j].l = st[j].l * alpha[j] + ps;
+            for (int dt = 0; dt < D / 16; ++dt) st[j].o[dt] *= alpha;
             st[j].m = m_new;
         }
     }
@@ -725,15 +719,18 @@ __device__ __forceinline__ void tile_dma(const uint16_t *sK, const uint16_t *sV,
     read_vt<D>(sV, kt, lane, fv);
 #pragma unroll
     for (int j = 0; j < OWN; ++j) {
-        if (j >= n_own) break;
-        // the running max rarely moves after the first tiles: rescale only then
-        if (__ballot(alpha[j] != 1.f)) {
+        bf16x8 pf;
+        float ps = 0.f;
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) st[j].o[dt] *= alpha[j];
+        for (int t = 0; t < 8; ++t) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sc[j][t], scale2, -st[j].m));
+            ps += p;
+            pf[t] = static_cast<__bf16>(p);  // round to nearest even
         }
+        st[j].l += ps;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
-            st[j].o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fv[dt], pf[j], st[j].o[dt], 0, 0, 0);
+            st[j].o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fv[dt], pf, st[j].o[dt], 0, 0, 0);
     }
 }
 
@@ -882,8 +879,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
         {                                                                                          \
             const int valid = TD_SUB_VALID(sc);                                                    \
             const int ntiles = (valid + kKeyTile - 1) / kKeyTile;                                  \
-            for (int kt = split_mode ? kt_first : 0; kt < ntiles; kt += split_mode ? kt_step : 1) \
-                tile_dma<D, OWNX>(buf, buf + kVOff, qf, n_own, kt, valid, scale2, lane, st);        \
+            for (int kt = split_mode ? kt_first : 0; kt < ntiles; kt += split_mode ? kt_step : 1) { \
+                tile_dma<D, OWNX>(buf, buf + kVOff, qf, kt, valid, scale2, lane, st);               \
+            }                                                                                      \
         }
             // sub-chunk sc sits in buffer sc % kRing; the kRing - 2 after it
             // stay in flight while it is waited for, and sub-chunk

@@ -101,6 +101,12 @@ __device__ __forceinline__ uint32_t xchg(uint32_t x) {
         return (__lane_id() >> 5) ? r[0] : r[1];
     }
 }
+// lane ^ 8 (DPP row_ror:8 within the 16-lane row): with levels 4 and 5 it
+// combines the 8 lanes l % 8 + 8 k of an aligned group of 64 only, keeping
+// lanes of different l % 8 apart.
+__device__ __forceinline__ float xor8_f(float x) {
+    return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x128, 0xF, 0xF, false));
+}
 template <int L> __device__ __forceinline__ int xchg_i(int x) {
     return static_cast<int>(xchg<L>(static_cast<uint32_t>(x)));
 }

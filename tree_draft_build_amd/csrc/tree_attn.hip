@@ -992,24 +992,30 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
 }
 
 // ---------------------------------------------------------------------------
-// attn_tree_combine: one wave per output row.  Lane j owns dims
-// 16 (j / 8) .. +15 and chunks c = j % 8 (mod 8): all partial loads of a row
-// are in flight at once, and the chunk groups are summed by the register
-// butterfly levels 0..2 (within 8 lanes).  Tree keys: each lane dots its 16
-// dims, levels 3..5 sum the 8 dim slices.
+// attn_tree_combine: lane j owns dims D/8 (j / 8) .. +D/8-1 of a row.  R = 1
+// (rows with many chunk partials): one row per wave, lane j takes chunks
+// c = j % 8 (mod 8), all partial loads of the row in flight at once, and the
+// chunk groups are summed by the register butterfly levels 0..2 (within 8
+// lanes).  R = 8 (rows with few partials): eight rows per wave, lane group
+// j % 8 takes row j % 8 and all its chunks.  Tree keys: each lane dots its
+// dims, and lane ^ 8, ^ 16, ^ 32 exchanges sum the 8 dim slices of the row.
 // ---------------------------------------------------------------------------
 constexpr int kCombineRows = kAttnThreads / kWave;  // waves per workgroup
 // The rows of the trees, (sequence b, KV head g, row r = tree row i * G +
 // head) with r < G (n_b + 1), are numbered b-major through the prefix sums
 // of hq (n_b + 1) (each workgroup computes them in LDS from the tree sizes),
-// and wave w takes rows w, w + W, ... of the W waves in the grid.  The grid
-// has one wave per row slot of the capacity, at most about twice the waves
-// the chip holds at the combine's register use (3 per SIMD).
+// and wave w takes the R rows R w .., then R (w + W) .., ... of the W waves
+// in the grid.  The grid has one wave per R row slots of the capacity, at
+// most about twice the waves the chip holds at the combine's register use
+// (3 per SIMD).
 constexpr int64_t kCombineWaves = 256 * 4 * 3 * 2;
-inline int combine_blocks(int64_t slots) {
+inline int combine_blocks(int64_t slots, int R) {
+    const int64_t waves = (slots + R - 1) / R;
     return static_cast<int>(std::max<int64_t>(
-        1, std::min<int64_t>((slots + kCombineRows - 1) / kCombineRows, kCombineWaves / kCombineRows)));
+        1, std::min<int64_t>((waves + kCombineRows - 1) / kCombineRows, kCombineWaves / kCombineRows)));
 }
+// Rows per combine wave: eight when the sequences average few chunks.
+inline int combine_rows_per_wave(int64_t n_chunks, int batch) { return n_chunks <= 12LL * batch ? 8 : 1; }
 
 // N consecutive elements (16-byte aligned) widened to float.
 template <typename T, int N>
@@ -1060,7 +1066,7 @@ __device__ __forceinline__ void widen(const u32x4 (&w)[raw_words<T, N>()], float
 
 // ACC: the grid carries one more workgroup per sequence, whose wave 0 runs
 // the acceptance walk (the verify step's last kernel).
-template <typename T, int D, bool ACC>
+template <typename T, int D, bool ACC, int R>
 __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     const T *__restrict__ q, const int2 *__restrict__ seqinfo, const T *__restrict__ k_tree,
     const T *__restrict__ v_tree, const uint64_t *__restrict__ mask,
@@ -1088,10 +1094,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
             return;
         }
     }
+    static_assert(R == 1 || R == 8, "one or eight rows per wave");
+    constexpr int kCG = 8 / R;  // chunk groups per row
     const int lane = threadIdx.x & 63;
     const int slice = lane >> 3;
-    const int cg = lane & 7;
-    auto combine_row = [&](int b, int g, int r) __attribute__((always_inline)) {
+    const int cg = R == 1 ? (lane & 7) : 0;
+    // row (b, g, r) of this lane (of its lane group when R = 8); `store`:
+    // a real row (a lane group past the last row repeats one, unstored)
+    auto combine_row = [&](int b, int g, int r, bool store) __attribute__((always_inline)) {
         const int i = r / group;
         const int h = g * group + r % group;
         T *orow = out + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + slice * kSlice;
@@ -1128,12 +1138,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
         float acc[kSlice];
 #pragma unroll
         for (int k = 0; k < kSlice; ++k) acc[k] = 0.f;
-        for (int c0 = 0; c0 < nch; c0 += 8 * kCB) {
+        for (int c0 = 0; c0 < nch; c0 += kCG * kCB) {
             float mv[kCB], lv[kCB];
             f32x4 ov[kCB][kSlice / 4];
 #pragma unroll
             for (int u = 0; u < kCB; ++u) {
-                const int cc = min(c0 + cg + 8 * u, nch - 1);  // in range; repeats are dropped below
+                const int cc = min(c0 + cg + kCG * u, nch - 1);  // in range; repeats are dropped below
                 const int64_t pr = prow_index(cb + cc, g, rg, rr, hkv, n_rg);
                 mv[u] = wm[pr];
                 lv[u] = wl[pr];
@@ -1147,7 +1157,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
             // get weight 0 (every partial read here was written, so finite).
             float mb = M;
 #pragma unroll
-            for (int u = 0; u < kCB; ++u) mb = fmaxf(mb, c0 + cg + 8 * u < nch ? mv[u] : -INFINITY);
+            for (int u = 0; u < kCB; ++u) mb = fmaxf(mb, c0 + cg + kCG * u < nch ? mv[u] : -INFINITY);
             const float base = mb == -INFINITY ? 0.f : mb;
             const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - base);
             Lsum *= fo;
@@ -1155,7 +1165,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
             for (int k = 0; k < kSlice; ++k) acc[k] *= fo;
 #pragma unroll
             for (int u = 0; u < kCB; ++u) {
-                const bool use = c0 + cg + 8 * u < nch && mv[u] != -INFINITY;
+                const bool use = c0 + cg + kCG * u < nch && mv[u] != -INFINITY;
                 const float f = use ? __builtin_amdgcn_exp2f(mv[u] - base) : 0.f;
                 Lsum += f * lv[u];
 #pragma unroll
@@ -1166,7 +1176,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
             M = mb;
         }
         // merge the 8 chunk groups (levels 0..2 of the lane exchanges)
-        {
+        if constexpr (R == 1) {
             float Mg = M;
             Mg = fmaxf(Mg, xchg_f<0>(Mg));
             Mg = fmaxf(Mg, xchg_f<1>(Mg));
@@ -1192,7 +1202,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
             float dot = 0.f;
 #pragma unroll
             for (int k = 0; k < kSlice; ++k) dot += qv[k] * kk[k];
-            dot += xchg_f<3>(dot);
+            dot += xor8_f(dot);
             dot += xchg_f<4>(dot);
             dot += xchg_f<5>(dot);
             const float sc = dot * scale2;
@@ -1239,7 +1249,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
                 }
             }
         }
-        if (cg == 0) {
+        if (cg == 0 && store) {
             const float inv = 1.f / Lsum;
 #pragma unroll
             for (int k = 0; k < kSlice; ++k) orow[k] = from_f32<T>(acc[k] * inv);
@@ -1250,13 +1260,17 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     // scanned in LDS)
     __shared__ uint32_t pre[TD_MAX_BATCH + 1];
     __shared__ uint32_t runs[kAttnThreads];
+    const uint32_t sub = R == 1 ? 0u : static_cast<uint32_t>(lane & 7);
+    const uint32_t step = static_cast<uint32_t>(n_blocks) * kCombineRows * R;
+    const uint32_t first = (blockIdx.x * kCombineRows + (threadIdx.x >> 6)) * R;
     if (batch == 1) {  // one sequence: no sums to share
+        if (n_nodes[0] < 0) return;  // a tree build that gave up: no rows
         const uint32_t total = static_cast<uint32_t>(hq) * (min(n_nodes[0], nq_max - 1) + 1);
         const uint32_t rows_g = static_cast<uint32_t>(group) * (min(n_nodes[0], nq_max - 1) + 1);
-        const uint32_t waves = static_cast<uint32_t>(n_blocks) * kCombineRows;
-        for (uint32_t t = blockIdx.x * kCombineRows + (threadIdx.x >> 6); t < total; t += waves) {
+        for (uint32_t t0 = first; t0 < total; t0 += step) {
+            const uint32_t t = min(t0 + sub, total - 1);
             const uint32_t g = t / rows_g;
-            combine_row(0, static_cast<int>(g), static_cast<int>(t - g * rows_g));
+            combine_row(0, static_cast<int>(g), static_cast<int>(t - g * rows_g), t0 + sub < total);
         }
         return;
     }
@@ -1297,8 +1311,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
         __syncthreads();
     }
     const uint32_t total = pre[batch];
-    const uint32_t waves = static_cast<uint32_t>(n_blocks) * kCombineRows;
-    for (uint32_t t = blockIdx.x * kCombineRows + (threadIdx.x >> 6); t < total; t += waves) {
+    for (uint32_t t0 = first; t0 < total; t0 += step) {
+        const uint32_t t = min(t0 + sub, total - 1);
         // the sequence of row t: the last b with pre[b] <= t (binary search)
         int lo = 0, hi = batch - 1;
         while (lo < hi) {
@@ -1310,7 +1324,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
         const uint32_t rest = t - pre[b];
         const uint32_t rows_g = static_cast<uint32_t>(group) * (min(n_nodes[b], nq_max - 1) + 1);
         const uint32_t g = rest / rows_g;
-        combine_row(b, static_cast<int>(g), static_cast<int>(rest - g * rows_g));
+        combine_row(b, static_cast<int>(g), static_cast<int>(rest - g * rows_g), t0 + sub < total);
     }
 }
 
@@ -1371,17 +1385,25 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
 #undef TD_SPLIT_BF
 #undef TD_SPLIT_BF_2
 #undef TD_SPLIT_BF2
-    const int blocks = combine_blocks(static_cast<int64_t>(batch) * hkv * pl.group * nq_max);
+    const int rpw = combine_rows_per_wave(pl.n_chunks, batch);
+    const int blocks = combine_blocks(static_cast<int64_t>(batch) * hkv * pl.group * nq_max, rpw);
 #define TD_COMBINE(ACC, NB, ARGS)                                                                \
-    TD_LAUNCH((attn_tree_combine<T, D, ACC>), dim3(static_cast<unsigned>(NB)),                    \
+    if (rpw == 8) TD_COMBINE_R(ACC, 8, NB, ARGS);                                                \
+    else TD_COMBINE_R(ACC, 1, NB, ARGS)
+#define TD_COMBINE_R(ACC, RR, NB, ARGS)                                                          \
+    TD_LAUNCH((attn_tree_combine<T, D, ACC, RR>), dim3(static_cast<unsigned>(NB)),               \
                        dim3(kAttnThreads), 0, st, static_cast<const T *>(q), seqinfo,             \
                        static_cast<const T *>(k_tree), static_cast<const T *>(v_tree), mask,      \
                        n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,      \
                        static_cast<const float *>(ws), prow_total, static_cast<T *>(out), blocks, \
                        ARGS)
-    if (acc) TD_COMBINE(true, blocks + batch, *acc);
-    else TD_COMBINE(false, blocks, AcceptArgs{});
+    if (acc) {
+        TD_COMBINE(true, blocks + batch, *acc);
+    } else {
+        TD_COMBINE(false, blocks, AcceptArgs{});
+    }
 #undef TD_COMBINE
+#undef TD_COMBINE_R
 }
 
 inline int sub_chunk(td_dtype dt) { return dt == TD_BF16 ? Sub<uint16_t>::CH : Sub<float>::CH; }

@@ -59,6 +59,18 @@ __device__ __forceinline__ void dma16(const void *g, void *lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 16, 0, 0);
 }
 
+// A compiler barrier: no memory operation is moved across it (the hardware
+// is not affected).
+__device__ __forceinline__ void pin_order() { asm volatile("" ::: "memory"); }
+
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (the N most recent); LDS and export counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void *)p));
 }
@@ -137,7 +149,7 @@ __device__ __forceinline__ TileId tile_of(int id, int row_tiles, int col_tiles) 
 }
 
 template <int RM, int MODE>
-__global__ __launch_bounds__(kGT) void gemm_rows(RowsA a, const uint16_t *__restrict__ w, int M,
+__global__ __launch_bounds__(kGT) void gemm_rows(RowsA a, const uint16_t *w, int M,
                                                  int N, int K, int k_slice, int row_tiles,
                                                  int col_tiles, float *__restrict__ part,
                                                  int2 *__restrict__ best) {
@@ -203,27 +215,72 @@ __global__ __launch_bounds__(kGT) void gemm_rows(RowsA a, const uint16_t *__rest
         }
     };
 
-    // chunk c sits in buffer c % 2; the next chunk's loads fly meanwhile
-    u32x4 w0[4][kCB], w1[4][kCB];
+    // Chunk c: A rows in LDS buffer c % 2 (one chunk ahead: the rows are
+    // few and stay in L2), this wave's W columns in register buffer c % 3
+    // (two chunks ahead: W streams from HBM, and its loads in flight set the
+    // rate).  Issue order: A(0) W(0) A(1) W(1) W(2), then after chunk c
+    // A(c + 2) W(c + 3); so when chunk c is waited for, the loads issued
+    // after its last one are exactly W(c + 1), A(c + 1) and W(c + 2): R
+    // direct A loads and 2 kWL W loads.  Every load is issued (chunks past
+    // the last repeat the last one), so that count never changes and the
+    // compiler's own waits for the W registers stay exact too.
+    u32x4 w0[4][kCB], w1[4][kCB], w2[4][kCB];
+    constexpr int kWL = 4 * kCB;  // W loads per chunk and lane
+    const int last = n_chunks - 1;
     issue(0, sa0);
+    pin_order();
     load_w(0, w0);
-    for (int c = 0; c < n_chunks; c += 2) {
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c have landed
-        __syncthreads();                // everyone's have; the other buffer is free
-        if (c + 1 < n_chunks) {
-            issue(c + 1, sa1);
-            load_w(c + 1, w1);
-        }
-        compute(sa0, w0);
+    pin_order();
+    issue(min(1, last), sa1);
+    pin_order();
+    load_w(min(1, last), w1);
+    load_w(min(2, last), w2);
+    // The barriers below are plain s_barrier: a __syncthreads() fence would
+    // wait for every load in flight (the direct LDS loads share the vector
+    // memory counter), W prefetches included.  The waits they need are
+    // explicit: each wave waits for its own direct loads of a chunk before
+    // the barrier that publishes it, and the A fragment reads wait for their
+    // data before the barrier that frees their buffer.
+    // The wait counts assume the program order of the loads: compiler
+    // barriers (pin_order) keep every load between the same waits and
+    // barriers, and the A loads of a chunk before the W loads that follow
+    // (w is not declared __restrict__: loads through a restricted read-only
+    // pointer count as invariant, and a compiler barrier would not hold them).
+    auto arrive = [&](int) __attribute__((always_inline)) {
+        pin_order();
+        wait_vm<kWL + R + kWL>();
+        __builtin_amdgcn_s_barrier();  // everyone's A rows of chunk c have landed
+        pin_order();
+    };
+    auto refill = [&](int c, uint16_t *buf, u32x4 (&wb)[4][kCB]) __attribute__((always_inline)) {
+        pin_order();
+        __builtin_amdgcn_s_barrier();  // everyone is done with chunk c's A buffer
+        pin_order();
+        issue(min(c + 2, last), buf);
+        pin_order();
+        load_w(min(c + 3, last), wb);
+        pin_order();
+    };
+    auto step = [&](int c, u32x4 (&wb)[4][kCB]) __attribute__((always_inline)) {
+        uint16_t *const buf = (c & 1) ? sa1 : sa0;
+        arrive(c);
+        compute(buf, wb);
+        refill(c, buf, wb);
+    };
+    // The first three chunks run before the loop, so that the loop is
+    // entered in the state it repeats (the compiler's own waits for the W
+    // registers are then exact instead of a full wait per trip).
+    step(0, w0);
+    if (n_chunks > 1) step(1, w1);
+    if (n_chunks > 2) step(2, w2);
+    for (int c = 3; c < n_chunks; c += 3) {
+        step(c, w0);
         if (c + 1 >= n_chunks) break;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (c + 2 < n_chunks) {
-            issue(c + 2, sa0);
-            load_w(c + 2, w0);
-        }
-        compute(sa1, w1);
+        step(c + 1, w1);
+        if (c + 2 >= n_chunks) break;
+        step(c + 2, w2);
     }
+    __builtin_amdgcn_s_waitcnt(0);
 
     // C fragment: lane l holds column l % 16, rows 4 (l / 16) + i
     if constexpr (MODE == 0) {

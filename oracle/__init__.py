@@ -31,7 +31,8 @@ def _load(path=None):
         if path is None and not os.path.exists(LIB_PATH):
             from . import build as _b
             _b.build()
-        lib = ctypes.CDLL(path or LIB_PATH)
+        # TD_ORACLE_LIB: another build of the same source (the sanitizer check)
+        lib = ctypes.CDLL(path or os.environ.get("TD_ORACLE_LIB") or LIB_PATH)
         P = c_void_p
         lib.or_draft_topk.argtypes = [P, c_int, c_int, c_int, c_int, c_int64, c_int, P, P, P]
         lib.or_build_tree.argtypes = [P, P, c_int, c_int, c_int, c_int, c_int, c_double, c_double,

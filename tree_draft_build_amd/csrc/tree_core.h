@@ -43,6 +43,14 @@ __device__ __forceinline__ uint32_t pack_key(int depth, int token, int parent) {
            static_cast<uint32_t>(parent);
 }
 
+// lane `src` (wave-uniform) of a double
+__device__ __forceinline__ double read_lane_d(double x, int src) {
+    const uint64_t u = __double_as_longlong(x);
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), src);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), src);
+    return __longlong_as_double(static_cast<long long>(static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32)));
+}
+
 // a precedes b
 __device__ __forceinline__ bool precedes(double la, uint32_t ka, double lb, uint32_t kb) {
     return la > lb || (la == lb && ka < kb);
@@ -80,9 +88,10 @@ struct TreeLds {
     double lr[TD_MAX_NODES + 1];
 };
 
-// Frontier slots per lane for a budget of n_max nodes (1 + 2 n_max entries).
+// Frontier slots per lane for a budget of n_max nodes: 1 + 2 (n_max - 1)
+// entries (each insertion but the last pushes at most two).
 __host__ __device__ inline int tree_slots(int n_max) {
-    const int need = 1 + 2 * n_max;
+    const int need = 1 + 2 * (n_max > 1 ? n_max - 1 : 0);
     return need <= 64 ? 1 : need <= 128 ? 2 : need <= 256 ? 4 : 8;
 }
 
@@ -99,13 +108,21 @@ __device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &
                                 int root_tok) {
 #pragma clang fp contract(off)
     const int K = P.K;
-    // frontier slots of this lane
-    double f_lr[SLOTS];
+    const bool stop = P.use_stop != 0;
+    // Frontier slots of this lane: log rho, order key, rank among the
+    // siblings, the parent's log rho (the next sibling's score is the
+    // parent's plus its table entry) and, for the stop rule, rho itself,
+    // computed when the entry is pushed so that its latency overlaps the
+    // selections that follow.  Nothing the selection loop reads is in LDS
+    // except the read-only top-K tables.
+    double f_lr[SLOTS], f_plr[SLOTS], f_rho[SLOTS];
     uint32_t f_key[SLOTS];
     int f_rank[SLOTS];
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
         f_lr[s] = -INFINITY;
+        f_plr[s] = 0.0;
+        f_rho[s] = 0.0;
         f_key[s] = kEmptyKey;
         f_rank[s] = 0;
     }
@@ -113,7 +130,7 @@ __device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &
     if (lane == 0) {
         f_lr[0] = t.lq[0];
         f_key[0] = pack_key(1, t.ids[0], 0);
-        f_rank[0] = 0;
+        f_rho[0] = stop ? exp(t.lq[0]) : 0.0;
     }
     int count = 1;  // entries ever pushed (uniform across lanes)
 
@@ -127,9 +144,13 @@ __device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &
     }
 
     while (n < P.n_max) {
+        // counters are wave-uniform: say so, keeping the loop's control scalar
+        n = __builtin_amdgcn_readfirstlane(n);
+        count = __builtin_amdgcn_readfirstlane(count);
         // lane-local best slot
         double bl = f_lr[0];
         uint32_t bk = f_key[0];
+        int bs = 0;
         double wl;
         uint32_t wk;
         if (n == 0) {
@@ -142,6 +163,7 @@ __device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &
                 if (precedes(f_lr[s], f_key[s], bl, bk)) {
                     bl = f_lr[s];
                     bk = f_key[s];
+                    bs = s;
                 }
             // wave-wide best (register butterfly)
             wl = bl;
@@ -162,73 +184,92 @@ __device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &
             TD_TREE_LEVEL(5)
 #undef TD_TREE_LEVEL
         }
+        // every lane holds the winner: make that explicit (scalar registers),
+        // so that the loop's exits and counters are uniform
+        wl = read_lane_d(wl, 0);
+        wk = __builtin_amdgcn_readfirstlane(wk);
         if (wk == kEmptyKey) break;  // no valid candidate left
         // selective verification: every remaining candidate scores at most
         // the best one, so the first one below the threshold ends the tree
         if (P.min_logrho < 0.0 && wl < P.min_logrho) break;
 
-        const double ahat_next = ahat + exp(wl);
-        const double s_next = ahat_next * P.l_ar / cost_model(n + 1, P.ca, P.cb, P.cc, P.knee);
-        if (P.use_stop && !(s_next > s_now)) break;
-
-        // the owner lane removes the entry and publishes its rank
+        // the owner lane (its best slot bs holds the entry) hands over the
+        // entry's rank, parent score and rho
         const bool owner = n == 0 ? lane == 0 : (bk == wk) && (bl == wl);
-        int my_rank = 0;
+        int my_rank = f_rank[0];
+        double my_plr = f_plr[0], my_rho = f_rho[0];
 #pragma unroll
-        for (int s = 0; s < SLOTS; ++s)
-            if (owner && f_key[s] == wk) {
+        for (int s = 1; s < SLOTS; ++s)
+            if (bs == s) {
                 my_rank = f_rank[s];
-                f_lr[s] = -INFINITY;
-                f_key[s] = kEmptyKey;
+                my_plr = f_plr[s];
+                my_rho = f_rho[s];
             }
         const unsigned long long ob = __ballot(owner);
         const int owner_lane = __ffsll(static_cast<long long>(ob)) - 1;
         const int rank = __builtin_amdgcn_readlane(my_rank, owner_lane);
+        const double plr = read_lane_d(my_plr, owner_lane);
+
+        if (stop) {
+            const double ahat_next = ahat + read_lane_d(my_rho, owner_lane);
+            const double s_next = ahat_next * P.l_ar / cost_model(n + 1, P.ca, P.cb, P.cc, P.knee);
+            if (!(s_next > s_now)) break;
+            ahat = ahat_next;
+            s_now = s_next;
+        }
+        // remove the entry
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s)
+            if (owner && bs == s) {
+                f_lr[s] = -INFINITY;
+                f_key[s] = kEmptyKey;
+            }
 
         const int depth = static_cast<int>(wk >> 26);
         const int token = static_cast<int>((wk >> 8) & 0x3ffffu);
         const int parent = static_cast<int>(wk & 0xffu);
         ++n;
-        if (lane == 0) {
+        if (lane == 0) {  // read back only after the loop
             t.tok[n] = token;
             t.par[n] = parent;
             t.dep[n] = depth;
             t.lr[n] = wl;
         }
-        wave_lds_sync();  // t.lr[parent] is read by every lane below
-        ahat = ahat_next;
-        s_now = s_next;
 
-        // lazy pushes: next sibling, then first child
-        if (rank + 1 < P.branch) {
-            const int e = count++;
-            const int j = (depth - 1) * K + rank + 1;
-            const double plr = parent == 0 ? 0.0 : t.lr[parent];
-            if (lane == (e & (kWave - 1))) {
+        // Lazy pushes: next sibling, then first child (none after the last
+        // node).  Entry e goes to lane e % 64, slot e / 64: the slot is
+        // chosen by a uniform branch, the lane by a select.
+        if (n == P.n_max) break;
+        auto put = [&](int e, double lr, uint32_t key, int rnk, double plr_) __attribute__((always_inline)) {
+            const int se = e >> 6;
+            const bool mine = lane == (e & (kWave - 1));
+            const double rho = stop ? exp(lr) : 0.0;
 #pragma unroll
-                for (int s = 0; s < SLOTS; ++s)
-                    if (s == (e >> 6)) {
-                        f_lr[s] = plr + t.lq[j];
-                        f_key[s] = pack_key(depth, t.ids[j], parent);
-                        f_rank[s] = rank + 1;
-                    }
-            }
+            for (int s = 0; s < SLOTS; ++s)
+                if (s == se) {
+                    f_lr[s] = mine ? lr : f_lr[s];
+                    f_key[s] = mine ? key : f_key[s];
+                    f_rank[s] = mine ? rnk : f_rank[s];
+                    f_plr[s] = mine ? plr_ : f_plr[s];
+                    f_rho[s] = mine ? rho : f_rho[s];
+                }
+        };
+        if (rank + 1 < P.branch) {
+            const int j = (depth - 1) * K + rank + 1;
+            put(count++, plr + t.lq[j], pack_key(depth, t.ids[j], parent), rank + 1, plr);
         }
         if (depth < P.block) {
-            const int e = count++;
             const int j = depth * K;
-            if (lane == (e & (kWave - 1))) {
-#pragma unroll
-                for (int s = 0; s < SLOTS; ++s)
-                    if (s == (e >> 6)) {
-                        f_lr[s] = wl + t.lq[j];
-                        f_key[s] = pack_key(depth + 1, t.ids[j], n);
-                        f_rank[s] = 0;
-                    }
-            }
+            put(count++, wl + t.lq[j], pack_key(depth + 1, t.ids[j], n), 0, wl);
         }
     }
     wave_lds_sync();
+    if (!stop) {  // A_hat(n) and S(n) of the tree built (sum in any order: float64)
+        double part = 0.0;
+        for (int i = 1 + lane; i <= n; i += kWave) part += exp(t.lr[i]);
+        ahat = P.ahat0 + wave_sum(part);
+        s_now = ahat * P.l_ar / cost_model(n, P.ca, P.cb, P.cc, P.knee);
+    }
     if constexpr (PREFILLED) __syncthreads();  // the prefill stores have landed
 
     const int W = P.n_max + 1;

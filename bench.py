@@ -56,6 +56,8 @@ def parse():
                     help="skip the multi-step decode loop with KV commit")
     ap.add_argument("--no-layer", dest="layer", action="store_false",
                     help="skip the one-layer verification pass and the tachometer")
+    ap.add_argument("--no-tachometer", dest="tachometer", action="store_false",
+                    help="with the one-layer pass, skip the tachometer's sweep over tree sizes")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="threads of the all-core oracle baseline (0: every core available)")
     return ap.parse_args()
@@ -496,10 +498,30 @@ def layer_rows(args):
 
     full_step()
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        full_step()
-    step_us = loop_us(g.replay)
+    if args.no_graph:
+        step_us = loop_us(full_step)
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            full_step()
+        step_us = loop_us(g.replay)
+
+    layer = {
+        "verify_layer": {
+            "workload": "qwen3_8b_tree one-layer verification (hidden 4096, vocab 151936)",
+            "rows": rows,
+            "step_value": round(1e6 / step_us, 1), "step_unit": "verify steps/s",
+            "step_us": round(step_us, 2),
+            "step": "kernel 1 (top-K, tree, mask), Q/K/V + RoPE (2 kernels), attention "
+                    "(2 kernels), LM-head argmax (2 kernels), acceptance; "
+                    + ("eager launches" if args.no_graph else "one graph"),
+            "kernel_roofline": {
+                "tree_qkv": roof("tree_qkv (projection + RoPE)", qkv_us, qkv_bytes,
+                                 2 * rows * sh.hidden * sh.qkv_out),
+                "lm_head_argmax": roof("lm_head_argmax", lm_us, lm_bytes,
+                                       2 * rows * sh.hidden * sh.vocab)}}}
+    if not args.tachometer:
+        return layer
 
     # ---- tachometer ----
     points = tach.measure(ids, lq, reps=10, warmup=2, **pass_kw)
@@ -514,18 +536,7 @@ def layer_rows(args):
         picked[name] = {"n_nodes": int(t_["n_nodes"][0]), "ahat": round(float(t_["ahat"][0]), 4),
                         "speedup_estimate": round(float(t_["speedup"][0]), 4)}
     return {
-        "verify_layer": {
-            "workload": "qwen3_8b_tree one-layer verification (hidden 4096, vocab 151936)",
-            "rows": rows,
-            "step_value": round(1e6 / step_us, 1), "step_unit": "verify steps/s",
-            "step_us": round(step_us, 2),
-            "step": "kernel 1 (top-K, tree, mask), Q/K/V + RoPE (2 kernels), attention "
-                    "(2 kernels), LM-head argmax (2 kernels), acceptance; one graph",
-            "kernel_roofline": {
-                "tree_qkv": roof("tree_qkv (projection + RoPE)", qkv_us, qkv_bytes,
-                                 2 * rows * sh.hidden * sh.qkv_out),
-                "lm_head_argmax": roof("lm_head_argmax", lm_us, lm_bytes,
-                                       2 * rows * sh.hidden * sh.vocab)}},
+        **layer,
         "tachometer": {
             "what": "the one-layer verification pass (Q/K/V, tree attention, LM-head argmax) "
                     "timed at tree sizes N, fitted to C(N) = a + b N + c max(0, N - knee)",

@@ -95,6 +95,7 @@ def test_topk_ragged_and_ties(td, V, K, dtype):
     x = np.round(rng.standard_normal((3, 5, V)) * 2, 1).astype(np.float32)  # many ties
     x[0, 0] = 1.5                                                           # all tied
     x[1, 1, -3:] = 40.0                                                     # tied top at the tail
+    x[2, 3] = np.linspace(-3.0, 9.0, V)                                     # ascending: every element a new max
     if dtype == "bf16":
         x = wl.f32_to_bf16_bits(x)
     ids, lq, lse = td.draft_topk(dev_logits(x), K)

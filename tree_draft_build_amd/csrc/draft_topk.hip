@@ -3,28 +3,32 @@
 // drafter's per-position marginals q_k, so every q_k of a candidate is needed).
 //
 // One kernel, grid (splits, rows).  Each workgroup streams one contiguous
-// slice of one vocabulary row with 16-byte loads (up to 4 per thread in
-// flight), keeping per lane a running max m and a float64 sum s of
-// exp(x - m), and a sorted register list of candidate keys.
+// slice of one vocabulary row with 16-byte loads (two batches of four per
+// thread in flight), keeping per lane a reference max m and a float64 sum s
+// of exp(x - m).  On whole batches the reference moves only when the batch
+// maximum passes it by more than 2^8 (one ballot per batch), and the
+// batch's 32 terms are summed pairwise in fp32 before they reach s.
 //
 // Candidates are 64-bit order keys, ord(logit) << 32 | ~id, so one unsigned
-// compare orders them by larger logit, then smaller id, and every
-// compare-exchange is branch-free.
+// compare orders them by larger logit, then smaller id.
 //
 // Exact pre-filter: after its first batch of loads each wave cuts its lanes
 // into KM >= K groups, takes every group's maximum and keeps tau = the
 // smallest of them.  Those KM maxima are distinct elements >= tau, so the
 // slice's K-th largest element is >= tau and no element below tau can be in
-// the top K: only elements >= tau enter a lane's list.
+// the top K.  The bound is raised the same way from the lanes' running
+// maxima as the stream goes on, and shared among the waves through LDS.
 //
-// Selection: the waves' bounds are pooled (their maximum still bounds the
-// workgroup's K-th largest from below), each wave compacts its lanes' list
-// entries above that bound into its LDS region, and every thread holding a
-// key ranks it by counting the keys that beat it (keys are distinct), so
-// the K best land in their slots in one parallel pass.  Should a wave hold
-// more than kWaveCap candidates (rows of many equal logits), a K-round
-// tournament over its lane lists (wave-wide key max per round) gives its K
-// best instead.  The
+// Candidates: the elements >= tau are appended to the wave's LDS region,
+// one ballot per element position and one store per candidate (a batch
+// whose lanes all stay below tau costs one ballot).  Selection: the waves'
+// bounds are pooled (their maximum still bounds the workgroup's K-th
+// largest from below), each wave packs its region's keys at or above that
+// bound, and every thread holding a key ranks it by counting the keys that
+// beat it (keys are distinct), so the K best land in their slots in one
+// parallel pass.  Should a region overflow (rows of many equal or ascending
+// logits), the workgroup selects again from its slice with sorted per-lane
+// lists of the best KM keys above the pooled bound.  The
 // workgroup publishes its (m, s, K keys) as epoch-tagged words; the row's
 // highest slice waits for every tag, bounds the row's K-th key from below by
 // the K-th best partial head, ranks the partial keys above that bound the
@@ -46,13 +50,14 @@ typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 constexpr int kTopkThreads = 256;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kBatch = 4;  // 16-byte vectors per thread in flight
-constexpr int kCandCap = 512;  // candidates ranked in LDS by counting
+constexpr int kCandCap = 1024;  // candidates held in LDS (kWaveCap per wave)
 // Words of a row's partials held by the merger: splits * (2K + 3) with
 // splits <= min(64, 1024 / K) is at most 2240 for every K <= 32.
 constexpr int kMergeWords = 2304;
 constexpr int kWaveCap = kCandCap / kTopkWaves;  // per wave
 static_assert(kWaveCap % 8 == 0 && kWaveCap >= 32, "regions hold whole groups of 8 keys");
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyTop = 8.f;  // log2 slack of the fast path's reference maximum
 
 // Order key: larger key = larger logit, then smaller id.  -0 becomes +0 first
 // so that the two zeros tie and the id decides.  0 is the empty key.
@@ -266,19 +271,16 @@ template <> struct Vec<float> {
     __device__ __forceinline__ static float scalar(const float *p) { return *p; }
 };
 
-// Lane state: running max m (and ml = m log2 e), float64 sum s of
-// 2^(x log2 e - ml) = exp(x - m), and the candidate list.
-template <int KM>
+// Lane state: reference max m (and ml = m log2 e) and the float64 sum s of
+// 2^(x log2 e - ml) = exp(x - m).
 struct LaneAcc {
     float m, ml;
     double s;
-    KeyList<KM> top;
 
     __device__ __forceinline__ void init() {
         m = -INFINITY;
         ml = -INFINITY;
         s = 0.0;
-        top.init();
     }
     template <int N>
     __device__ __forceinline__ static float vmax(const float (&x)[N]) {
@@ -302,21 +304,34 @@ struct LaneAcc {
             s += static_cast<double>(ls);
         }
     }
-    // candidates: every element >= tau (the list keeps the lane's best KM).
-    // One insertion per loop trip over the lane's pending elements.
-    template <int N>
-    __device__ __forceinline__ void add_cand(const float (&x)[N], int base_id, float tau) {
-        uint32_t pend = 0;
-#pragma unroll
-        for (int j = 0; j < N; ++j) pend |= (x[j] >= tau ? 1u : 0u) << j;
-        while (pend) {
-            const int j = __builtin_ctz(pend);
-            pend &= pend - 1;
-            float xj = x[0];
-#pragma unroll
-            for (int q = 1; q < N; ++q) xj = (q == j) ? x[q] : xj;
-            top.insert(cand_key(xj, base_id + j));
+    // A batch of NB full vectors with maximum bm, on the fast path: the
+    // reference maximum moves only when the batch passes it by more than
+    // 2^kLazyTop (one ballot per batch), so exponent arguments stay <= 8 and
+    // fp32 keeps them to a few ulp; the batch's terms are summed pairwise
+    // in fp32 and added to the float64 sum once.  With ml = -inf the batch
+    // holds only -inf elements (a finite one moves the reference), and an
+    // offset of 0 maps them to exp2(-inf) = 0.
+    template <int NB, int N>
+    __device__ __forceinline__ void add_batch(const float (&x)[NB][N], float bm) {
+        const float bl = bm * kLog2e;
+        if (__ballot(bl > ml + kLazyTop)) {
+            if (bl > ml + kLazyTop) {
+                s *= static_cast<double>(__builtin_amdgcn_exp2f(ml - bl));
+                m = bm;
+                ml = bl;
+            }
         }
+        const float off = ml == -INFINITY ? 0.f : -ml;
+        float e[NB * N];
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+#pragma unroll
+            for (int j = 0; j < N; ++j) e[u * N + j] = __builtin_amdgcn_exp2f(fmaf(x[u][j], kLog2e, off));
+#pragma unroll
+        for (int w = 1; w < NB * N; w *= 2)
+#pragma unroll
+            for (int j = 0; j + w < NB * N; j += 2 * w) e[j] += e[j + w];
+        s += static_cast<double>(e[0]);
     }
 };
 
@@ -331,6 +346,12 @@ __device__ __forceinline__ int count_above_lds(const uint64_t *buf, int n8, uint
         r += (a.x > x) + (a.y > x) + (c.x > x) + (c.y > x) + (d.x > x) + (d.y > x) + (e.x > x) + (e.y > x);
     }
     return r;
+}
+
+// Number of lanes below this one whose bit is set in m.
+__device__ __forceinline__ int lane_rank(uint64_t m) {
+    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
 }
 
 __device__ __forceinline__ uint64_t readlane64(uint64_t x, int j) {
@@ -398,6 +419,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     __shared__ double sm_s[kTopkWaves];
     __shared__ __align__(16) uint64_t sm_cand[kCandCap];
     __shared__ float sm_tau[kTopkWaves];
+    __shared__ bool sm_over[kTopkWaves];
+    __shared__ __align__(16) uint64_t sm_wtop[kTopkWaves * TD_MAX_TOPK];
     __shared__ __align__(16) float sm_live[kTopkWaves];
     static_assert(kTopkWaves == 4, "the live bounds are read as one 16-byte vector");
     __shared__ __align__(16) uint64_t sm_heads[kWave];
@@ -407,8 +430,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     __shared__ uint32_t sm_epoch;
     __shared__ int sm_fail;
 
-    LaneAcc<KM> acc;
+    LaneAcc acc;
     acc.init();
+    // This wave's candidate region: the keys of the elements that reached the
+    // wave's bound when they were seen, appended in any order.  wn counts
+    // every append (wave-uniform); keys past kWaveCap are not stored, and the
+    // slice is then selected again on the exact path after the stream.
+    uint64_t *const wcand = &sm_cand[wave * kWaveCap];
+    int wn = 0;
+    bool wover = false;  // some append found the region full (wave-uniform)
 
     // scalar head up to the first 16-byte boundary (rows need only element
     // alignment), full 16-byte vectors, then a scalar tail
@@ -420,17 +450,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + vlo);
     constexpr int kStep = kBatch * kTopkThreads;
 
-    // ---- first two batches in flight, then the row ticket ----
-    float hx[1] = {-INFINITY};
+    // ---- the head element, the first two batches, then the row ticket ----
+    // (loads complete in issue order: every thread loads the head element,
+    // lanes past the head an element of the row that is not used, so that
+    // waiting for it never waits for the batches)
     const bool has_head = tid < vlo - lo;
     const int head_id = lo + tid;
-    if (has_head) hx[0] = Vec<T>::scalar(rowp + head_id);
+    const float hraw = Vec<T>::scalar(rowp + (has_head ? head_id : min(lo, vocab - 1)));
+    // The batches' loads are issued unconditionally too: a slice without a
+    // whole vector reads the 16-byte block holding an element of the row
+    // (memory of the row's page), whose values are not used.
+    const T *blk = rowp + min(lo, vocab - 1);
+    blk -= (reinterpret_cast<uintptr_t>(blk) & 15) / sizeof(T);  // pointer arithmetic: stays global
+    const u32x4 *vld = nvec > 0 ? vp : reinterpret_cast<const u32x4 *>(blk);
+    const int last = max(nvec - 1, 0);
     u32x4 wa[kBatch], wb[kBatch];
-    const int last = nvec - 1;
-    if (nvec > 0) {
-        load_batch<T>(wa, vp, tid, last);
-        load_batch<T>(wb, vp, tid + kStep, last);
-    }
+    load_batch<T>(wa, vld, tid, last);
+    load_batch<T>(wb, vld, tid + kStep, last);
     // the waves' live bounds start at -inf for everyone before anyone reads them
     if (tid < kTopkWaves) sm_live[tid] = -INFINITY;
     __syncthreads();
@@ -441,10 +477,64 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     }
     const int PS = PW + 1;  // words per workgroup slot
     uint64_t *slot = W.part + (static_cast<int64_t>(row) * splits + sp) * PS;
-    uint64_t r_ep = 0;
-    if (tid == 0) r_ep = fetch(slot);
+    // the epoch is the slot word's low half (the high half stays zero); every
+    // thread reads it (one request per wave), which keeps the load counts exact
+    const uint32_t r_ep = fetch(reinterpret_cast<const uint32_t *>(slot));
+
+    float tau = -INFINITY;
+    // Appends the elements of x (ids base_id ..) that reach the bound, in
+    // lanes where `live`: a wave-uniform call.  Each lane marks its pending
+    // elements, then every trip of the loop appends each lane's lowest
+    // pending one (one ballot, one LDS store per candidate); the trips are
+    // as many as the most candidates a lane has in x.  vm bounds x from above.
+    auto cand_vec = [&](const auto &x, float vm, int base_id, bool live) {
+        constexpr int n = sizeof(x) / sizeof(float);
+        if (!__ballot(live && vm >= tau)) return;
+        uint32_t pend = 0;
+#pragma unroll
+        for (int j = 0; j < n; ++j) pend |= (live && x[j] >= tau ? 1u : 0u) << j;
+        for (;;) {
+            const uint64_t m = __ballot(pend != 0);
+            if (!m) break;
+            if (pend) {
+                const int j = __builtin_ctz(pend);
+                pend &= pend - 1;
+                float xj = x[0];
+#pragma unroll
+                for (int q = 1; q < n; ++q) xj = q == j ? x[q] : xj;
+                const int pos = wn + lane_rank(m);
+                if (pos < kWaveCap) wcand[pos] = cand_key(xj, base_id + j);
+            }
+            wn += __popcll(m);
+            wover = wover || wn > kWaveCap;
+        }
+    };
+    // Keeps the K best keys of the region (ranked by counting; keys are
+    // distinct) and raises the bound to the value of the K-th: every element
+    // at or above the bound was appended, so that is the K-th largest the
+    // wave has seen, and elements equal to it still pass the bound (a
+    // smaller id beats it).  After an overflow the stored keys are a subset
+    // and their K-th is still a valid bound.
+    uint64_t *const wtop = &sm_wtop[wave * TD_MAX_TOPK];
+    auto compact = [&]() {
+        const int n = min(wn, kWaveCap);
+        const int n8 = (n + 7) & ~7;
+        if (lane < 8 && n + lane < n8) wcand[n + lane] = 0;
+        wave_lds_sync();
+        for (int e = lane; e < n; e += kWave) {
+            const uint64_t mine = wcand[e];
+            const int r = count_above_lds(wcand, n8, mine);
+            if (r < K) wtop[r] = mine;
+        }
+        wave_lds_sync();
+        if (lane < K && lane < n) wcand[lane] = wtop[lane];
+        wave_lds_sync();
+        if (n >= K) tau = fmaxf(tau, key_value(wcand[K - 1]));
+        wn = min(n, K);
+    };
 
     // ---- batch 0: exp sums, then the pre-filter bound ----
+    float hx[1] = {has_head ? hraw : -INFINITY};
     float lmax = hx[0];
     if (has_head) acc.add_exp(hx, hx[0]);
 #pragma unroll
@@ -453,7 +543,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
         if (i < nvec) {
             float x[N];
             Vec<T>::unpack(wa[u], x);
-            const float vm = LaneAcc<KM>::vmax(x);
+            const float vm = LaneAcc::vmax(x);
             acc.add_exp(x, vm);
             lmax = fmaxf(lmax, vm);
         }
@@ -461,42 +551,60 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     // Pre-filter bound: cut the wave into KM groups of 64/KM lanes; tau = the
     // smallest of the groups' maxima.  The KM group maxima are KM >= K
     // distinct elements >= tau, so the slice's K-th largest is >= tau.
-    float tau = group_max_min<KM>(lmax);
-    if (has_head && hx[0] >= tau) acc.add_cand(hx, head_id, tau);
+    tau = group_max_min<KM>(lmax);
+    cand_vec(hx, hx[0], head_id, has_head);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
         const int i = tid + u * kTopkThreads;
-        if (i < nvec) {
-            float x[N];
-            Vec<T>::unpack(wa[u], x);
-            if (LaneAcc<KM>::vmax(x) >= tau) acc.add_cand(x, vlo + i * N, tau);
-        }
+        float x[N];
+        Vec<T>::unpack(wa[u], x);
+        cand_vec(x, LaneAcc::vmax(x), vlo + i * N, i < nvec);
     }
+    // (a slice of a few batches gains nothing from a tighter bound)
+    if (wn > 2 * K && nvec > 4 * kStep) compact();
 
     // ---- remaining batches, the next batch's loads in flight ----
+    const int wbase = tid & ~(kWave - 1);
+    // a batch that ends past the slice in some lane of the wave
     auto process = [&](const u32x4 (&w)[kBatch], int i0) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int i = i0 + u * kTopkThreads;
-            if (i < nvec) {
-                float x[N];
-                Vec<T>::unpack(w[u], x);
-                const float vm = LaneAcc<KM>::vmax(x);
-                acc.add_exp(x, vm);
-                if (vm >= tau) acc.add_cand(x, vlo + i * N, tau);
-            }
+            float x[N];
+            Vec<T>::unpack(w[u], x);
+            const float vm = LaneAcc::vmax(x);
+            if (i < nvec) acc.add_exp(x, vm);
+            cand_vec(x, vm, vlo + i * N, i < nvec);
         }
     };
-    // The loop runs in step for the whole wave (its lanes' indices differ by
-    // less than kStep), so the bound can be tightened with lane exchanges:
-    // the KM group maxima of the lanes' best candidates are KM distinct
-    // elements seen so far, so the slice's K-th largest is >= their minimum.
-    // Each wave's bound also bounds the workgroup's K-th largest, so the waves
-    // share them through LDS (a stale value is still a valid bound): every
-    // wave filters with the best of the four.
+    // Fast path for a batch whose vectors are all inside the slice for every
+    // lane of the wave (a wave-uniform test): no per-vector range checks, the
+    // batch-level sum, and candidates looked at only when some lane's batch
+    // maximum reaches the bound.
+    auto process_full = [&](const u32x4 (&w)[kBatch], int i0) {
+        float x[kBatch][N];
+        float vm[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            Vec<T>::unpack(w[u], x[u]);
+            vm[u] = LaneAcc::vmax(x[u]);
+        }
+        static_assert(kBatch == 4, "batch maximum over four vectors");
+        const float bm = fmaxf(fmaxf(vm[0], vm[1]), fmaxf(vm[2], vm[3]));
+        acc.add_batch(x, bm);
+        if (__ballot(bm >= tau)) {
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) cand_vec(x[u], vm[u], vlo + (i0 + u * kTopkThreads) * N, true);
+        }
+    };
+    // every lane's last vector of the batch starting at k is inside the slice
+    auto full_batch = [&](int k) { return wbase + (kWave - 1) + k + (kBatch - 1) * kTopkThreads < nvec; };
+    // The bound is tightened by compacting the region once it holds more
+    // than 2K keys.  Each wave's bound also bounds the workgroup's K-th
+    // largest, so the waves share them through LDS (a stale value is still a
+    // valid bound): every wave filters with the best of the four.
     auto tighten = [&]() {
-        const float head = acc.top.k[0] ? key_value(acc.top.k[0]) : -INFINITY;
-        tau = fmaxf(tau, group_max_min<KM>(head));
+        if (wn > 2 * K) compact();
         if (lane == 0) sm_live[wave] = tau;
         const u32x4 lv = *reinterpret_cast<const u32x4 *>(sm_live);
         tau = fmaxf(tau, fmaxf(fmaxf(__uint_as_float(lv.x), __uint_as_float(lv.y)),
@@ -505,29 +613,35 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     // Batch k sits in wb for odd k / kStep, wa for even; each buffer is
     // refilled with the batch two ahead as soon as it has been processed
     // (unconditionally: past the slice the loads repeat its last vector).
-    const int wbase = tid & ~(kWave - 1);
+    // The bound is tightened once per two batches.
     if (wbase + kStep < nvec) {
-        load_batch<T>(wa, vp, tid + 2 * kStep, last);
+        load_batch<T>(wa, vld, tid + 2 * kStep, last);
         for (int k = kStep;;) {
-            process(wb, tid + k);
-            load_batch<T>(wb, vp, tid + k + 2 * kStep, last);
-            tighten();
+            if (full_batch(k)) process_full(wb, tid + k);
+            else process(wb, tid + k);
+            load_batch<T>(wb, vld, tid + k + 2 * kStep, last);
             k += kStep;
             if (wbase + k >= nvec) break;
-            process(wa, tid + k);
-            load_batch<T>(wa, vp, tid + k + 2 * kStep, last);
+            if (full_batch(k)) process_full(wa, tid + k);
+            else process(wa, tid + k);
+            load_batch<T>(wa, vld, tid + k + 2 * kStep, last);
             tighten();
             k += kStep;
             if (wbase + k >= nvec) break;
         }
     }
-    for (int e = tail0 + tid; e < hi; e += kTopkThreads) {
-        float x[1] = {Vec<T>::scalar(rowp + e)};
-        acc.add_exp(x, x[0]);
-        if (x[0] >= tau) acc.add_cand(x, e, tau);
+    {  // the scalar tail: fewer than N elements, one per thread
+        const int e = tail0 + tid;
+        const bool in = e < hi;
+        float xt[1] = {-INFINITY};
+        if (in) {
+            xt[0] = Vec<T>::scalar(rowp + e);
+            acc.add_exp(xt, xt[0]);
+        }
+        cand_vec(xt, xt[0], e, in);
     }
 
-    // ---- workgroup partial: (log2 max, sum) and the top K of the lanes' lists ----
+    // ---- workgroup partial: (log2 max, sum) and the top K of the candidates ----
     const float wml = wave_max(acc.ml);
     const double contrib =
         (acc.m == -INFINITY) ? 0.0 : acc.s * static_cast<double>(__builtin_amdgcn_exp2f(acc.ml - wml));
@@ -536,38 +650,78 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
         sm_m[wave] = wml;
         sm_s[wave] = ws_sum;
         sm_tau[wave] = tau;
+        sm_over[wave] = wover;
     }
     if (tid == 0) {
-        sm_epoch = static_cast<uint32_t>(r_ep);
+        sm_epoch = r_ep;
         sm_fail = 0;
     }
     if (tid < KM) sm_win[tid] = 0;
     __syncthreads();
     // Each wave's bound is at most the workgroup's K-th largest element, so
-    // their maximum is one too: only list entries at or above it compete.
+    // their maximum is one too: only candidates at or above it compete.
     float tau_wg = sm_tau[0];
+    bool over = sm_over[0];
 #pragma unroll
-    for (int q = 1; q < kTopkWaves; ++q) tau_wg = fmaxf(tau_wg, sm_tau[q]);
-    int n_l = 0;
-#pragma unroll
-    for (int j = 0; j < KM; ++j) n_l += acc.top.k[j] != 0 && key_value(acc.top.k[j]) >= tau_wg;
-    constexpr int kCountBits = KM <= 4 ? 3 : KM <= 8 ? 4 : KM <= 16 ? 5 : 6;
+    for (int q = 1; q < kTopkWaves; ++q) {
+        tau_wg = fmaxf(tau_wg, sm_tau[q]);
+        over = over || sm_over[q];
+    }
     int Cw = 0;
-    const int off = wave_prefix<kCountBits>(n_l, lane, Cw);
-    uint64_t *wcand = &sm_cand[wave * kWaveCap];
-    if (Cw <= kWaveCap) {
-        // the lists are sorted, so the entries that compete come first
-#pragma unroll
-        for (int j = 0; j < KM; ++j)
-            if (j < n_l) wcand[off + j] = acc.top.k[j];
+    if (!over) {
+        // keep the region's keys at or above the bound, packed at its start
+        // (a trip writes only slots it has read)
+        for (int e0 = 0; e0 < wn; e0 += kWave) {
+            const int e = e0 + lane;
+            const uint64_t k = e < wn ? wcand[e] : 0;
+            const bool keep = k != 0 && key_value(k) >= tau_wg;
+            const uint64_t m = __ballot(keep);
+            wave_lds_sync();
+            if (keep) wcand[Cw + lane_rank(m)] = k;
+            Cw += __popcll(m);
+        }
     } else {
-        // many equal logits: the wave's K best by a K-round tournament
-        uint64_t win[KM];
-        wave_select<KM, KM>(acc.top, K, win);
-        if (lane == 0)
+        // A region overflowed (rows of many equal or ascending logits): every
+        // wave selects again from its share of the slice with a sorted list
+        // of its best KM keys per lane, keeping only elements >= tau_wg.
+        KeyList<KM> top;
+        top.init();
+        auto insert_vec = [&](const auto &x, int base_id, bool live) {
+            constexpr int n = sizeof(x) / sizeof(float);
 #pragma unroll
-            for (int j = 0; j < KM; ++j) wcand[j] = win[j];
-        Cw = KM;
+            for (int j = 0; j < n; ++j)
+                if (live && x[j] >= tau_wg) top.insert(cand_key(x[j], base_id + j));
+        };
+        insert_vec(hx, head_id, has_head);
+        for (int i = tid; i < nvec; i += kTopkThreads) {
+            float x[N];
+            Vec<T>::unpack(vp[i], x);
+            insert_vec(x, vlo + i * N, true);
+        }
+        {
+            const int e = tail0 + tid;
+            float xt[1] = {-INFINITY};
+            if (e < hi) xt[0] = Vec<T>::scalar(rowp + e);
+            insert_vec(xt, e, e < hi);
+        }
+        int n_l = 0;
+#pragma unroll
+        for (int j = 0; j < KM; ++j) n_l += top.k[j] != 0;
+        constexpr int kCountBits = KM <= 4 ? 3 : KM <= 8 ? 4 : KM <= 16 ? 5 : 6;
+        const int off = wave_prefix<kCountBits>(n_l, lane, Cw);
+        if (Cw <= kWaveCap) {
+#pragma unroll
+            for (int j = 0; j < KM; ++j)
+                if (j < n_l) wcand[off + j] = top.k[j];
+        } else {
+            // the wave's K best by a K-round tournament
+            uint64_t win[KM];
+            wave_select<KM, KM>(top, K, win);
+            if (lane == 0)
+#pragma unroll
+                for (int j = 0; j < KM; ++j) wcand[j] = win[j];
+            Cw = KM;
+        }
     }
     // pad the region to a multiple of 8 keys with empty (0) keys
     const int C8 = (Cw + 7) & ~7;

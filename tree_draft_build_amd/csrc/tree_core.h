@@ -104,7 +104,7 @@ __host__ __device__ inline int tree_slots(int n_max) {
 // meet this wave at a workgroup barrier before the tree's own entries are
 // written; only entries 0..n are written here then.
 template <int SLOTS, bool PREFILLED = false>
-__device__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &o, int b, int lane,
+__device__ __forceinline__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &o, int b, int lane,
                                 int root_tok) {
 #pragma clang fp contract(off)
     const int K = P.K;

@@ -88,6 +88,11 @@ struct AttnPlan {
     int64_t items;     // n_chunks * hkv split work items
 };
 
+// Split work items the chunk length aims at: about one workgroup per compute
+// unit, so that each streams one long chunk (every workgroup start and end
+// drains its ring once) and few partials are written.
+constexpr int64_t kAttnItems = 256;
+
 inline AttnPlan attn_plan(int batch, int nq_max, int hq, int hkv, int64_t total_ctx, int CH) {
     AttnPlan p;
     p.group = hq / hkv;
@@ -95,11 +100,11 @@ inline AttnPlan attn_plan(int batch, int nq_max, int hq, int hkv, int64_t total_
     // one row block holds 4 own row groups: as many as the registers allow,
     // so that a chunk's keys stream once for every tree row where they can
     p.own = std::max(1, (p.n_rg + kAttnWaves - 1) / kAttnWaves);
-    // about 1024 work items over the context; longer chunks keep the partial
-    // traffic small when the context is long
+    // about kAttnItems work items over the context; longer chunks keep the
+    // partial traffic small when the context is long
     const int64_t work = std::max<int64_t>(1, total_ctx) * hkv;
     int chunk = CH;
-    while (chunk < 32 * CH && work / chunk > 1024) chunk *= 2;
+    while (chunk < 32 * CH && work / chunk > kAttnItems) chunk *= 2;
     p.chunk = chunk;
     p.n_chunks = (total_ctx + chunk - 1) / chunk + batch;
     p.items = static_cast<int64_t>(hkv) * p.n_chunks;
@@ -471,42 +476,43 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_f32(
 // straight from HBM into a ring of LDS buffers (global_load_lds, 16 bytes per
 // lane) while one buffer is computed on, and no register holds staged data:
 // two buffers of 128 keys (chunks of up to 512 keys: fewer, larger steps), or
-// four of 64 keys (longer chunks: three sub-chunks in flight during the
-// compute, 96 KB per compute unit instead of 64).  K and V sit key-major in
-// LDS, each key row padded:
-//   K rows of D/8 + 1 16-byte pieces: S^T = K Q^T reads 16 consecutive key
-//     rows at one piece (A operand), and those fall in distinct banks;
-//   V rows of D/8 + 2 pieces: O^T += V^T P^T needs V transposed, which
-//     ds_read_b64_tr_b16 delivers.  Within a group of 16 lanes it hands lane
-//     i, as element j, element i % 4 of the 4 elements at the address of lane
-//     4 j + i / 4, so lane m of group G addresses 4 head dims of key
-//     4 G + m / 4: lane i then holds head dim i of keys 4 G .. 4 G + 3 (and,
-//     from a second read, of keys 16 + 4 G ..), the order in which S^T leaves
-//     P in registers.  The 4 keys' 32-byte reads fall in distinct banks.
-// The pad pieces of a row load a copy of its last piece (same instruction,
-// no extra HBM traffic).
+// five of 64 keys (longer chunks: four sub-chunks, 128 KB, in flight per
+// compute unit during the compute).  K and V sit key-major in LDS with no
+// padding; the 16-byte pieces of a row are permuted instead, so that the
+// reads below fall in distinct banks:
+//   K: piece p of key row r sits at piece p ^ kswz(r).  S^T = K Q^T reads 16
+//     consecutive key rows at one piece (A operand): 16 distinct pieces;
+//   V: 32-byte segment s of key row r sits at segment s ^ vswz(r).
+//     O^T += V^T P^T needs V transposed, which ds_read_b64_tr_b16 delivers.
+//     Within a group of 16 lanes it hands lane i, as element j, element i % 4
+//     of the 4 elements at the address of lane 4 j + i / 4, so lane m of
+//     group G addresses 4 head dims of key 4 G + m / 4: lane i then holds head
+//     dim i of keys 4 G .. 4 G + 3 (and, from a second read, of keys 16 + 4 G
+//     ..), the order in which S^T leaves P in registers.  The 8 keys of a half
+//     wave read one segment each, in 8 distinct segments.
+// Both swizzles repeat every 16 rows, so a lane's offsets inside a row are
+// the same for every tile and half tile, and the direct loads only choose
+// which global piece each lane's slot receives.
 // ---------------------------------------------------------------------------
-// buffers of the ring for a sub-chunk of SUB keys (the LDS holds 256 keys)
-template <int SUB> constexpr int ring_of() { return SUB == 64 ? 4 : 2; }
+// buffers of the ring for a sub-chunk of SUB keys
+template <int SUB> constexpr int ring_of() { return SUB == 64 ? 5 : 2; }
 constexpr int kRingChunk = 1024;  // chunks of at least this many keys take 64-key sub-chunks
 
-template <int D> constexpr int rk_pieces() { return D / 8 + 1; }
-template <int D> constexpr int rv_pieces() { return D / 8 + 2; }
-// LDS slots of one K or V region: whole rounds of 16-byte loads of the
-// workgroup, so every wave issues the same, compile-time number of direct
-// loads (the compiler can then wait for an earlier load without waiting for
-// them); the slots past the rows take copies of the last row.
-template <int SUB, int R> constexpr int region_slots() {
-    return (SUB * R + kAttnThreads - 1) / kAttnThreads * kAttnThreads;
+template <int D> __host__ __device__ constexpr int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D> __host__ __device__ constexpr int vswz(int r) { return D == 128 ? (r & 7) : ((r >> 1) & 3); }
+// LDS slots (16-byte pieces) of one K or V region: whole rounds of 16-byte
+// loads of the workgroup, so every wave issues the same, compile-time number
+// of direct loads (the compiler can then wait for an earlier load without
+// waiting for them).
+template <int SUB, int D> constexpr int region_slots() {
+    static_assert(D == 64 || D == 128, "head dims of the bf16 split kernel");
+    static_assert(SUB * (D / 8) % kAttnThreads == 0, "whole rounds of direct loads");
+    return SUB * (D / 8);
 }
-template <int SUB, int D> constexpr int sub_k_elems() { return region_slots<SUB, rk_pieces<D>()>() * 8; }
-template <int SUB, int D> constexpr int sub_elems() {
-    return (region_slots<SUB, rk_pieces<D>()>() + region_slots<SUB, rv_pieces<D>()>()) * 8;
-}
+template <int SUB, int D> constexpr int sub_k_elems() { return region_slots<SUB, D>() * 8; }
+template <int SUB, int D> constexpr int sub_elems() { return 2 * region_slots<SUB, D>() * 8; }
 // direct-load instructions each wave issues per sub-chunk (K and V)
-template <int SUB, int D> constexpr int sub_loads() {
-    return (region_slots<SUB, rk_pieces<D>()>() + region_slots<SUB, rv_pieces<D>()>()) / kAttnThreads;
-}
+template <int SUB, int D> constexpr int sub_loads() { return 2 * region_slots<SUB, D>() / kAttnThreads; }
 
 // Wait until at most N of this wave's vector-memory loads are outstanding
 // (the N most recent); LDS and export counters untouched.
@@ -529,27 +535,23 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void *)p));
 }
 
-// Enqueue the direct loads of one sub-chunk's K or V rows (LDS rows of R
-// pieces; rows at or past `valid` repeat key valid - 1 and are masked later).
-template <int SUB, int D, int R>
+// Enqueue the direct loads of one sub-chunk's K (V = false) or V rows: the
+// lane of LDS slot `slot` (row slot / P, permuted piece slot % P) loads the
+// global piece that belongs there; rows at or past `valid` repeat key
+// valid - 1 and are masked later.
+template <int SUB, int D, bool V>
 __device__ __forceinline__ void issue_rows(const uint16_t *gbase, int ks32, int valid, uint16_t *lds,
                                            int wave, int lane) {
     constexpr int P = D / 8;
-    constexpr int kRounds = region_slots<SUB, R>() / kAttnThreads;
-    // slot of this lane in round r: (r 4 + wave) 64 + lane; its (row, piece)
-    // advance by (256 / R, 256 % R) per round
-    int row = (wave * kWave + lane) / R;
-    int piece = (wave * kWave + lane) % R;
+    constexpr int kRounds = region_slots<SUB, D>() / kAttnThreads;
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
         const int slot0 = (r * kAttnWaves + wave) * kWave;  // first slot of this wave (uniform)
-        lds_dma16(gbase + min(row, valid - 1) * ks32 + 8 * min(piece, P - 1), lds + 8 * slot0);
-        row += kAttnThreads / R;
-        piece += kAttnThreads % R;
-        if (piece >= R) {
-            piece -= R;
-            ++row;
-        }
+        const int slot = slot0 + lane;
+        const int row = slot / P;
+        const int pp = slot % P;
+        const int piece = V ? ((((pp >> 1) ^ vswz<D>(row)) << 1) | (pp & 1)) : (pp ^ kswz<D>(row));
+        lds_dma16(gbase + min(row, valid - 1) * ks32 + 8 * piece, lds + 8 * slot0);
     }
 }
 
@@ -559,36 +561,49 @@ __device__ __forceinline__ void issue_rows(const uint16_t *gbase, int ks32, int 
 // schedule of the plain loads waits for each read before issuing the next.
 template <int D>
 __device__ __forceinline__ void read_k(const uint16_t *sK, int kt, int lane, bf16x8 (&fk)[2][D / 32]) {
-    constexpr int RK = rk_pieces<D>();
+    constexpr int P = D / 8;
     const int col = lane & 15;
     const int h4 = lane >> 4;
-    const uint32_t a0 = lds_addr(sK + (kt * kKeyTile + col) * RK * 8 + 8 * h4);
-    const uint32_t a1 = lds_addr(sK + (kt * kKeyTile + 16 + col) * RK * 8 + 8 * h4);
+    // Row kt 32 + 16 hf + col has swizzle sw = kswz(col) in both halves, and
+    // piece h4 + 4 ks of it sits at (h4 ^ (sw & 3)) + 4 (ks ^ (sw >> 2)): the
+    // address of ks is x ^ (64 ks) for the ks = 0 address x (the ring is
+    // 256-byte aligned and rows are 128 or 256 bytes, so bits 6 and 7 of
+    // the row base are zero).  Temporaries t0 / t1 hold the others in turn,
+    // each rewritten only after another pair of reads has been issued.
+    const int sw = kswz<D>(col);
+    const uint32_t x = (lds_addr(sK) + (kt * kKeyTile + col) * P * 16 + 16 * (h4 ^ (sw & 3))) |
+                       static_cast<uint32_t>((sw >> 2) << 6);
     u32x4 t[2 * (D / 32)];
+    uint32_t t0, t1;
     if constexpr (D == 128) {
         asm volatile(
-            "ds_read_b128 %0, %8\n"
-            "ds_read_b128 %1, %8 offset:64\n"
-            "ds_read_b128 %2, %8 offset:128\n"
-            "ds_read_b128 %3, %8 offset:192\n"
-            "ds_read_b128 %4, %9\n"
-            "ds_read_b128 %5, %9 offset:64\n"
-            "ds_read_b128 %6, %9 offset:128\n"
-            "ds_read_b128 %7, %9 offset:192\n"
+            "v_xor_b32 %8, 64, %10\n"
+            "v_xor_b32 %9, 0x80, %10\n"
+            "ds_read_b128 %0, %10\n"
+            "ds_read_b128 %4, %10 offset:4096\n"
+            "ds_read_b128 %1, %8\n"
+            "ds_read_b128 %5, %8 offset:4096\n"
+            "ds_read_b128 %2, %9\n"
+            "ds_read_b128 %6, %9 offset:4096\n"
+            "v_xor_b32 %8, 0xc0, %10\n"
+            "ds_read_b128 %3, %8\n"
+            "ds_read_b128 %7, %8 offset:4096\n"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]),
-              "=&v"(t[6]), "=&v"(t[7])
-            : "v"(a0), "v"(a1));
+              "=&v"(t[6]), "=&v"(t[7]), "=&v"(t0), "=&v"(t1)
+            : "v"(x));
     } else {
         asm volatile(
-            "ds_read_b128 %0, %4\n"
-            "ds_read_b128 %1, %4 offset:64\n"
-            "ds_read_b128 %2, %5\n"
-            "ds_read_b128 %3, %5 offset:64\n"
+            "v_xor_b32 %4, 64, %6\n"
+            "ds_read_b128 %0, %6\n"
+            "ds_read_b128 %2, %6 offset:2048\n"
+            "ds_read_b128 %1, %4\n"
+            "ds_read_b128 %3, %4 offset:2048\n"
             "s_waitcnt lgkmcnt(0)"
-            : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
-            : "v"(a0), "v"(a1));
+            : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t0), "=&v"(t1)
+            : "v"(x));
     }
+    (void)t1;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -600,50 +615,66 @@ __device__ __forceinline__ void read_k(const uint16_t *sK, int kt, int lane, bf1
 // builtin makes it wait for the other buffer's loads first.
 template <int D>
 __device__ __forceinline__ void read_vt(const uint16_t *sV, int kt, int lane, bf16x8 (&fv)[D / 16]) {
-    constexpr int RV = rv_pieces<D>();
+    constexpr int P = D / 8;
     const int G = lane >> 4;
     const int m = lane & 15;
-    const int key0 = kt * kKeyTile + 4 * G + (m >> 2);
-    const uint32_t a0 = lds_addr(sV + key0 * RV * 8 + 4 * (m & 3));
-    const uint32_t a1 = lds_addr(sV + (key0 + 16) * RV * 8 + 4 * (m & 3));
+    // key row kt 32 + 4 G + m / 4 (and 16 further, same swizzle), dims
+    // 16 s + 4 (m % 4) .. of segment s, which sits at segment s ^ w: the
+    // address of segment s is x ^ (32 s) for the s = 0 address x (bits 5..7
+    // of the row base are zero).  Temporaries t0 / t1 hold the others in turn,
+    // each rewritten only after another pair of reads has been issued.
+    const int r0 = kt * kKeyTile + 4 * G + (m >> 2);
+    const int w = vswz<D>(r0);
+    const uint32_t x = (lds_addr(sV) + r0 * P * 16 + 8 * (m & 3)) | static_cast<uint32_t>(w << 5);
     u2_t t[2 * (D / 16)];
+    uint32_t t0, t1;
     if constexpr (D == 128) {
         asm volatile(
-            "ds_read_b64_tr_b16 %0, %16\n"
-            "ds_read_b64_tr_b16 %1, %17\n"
-            "ds_read_b64_tr_b16 %2, %16 offset:32\n"
-            "ds_read_b64_tr_b16 %3, %17 offset:32\n"
-            "ds_read_b64_tr_b16 %4, %16 offset:64\n"
-            "ds_read_b64_tr_b16 %5, %17 offset:64\n"
-            "ds_read_b64_tr_b16 %6, %16 offset:96\n"
-            "ds_read_b64_tr_b16 %7, %17 offset:96\n"
-            "ds_read_b64_tr_b16 %8, %16 offset:128\n"
-            "ds_read_b64_tr_b16 %9, %17 offset:128\n"
-            "ds_read_b64_tr_b16 %10, %16 offset:160\n"
-            "ds_read_b64_tr_b16 %11, %17 offset:160\n"
-            "ds_read_b64_tr_b16 %12, %16 offset:192\n"
-            "ds_read_b64_tr_b16 %13, %17 offset:192\n"
-            "ds_read_b64_tr_b16 %14, %16 offset:224\n"
-            "ds_read_b64_tr_b16 %15, %17 offset:224\n"
+            "v_xor_b32 %16, 32, %18\n"
+            "v_xor_b32 %17, 64, %18\n"
+            "ds_read_b64_tr_b16 %0, %18\n"
+            "ds_read_b64_tr_b16 %1, %18 offset:4096\n"
+            "ds_read_b64_tr_b16 %2, %16\n"
+            "ds_read_b64_tr_b16 %3, %16 offset:4096\n"
+            "ds_read_b64_tr_b16 %4, %17\n"
+            "ds_read_b64_tr_b16 %5, %17 offset:4096\n"
+            "v_xor_b32 %16, 0x60, %18\n"
+            "ds_read_b64_tr_b16 %6, %16\n"
+            "ds_read_b64_tr_b16 %7, %16 offset:4096\n"
+            "v_xor_b32 %17, 0x80, %18\n"
+            "ds_read_b64_tr_b16 %8, %17\n"
+            "ds_read_b64_tr_b16 %9, %17 offset:4096\n"
+            "v_xor_b32 %16, 0xa0, %18\n"
+            "ds_read_b64_tr_b16 %10, %16\n"
+            "ds_read_b64_tr_b16 %11, %16 offset:4096\n"
+            "v_xor_b32 %17, 0xc0, %18\n"
+            "ds_read_b64_tr_b16 %12, %17\n"
+            "ds_read_b64_tr_b16 %13, %17 offset:4096\n"
+            "v_xor_b32 %16, 0xe0, %18\n"
+            "ds_read_b64_tr_b16 %14, %16\n"
+            "ds_read_b64_tr_b16 %15, %16 offset:4096\n"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]),
               "=&v"(t[6]), "=&v"(t[7]), "=&v"(t[8]), "=&v"(t[9]), "=&v"(t[10]), "=&v"(t[11]),
-              "=&v"(t[12]), "=&v"(t[13]), "=&v"(t[14]), "=&v"(t[15])
-            : "v"(a0), "v"(a1));
+              "=&v"(t[12]), "=&v"(t[13]), "=&v"(t[14]), "=&v"(t[15]), "=&v"(t0), "=&v"(t1)
+            : "v"(x));
     } else {
         asm volatile(
-            "ds_read_b64_tr_b16 %0, %8\n"
-            "ds_read_b64_tr_b16 %1, %9\n"
-            "ds_read_b64_tr_b16 %2, %8 offset:32\n"
-            "ds_read_b64_tr_b16 %3, %9 offset:32\n"
-            "ds_read_b64_tr_b16 %4, %8 offset:64\n"
-            "ds_read_b64_tr_b16 %5, %9 offset:64\n"
-            "ds_read_b64_tr_b16 %6, %8 offset:96\n"
-            "ds_read_b64_tr_b16 %7, %9 offset:96\n"
+            "v_xor_b32 %8, 32, %10\n"
+            "v_xor_b32 %9, 64, %10\n"
+            "ds_read_b64_tr_b16 %0, %10\n"
+            "ds_read_b64_tr_b16 %1, %10 offset:2048\n"
+            "ds_read_b64_tr_b16 %2, %8\n"
+            "ds_read_b64_tr_b16 %3, %8 offset:2048\n"
+            "ds_read_b64_tr_b16 %4, %9\n"
+            "ds_read_b64_tr_b16 %5, %9 offset:2048\n"
+            "v_xor_b32 %8, 0x60, %10\n"
+            "ds_read_b64_tr_b16 %6, %8\n"
+            "ds_read_b64_tr_b16 %7, %8 offset:2048\n"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]),
-              "=&v"(t[6]), "=&v"(t[7])
-            : "v"(a0), "v"(a1));
+              "=&v"(t[6]), "=&v"(t[7]), "=&v"(t0), "=&v"(t1)
+            : "v"(x));
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
@@ -745,16 +776,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
     int nq_max, int hq, int hkv, int group, int n_rg, int chunk, float scale2,
     float *__restrict__ ws, int64_t prow_total, int2 *__restrict__ seqinfo) {
     // kRing buffers, each K then V of one sub-chunk; the merge scratch of
-    // split mode reuses buffer 0 once no load is in flight
+    // split mode reuses the ring once no load is in flight
     constexpr int kSubB = SUB;
     constexpr int kRing = ring_of<SUB>();
     constexpr int kSubElems = sub_elems<SUB, D>();
-    __shared__ __attribute__((aligned(16))) uint16_t sring[kRing * kSubElems];
+    __shared__ __attribute__((aligned(256))) uint16_t sring[kRing * kSubElems];
     uint16_t *const sbuf0 = sring;
     constexpr int kVOff = sub_k_elems<SUB, D>();  // the V region follows the K region
     constexpr int kLoads = sub_loads<SUB, D>();
-    static_assert(2 * kLoads < 64, "two sub-chunks' loads fit the wait counter");
-    auto ring = [&](int sc) { return sring + (sc & (kRing - 1)) * kSubElems; };
+    static_assert((kRing - 2) * kLoads < 64, "the loads of the sub-chunks in flight fit the wait counter");
+    auto ring = [&](int sc) { return sring + (sc % kRing) * kSubElems; };
 
     const int64_t c = blockIdx.x / hkv;
     const int g = static_cast<int>(blockIdx.x % hkv);
@@ -786,9 +817,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
     {                                                                                          \
         const int64_t s0_ = (k0 + static_cast<int64_t>(sc) * kSubB) * kstride;               \
         const int v_ = TD_SUB_VALID(sc);                                                       \
-        issue_rows<SUB, D, rk_pieces<D>()>(v_ > 0 ? kbase + s0_ : q, static_cast<int>(kstride), \
+        issue_rows<SUB, D, false>(v_ > 0 ? kbase + s0_ : q, static_cast<int>(kstride),         \
                                       v_ > 0 ? v_ : 1, buf, wave, lane);                       \
-        issue_rows<SUB, D, rv_pieces<D>()>(v_ > 0 ? vbase + s0_ : q, static_cast<int>(kstride), \
+        issue_rows<SUB, D, true>(v_ > 0 ? vbase + s0_ : q, static_cast<int>(kstride),          \
                                       v_ > 0 ? v_ : 1, buf + kVOff, wave, lane);               \
     }
     const int nn_b = n_nodes[b];  // in flight while the first loads are issued
@@ -888,7 +919,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
             // sc + kRing - 1 goes into the buffer sub-chunk sc - 1 used
             for (int sc = 0; sc < n_sub; ++sc) {
                 const int ahead = min(kRing - 2, n_sub - 1 - sc);  // sub-chunks issued after sc
-                if (ahead >= 2) wait_vm<2 * kLoads>();
+                if (kRing > 4 && ahead >= 3) wait_vm<(kRing > 4 ? 3 : 0) * kLoads>();
+                else if (ahead >= 2) wait_vm<2 * kLoads>();
                 else if (ahead == 1) wait_vm<kLoads>();
                 else wait_vm<0>();
                 __syncthreads();  // everyone's loads of sc have landed; buffer sc - 1 is free
@@ -930,8 +962,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
                 // split mode: kt_step waves per row group merge through LDS
                 constexpr int kMP = D + 4;
                 static_assert((2 * kAttnWaves * kRowsPerGroup + kAttnWaves * kRowsPerGroup * kMP) * 4 <=
-                                  kSubElems * 2,
-                              "the merge area fits one sub-chunk buffer");
+                                  kRing * kSubElems * 2,
+                              "the merge area fits the ring");
                 float *mw = reinterpret_cast<float *>(sbuf0);      // [4][16]
                 float *lw = mw + kAttnWaves * kRowsPerGroup;       // [4][16]
                 float *ow = lw + kAttnWaves * kRowsPerGroup;       // [4][16][kMP]

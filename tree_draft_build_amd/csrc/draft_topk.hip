@@ -564,7 +564,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     if (wn > 2 * K && nvec > 4 * kStep) compact();
 
     // ---- remaining batches, the next batch's loads in flight ----
-    const int wbase = tid & ~(kWave - 1);
+    const int wbase = __builtin_amdgcn_readfirstlane(tid & ~(kWave - 1));  // wave-uniform
     // a batch that ends past the slice in some lane of the wave
     auto process = [&](const u32x4 (&w)[kBatch], int i0) {
 #pragma unroll

@@ -135,25 +135,64 @@ __device__ __forceinline__ int64_t seq_len(const int64_t *__restrict__ off,
     return lens ? std::max<int64_t>(0, std::min<int64_t>(lens[s], region)) : region;
 }
 
+// Inclusive sum over lanes 0..i of the wave, in lane i: row shifts within
+// each row of 16 lanes, then the rows' totals broadcast onwards (lanes with
+// no source add 0).
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+    return v;
+}
+
 // Locate chunk c of the contexts: sequence b, its key range, its first chunk
-// index and its chunk count.
+// index and its chunk count.  A wave-uniform call: lane j takes sequence
+// s0 + j of each group of 64 (all lanes' loads in flight at once), an
+// inclusive scan of the chunk counts over the lanes finds the sequence whose
+// chunks cover c, and every lane gets the same result.  (A group's chunk
+// count fits 32 bits: a chunk holds at least 128 keys of the K buffer.)
 __device__ __forceinline__ bool find_chunk(const int64_t *__restrict__ off,
                                            const int64_t *__restrict__ lens, int batch, int chunk,
                                            int64_t c, int &b, int64_t &k0, int64_t &k1,
                                            int64_t &cbase, int &nch) {
-    int64_t acc = 0;
-    for (int s = 0; s < batch; ++s) {
-        const int64_t L = seq_len(off, lens, s);
+    if (batch == 1) {  // one sequence: uniform loads (scalar cache), no scan
+        const int64_t L = seq_len(off, lens, 0);
         const int64_t n = chunks_of(L, chunk);
-        if (c < acc + n) {
-            b = s;
-            k0 = (c - acc) * chunk;
-            k1 = std::min<int64_t>(L, k0 + chunk);
-            cbase = acc;
-            nch = static_cast<int>(n);
+        if (c >= n) return false;
+        b = 0;
+        cbase = 0;
+        k0 = c * chunk;
+        k1 = std::min<int64_t>(L, k0 + chunk);
+        nch = static_cast<int>(n);
+        return true;
+    }
+    const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+    int64_t acc = 0;
+    for (int s0 = 0; s0 < batch; s0 += kWave) {
+        const int s = s0 + lane;
+        const bool in = s < batch;
+        const int64_t L = in ? seq_len(off, lens, s) : 0;
+        const uint32_t n = in ? static_cast<uint32_t>(chunks_of(L, chunk)) : 0u;
+        const uint32_t inc = wave_incl_sum(n);
+        const uint64_t hit = __ballot(in && c < acc + static_cast<int64_t>(inc));
+        if (hit) {
+            const int j = __ffsll(static_cast<long long>(hit)) - 1;  // uniform
+            const uint32_t incj = __builtin_amdgcn_readlane(inc, j);
+            const uint32_t nj = __builtin_amdgcn_readlane(n, j);
+            const int64_t Lj = static_cast<int64_t>(
+                (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(L >> 32), j))) << 32) |
+                static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(L), j)));
+            b = s0 + j;
+            cbase = acc + static_cast<int64_t>(incj) - static_cast<int64_t>(nj);
+            k0 = (c - cbase) * chunk;
+            k1 = std::min<int64_t>(Lj, k0 + chunk);
+            nch = static_cast<int>(nj);
             return true;
         }
-        acc += n;
+        acc += static_cast<int64_t>(__builtin_amdgcn_readlane(inc, kWave - 1));
     }
     return false;
 }
@@ -1131,6 +1170,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     const int lane = threadIdx.x & 63;
     const int slice = lane >> 3;
     const int cg = R == 1 ? (lane & 7) : 0;
+    // one sequence: its record is loaded with the tree size, one round trip
+    // before the partials rather than two
+    int2 si0 = int2{0, 0};
+    int nn0 = 0;
+    if (batch == 1) {
+        nn0 = n_nodes[0];
+        si0 = seqinfo[0];
+    }
     // row (b, g, r) of this lane (of its lane group when R = 8); `store`:
     // a real row (a lane group past the last row repeats one, unstored)
     auto combine_row = [&](int b, int g, int r, bool store) __attribute__((always_inline)) {
@@ -1153,7 +1200,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
         for (int wd = 0; wd < 4; ++wd) mw[wd] = wd < words ? mrow[wd] : 0;
 
         // first chunk and chunk count of sequence b (left by the split kernel)
-        const int2 si = seqinfo[b];
+        const int2 si = batch == 1 ? si0 : seqinfo[b];
         const int64_t cb = si.x;
         const int nch = si.y;
         const int rg = r / kRowsPerGroup;
@@ -1296,9 +1343,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     const uint32_t step = static_cast<uint32_t>(n_blocks) * kCombineRows * R;
     const uint32_t first = (blockIdx.x * kCombineRows + (threadIdx.x >> 6)) * R;
     if (batch == 1) {  // one sequence: no sums to share
-        if (n_nodes[0] < 0) return;  // a tree build that gave up: no rows
-        const uint32_t total = static_cast<uint32_t>(hq) * (min(n_nodes[0], nq_max - 1) + 1);
-        const uint32_t rows_g = static_cast<uint32_t>(group) * (min(n_nodes[0], nq_max - 1) + 1);
+        if (nn0 < 0) return;  // a tree build that gave up: no rows
+        const uint32_t total = static_cast<uint32_t>(hq) * (min(nn0, nq_max - 1) + 1);
+        const uint32_t rows_g = static_cast<uint32_t>(group) * (min(nn0, nq_max - 1) + 1);
         for (uint32_t t0 = first; t0 < total; t0 += step) {
             const uint32_t t = min(t0 + sub, total - 1);
             const uint32_t g = t / rows_g;

@@ -165,24 +165,31 @@ __device__ __forceinline__ void build_tree_wave(TreeLds &t, const TreeParams &P,
                     bk = f_key[s];
                     bs = s;
                 }
-            // wave-wide best (register butterfly)
-            wl = bl;
-            wk = bk;
-#define TD_TREE_LEVEL(L)                                       \
-            {                                                  \
-                const double ol = xchg_d<L>(wl);               \
-                const uint32_t ok = xchg<L>(wk);               \
-                const bool take = precedes(ol, ok, wl, wk);    \
-                wl = take ? ol : wl;                           \
-                wk = take ? ok : wk;                           \
+            // wave-wide largest log rho (register butterfly on the score
+            // alone), then the lanes that hold it: one in general, several
+            // only for equal scores, when the smallest key among them wins
+            double m = bl;
+            m = fmax(m, xchg_d<0>(m));
+            m = fmax(m, xchg_d<1>(m));
+            m = fmax(m, xchg_d<2>(m));
+            m = fmax(m, xchg_d<3>(m));
+            m = fmax(m, xchg_d<4>(m));
+            m = fmax(m, xchg_d<5>(m));
+            wl = read_lane_d(m, 0);
+            const bool at = bl == wl;
+            const unsigned long long hold = __ballot(at);
+            uint32_t kk = at ? bk : kEmptyKey;
+            if (__popcll(hold) > 1) {
+                kk = min(kk, xchg<0>(kk));
+                kk = min(kk, xchg<1>(kk));
+                kk = min(kk, xchg<2>(kk));
+                kk = min(kk, xchg<3>(kk));
+                kk = min(kk, xchg<4>(kk));
+                kk = min(kk, xchg<5>(kk));
             }
-            TD_TREE_LEVEL(0)
-            TD_TREE_LEVEL(1)
-            TD_TREE_LEVEL(2)
-            TD_TREE_LEVEL(3)
-            TD_TREE_LEVEL(4)
-            TD_TREE_LEVEL(5)
-#undef TD_TREE_LEVEL
+            wk = kk;
+            // the first holding lane has the winner's key in either case
+            wk = __builtin_amdgcn_readlane(wk, __ffsll(static_cast<long long>(hold)) - 1);
         }
         // every lane holds the winner: make that explicit (scalar registers),
         // so that the loop's exits and counters are uniform

@@ -1143,7 +1143,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     const T *__restrict__ v_tree, const uint64_t *__restrict__ mask,
     const int32_t *__restrict__ n_nodes, int batch, int nq_max, int hq, int hkv, int group, int n_rg,
     int chunk, float scale2, const float *__restrict__ ws, int64_t prow_total, T *__restrict__ out,
-    int n_blocks, AcceptArgs accept) {
+    int n_blocks, int nch_max, AcceptArgs accept) {
     constexpr int kSlice = D / 8;  // dims per lane group
     const int rows_per_bg = group * nq_max;
     if constexpr (ACC) {
@@ -1180,7 +1180,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     }
     // row (b, g, r) of this lane (of its lane group when R = 8); `store`:
     // a real row (a lane group past the last row repeats one, unstored)
-    auto combine_row = [&](int b, int g, int r, bool store) __attribute__((always_inline)) {
+    auto combine_row = [&](int b, int g, int r, bool store, auto one_seq) __attribute__((always_inline)) {
+        constexpr bool kOne = decltype(one_seq)::value;
         const int i = r / group;
         const int h = g * group + r % group;
         T *orow = out + ((static_cast<int64_t>(b) * nq_max + i) * hq + h) * D + slice * kSlice;
@@ -1199,10 +1200,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd) mw[wd] = wd < words ? mrow[wd] : 0;
 
-        // first chunk and chunk count of sequence b (left by the split kernel)
-        const int2 si = batch == 1 ? si0 : seqinfo[b];
-        const int64_t cb = si.x;
+        // first chunk and chunk count of sequence b (left by the split kernel).
+        // One sequence: its chunks start at 0 and number at most nch_max
+        // (known on the host), so the partials' loads go out with the record
+        // and the chunks past its count are dropped below.
+        const int2 si = kOne ? si0 : seqinfo[b];
         const int nch = si.y;
+        const int64_t cb = kOne ? 0 : si.x;
+        const int nch_l = kOne ? nch_max : nch;
         const int rg = r / kRowsPerGroup;
         const int rr = r % kRowsPerGroup;
         const float *wm = ws;
@@ -1217,12 +1222,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
         float acc[kSlice];
 #pragma unroll
         for (int k = 0; k < kSlice; ++k) acc[k] = 0.f;
-        for (int c0 = 0; c0 < nch; c0 += kCG * kCB) {
+        for (int c0 = 0; c0 < nch_l; c0 += kCG * kCB) {
             float mv[kCB], lv[kCB];
             f32x4 ov[kCB][kSlice / 4];
 #pragma unroll
             for (int u = 0; u < kCB; ++u) {
-                const int cc = min(c0 + cg + kCG * u, nch - 1);  // in range; repeats are dropped below
+                const int cc = min(c0 + cg + kCG * u, nch_l - 1);  // in range; repeats are dropped below
                 const int64_t pr = prow_index(cb + cc, g, rg, rr, hkv, n_rg);
                 mv[u] = wm[pr];
                 lv[u] = wl[pr];
@@ -1232,8 +1237,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
             }
             // Branch-free on purpose: every loaded value is used, so the
             // compiler keeps all of a trip's loads in flight together instead of
-            // sinking the O loads behind the m loads.  Repeated and empty chunks
-            // get weight 0 (every partial read here was written, so finite).
+            // sinking the O loads behind the m loads.  Repeated, empty and (one
+            // sequence) never-written chunks are selected away, not weighted by
+            // 0: a slot past the sequence's chunks may hold anything.
             float mb = M;
 #pragma unroll
             for (int u = 0; u < kCB; ++u) mb = fmaxf(mb, c0 + cg + kCG * u < nch ? mv[u] : -INFINITY);
@@ -1246,11 +1252,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
             for (int u = 0; u < kCB; ++u) {
                 const bool use = c0 + cg + kCG * u < nch && mv[u] != -INFINITY;
                 const float f = use ? __builtin_amdgcn_exp2f(mv[u] - base) : 0.f;
-                Lsum += f * lv[u];
+                Lsum += use ? f * lv[u] : 0.f;
 #pragma unroll
                 for (int k4 = 0; k4 < kSlice / 4; ++k4)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[4 * k4 + e] += f * ov[u][k4][e];
+                    for (int e = 0; e < 4; ++e) acc[4 * k4 + e] += use ? f * ov[u][k4][e] : 0.f;
             }
             M = mb;
         }
@@ -1343,13 +1349,25 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
     const uint32_t step = static_cast<uint32_t>(n_blocks) * kCombineRows * R;
     const uint32_t first = (blockIdx.x * kCombineRows + (threadIdx.x >> 6)) * R;
     if (batch == 1) {  // one sequence: no sums to share
-        if (nn0 < 0) return;  // a tree build that gave up: no rows
-        const uint32_t total = static_cast<uint32_t>(hq) * (min(nn0, nq_max - 1) + 1);
-        const uint32_t rows_g = static_cast<uint32_t>(group) * (min(nn0, nq_max - 1) + 1);
+        // the root's rows (node 0 of every head) need no tree size: their
+        // loads go out before it arrives; a tree build that gave up
+        // (n_nodes < 0) has no rows, so nothing is stored then
+        const uint32_t roots = static_cast<uint32_t>(hq);
+        for (uint32_t t0 = first; t0 < roots; t0 += step) {
+            const uint32_t t = min(t0 + sub, roots - 1);
+            combine_row(0, static_cast<int>(t / group), static_cast<int>(t % group),
+                        t0 + sub < roots && nn0 >= 0, std::true_type{});
+        }
+        if (nn0 <= 0) return;
+        // then nodes 1 .. n: row r = group i + head offset of KV head g
+        const uint32_t n1 = static_cast<uint32_t>(min(nn0, nq_max - 1));
+        const uint32_t rows_g = static_cast<uint32_t>(group) * n1;
+        const uint32_t total = static_cast<uint32_t>(hkv) * rows_g;
         for (uint32_t t0 = first; t0 < total; t0 += step) {
             const uint32_t t = min(t0 + sub, total - 1);
             const uint32_t g = t / rows_g;
-            combine_row(0, static_cast<int>(g), static_cast<int>(t - g * rows_g), t0 + sub < total);
+            combine_row(0, static_cast<int>(g), group + static_cast<int>(t - g * rows_g), t0 + sub < total,
+                        std::true_type{});
         }
         return;
     }
@@ -1403,7 +1421,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
         const uint32_t rest = t - pre[b];
         const uint32_t rows_g = static_cast<uint32_t>(group) * (min(n_nodes[b], nq_max - 1) + 1);
         const uint32_t g = rest / rows_g;
-        combine_row(b, static_cast<int>(g), static_cast<int>(rest - g * rows_g), t0 + sub < total);
+        combine_row(b, static_cast<int>(g), static_cast<int>(rest - g * rows_g), t0 + sub < total,
+                    std::false_type{});
     }
 }
 
@@ -1465,6 +1484,8 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
 #undef TD_SPLIT_BF_2
 #undef TD_SPLIT_BF2
     const int rpw = combine_rows_per_wave(pl.n_chunks, batch);
+    // one sequence: at most n_chunks - 1 chunks (the plan adds one per sequence)
+    const int nch_max = batch == 1 ? static_cast<int>(std::max<int64_t>(1, pl.n_chunks - 1)) : 0;
     const int blocks = combine_blocks(static_cast<int64_t>(batch) * hkv * pl.group * nq_max, rpw);
 #define TD_COMBINE(ACC, NB, ARGS)                                                                \
     if (rpw == 8) TD_COMBINE_R(ACC, 8, NB, ARGS);                                                \
@@ -1475,7 +1496,7 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
                        static_cast<const T *>(k_tree), static_cast<const T *>(v_tree), mask,      \
                        n_nodes, batch, nq_max, hq, hkv, pl.group, pl.n_rg, pl.chunk, scale2,      \
                        static_cast<const float *>(ws), prow_total, static_cast<T *>(out), blocks, \
-                       ARGS)
+                       nch_max, ARGS)
     if (acc) {
         TD_COMBINE(true, blocks + batch, *acc);
     } else {

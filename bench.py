@@ -274,32 +274,43 @@ def measure(cfg, args, steps, warmup):
     assert int(vs.tree["n_nodes"][0]) == int(tnp["n_nodes"][0])
 
     # ---------------- the step's kernels, timed apart ----------------
-    # Kernel 1 (top-K + tree + mask) alone, and kernels 2-3 (attention +
-    # acceptance) alone, each over the same number of launches.  Two figures:
-    #  - duration: HIP events attached to the kernels' own dispatch
-    #    (td_verify_step_events), one pair per launch, averaged: the
-    #    kernels' execution time as a kernel-trace profiler reports it;
-    #  - loop: graph replays of back-to-back launches between two events on
-    #    the launch stream, divided by the count (includes the launch gaps).
-    def kernel_ms(stages, count):
+    # Two launch units.  With the context split inside the first kernel
+    # (short contexts, few top-K workgroups) the step runs two kernels:
+    # kernel 1 (top-K + tree + mask + context split) and kernel 2 (combine +
+    # accept); otherwise three: kernel 1 (top-K + tree + mask) and kernels
+    # 2-3 (split + combine + accept).  Each unit is timed inside whole steps:
+    #  - duration: HIP events attached to the unit's first and last kernels'
+    #    own dispatch (td_verify_step_kernel_events), one pair per step,
+    #    averaged: the kernels' execution time as a kernel-trace profiler
+    #    reports it;
+    #  - loop (three-kernel steps only): graph replays of back-to-back
+    #    launches of the unit's stage between two events on the launch
+    #    stream, divided by the count (includes the launch gaps).
+    n_kernels = vs.kernels()
+    fused_split = n_kernels == 2
+
+    def kernel_ms(first, last, count):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(count)]
         for a, b_ in evs:            # create the HIP events behind them
             a.record(stream)
             b_.record(stream)
         for i in range(warmup):
-            fused(i, stages)
+            fused(i)
         torch.cuda.synchronize()
         for i, (a, b_) in enumerate(evs):
             vs.args = args_per_set[(warmup + i) % n_sets]
-            vs.run_timed(a, b_, stages=stages)
+            vs.run_kernels_timed(first, last, a, b_)
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(b_) for a, b_ in evs]))
 
-    k1_ms = kernel_ms(td.TD_STEP_DRAFT, steps)
-    k23_ms = kernel_ms(td.TD_STEP_VERIFY, steps)
-    k1_loop_ms = timed(make_runner(td.TD_STEP_DRAFT), steps)
-    k23_loop_ms = timed(make_runner(td.TD_STEP_VERIFY), steps)
+    k1_ms = kernel_ms(0, 0, steps)
+    k23_ms = kernel_ms(1, n_kernels - 1, steps)
+    if fused_split:
+        k1_loop_ms = k23_loop_ms = None
+    else:
+        k1_loop_ms = timed(make_runner(td.TD_STEP_DRAFT), steps)
+        k23_loop_ms = timed(make_runner(td.TD_STEP_VERIFY), steps)
 
     # ---------------- per-stage calls (HIP events, eager) ----------------
     names = ["draft_topk", "build_tree+tree_mask", "tree_verify_attn", "accept"]
@@ -331,11 +342,13 @@ def measure(cfg, args, steps, warmup):
     # (b)+(b'): node arrays (token, parent, depth 4 B; log rho 8 B) + mask rows
     bytes_b = b * nq * (20 + 8 * W)
     # (c): K/V of context and tree read once, q read and out written once
+    bytes_kv_ctx = int((2 * cfg.hkv * cfg.head_dim * esz * L).sum())
     bytes_c = int((2 * cfg.hkv * cfg.head_dim * esz * (L + rows)).sum()
                   + 2 * (rows.sum()) * cfg.hq * cfg.head_dim * esz)
     depth = tnp["node_depth"]
     anc = int(sum((depth[i, :rows[i]] + 1).sum() for i in range(b)))
-    flops_c = int(4 * cfg.hq * cfg.head_dim * (rows * L).sum() + 4 * cfg.hq * cfg.head_dim * anc)
+    flops_ctx = int(4 * cfg.hq * cfg.head_dim * (rows * L).sum())
+    flops_c = flops_ctx + int(4 * cfg.hq * cfg.head_dim * anc)
     ridge = MFMA_BF16_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
     def roofline(kernel, ms, loop_ms, nbytes, nflops):
@@ -351,16 +364,25 @@ def measure(cfg, args, steps, warmup):
                  avg_launch_us=round(ms * 1e3, 2), timing="HIP events on the kernels' dispatch",
                  hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
                  mfma_frac=round(tfs / MFMA_BF16_TFLOPS, 5) if nflops else None,
-                 loop_us_per_launch=round(loop_ms * 1e3, 2))
+                 loop_us_per_launch=None if loop_ms is None else round(loop_ms * 1e3, 2))
         return r
 
-    k1 = roofline("topk_tree (kernel 1: top-K + tree + mask)", k1_ms, k1_loop_ms,
-                  bytes_a + bytes_b, 0)
-    k23 = roofline("attention + acceptance (kernels 2-3)", k23_ms, k23_loop_ms, bytes_c, flops_c)
+    if fused_split:
+        # kernel 1 also reads the context K/V; kernel 2 the tree K/V, q and out
+        u1, u2 = "draft+split", "combine+accept"
+        k1 = roofline("draft+split (kernel 1: top-K + tree + mask + context split)", k1_ms, k1_loop_ms,
+                      bytes_a + bytes_b + bytes_kv_ctx, flops_ctx)
+        k23 = roofline("combine + acceptance (kernel 2)", k23_ms, k23_loop_ms,
+                       bytes_c - bytes_kv_ctx, flops_c - flops_ctx)
+    else:
+        u1, u2 = "topk_tree", "attention+accept"
+        k1 = roofline("topk_tree (kernel 1: top-K + tree + mask)", k1_ms, k1_loop_ms,
+                      bytes_a + bytes_b, 0)
+        k23 = roofline("attention + acceptance (kernels 2-3)", k23_ms, k23_loop_ms, bytes_c, flops_c)
     measured = hbm_traffic(cfg.name)
     if measured:
-        k1["traffic"] = measured.get("topk_tree")
-        k23["traffic"] = measured.get("attention+accept")
+        k1["traffic"] = measured.get(u1)
+        k23["traffic"] = measured.get(u2)
     roof = k1 if k1_ms >= k23_ms else k23
 
     result = {
@@ -381,11 +403,11 @@ def measure(cfg, args, steps, warmup):
                    "n_max": cfg.n_max, "stop": "S(N)" if cfg.use_stop else "fixed",
                    "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": cfg.head_dim,
                    "ctx_total": total_ctx, "n_nodes": [int(v) for v in nn[:8]],
-                   "step": "td_verify_step (3 kernels)", "graph": use_graph, "graph_steps": G,
+                   "step": f"td_verify_step ({n_kernels} kernels)", "graph": use_graph, "graph_steps": G,
                    "input_sets": n_sets, "parallelism": "single GPU"},
         "roofline": roof,
-        "kernels_us": {"topk_tree": round(k1_ms * 1e3, 2), "attention+accept": round(k23_ms * 1e3, 2)},
-        "kernel_roofline": {"topk_tree": k1, "attention+accept": k23},
+        "kernels_us": {u1: round(k1_ms * 1e3, 2), u2: round(k23_ms * 1e3, 2)},
+        "kernel_roofline": {u1: k1, u2: k23},
         "stages_us": {n: round(t * 1e3, 2) for n, t in zip(names, stage_ms)},
         "stage_roofline": {
             "draft_topk": {"bytes": bytes_a, "GB/s": round(bytes_a / (stage_ms[0] * 1e-3) / 1e9, 1)},

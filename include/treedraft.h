@@ -361,7 +361,11 @@ td_status td_lm_head_argmax(const void *hidden_rows, const void *w_lm, const int
  * kernels instead of the five calls' seven: (1) top-K of every position,
  * then, by the last position of each sequence to finish, that sequence's
  * tree and mask rows; (2) the split-KV context attention; (3) the partial
- * merge with the tree keys, and the acceptance walk.  Every result equals
+ * merge with the tree keys, and the acceptance walk.  A call of both stages
+ * with bf16 attention at head dim 128, topk <= 8, short contexts (key
+ * chunks of at most 128 keys: about 4096 context tokens in all at 8 KV
+ * heads) and at most 256 top-K workgroups runs (2) inside (1), as extra
+ * workgroups that wait only for their sequence's tree size: two kernels.  Every result equals
  * what the five calls above produce on the same inputs, into the same
  * output arrays (the fields below use their names, layouts and rules).
  * nq_max = n_max + 1.  target_token [batch][n_max+1] is an input: the
@@ -447,6 +451,26 @@ td_status td_verify_step(const td_step_args *args, void *workspace, size_t works
  */
 td_status td_verify_step_events(const td_step_args *args, void *workspace, size_t workspace_bytes,
                                 void *stream, void *start_event, void *stop_event);
+
+/* ------------------------------------------------------------------------
+ * td_verify_step_kernels -- the number of kernels td_verify_step enqueues
+ * for args (a measurement aid, like the two calls below): 1 for
+ * TD_STEP_DRAFT, 2 for TD_STEP_VERIFY, and for both stages 3, or 2 when the
+ * context split runs inside the first kernel (see td_verify_step).  0 when
+ * the shape fields are invalid.  Reads only the host-side fields.
+ */
+int32_t td_verify_step_kernels(const td_step_args *args);
+
+/* ------------------------------------------------------------------------
+ * td_verify_step_kernel_events -- td_verify_step_events for a range of the
+ * call's kernels (0-based, in launch order): start_event is recorded when
+ * kernel first_kernel begins and stop_event when kernel last_kernel ends,
+ * while the whole step runs as usual.  TD_EINVAL (nothing enqueued) when
+ * 0 <= first_kernel <= last_kernel < td_verify_step_kernels(args) fails.
+ */
+td_status td_verify_step_kernel_events(const td_step_args *args, void *workspace,
+                                       size_t workspace_bytes, void *stream, int32_t first_kernel,
+                                       int32_t last_kernel, void *start_event, void *stop_event);
 
 /* ------------------------------------------------------------------------
  * td_verify_step_noalloc -- td_verify_step for callers that cannot allocate

@@ -25,7 +25,7 @@ def b():
 
 def test_every_declared_symbol_is_exported(b):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     for n in names:
         assert hasattr(b.lib, n), n
     assert sorted(b.EXPORTED) == names
@@ -202,3 +202,45 @@ def test_fit_cost_validation(b):
         b.fit_cost(np.array([1.0, 2.0]), np.array([1.0, 2.0]), 0, 4)
     with pytest.raises(b.TreedraftError):
         b.fit_cost(np.array([1.0, 2.0, 3.0]), np.array([1.0, 2.0, 3.0]), 5, 4)
+
+
+def test_step_kernel_count(b):
+    """td_verify_step_kernels: the context split joins the first kernel for
+    short bf16 contexts at head dim 128 with topk <= 8 and few top-K
+    workgroups, and only when both stages run (host-side fields only)."""
+    a = b.StepArgs()
+    assert b.lib.td_verify_step_kernels(None) == 0
+    assert b.lib.td_verify_step_kernels(ctypes.byref(a)) == 0  # no shape
+    a.batch, a.block, a.vocab, a.pos_stride, a.topk = 1, 16, 151936, 151936, 8
+    a.n_max, a.hq, a.hkv, a.head_dim, a.total_ctx, a.max_ctx = 64, 32, 8, 128, 4096, 4096
+    a.logits_dtype = a.attn_dtype = b.TD_BF16
+    assert b.lib.td_verify_step_kernels(ctypes.byref(a)) == 2
+    a.stages = b.TD_STEP_DRAFT
+    assert b.lib.td_verify_step_kernels(ctypes.byref(a)) == 1
+    a.stages = b.TD_STEP_VERIFY
+    assert b.lib.td_verify_step_kernels(ctypes.byref(a)) == 2
+    a.stages = 4
+    assert b.lib.td_verify_step_kernels(ctypes.byref(a)) == 0
+    a.stages = 0
+    for field, value in (("total_ctx", 8192), ("batch", 64), ("topk", 16), ("head_dim", 64),
+                         ("attn_dtype", b.TD_F32)):
+        old = getattr(a, field)
+        setattr(a, field, value)
+        if field == "batch":
+            a.total_ctx = 64 * 4096
+        assert b.lib.td_verify_step_kernels(ctypes.byref(a)) == 3, field
+        setattr(a, field, old)
+        a.total_ctx = 4096
+    a.logits_dtype = b.TD_F32  # the logits' type does not matter
+    assert b.lib.td_verify_step_kernels(ctypes.byref(a)) == 2
+
+
+def test_step_kernel_events_validation(b):
+    a = b.StepArgs()
+    a.batch, a.block, a.vocab, a.pos_stride, a.topk = 1, 16, 151936, 151936, 8
+    a.n_max, a.hq, a.hkv, a.head_dim, a.total_ctx, a.max_ctx = 64, 32, 8, 128, 4096, 4096
+    a.logits_dtype = a.attn_dtype = b.TD_BF16
+    for first, last in ((-1, 0), (1, 0), (0, 2), (2, 2)):
+        assert b.lib.td_verify_step_kernel_events(ctypes.byref(a), FAKE, 1 << 30, None, first, last,
+                                                  None, None) == 1
+        assert "kernel range" in b.last_error()

@@ -30,7 +30,8 @@ EXPORTED = ["td_abi_version", "td_last_error", "td_draft_topk_workspace", "td_dr
             "td_tree_verify_attn", "td_accept", "td_step_args_bytes", "td_verify_step_workspace",
             "td_verify_step", "td_workspace_status", "td_verify_step_noalloc",
             "td_verify_step_events", "td_kv_commit", "td_flex_budget",
-            "td_verify_layer_workspace", "td_tree_qkv", "td_lm_head_argmax", "td_fit_cost"]
+            "td_verify_layer_workspace", "td_tree_qkv", "td_lm_head_argmax", "td_fit_cost",
+            "td_verify_step_kernels", "td_verify_step_kernel_events"]
 
 
 class StepArgs(ctypes.Structure):
@@ -102,10 +103,14 @@ def _load():
     lib.td_workspace_status.argtypes = [P, c_size_t, P]
     lib.td_verify_step_noalloc.argtypes = [ctypes.POINTER(StepArgs), P]
     lib.td_verify_step_events.argtypes = [ctypes.POINTER(StepArgs), P, c_size_t, P, P, P]
+    lib.td_verify_step_kernels.argtypes = [ctypes.POINTER(StepArgs)]
+    lib.td_verify_step_kernels.restype = c_int32
+    lib.td_verify_step_kernel_events.argtypes = [ctypes.POINTER(StepArgs), P, c_size_t, P, c_int32,
+                                                 c_int32, P, P]
     for name in ("td_draft_topk", "td_build_tree", "td_tree_mask", "td_tree_verify_attn",
                  "td_accept", "td_verify_step", "td_workspace_status", "td_verify_step_noalloc",
                  "td_verify_step_events", "td_kv_commit", "td_tree_qkv",
-                 "td_lm_head_argmax"):
+                 "td_lm_head_argmax", "td_verify_step_kernel_events"):
         getattr(lib, name).restype = c_int
     if lib.td_step_args_bytes() != ctypes.sizeof(StepArgs):
         raise ImportError("td_step_args layout differs between the library and this binding")
@@ -486,6 +491,22 @@ class VerifyStep:
         _check(lib.td_verify_step_events(ctypes.byref(self.args), _ptr(self.workspace),
                                          self.workspace.numel(), _stream(stream),
                                          c_void_p(start.cuda_event), c_void_p(stop.cuda_event)))
+
+    def kernels(self, stages=0):
+        """How many kernels the step enqueues for these arguments (both
+        stages: 2 when the context split runs inside the first kernel, else 3)."""
+        self.args.stages = stages
+        return int(lib.td_verify_step_kernels(ctypes.byref(self.args)))
+
+    def run_kernels_timed(self, first, last, start, stop, stream=None, stages=0):
+        """Enqueue the whole step with torch timing events on its kernels
+        first .. last (0-based, launch order): start.elapsed_time(stop) is
+        their execution time, first start to last end (both events must have
+        been recorded once before, so that their HIP events exist)."""
+        self.args.stages = stages
+        _check(lib.td_verify_step_kernel_events(ctypes.byref(self.args), _ptr(self.workspace),
+                                                self.workspace.numel(), _stream(stream), first, last,
+                                                c_void_p(start.cuda_event), c_void_p(stop.cuda_event)))
 
     def run(self, stream=None, stages=0):
         """Enqueue the step (stages: TD_STEP_DRAFT | TD_STEP_VERIFY, 0 = both)."""

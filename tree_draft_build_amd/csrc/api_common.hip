@@ -62,10 +62,12 @@ extern "C" td_status td_workspace_status(void *workspace, size_t workspace_bytes
         set_error("td_workspace_status: clearing the status word failed: %s", hipGetErrorString(e));
         return TD_EHIP;
     }
-    set_error("a cross-workgroup hand-off gave up waiting (%s%s%s); the workspace was not "
+    set_error("a cross-workgroup hand-off gave up waiting (%s%s%s%s%s); the workspace was not "
               "zero-filled after a shape change, or was shared by overlapping calls",
               (word & kStatusMerge) ? "row merge: lse NaN" : "",
-              (word & kStatusMerge) && (word & kStatusTree) ? ", " : "",
-              (word & kStatusTree) ? "tree build: n_nodes -1" : "");
+              (word & kStatusMerge) && (word & (kStatusTree | kStatusSplit)) ? ", " : "",
+              (word & kStatusTree) ? "tree build: n_nodes -1" : "",
+              (word & kStatusTree) && (word & kStatusSplit) ? ", " : "",
+              (word & kStatusSplit) ? "context split: attention partials not written" : "");
     return TD_ESYNC;
 }

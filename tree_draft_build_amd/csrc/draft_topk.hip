@@ -36,7 +36,9 @@
 // ids and log q = l - lse.
 
 #include <algorithm>
+#include <type_traits>
 
+#include "attn_split.h"
 #include "step_launch.h"
 #include "td_internal.h"
 #include "tree_core.h"
@@ -56,7 +58,6 @@ constexpr int kCandCap = 1024;  // candidates held in LDS (kWaveCap per wave)
 constexpr int kMergeWords = 2304;
 constexpr int kWaveCap = kCandCap / kTopkWaves;  // per wave
 static_assert(kWaveCap % 8 == 0 && kWaveCap >= 32, "regions hold whole groups of 8 keys");
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyTop = 8.f;  // log2 slack of the fast path's reference maximum
 
 // Order key: larger key = larger logit, then smaller id.  -0 becomes +0 first
@@ -394,18 +395,38 @@ __device__ __forceinline__ void load_batch(u32x4 (&w)[kBatch], const u32x4 *vp, 
 // FUSE: the verify step's first kernel.  The row mergers also leave their
 // row's results as tagged words, and the merger of each sequence's last row
 // gathers them and builds that sequence's tree (and mask rows) in wave 0.
+// The workgroup's LDS (the verify step's fused first kernel overlays it with
+// the context split's key buffer).
+struct NoTree {};
+template <int KM, bool FUSE>
+struct TopkLds {
+    float m[kTopkWaves];
+    double s[kTopkWaves];
+    alignas(16) uint64_t cand[kCandCap];
+    float tau[kTopkWaves];
+    bool over[kTopkWaves];
+    alignas(16) uint64_t wtop[kTopkWaves * TD_MAX_TOPK];
+    alignas(16) float live[kTopkWaves];
+    alignas(16) uint64_t heads[kWave];
+    int cnt[kTopkWaves];
+    uint64_t win[KM];
+    uint32_t part[kMergeWords];
+    uint32_t epoch;
+    int fail;
+    double lse;
+    std::conditional_t<FUSE, TreeLds, NoTree> tl;
+};
+
+// Workgroup (slice sp, logit row `row`) of a launch over `rows` rows.
 template <typename T, int KM, bool FUSE, int SLOTS>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict__ logits,
-                                                            int vocab, int64_t pos_stride,
-                                                            int slice, int splits, int K, void *ws,
-                                                            int32_t *__restrict__ topk_id,
-                                                            double *__restrict__ topk_logq,
-                                                            double *__restrict__ lse_out,
-                                                            TreeParams tp, TreeOut to) {
+__device__ __forceinline__ void topk_body(const T *__restrict__ logits, int vocab, int64_t pos_stride,
+                                          int slice, int splits, int K, void *ws,
+                                          int32_t *__restrict__ topk_id,
+                                          double *__restrict__ topk_logq,
+                                          double *__restrict__ lse_out, const TreeParams &tp,
+                                          const TreeOut &to, int sp, int row, int rows,
+                                          TopkLds<KM, FUSE> &L) {
     constexpr int N = Vec<T>::N;
-    const int sp = blockIdx.x;
-    const int row = blockIdx.y;
-    const int rows = gridDim.y;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
@@ -415,20 +436,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     const TopkWs W = topk_ws(ws, rows, static_cast<int64_t>(rows) * splits, K);
     const int PW = part_words(K);
 
-    __shared__ float sm_m[kTopkWaves];
-    __shared__ double sm_s[kTopkWaves];
-    __shared__ __align__(16) uint64_t sm_cand[kCandCap];
-    __shared__ float sm_tau[kTopkWaves];
-    __shared__ bool sm_over[kTopkWaves];
-    __shared__ __align__(16) uint64_t sm_wtop[kTopkWaves * TD_MAX_TOPK];
-    __shared__ __align__(16) float sm_live[kTopkWaves];
+    float(&sm_m)[kTopkWaves] = L.m;
+    double(&sm_s)[kTopkWaves] = L.s;
+    uint64_t(&sm_cand)[kCandCap] = L.cand;
+    float(&sm_tau)[kTopkWaves] = L.tau;
+    bool(&sm_over)[kTopkWaves] = L.over;
+    uint64_t(&sm_wtop)[kTopkWaves * TD_MAX_TOPK] = L.wtop;
+    float(&sm_live)[kTopkWaves] = L.live;
     static_assert(kTopkWaves == 4, "the live bounds are read as one 16-byte vector");
-    __shared__ __align__(16) uint64_t sm_heads[kWave];
-    __shared__ int sm_cnt[kTopkWaves];
-    __shared__ uint64_t sm_win[KM];
-    __shared__ uint32_t sm_part[kMergeWords];
-    __shared__ uint32_t sm_epoch;
-    __shared__ int sm_fail;
+    uint64_t(&sm_heads)[kWave] = L.heads;
+    int(&sm_cnt)[kTopkWaves] = L.cnt;
+    uint64_t(&sm_win)[KM] = L.win;
+    uint32_t(&sm_part)[kMergeWords] = L.part;
+    uint32_t &sm_epoch = L.epoch;
+    int &sm_fail = L.fail;
 
     LaneAcc acc;
     acc.init();
@@ -810,7 +831,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     __syncthreads();
 
     // ---- wave 1: the row's normaliser, while wave 0 selects the row's top K ----
-    __shared__ double sm_lse;
+    double &sm_lse = L.lse;
     if (wave == 1) {
         float ml = -INFINITY;
         double ssum = 0.0;
@@ -916,7 +937,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
     if constexpr (FUSE) {
         // leave the row's results for the sequence's tree builder (the merger
         // of the sequence's last row, which keeps its own row in LDS)
-        __shared__ TreeLds tl;
+        TreeLds &tl = L.tl;
         const uint32_t stag = tag;  // every slot of a workspace holds the same epoch
         const int b = row / tp.block;
         const int rl = row - b * tp.block;
@@ -973,6 +994,51 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict_
             raise_status(W.status, kStatusTree);
         }
     }
+}
+
+template <typename T, int KM, bool FUSE, int SLOTS>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const T *__restrict__ logits,
+                                                            int vocab, int64_t pos_stride,
+                                                            int slice, int splits, int K, void *ws,
+                                                            int32_t *__restrict__ topk_id,
+                                                            double *__restrict__ topk_logq,
+                                                            double *__restrict__ lse_out,
+                                                            TreeParams tp, TreeOut to) {
+    __shared__ TopkLds<KM, FUSE> lds;
+    topk_body<T, KM, FUSE, SLOTS>(logits, vocab, pos_stride, slice, splits, K, ws, topk_id, topk_logq,
+                                  lse_out, tp, to, blockIdx.x, blockIdx.y, gridDim.y, lds);
+}
+
+// ---------------------------------------------------------------------------
+// The verify step's first kernel with the context split folded in: one
+// launch fewer, and the split's loads and first row groups run while the
+// draft is still being selected.  Workgroups 0 .. topk_wgs - 1 are the top-K
+// and tree workgroups (slice sp of row r at index r * splits + sp, the order
+// of the two-dimensional launch, so every hand-off still waits only on
+// lower indices); the others are split work items, which wait only for the
+// tree builders' size words.  The two roles share the LDS, so two
+// workgroups fit a compute unit.
+// ---------------------------------------------------------------------------
+template <int KM, int D>
+union DraftSplitLds {
+    TopkLds<KM, true> t;
+    FusedSplitLds<D> s;
+};
+
+template <typename T, int KM, int SLOTS, int D>
+__global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(
+    const T *__restrict__ logits, int vocab, int64_t pos_stride, int slice, int splits, int rows, int K,
+    void *ws, int32_t *__restrict__ topk_id, double *__restrict__ topk_logq, double *__restrict__ lse_out,
+    TreeParams tp, TreeOut to, int topk_wgs, SplitArgs sa) {
+    static_assert(kTopkThreads == kAttnThreads, "one workgroup size for both roles");
+    __shared__ DraftSplitLds<KM, D> lds;
+    const int wg = blockIdx.x;
+    if (wg < topk_wgs) {
+        topk_body<T, KM, true, SLOTS>(logits, vocab, pos_stride, slice, splits, K, ws, topk_id, topk_logq,
+                                      lse_out, tp, to, wg % splits, wg / splits, rows, lds.t);
+        return;
+    }
+    fused_split<D>(sa, wg - topk_wgs, lds.s);
 }
 
 // Split plan.  When every row can be cut into slices of at most kOneRound
@@ -1079,6 +1145,68 @@ void launch_topk_tree(const void *logits, td_dtype dtype, int batch, int block, 
                                 lse, tp, to, st);
         break;
     }
+}
+
+// The fused first kernel serves steps whose split chunks fit its one buffer
+// (short contexts: one chunk of at most kFusedKeys keys per work item) and
+// whose top-K takes at most one workgroup per compute unit, with bf16
+// attention at head dim 128 and K <= 8; the others keep the split kernel.
+bool step_fuses_split(int batch, int block, int vocab, int K, int nq_max, int hq, int hkv, int head_dim,
+                      int64_t total_ctx, td_dtype attn_dtype) {
+    if (attn_dtype != TD_BF16 || head_dim != 128 || K > 8) return false;
+    const int64_t rows = static_cast<int64_t>(batch) * block;
+    const TopkPlan tk = topk_plan(rows, vocab, K);
+    if (rows * tk.splits > kCUs) return false;
+    const AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, Sub<uint16_t>::CH);
+    return pl.chunk == kFusedKeys && pl.items <= 2 * kCUs;
+}
+
+void launch_topk_tree_split(const void *logits, td_dtype dtype, int batch, int block, int vocab,
+                            int64_t pos_stride, int K, void *ws, int32_t *topk_id, double *topk_logq,
+                            double *lse, const TreeParams &tp, const TreeOut &to, const SplitInputs &si,
+                            hipStream_t st) {
+    const int rows = batch * block;
+    const TopkPlan tk = topk_plan(rows, vocab, K);
+    const AttnPlan pl = attn_plan(batch, si.nq_max, si.hq, si.hkv, si.total_ctx, Sub<uint16_t>::CH);
+    SplitArgs sa;
+    sa.q = static_cast<const uint16_t *>(si.q);
+    sa.k_ctx = static_cast<const uint16_t *>(si.k_ctx);
+    sa.v_ctx = static_cast<const uint16_t *>(si.v_ctx);
+    sa.ctx_offsets = si.off;
+    sa.ctx_lengths = si.lens;
+    sa.ready = to.ready;
+    sa.status = static_cast<uint32_t *>(ws);
+    sa.batch = batch;
+    sa.nq_max = si.nq_max;
+    sa.hq = si.hq;
+    sa.hkv = si.hkv;
+    sa.group = pl.group;
+    sa.n_rg = pl.n_rg;
+    sa.chunk = pl.chunk;
+    sa.scale2 = si.scale * kLog2e;
+    sa.ws = static_cast<float *>(si.ws);
+    sa.prow_total = split_prow_total(pl, si.hkv);
+    sa.seqinfo = split_seqinfo(si.ws, pl, si.hkv, 128);
+    const int topk_wgs = rows * tk.splits;
+    const dim3 grid(static_cast<unsigned>(topk_wgs + pl.items));
+#define TD_FUSED(TT, KMM, SL)                                                                      \
+    TD_LAUNCH((topk_split_kernel<TT, KMM, SL, 128>), grid, dim3(kTopkThreads), 0, st,             \
+              static_cast<const TT *>(logits), vocab, pos_stride, tk.slice, tk.splits, rows, K, ws, \
+              topk_id, topk_logq, lse, tp, to, topk_wgs, sa)
+#define TD_FUSED_SL(TT, KMM)                                                                       \
+    switch (tree_slots(tp.n_max)) {                                                                \
+    case 1: TD_FUSED(TT, KMM, 1); break;                                                           \
+    case 2: TD_FUSED(TT, KMM, 2); break;                                                           \
+    case 4: TD_FUSED(TT, KMM, 4); break;                                                           \
+    default: TD_FUSED(TT, KMM, 8); break;                                                          \
+    }
+    if (dtype == TD_BF16) {
+        if (K <= 4) { TD_FUSED_SL(uint16_t, 4) } else { TD_FUSED_SL(uint16_t, 8) }
+    } else {
+        if (K <= 4) { TD_FUSED_SL(float, 4) } else { TD_FUSED_SL(float, 8) }
+    }
+#undef TD_FUSED_SL
+#undef TD_FUSED
 }
 
 }  // namespace td

@@ -18,6 +18,7 @@ struct TreeOut;
 constexpr size_t kStatusBytes = 16;
 constexpr uint32_t kStatusMerge = 1u;  // a row merger gave up (lse NaN)
 constexpr uint32_t kStatusTree = 2u;   // a tree builder gave up (n_nodes -1)
+constexpr uint32_t kStatusSplit = 4u;  // a context-split workgroup gave up waiting for its tree size
 
 // children per node of the tree builders: branch in 1..K, else K
 inline int tree_branch(int branch, int K) { return branch >= 1 && branch <= K ? branch : K; }
@@ -32,6 +33,25 @@ void launch_topk_tree(const void *logits, td_dtype dtype, int batch, int block, 
                       int64_t pos_stride, int K, void *ws, int32_t *topk_id, double *topk_logq,
                       double *lse, const TreeParams &tp, const TreeOut &to, hipStream_t st);
 
+// Context-attention inputs of the verify step's fused first kernel (bf16,
+// head dim 128); ws is the attention part of the step workspace.
+struct SplitInputs {
+    const void *q, *k_ctx, *v_ctx;
+    const int64_t *off, *lens;
+    int64_t total_ctx;
+    int nq_max, hq, hkv;
+    float scale;
+    void *ws;
+};
+// Whether the verify step runs its context split inside the first kernel.
+bool step_fuses_split(int batch, int block, int vocab, int K, int nq_max, int hq, int hkv, int head_dim,
+                      int64_t total_ctx, td_dtype attn_dtype);
+// The first kernel with the context split (TreeOut::ready must be set).
+void launch_topk_tree_split(const void *logits, td_dtype dtype, int batch, int block, int vocab,
+                            int64_t pos_stride, int K, void *ws, int32_t *topk_id, double *topk_logq,
+                            double *lse, const TreeParams &tp, const TreeOut &to, const SplitInputs &si,
+                            hipStream_t st);
+
 // Tree attention; with accept_* set, the combine kernel also runs the
 // acceptance walk of every sequence.
 // With commit set, the acceptance workgroup of each sequence then appends the
@@ -42,6 +62,7 @@ struct AcceptArgs {
     int32_t *accept_len, *accept_path, *bonus_token;
     int commit;
     CommitArgs cm;
+    uint64_t *ready;  // [batch] tree-size words of the fused first kernel, cleared here (or null)
 };
 size_t attn_workspace_bytes(int batch, int nq_max, int hq, int hkv, int head_dim,
                             int64_t total_ctx, td_dtype dtype);
@@ -49,7 +70,7 @@ void launch_attention(const void *q, const void *k_ctx, const void *v_ctx, const
                       const int64_t *lens, int64_t total_ctx, const void *k_tree, const void *v_tree,
                       const uint64_t *mask, const int32_t *n_nodes, int batch, int nq_max, int hq,
                       int hkv, int head_dim, float scale, td_dtype dtype, void *ws, void *out,
-                      const AcceptArgs *acc, hipStream_t st);
+                      const AcceptArgs *acc, hipStream_t st, bool split = true);
 
 // Argument checks shared by the per-stage entry points and the fused step
 // (they record td_last_error text and return the status).

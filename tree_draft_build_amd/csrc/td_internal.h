@@ -40,19 +40,24 @@ inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s);
 // td_verify_step_events for the duration of one call): the first launch
 // records `start` when it begins executing, every launch records `stop` when
 // it ends, so the last launch's end stands.  Both null: plain launches.
+// Events attached to the calling thread's next launches: start to launch
+// `first` and stop to launches first .. last (the last one recorded counts);
+// `next` numbers the launches made meanwhile.
 struct LaunchEvents {
     hipEvent_t start, stop;
+    int first, last, next;
 };
 extern thread_local LaunchEvents t_launch_events;
 
 // hipLaunchKernelGGL, with the thread's launch events attached when set.
 #define TD_LAUNCH(KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                      \
     do {                                                                                       \
-        if (::td::t_launch_events.start || ::td::t_launch_events.stop) {                       \
-            hipEvent_t td_start_ = ::td::t_launch_events.start;                               \
-            ::td::t_launch_events.start = nullptr;                                             \
-            hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, td_start_,               \
-                                  ::td::t_launch_events.stop, 0, __VA_ARGS__);                 \
+        ::td::LaunchEvents &td_ev_ = ::td::t_launch_events;                                    \
+        const int td_i_ = td_ev_.start || td_ev_.stop ? td_ev_.next++ : -1;                    \
+        hipEvent_t td_a_ = td_i_ == td_ev_.first ? td_ev_.start : nullptr;                     \
+        hipEvent_t td_b_ = td_i_ >= td_ev_.first && td_i_ <= td_ev_.last ? td_ev_.stop : nullptr; \
+        if (td_a_ || td_b_) {                                                                  \
+            hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, td_a_, td_b_, 0, __VA_ARGS__); \
         } else {                                                                               \
             hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);               \
         }                                                                                      \

@@ -29,6 +29,7 @@ constexpr uint32_t kEmptyKey = 0xffffffffu;
 // Token ids fit in 18 bits (TD_MAX_VOCAB = 2^18); the frontier key packs them
 // so, and the builders mask the ids they load with this before packing.
 constexpr uint32_t kTokenMask = 0x3ffffu;
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e): exponentials are taken in base 2
 
 // LDS ordering inside one wavefront: LDS operations of a wave complete in
 // issue order; this keeps the compiler from moving them and waits for them.
@@ -76,6 +77,11 @@ struct TreeOut {
     int32_t *n_nodes, *node_token, *node_parent, *node_depth;
     double *node_logrho, *ahat, *speedup;  // ahat / speedup may be null
     uint64_t *mask;                        // null: no mask rows
+    // Non-null in the verify step's fused first kernel: word b receives
+    // (1 << 32) | n of sequence b as soon as its tree size n is final, for
+    // the context-split workgroups of the same launch; the step's last
+    // kernel clears it again.
+    uint64_t *ready;
 };
 
 // LDS of one tree build: the top-K tables and the inserted nodes
@@ -270,6 +276,9 @@ __device__ __forceinline__ void build_tree_wave(TreeLds &t, const TreeParams &P,
             put(count++, wl + t.lq[j], pack_key(depth + 1, t.ids[j], n), 0, wl);
         }
     }
+    if (o.ready && lane == 0)  // one 8-byte word: the size is never seen without its flag
+        __hip_atomic_store(o.ready + b, (uint64_t{1} << 32) | static_cast<uint32_t>(n), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     wave_lds_sync();
     if (!stop) {  // A_hat(n) and S(n) of the tree built (sum in any order: float64)
         double part = 0.0;

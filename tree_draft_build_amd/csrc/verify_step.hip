@@ -1,5 +1,5 @@
 // td_verify_step: the verify step of budget-aware tree speculative decoding
-// (BASTION, "Methodik" §1-§3) as three kernels.  Kernel boundaries cost a few
+// (BASTION, "Methodik" §1-§3) as three kernels, or two.  Kernel boundaries cost a few
 // microseconds each on this GPU, which at batch 1 is as much as the stages'
 // own memory time, so the step fuses what the five stage calls keep apart:
 //   1. top-K of every position; the last position of each sequence to finish
@@ -7,6 +7,10 @@
 //   2. split-KV context attention;
 //   3. partial merge with the ancestor-masked tree keys, plus the acceptance
 //      walk of every sequence.
+// For short contexts (chunks of at most 128 keys) and a top-K of at most one
+// workgroup per compute unit, kernel 2's work items join kernel 1 as extra
+// workgroups: they load their keys and compute while the draft is selected,
+// and wait only for their sequence's tree size.
 // The device code is the stage calls' own.
 
 #include <algorithm>
@@ -22,8 +26,19 @@ namespace {
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// The workspace: the top-K part (status word, hand-off words), the tree-size
+// words of the fused first kernel (one per sequence), then the attention
+// partials.
+size_t ready_offset(const td_step_args *a) {
+    return topk_workspace_bytes(a->batch, a->block, a->vocab, a->topk);
+}
 size_t topk_part(const td_step_args *a) {
-    return round_up(topk_workspace_bytes(a->batch, a->block, a->vocab, a->topk), 256);
+    return round_up(ready_offset(a) + static_cast<size_t>(a->batch) * 8, 256);
+}
+
+bool fuses_split(const td_step_args *a) {
+    return step_fuses_split(a->batch, a->block, a->vocab, a->topk, a->n_max + 1, a->hq, a->hkv,
+                            a->head_dim, a->total_ctx, a->attn_dtype);
 }
 
 }  // namespace
@@ -101,14 +116,25 @@ td_status launch_step(const td_step_args *a, void *workspace, void *stream) {
     const int nq_max = a->n_max + 1;
     hipStream_t s = as_stream(stream);
     char *ws = static_cast<char *>(workspace);
+    uint64_t *ready = reinterpret_cast<uint64_t *>(ws + ready_offset(a));
+    // both stages in one call: the context split may join the first kernel
+    const bool fuse = draft && verify && fuses_split(a);
     if (draft) {
         const TreeParams tp{a->block, a->topk, a->n_max, a->use_stop, a->cost_a, a->cost_b,
                             a->cost_c, a->cost_knee, a->l_ar, a->ahat0, a->root_token,
                             tree_branch(a->branch, a->topk), a->min_logrho};
         const TreeOut to{a->n_nodes, a->node_token, a->node_parent, a->node_depth,
-                         a->node_logrho, a->ahat, a->speedup, a->mask};
-        launch_topk_tree(a->logits, a->logits_dtype, a->batch, a->block, a->vocab, a->pos_stride,
-                         a->topk, ws, a->topk_id, a->topk_logq, a->lse, tp, to, s);
+                         a->node_logrho, a->ahat, a->speedup, a->mask, fuse ? ready : nullptr};
+        if (fuse) {
+            const SplitInputs si{a->q, a->k_ctx, a->v_ctx, a->ctx_offsets, a->ctx_lengths, a->total_ctx,
+                                 nq_max, a->hq, a->hkv, a->scale, ws + topk_part(a)};
+            launch_topk_tree_split(a->logits, a->logits_dtype, a->batch, a->block, a->vocab,
+                                   a->pos_stride, a->topk, ws, a->topk_id, a->topk_logq, a->lse, tp,
+                                   to, si, s);
+        } else {
+            launch_topk_tree(a->logits, a->logits_dtype, a->batch, a->block, a->vocab, a->pos_stride,
+                             a->topk, ws, a->topk_id, a->topk_logq, a->lse, tp, to, s);
+        }
     }
     if (verify) {
         AcceptArgs acc{a->node_token, a->node_parent, a->target_token, a->n_max, a->block,
@@ -122,9 +148,11 @@ td_status launch_step(const td_step_args *a, void *workspace, void *stream) {
                                 a->ctx_offsets, a->ctx_lengths, a->next_root, nq_max,
                                 a->hkv * a->head_dim * esz / 16};
         }
+        acc.ready = ready;
         launch_attention(a->q, a->k_ctx, a->v_ctx, a->ctx_offsets, a->ctx_lengths, a->total_ctx, a->k_tree,
                          a->v_tree, a->mask, a->n_nodes, a->batch, nq_max, a->hq, a->hkv,
-                         a->head_dim, a->scale, a->attn_dtype, ws + topk_part(a), a->out, &acc, s);
+                         a->head_dim, a->scale, a->attn_dtype, ws + topk_part(a), a->out, &acc, s,
+                         !fuse);
     }
     return check_launch("td_verify_step");
 }
@@ -146,12 +174,38 @@ extern "C" td_status td_verify_step(const td_step_args *a, void *workspace, size
     return launch_step(a, workspace, stream);
 }
 
+extern "C" int32_t td_verify_step_kernels(const td_step_args *a) {
+    if (!a || td_verify_step_workspace(a) == 0) return 0;
+    const int stages = a->stages == 0 ? (TD_STEP_DRAFT | TD_STEP_VERIFY) : a->stages;
+    if (stages & ~(TD_STEP_DRAFT | TD_STEP_VERIFY)) return 0;
+    const bool draft = stages & TD_STEP_DRAFT;
+    const bool verify = stages & TD_STEP_VERIFY;
+    if (draft && verify && fuses_split(a)) return 2;
+    return (draft ? 1 : 0) + (verify ? 2 : 0);
+}
+
 extern "C" td_status td_verify_step_events(const td_step_args *a, void *workspace,
                                            size_t workspace_bytes, void *stream, void *start_event,
                                            void *stop_event) {
-    t_launch_events = {static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+    t_launch_events = {static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event), 0,
+                       0x7fffffff, 0};
     const td_status st = td_verify_step(a, workspace, workspace_bytes, stream);
-    t_launch_events = {nullptr, nullptr};
+    t_launch_events = {};
+    return st;
+}
+
+extern "C" td_status td_verify_step_kernel_events(const td_step_args *a, void *workspace,
+                                                  size_t workspace_bytes, void *stream,
+                                                  int32_t first_kernel, int32_t last_kernel,
+                                                  void *start_event, void *stop_event) {
+    clear_error();
+    const int n = td_verify_step_kernels(a);
+    if (n > 0 && (first_kernel < 0 || last_kernel < first_kernel || last_kernel >= n))
+        return fail(TD_EINVAL, "td_verify_step_kernel_events: kernel range outside the call's kernels");
+    t_launch_events = {static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event),
+                       first_kernel, last_kernel, 0};
+    const td_status st = td_verify_step(a, workspace, workspace_bytes, stream);
+    t_launch_events = {};
     return st;
 }
 

@@ -137,6 +137,12 @@ CONFIGS["tiny_masksens"] = CONFIGS["tiny_fixed"].replace(
 # two sequences of 8 positions with K = 4 (16 slices per row), and four
 # sequences of 16 positions with fewer slices per row (4) than K = 8.
 CONFIGS["two_seq_k4"] = CONFIGS["tiny_fixed"].replace(name="two_seq_k4", index=13, batch=2)
+# Several short ragged contexts at head dim 128 in bf16 (K = 4, GQA 16/4):
+# the verify step then runs the context split inside its first kernel, with
+# trees of 7 row groups per KV head (more than one per wave).
+CONFIGS["fused_ragged"] = CONFIGS["qwen3_8b"].replace(
+    name="fused_ragged", index=15, batch=4, block=4, vocab=32000, topk=4, n_max=24,
+    use_stop=False, hq=16, hkv=4, ctx_law="uniform", ctx_p0=1, ctx_p1=1500, target_seed=104)
 CONFIGS["few_slices"] = CONFIGS["tiny_fixed"].replace(
     name="few_slices", index=14, batch=4, block=16, vocab=65000, logit_dtype="bf16", topk=8,
     spike_lo=0.0, spike_hi=12.0)

@@ -8,11 +8,13 @@ Cache cannot serve a step from the previous one.
 
 Prints one JSON line (rank 0, one GPU):
   value        verify steps per second over the K timed steps
-  roofline     the dominant kernel's algorithmic bytes (or flops) / its
+  roofline     the dominant launch unit's algorithmic bytes (or flops) / its
                average duration, measured with HIP events attached to the
-               kernel's own dispatch (td_verify_step_events) over K launches
-  tree_row     the same shape with the tree fixed at N = 64 (65 query rows):
-               the attention kernels' HBM and MFMA fractions at a full tree
+               kernels' own dispatch inside whole steps
+               (td_verify_step_kernel_events) over K steps.  Units: kernel 1
+               (top-K + tree + mask, plus the context split where it runs
+               there) and the rest of the step
+  tree_row     the same shape with the tree fixed at N = 64 (65 query rows)
   streaming    64 independent sequences of the headline shape per step
   cpu_baseline the CPU oracle timed on a bounded sample of the same workload,
                on all host cores (and on one thread)

@@ -295,13 +295,13 @@ def test_attention_mask_sensitive(td, name):
 @pytest.mark.parametrize("law", ["normal", "mask_sensitive"])
 def test_attention_row_group_paths(td, law):
     """Every tree row of sequences whose trees take each of the split kernel's
-    row-group paths, in a grid of more than two work items per compute unit
-    (8 sequences x 4096 keys x 8 KV heads: 1088 work items), where trees of
-    more than 4 row groups of 16 rows take 5 row groups per wave (the early
-    score MFMAs of the next row group and their hand-over are used from the
-    second row group on): 17, 11, 5, 8 and 4 row groups (n_nodes 64, 40, 16,
-    30, 12), then 13 and 16 (50, 63); one sequence has no tree beyond the
-    root."""
+    row-group paths (8 sequences x 4096 keys x 8 KV heads: 1024-key chunks,
+    320 work items, the 64-key ring), where trees of more than 4 row groups
+    of 16 rows take 3 row groups per wave in row blocks of at most 12:
+    17 row groups (n_nodes 64) in blocks of 9 and 8; 11, 5, 8 and 4
+    (n_nodes 40, 16, 30, 12) in one block; 13 and 16 (50, 63) in two; one
+    sequence has no tree beyond the root.  (Five row groups per wave are
+    checked row by row by the long pipeline case.)"""
     say("attn row-group paths", law)
     cfg = wl.CONFIGS["qwen3_8b"].replace(name="rg5", index=52, batch=8, n_max=64, use_stop=False,
                                          ctx_law="fixed", ctx_p0=4096, attn_law=law)

@@ -1036,9 +1036,10 @@ inline int2 *split_seqinfo(void *ws, const AttnPlan &pl, int hkv, int D) {
 // workgroup runs beside the draft workgroups of the same launch: it loads
 // its chunk into one LDS buffer and the queries of row group `wave` (every
 // query row exists in memory, whatever the tree size), computes that row
-// group over the whole chunk, and only then waits for the sequence's tree
-// size, which the tree builder publishes as one tagged word.  The rows
-// inside the tree are stored; a larger tree continues with row groups
+// group over the whole chunk, stores the root's rows (tree row 0 is in every
+// tree), and only then waits for the sequence's tree size, which the tree
+// builder publishes as one tagged word.  The other rows inside the tree are
+// stored after it; a larger tree continues with row groups
 // wave + 4, wave + 8, ... from the same buffer (their queries loaded one
 // group ahead).  The partials and chunk records are those of
 // attn_split_bf16.
@@ -1117,8 +1118,10 @@ __device__ __forceinline__ void fused_split(const SplitArgs &a, int64_t item, Fu
         st[0].l += xchg_f<5>(st[0].l);
         return st[0];
     };
-    auto put = [&](int rg, const RowState<D> &st, int rows_b) __attribute__((always_inline)) {
-        if (rg * kRowsPerGroup + col >= rows_b) return;
+    // rows lo .. hi - 1 of row group rg
+    auto put = [&](int rg, const RowState<D> &st, int lo, int hi) __attribute__((always_inline)) {
+        const int r = rg * kRowsPerGroup + col;
+        if (r < lo || r >= hi) return;
         const int64_t pr = prow_index(c, g, rg, col, a.hkv, a.n_rg);
         if (h4 == 0) {
             wm[pr] = st.m;
@@ -1136,7 +1139,10 @@ __device__ __forceinline__ void fused_split(const SplitArgs &a, int64_t item, Fu
     __syncthreads();  // every wave's part of the chunk is in LDS
     RowState<D> st0;
     st0.init();
-    if (wave < a.n_rg) st0 = run(qf);
+    if (wave < a.n_rg) {
+        st0 = run(qf);
+        put(wave, st0, 0, a.group);  // the root's rows are in every tree: stored now
+    }
 
     // the tree size (wave 0 polls; the others wait at the barrier)
     if (wave == 0) {
@@ -1156,12 +1162,12 @@ __device__ __forceinline__ void fused_split(const SplitArgs &a, int64_t item, Fu
     if (nn == kNoTree) return;
     const int rows_b = a.group * min(nn + 1, a.nq_max);  // 0 when the build gave up (nn = -1)
     const int n_rg_b = (rows_b + kRowsPerGroup - 1) / kRowsPerGroup;
-    if (wave < n_rg_b) put(wave, st0, rows_b);
+    if (wave < n_rg_b) put(wave, st0, a.group, rows_b);
     for (int rg = wave + kAttnWaves; rg < n_rg_b; rg += kAttnWaves) {
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) qf[0][ks] = qn[0][ks];
         if (rg + kAttnWaves < n_rg_b) load_q(rg + kAttnWaves, qn);
-        put(rg, run(qf), rows_b);
+        put(rg, run(qf), 0, rows_b);
     }
 }
 

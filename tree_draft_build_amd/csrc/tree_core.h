@@ -109,26 +109,23 @@ __host__ __device__ inline int tree_slots(int n_max) {
 // mask row past the root as if beyond the tree (prefill_tree_outputs) and
 // meet this wave at a workgroup barrier before the tree's own entries are
 // written; only entries 0..n are written here then.
-template <int SLOTS, bool PREFILLED = false>
-__device__ __forceinline__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &o, int b, int lane,
-                                int root_tok) {
+template <int SLOTS, bool PREFILLED, bool STOP>
+__device__ __forceinline__ void build_tree_wave_t(TreeLds &t, const TreeParams &P, const TreeOut &o, int b,
+                                                  int lane, int root_tok) {
 #pragma clang fp contract(off)
     const int K = P.K;
-    const bool stop = P.use_stop != 0;
+    constexpr bool stop = STOP;
     // Frontier slots of this lane: log rho, order key, rank among the
-    // siblings, the parent's log rho (the next sibling's score is the
-    // parent's plus its table entry) and, for the stop rule, rho itself,
-    // computed when the entry is pushed so that its latency overlaps the
-    // selections that follow.  Nothing the selection loop reads is in LDS
-    // except the read-only top-K tables.
-    double f_lr[SLOTS], f_plr[SLOTS], f_rho[SLOTS];
+    // siblings and the parent's log rho (the next sibling's score is the
+    // parent's plus its table entry).  Nothing the selection loop reads is
+    // in LDS except the read-only top-K tables.
+    double f_lr[SLOTS], f_plr[SLOTS];
     uint32_t f_key[SLOTS];
     int f_rank[SLOTS];
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
         f_lr[s] = -INFINITY;
         f_plr[s] = 0.0;
-        f_rho[s] = 0.0;
         f_key[s] = kEmptyKey;
         f_rank[s] = 0;
     }
@@ -136,7 +133,6 @@ __device__ __forceinline__ void build_tree_wave(TreeLds &t, const TreeParams &P,
     if (lane == 0) {
         f_lr[0] = t.lq[0];
         f_key[0] = pack_key(1, t.ids[0], 0);
-        f_rho[0] = stop ? exp(t.lq[0]) : 0.0;
     }
     int count = 1;  // entries ever pushed (uniform across lanes)
 
@@ -157,20 +153,24 @@ __device__ __forceinline__ void build_tree_wave(TreeLds &t, const TreeParams &P,
         double bl = f_lr[0];
         uint32_t bk = f_key[0];
         int bs = 0;
+#pragma unroll
+        for (int s = 1; s < SLOTS; ++s)
+            if (precedes(f_lr[s], f_key[s], bl, bk)) {
+                bl = f_lr[s];
+                bk = f_key[s];
+                bs = s;
+            }
+        // The stop rule for this lane's own best entry: A_hat and S with it
+        // inserted (rho = exp(log rho)), computed beside the selection below,
+        // whose winner's values are then taken from its lane.
+        double ah_mine = 0.0, s_mine = 0.0;
+        if constexpr (STOP) {
+            ah_mine = ahat + exp(bl);
+            s_mine = ah_mine * P.l_ar / cost_model(n + 1, P.ca, P.cb, P.cc, P.knee);
+        }
         double wl;
         uint32_t wk;
-        if (n == 0) {
-            // the frontier holds entry 0 alone (lane 0, slot 0)
-            wl = t.lq[0];
-            wk = pack_key(1, t.ids[0], 0);
-        } else {
-#pragma unroll
-            for (int s = 1; s < SLOTS; ++s)
-                if (precedes(f_lr[s], f_key[s], bl, bk)) {
-                    bl = f_lr[s];
-                    bk = f_key[s];
-                    bs = s;
-                }
+        {
             // wave-wide largest log rho (register butterfly on the score
             // alone), then the lanes that hold it: one in general, several
             // only for equal scores, when the smallest key among them wins
@@ -208,26 +208,24 @@ __device__ __forceinline__ void build_tree_wave(TreeLds &t, const TreeParams &P,
 
         // the owner lane (its best slot bs holds the entry) hands over the
         // entry's rank, parent score and rho
-        const bool owner = n == 0 ? lane == 0 : (bk == wk) && (bl == wl);
+        const bool owner = (bk == wk) && (bl == wl);
         int my_rank = f_rank[0];
-        double my_plr = f_plr[0], my_rho = f_rho[0];
+        double my_plr = f_plr[0];
 #pragma unroll
         for (int s = 1; s < SLOTS; ++s)
             if (bs == s) {
                 my_rank = f_rank[s];
                 my_plr = f_plr[s];
-                my_rho = f_rho[s];
             }
         const unsigned long long ob = __ballot(owner);
         const int owner_lane = __ffsll(static_cast<long long>(ob)) - 1;
         const int rank = __builtin_amdgcn_readlane(my_rank, owner_lane);
         const double plr = read_lane_d(my_plr, owner_lane);
 
-        if (stop) {
-            const double ahat_next = ahat + read_lane_d(my_rho, owner_lane);
-            const double s_next = ahat_next * P.l_ar / cost_model(n + 1, P.ca, P.cb, P.cc, P.knee);
+        if constexpr (STOP) {
+            const double s_next = read_lane_d(s_mine, owner_lane);
             if (!(s_next > s_now)) break;
-            ahat = ahat_next;
+            ahat = read_lane_d(ah_mine, owner_lane);
             s_now = s_next;
         }
         // remove the entry
@@ -256,7 +254,6 @@ __device__ __forceinline__ void build_tree_wave(TreeLds &t, const TreeParams &P,
         auto put = [&](int e, double lr, uint32_t key, int rnk, double plr_) __attribute__((always_inline)) {
             const int se = e >> 6;
             const bool mine = lane == (e & (kWave - 1));
-            const double rho = stop ? exp(lr) : 0.0;
 #pragma unroll
             for (int s = 0; s < SLOTS; ++s)
                 if (s == se) {
@@ -264,7 +261,6 @@ __device__ __forceinline__ void build_tree_wave(TreeLds &t, const TreeParams &P,
                     f_key[s] = mine ? key : f_key[s];
                     f_rank[s] = mine ? rnk : f_rank[s];
                     f_plr[s] = mine ? plr_ : f_plr[s];
-                    f_rho[s] = mine ? rho : f_rho[s];
                 }
         };
         if (rank + 1 < P.branch) {
@@ -325,6 +321,17 @@ __device__ __forceinline__ void build_tree_wave(TreeLds &t, const TreeParams &P,
         if (o.ahat) o.ahat[b] = ahat;
         if (o.speedup) o.speedup[b] = s_now;
     }
+}
+
+// Build sequence b's tree (see build_tree_wave_t), with or without the
+// S(N) stop.
+template <int SLOTS, bool PREFILLED = false>
+__device__ __forceinline__ void build_tree_wave(TreeLds &t, const TreeParams &P, const TreeOut &o, int b, int lane,
+                                                int root_tok) {
+    if (P.use_stop != 0)
+        build_tree_wave_t<SLOTS, PREFILLED, true>(t, P, o, b, lane, root_tok);
+    else
+        build_tree_wave_t<SLOTS, PREFILLED, false>(t, P, o, b, lane, root_tok);
 }
 
 // The outputs of sequence b past the root as if beyond the tree (token,

@@ -675,8 +675,9 @@ def decode_row(cfg, args, steps, warmup):
             "tokens_per_step": round(tokens, 3),
             "tokens_per_s": round(tokens * 1e3 / ms, 1),
             "context_growth": [int(v) for v in grown[:4]],
-            "note": "kernels 1-3 per step, the KV commit fused into kernel 3, which also "
-                    "writes the bonus as the next step's root"}
+            "kernels_per_step": vs.kernels(),
+            "note": "one td_verify_step call per step; the KV commit runs in its last kernel, "
+                    "which also writes the bonus as the next step's root"}
 
 
 def _code_tokens(text):

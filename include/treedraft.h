@@ -363,9 +363,10 @@ td_status td_lm_head_argmax(const void *hidden_rows, const void *w_lm, const int
  * tree and mask rows; (2) the split-KV context attention; (3) the partial
  * merge with the tree keys, and the acceptance walk.  A call of both stages
  * with bf16 attention at head dim 128, topk <= 8, short contexts (key
- * chunks of at most 128 keys: about 4096 context tokens in all at 8 KV
- * heads) and at most 256 top-K workgroups runs (2) inside (1), as extra
- * workgroups that wait only for their sequence's tree size: two kernels.  Every result equals
+ * chunks of 128 keys in at most about 512 work items: up to about 8192
+ * context tokens in all at 8 KV heads) and at most 256 top-K workgroups
+ * runs (2) inside (1), as extra workgroups that wait only for their
+ * sequence's tree size: two kernels.  Every result equals
  * what the five calls above produce on the same inputs, into the same
  * output arrays (the fields below use their names, layouts and rules).
  * nq_max = n_max + 1.  target_token [batch][n_max+1] is an input: the

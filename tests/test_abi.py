@@ -222,7 +222,7 @@ def test_step_kernel_count(b):
     a.stages = 4
     assert b.lib.td_verify_step_kernels(ctypes.byref(a)) == 0
     a.stages = 0
-    for field, value in (("total_ctx", 8192), ("batch", 64), ("topk", 16), ("head_dim", 64),
+    for field, value in (("total_ctx", 16384), ("batch", 64), ("topk", 16), ("head_dim", 64),
                          ("attn_dtype", b.TD_F32)):
         old = getattr(a, field)
         setattr(a, field, value)
@@ -232,6 +232,8 @@ def test_step_kernel_count(b):
         setattr(a, field, old)
         a.total_ctx = 4096
     a.logits_dtype = b.TD_F32  # the logits' type does not matter
+    assert b.lib.td_verify_step_kernels(ctypes.byref(a)) == 2
+    a.total_ctx = a.max_ctx = 8192  # 128-key chunks up to about 512 work items
     assert b.lib.td_verify_step_kernels(ctypes.byref(a)) == 2
 
 

@@ -51,19 +51,24 @@ struct AttnPlan {
 // unit, so that each streams one long chunk (every workgroup start and end
 // drains its ring once) and few partials are written.
 constexpr int64_t kAttnItems = 256;
+// The verify step's fused first kernel (the split beside one top-K workgroup
+// per compute unit, two workgroups per unit) keeps 128-key chunks up to
+// about this many work items.
+constexpr int64_t kFusedItems = 512;
 
-inline AttnPlan attn_plan(int batch, int nq_max, int hq, int hkv, int64_t total_ctx, int CH) {
+inline AttnPlan attn_plan(int batch, int nq_max, int hq, int hkv, int64_t total_ctx, int CH,
+                          int64_t aim = kAttnItems) {
     AttnPlan p;
     p.group = hq / hkv;
     p.n_rg = (p.group * nq_max + kRowsPerGroup - 1) / kRowsPerGroup;
     // one row block holds 4 own row groups: as many as the registers allow,
     // so that a chunk's keys stream once for every tree row where they can
     p.own = std::max(1, (p.n_rg + kAttnWaves - 1) / kAttnWaves);
-    // about kAttnItems work items over the context; longer chunks keep the
+    // about `aim` work items over the context; longer chunks keep the
     // partial traffic small when the context is long
     const int64_t work = std::max<int64_t>(1, total_ctx) * hkv;
     int chunk = CH;
-    while (chunk < 32 * CH && work / chunk > kAttnItems) chunk *= 2;
+    while (chunk < 32 * CH && work / chunk > aim) chunk *= 2;
     p.chunk = chunk;
     p.n_chunks = (total_ctx + chunk - 1) / chunk + batch;
     p.items = static_cast<int64_t>(hkv) * p.n_chunks;

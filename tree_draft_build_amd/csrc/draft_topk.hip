@@ -1157,8 +1157,8 @@ bool step_fuses_split(int batch, int block, int vocab, int K, int nq_max, int hq
     const int64_t rows = static_cast<int64_t>(batch) * block;
     const TopkPlan tk = topk_plan(rows, vocab, K);
     if (rows * tk.splits > kCUs) return false;
-    const AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, Sub<uint16_t>::CH);
-    return pl.chunk == kFusedKeys && pl.items <= 2 * kCUs;
+    const AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, Sub<uint16_t>::CH, kFusedItems);
+    return pl.chunk == kFusedKeys && pl.items <= kFusedItems + static_cast<int64_t>(batch) * hkv;
 }
 
 void launch_topk_tree_split(const void *logits, td_dtype dtype, int batch, int block, int vocab,
@@ -1167,7 +1167,7 @@ void launch_topk_tree_split(const void *logits, td_dtype dtype, int batch, int b
                             hipStream_t st) {
     const int rows = batch * block;
     const TopkPlan tk = topk_plan(rows, vocab, K);
-    const AttnPlan pl = attn_plan(batch, si.nq_max, si.hq, si.hkv, si.total_ctx, Sub<uint16_t>::CH);
+    const AttnPlan pl = attn_plan(batch, si.nq_max, si.hq, si.hkv, si.total_ctx, Sub<uint16_t>::CH, kFusedItems);
     SplitArgs sa;
     sa.q = static_cast<const uint16_t *>(si.q);
     sa.k_ctx = static_cast<const uint16_t *>(si.k_ctx);

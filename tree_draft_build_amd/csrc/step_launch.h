@@ -65,7 +65,7 @@ struct AcceptArgs {
     uint64_t *ready;  // [batch] tree-size words of the fused first kernel, cleared here (or null)
 };
 size_t attn_workspace_bytes(int batch, int nq_max, int hq, int hkv, int head_dim,
-                            int64_t total_ctx, td_dtype dtype);
+                            int64_t total_ctx, td_dtype dtype, bool fused_plan = false);
 void launch_attention(const void *q, const void *k_ctx, const void *v_ctx, const int64_t *off,
                       const int64_t *lens, int64_t total_ctx, const void *k_tree, const void *v_tree,
                       const uint64_t *mask, const int32_t *n_nodes, int batch, int nq_max, int hq,

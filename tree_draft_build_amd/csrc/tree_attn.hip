@@ -515,8 +515,9 @@ inline size_t attn_ws_size(const AttnPlan &pl, int batch, int hkv, int D) {
 }  // namespace
 
 size_t attn_workspace_bytes(int batch, int nq_max, int hq, int hkv, int head_dim,
-                            int64_t total_ctx, td_dtype dtype) {
-    const AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, sub_chunk(dtype));
+                            int64_t total_ctx, td_dtype dtype, bool fused_plan) {
+    const AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, sub_chunk(dtype),
+                                  fused_plan ? kFusedItems : kAttnItems);
     return std::max<size_t>(16, attn_ws_size(pl, batch, hkv, head_dim));
 }
 
@@ -525,7 +526,9 @@ void launch_attention(const void *q, const void *k_ctx, const void *v_ctx, const
                       const uint64_t *mask, const int32_t *n_nodes, int batch, int nq_max, int hq,
                       int hkv, int head_dim, float scale, td_dtype dtype, void *ws, void *out,
                       const AcceptArgs *acc, hipStream_t st, bool split) {
-    const AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, sub_chunk(dtype));
+    // without the split, the partials are the fused first kernel's (its plan)
+    const AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, sub_chunk(dtype),
+                                  split ? kAttnItems : kFusedItems);
     const bool bf = dtype == TD_BF16;
 #define TD_ATTN(T, DD)                                                                          \
     launch_attn<T, DD>(q, k_ctx, v_ctx, off, lens, k_tree, v_tree, mask, n_nodes, batch, nq_max, hq, \

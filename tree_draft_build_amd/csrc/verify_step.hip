@@ -59,7 +59,12 @@ extern "C" size_t td_verify_step_workspace(const td_step_args *a) {
                                                               a->head_dim, a->total_ctx, TD_BF16),
                                          attn_workspace_bytes(a->batch, nq_max, a->hq, a->hkv,
                                                               a->head_dim, a->total_ctx, TD_F32));
-    return topk_part(a) + attn;
+    // a call of both stages may run the split in the first kernel, with that
+    // kernel's plan (128-key chunks): room for either plan's partials
+    const size_t fused = fuses_split(a) ? attn_workspace_bytes(a->batch, nq_max, a->hq, a->hkv, a->head_dim,
+                                                               a->total_ctx, a->attn_dtype, true)
+                                        : 0;
+    return topk_part(a) + std::max(attn, fused);
 }
 
 namespace {

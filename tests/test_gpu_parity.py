@@ -317,6 +317,29 @@ def test_attention_row_group_paths(td, law):
                    n_nodes[b0:b1])
 
 
+@pytest.mark.parametrize("law", ["normal", "mask_sensitive"])
+def test_attention_five_group_path(td, law):
+    """The split kernel's five-row-groups-per-wave path on every tree row:
+    64 sequences x 512 keys x 8 KV heads make 96 chunks of 1024 keys, 768
+    work items (more than two per compute unit), so trees of more than 4
+    row groups take 5 per wave on the 64-key ring.  Trees of 17, 11, 5, 8,
+    4, 13, 16 and 1 row groups (n_nodes 64, 40, 16, 30, 12, 50, 63, 0) repeat
+    over the batch; sequences 0-7 and 63 are compared with the oracle."""
+    say("attn five-group path", law)
+    cfg = wl.CONFIGS["qwen3_8b"].replace(name="rg5b", index=53, batch=64, n_max=64, use_stop=False,
+                                         ctx_law="fixed", ctx_p0=512, attn_law=law)
+    inp = wl.make_attn_inputs(cfg)
+    n_nodes = np.resize(np.array([64, 40, 16, 30, 12, 50, 63, 0], np.int32), cfg.batch)
+    par = random_parents(np.random.default_rng(53), n_nodes, cfg.nq_max)
+    got, mask = run_attn(td, cfg, inp, par, n_nodes)
+    for b0, b1 in ((0, 8), (63, 64)):
+        want = oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
+                                inp["k_tree"], inp["v_tree"], mask, n_nodes, cfg.hq, cfg.hkv,
+                                cfg.head_dim, wl.attn_scale(cfg), seqs=(b0, b1))
+        attn_close(got[b0:b1], want, "bf16", f"five-group path {law} seqs {b0}..{b1 - 1}",
+                   n_nodes[b0:b1])
+
+
 # ---------------------------------------------------------------------------
 # end to end: the whole path on the GPU vs the whole path in the oracle
 # ---------------------------------------------------------------------------

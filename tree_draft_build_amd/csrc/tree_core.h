@@ -144,6 +144,18 @@ __device__ __forceinline__ void build_tree_wave_t(TreeLds &t, const TreeParams &
         t.dep[0] = 0;
         t.lr[0] = 0.0;
     }
+    // Inserted node i's record (token, parent, depth, log rho) stays in lane
+    // i % 64, slot i / 64, until the loop ends: no LDS store inside the loop,
+    // so its table reads never queue behind one.
+    int r_tok[SLOTS], r_par[SLOTS], r_dep[SLOTS];
+    double r_lr[SLOTS];
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+        r_tok[s] = 0;
+        r_par[s] = -1;
+        r_dep[s] = 0;
+        r_lr[s] = 0.0;
+    }
 
     while (n < P.n_max) {
         // counters are wave-uniform: say so, keeping the loop's control scalar
@@ -240,11 +252,17 @@ __device__ __forceinline__ void build_tree_wave_t(TreeLds &t, const TreeParams &
         const int token = static_cast<int>((wk >> 8) & 0x3ffffu);
         const int parent = static_cast<int>(wk & 0xffu);
         ++n;
-        if (lane == 0) {  // read back only after the loop
-            t.tok[n] = token;
-            t.par[n] = parent;
-            t.dep[n] = depth;
-            t.lr[n] = wl;
+        {
+            const int rs = n >> 6;  // uniform
+            const bool mine = lane == (n & (kWave - 1));
+#pragma unroll
+            for (int s = 0; s < SLOTS; ++s)
+                if (s == rs) {
+                    r_tok[s] = mine ? token : r_tok[s];
+                    r_par[s] = mine ? parent : r_par[s];
+                    r_dep[s] = mine ? depth : r_dep[s];
+                    r_lr[s] = mine ? wl : r_lr[s];
+                }
         }
 
         // Lazy pushes: next sibling, then first child (none after the last
@@ -263,13 +281,25 @@ __device__ __forceinline__ void build_tree_wave_t(TreeLds &t, const TreeParams &
                     f_plr[s] = mine ? plr_ : f_plr[s];
                 }
         };
-        if (rank + 1 < P.branch) {
-            const int j = (depth - 1) * K + rank + 1;
-            put(count++, plr + t.lq[j], pack_key(depth, t.ids[j], parent), rank + 1, plr);
-        }
-        if (depth < P.block) {
-            const int j = depth * K;
-            put(count++, wl + t.lq[j], pack_key(depth + 1, t.ids[j], n), 0, wl);
+        // both table entries are read at once (an unused one reads entry 0)
+        const bool sib = rank + 1 < P.branch;
+        const bool kid = depth < P.block;
+        const int j_sib = sib ? (depth - 1) * K + rank + 1 : 0;
+        const int j_kid = kid ? depth * K : 0;
+        const double lq_sib = t.lq[j_sib], lq_kid = t.lq[j_kid];
+        const int id_sib = t.ids[j_sib], id_kid = t.ids[j_kid];
+        if (sib) put(count++, plr + lq_sib, pack_key(depth, id_sib, parent), rank + 1, plr);
+        if (kid) put(count++, wl + lq_kid, pack_key(depth + 1, id_kid, n), 0, wl);
+    }
+    // the records of nodes 1..n to LDS (node 0's were written above)
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+        const int i = s * kWave + lane;
+        if (i >= 1 && i <= n) {
+            t.tok[i] = r_tok[s];
+            t.par[i] = r_par[s];
+            t.dep[i] = r_dep[s];
+            t.lr[i] = r_lr[s];
         }
     }
     if (o.ready && lane == 0)  // one 8-byte word: the size is never seen without its flag

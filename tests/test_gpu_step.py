@@ -265,6 +265,30 @@ def test_split_inside_first_kernel_modes(td):
     assert s.status() == td.TD_OK
 
 
+@pytest.mark.parametrize("kw", [dict(logit_dtype="f32"), dict(n_max=100), dict(n_max=200, topk=8),
+                                dict(use_stop=True, n_max=64)])
+def test_split_inside_first_kernel_variants(td, kw):
+    """The two-kernel step beyond the ragged workload's own settings: float32
+    logits, 4 and 8 frontier slots per lane (trees of 101 and 201 rows: 26
+    and 51 row groups per KV head, most of them after the tree size
+    arrives) and the S(N) stop, against the stage calls."""
+    cfg = wl.CONFIGS["fused_ragged"].replace(**kw)
+    print("[case] split inside kernel 1:", kw, flush=True)
+    x, inp, d = inputs(cfg)
+    ref = modular(td, cfg, d, None)
+    tree_np = {k: ref[k].numpy() for k in ("node_token", "node_parent", "n_nodes")}
+    tg = dev(targets_by_path(cfg, wl.logits_as_f64(x, cfg.logit_dtype), tree_np))
+    ref = modular(td, cfg, d, tg)
+    s = make_step(td, cfg, d)
+    assert split_inside(s)
+    s.set_inputs(d["logits"], d["q"], d["k_ctx"], d["v_ctx"], d["off"], d["k_tree"], d["v_tree"], tg)
+    for rep in range(2):
+        s.run()
+        torch.cuda.synchronize()
+        assert_same(ref, step_outputs(s), f"{kw} call {rep}", exact_out=False)
+    assert s.status() == td.TD_OK
+
+
 def test_split_inside_first_kernel_ragged_against_oracle(td):
     """Four sequences of ragged short contexts, one of them empty, through
     the two-kernel step: trees, attention and acceptance against the oracle."""

@@ -572,8 +572,8 @@ def layer_rows(args):
 
 
 def decode_row(cfg, args, steps, warmup):
-    """The verify step in a synthetic decode loop: each step runs kernels 1-3
-    with the commit fused into kernel 3, so the accepted path's keys and
+    """The verify step in a synthetic decode loop: each step is one
+    td_verify_step call with the commit fused into its last kernel, so the accepted path's keys and
     values are appended to the context (which grows in place inside a region
     of room steps * (block + 1) rows) and the bonus token becomes the next
     root; per-step inputs (logits, tree queries and K/V) rotate over 8 sets.
@@ -608,7 +608,7 @@ def decode_row(cfg, args, steps, warmup):
         vc[int(off[b]):int(off[b]) + int(L0[b])] = up(inp0["v_ctx"][o:o + int(L0[b])])
     goff = torch.from_numpy(off).to(dev)
     lens = torch.from_numpy(L0.copy()).to(dev)
-    # kernel 1 reads the root as it starts, kernel 3 of the same step writes
+    # kernel 1 reads the root as it starts, the last kernel of the same step writes
     # the bonus into the same array afterwards: the next step's root
     root = torch.zeros(cfg.batch, dtype=torch.int32, device=dev)
     vs = td.VerifyStep(batch=cfg.batch, block=cfg.block, vocab=cfg.vocab, topk=cfg.topk,

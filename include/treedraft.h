@@ -378,7 +378,7 @@ td_status td_lm_head_argmax(const void *hidden_rows, const void *w_lm, const int
  * every call leaves it ready for the next call of the same shape.  Calls
  * that overlap in time must not share a workspace.  A broken hand-off is
  * reported by td_workspace_status (see there for the sentinels).
- * With commit != 0 the step also performs td_kv_commit (inside kernel 3,
+ * With commit != 0 the step also performs td_kv_commit (inside its last kernel,
  * after each sequence's acceptance walk): ctx_lengths must then be set, and
  * k_ctx / v_ctx are written (rows past each context) as k_cache / v_cache.
  * stages selects the kernels a call enqueues: TD_STEP_DRAFT (kernel 1: top-K,

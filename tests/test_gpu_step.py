@@ -326,6 +326,54 @@ def test_split_inside_first_kernel_ragged_against_oracle(td):
     assert s.status() == td.TD_OK
 
 
+@pytest.mark.parametrize("name", ["qwen3_8b_stress", "two_seq_k4"])
+def test_step_graph_replays(td, name):
+    """Steps captured in a HIP graph (input sets A, B, A), replayed several
+    times with eager steps on set B between the replays: every replay and
+    every eager call gives the stage calls' results (the hand-off words and,
+    in the two-kernel form, the tree-size words are left ready by each call
+    for the next, captured or not)."""
+    from tree_draft_build_amd.binding import StepArgs
+    cfg_a = wl.CONFIGS[name]
+    cfg_b = cfg_a.replace(index=cfg_a.index + 40)
+    print("[case] step graph replays", name, flush=True)
+    sets = []
+    for cfg in (cfg_a, cfg_b):
+        x, inp, d = inputs(cfg)
+        r = modular(td, cfg, d, None)
+        tree_np = {k: r[k].numpy() for k in ("node_token", "node_parent", "n_nodes")}
+        tg = dev(targets_by_path(cfg, wl.logits_as_f64(x, cfg.logit_dtype), tree_np))
+        sets.append((d, tg, modular(td, cfg, d, tg)))
+    (da, _, _), (db, _, _) = sets
+    assert da["total"] == db["total"]
+    s = make_step(td, cfg_a, da)
+    exact = not split_inside(s)
+    args = []
+    for d, tg, _ in sets:
+        s.set_inputs(d["logits"], d["q"], d["k_ctx"], d["v_ctx"], d["off"], d["k_tree"], d["v_tree"], tg)
+        args.append(StepArgs.from_buffer_copy(s.args))
+    keep = [sets[0][0], sets[1][0]]  # the graph reads these buffers
+    s.args = StepArgs.from_buffer_copy(args[0])
+    s.run()                       # outside the capture first: the workspace is in use
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for j in (0, 1, 0):
+            s.args = StepArgs.from_buffer_copy(args[j])
+            s.run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        assert_same(sets[0][2], step_outputs(s), f"{name} replay {rep}", exact)
+        s.args = StepArgs.from_buffer_copy(args[1])
+        s.run()                   # eager work between replays
+        torch.cuda.synchronize()
+        assert_same(sets[1][2], step_outputs(s), f"{name} eager after replay {rep}", exact)
+    assert s.status() == td.TD_OK
+    del keep
+
+
 def _scramble_epochs(ws, nbytes):
     """Every 8-byte word of the first nbytes (past the 16-byte status header)
     set to its own index: the workgroups' epoch words then all differ, so no

@@ -68,8 +68,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by sequence with no exchange; see the design notes)",
+        print(f"bench.py: the verify step runs on one GPU; --gpus {args.gpus} is not supported "
+              "(it would shard by sequence, with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
     import torch

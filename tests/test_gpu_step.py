@@ -86,12 +86,14 @@ def inputs(cfg):
 
 def assert_same(a, b, what, exact_out=True):
     """Every output bit for bit; with exact_out False the attention output
-    within one bf16 rounding step instead (a step whose context split runs
-    inside its first kernel sums each chunk's keys in another order)."""
+    within two bf16 rounding steps instead: a step whose context split runs
+    inside its first kernel sums each chunk's keys in another order, and both
+    forms round their chunk partials' O rows to bf16 (2^-9 each), so the two
+    can differ by the output's own rounding step plus the partials'."""
     for k in a:
         if k == "out" and not exact_out:
             x, y = a[k].float(), b[k].float()
-            assert torch.allclose(x, y, rtol=2.0 ** -7, atol=1e-3), \
+            assert torch.allclose(x, y, rtol=2.0 ** -6, atol=2e-3), \
                 f"{what}: out differs by {(x - y).abs().max().item():.3g}"
         else:
             assert torch.equal(a[k], b[k]), f"{what}: {k} differs"

@@ -165,6 +165,22 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) { return f32_to_bf16(x); }
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 
+// Partial rows of the split (m, l, then O[D] per row, in three regions):
+// m and l in float32; O in bf16 for bf16 attention (half the bytes the
+// combine reads back; its rounding is far below the output's own bf16
+// rounding) and in float32 for float32 attention.
+template <typename T> struct PartialO;
+template <> struct PartialO<uint16_t> { using type = uint16_t; };
+template <> struct PartialO<float> { using type = float; };
+__host__ __device__ constexpr int partial_o_bytes(bool bf16) { return bf16 ? 2 : 4; }
+// four consecutive O values of a partial row
+__device__ __forceinline__ void put_o4(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
+__device__ __forceinline__ void put_o4(uint16_t *p, f32x4 v) {
+    *reinterpret_cast<u32x2 *>(p) =
+        u32x2{static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16),
+              static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16)};
+}
+
 __device__ __forceinline__ int slot_key(int h4, int t) { return t < 4 ? 4 * h4 + t : 12 + 4 * h4 + t; }
 
 // ---------------------------------------------------------------------------
@@ -944,7 +960,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
 
             float *wm = ws;
             float *wl = ws + prow_total;
-            float *wo = ws + 2 * prow_total;
+            uint16_t *wo = reinterpret_cast<uint16_t *>(ws + 2 * prow_total);
             if (!split_mode || kt_step == 1) {
                 // each owned row group is complete in this wave: store its rows
 #pragma unroll
@@ -959,7 +975,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
                     }
 #pragma unroll
                     for (int dt = 0; dt < D / 16; ++dt)
-                        *reinterpret_cast<f32x4 *>(&wo[pr * D + 16 * dt + 4 * h4]) = st[j].o[dt];
+                        put_o4(&wo[pr * D + 16 * dt + 4 * h4], st[j].o[dt]);
                 }
             } else {
                 // split mode: kt_step waves per row group merge through LDS
@@ -1011,8 +1027,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
                     }
 #pragma unroll
                     for (int k = 0; k < kPer; k += 4)
-                        *reinterpret_cast<f32x4 *>(&wo[pr * D + ds + k]) =
-                            f32x4{acc[k], acc[k + 1], acc[k + 2], acc[k + 3]};
+                        put_o4(&wo[pr * D + ds + k], f32x4{acc[k], acc[k + 1], acc[k + 2], acc[k + 3]});
                 }
                 __syncthreads();  // LDS is reused by the next row block
             }
@@ -1026,13 +1041,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
 #undef TD_SUB_VALID
 }
 
-// Partial rows of a plan (the split kernel's output): m, l, then O[D] per row;
-// the per-sequence chunk records follow them.
+// Partial rows of a plan (the split kernel's output): m and l (float32), then
+// O[D] (o_bytes each) per row; the per-sequence chunk records follow them.
 inline int64_t split_prow_total(const AttnPlan &pl, int hkv) {
     return pl.n_chunks * hkv * pl.n_rg * kRowsPerGroup;
 }
-inline int2 *split_seqinfo(void *ws, const AttnPlan &pl, int hkv, int D) {
-    return reinterpret_cast<int2 *>(static_cast<float *>(ws) + split_prow_total(pl, hkv) * (2 + D));
+inline size_t split_partial_bytes(const AttnPlan &pl, int hkv, int D, int o_bytes) {
+    return static_cast<size_t>(split_prow_total(pl, hkv)) * (8 + static_cast<size_t>(D) * o_bytes);
+}
+inline int2 *split_seqinfo(void *ws, const AttnPlan &pl, int hkv, int D, int o_bytes) {
+    return reinterpret_cast<int2 *>(static_cast<char *>(ws) + split_partial_bytes(pl, hkv, D, o_bytes));
 }
 
 // ---------------------------------------------------------------------------
@@ -1113,7 +1131,7 @@ __device__ __forceinline__ void fused_split(const SplitArgs &a, int64_t item, Fu
     const int ntiles = (valid + kKeyTile - 1) / kKeyTile;
     float *wm = a.ws;
     float *wl = a.ws + a.prow_total;
-    float *wo = a.ws + 2 * a.prow_total;
+    uint16_t *wo = reinterpret_cast<uint16_t *>(a.ws + 2 * a.prow_total);
     // one row group (queries qf) over the whole chunk
     auto run = [&](const bf16x8 (&qf)[1][D / 32]) __attribute__((always_inline)) {
         RowState<D> st[1];
@@ -1134,7 +1152,7 @@ __device__ __forceinline__ void fused_split(const SplitArgs &a, int64_t item, Fu
         }
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
-            *reinterpret_cast<f32x4 *>(&wo[pr * D + 16 * dt + 4 * h4]) = st.o[dt];
+            put_o4(&wo[pr * D + 16 * dt + 4 * h4], st.o[dt]);
     };
 
     bf16x8 qf[1][D / 32], qn[1][D / 32];

@@ -1186,7 +1186,7 @@ void launch_topk_tree_split(const void *logits, td_dtype dtype, int batch, int b
     sa.scale2 = si.scale * kLog2e;
     sa.ws = static_cast<float *>(si.ws);
     sa.prow_total = split_prow_total(pl, si.hkv);
-    sa.seqinfo = split_seqinfo(si.ws, pl, si.hkv, 128);
+    sa.seqinfo = split_seqinfo(si.ws, pl, si.hkv, 128, partial_o_bytes(true));
     const int topk_wgs = rows * tk.splits;
     const dim3 grid(static_cast<unsigned>(topk_wgs + pl.items));
 #define TD_FUSED(TT, KMM, SL)                                                                      \

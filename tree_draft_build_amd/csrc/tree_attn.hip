@@ -208,7 +208,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
         const int rr = r % kRowsPerGroup;
         const float *wm = ws;
         const float *wl = ws + prow_total;
-        const float *wo = ws + 2 * prow_total;
+        using PO = typename PartialO<T>::type;
+        const PO *wo = reinterpret_cast<const PO *>(ws + 2 * prow_total);
 
         // context partials: lane group cg takes chunks cg, cg + 8, ...; up to
         // kCB of them per trip with all their loads in flight, merged online
@@ -220,16 +221,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
         for (int k = 0; k < kSlice; ++k) acc[k] = 0.f;
         for (int c0 = 0; c0 < nch_l; c0 += kCG * kCB) {
             float mv[kCB], lv[kCB];
-            f32x4 ov[kCB][kSlice / 4];
+            float ov[kCB][kSlice];
 #pragma unroll
             for (int u = 0; u < kCB; ++u) {
                 const int cc = min(c0 + cg + kCG * u, nch_l - 1);  // in range; repeats are dropped below
                 const int64_t pr = prow_index(cb + cc, g, rg, rr, hkv, n_rg);
                 mv[u] = wm[pr];
                 lv[u] = wl[pr];
-                const f32x4 *op = reinterpret_cast<const f32x4 *>(&wo[pr * D + slice * kSlice]);
-#pragma unroll
-                for (int k4 = 0; k4 < kSlice / 4; ++k4) ov[u][k4] = op[k4];
+                load_slice<PO, kSlice>(&wo[pr * D + slice * kSlice], ov[u]);
             }
             // Branch-free on purpose: every loaded value is used, so the
             // compiler keeps all of a trip's loads in flight together instead of
@@ -250,9 +249,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_tree_combine(
                 const float f = use ? __builtin_amdgcn_exp2f(mv[u] - base) : 0.f;
                 Lsum += use ? f * lv[u] : 0.f;
 #pragma unroll
-                for (int k4 = 0; k4 < kSlice / 4; ++k4)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[4 * k4 + e] += use ? f * ov[u][k4][e] : 0.f;
+                for (int k = 0; k < kSlice; ++k) acc[k] += use ? f * ov[u][k] : 0.f;
             }
             M = mb;
         }
@@ -430,7 +427,7 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
                  bool split) {
     const float scale2 = scale * kLog2e;
     const int64_t prow_total = split_prow_total(pl, hkv);
-    int2 *seqinfo = split_seqinfo(ws, pl, hkv, D);
+    int2 *seqinfo = split_seqinfo(ws, pl, hkv, D, sizeof(T));
 #define TD_SPLIT(OWN)                                                                          \
     TD_LAUNCH((attn_split_f32<D, OWN>), dim3(static_cast<unsigned>(pl.n_chunks * hkv)), \
                        dim3(kAttnThreads), 0, st, static_cast<const float *>(q),                \
@@ -507,9 +504,8 @@ void launch_attn(const void *q, const void *k_ctx, const void *v_ctx, const int6
 
 inline int sub_chunk(td_dtype dt) { return dt == TD_BF16 ? Sub<uint16_t>::CH : Sub<float>::CH; }
 
-inline size_t attn_ws_size(const AttnPlan &pl, int batch, int hkv, int D) {
-    const int64_t prow_total = pl.n_chunks * hkv * pl.n_rg * kRowsPerGroup;
-    return static_cast<size_t>(prow_total) * (2 + D) * sizeof(float) + static_cast<size_t>(batch) * 8;
+inline size_t attn_ws_size(const AttnPlan &pl, int batch, int hkv, int D, td_dtype dtype) {
+    return split_partial_bytes(pl, hkv, D, partial_o_bytes(dtype == TD_BF16)) + static_cast<size_t>(batch) * 8;
 }
 
 }  // namespace
@@ -518,7 +514,7 @@ size_t attn_workspace_bytes(int batch, int nq_max, int hq, int hkv, int head_dim
                             int64_t total_ctx, td_dtype dtype, bool fused_plan) {
     const AttnPlan pl = attn_plan(batch, nq_max, hq, hkv, total_ctx, sub_chunk(dtype),
                                   fused_plan ? kFusedItems : kAttnItems);
-    return std::max<size_t>(16, attn_ws_size(pl, batch, hkv, head_dim));
+    return std::max<size_t>(16, attn_ws_size(pl, batch, hkv, head_dim, dtype));
 }
 
 void launch_attention(const void *q, const void *k_ctx, const void *v_ctx, const int64_t *off,

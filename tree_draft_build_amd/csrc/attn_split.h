@@ -1064,8 +1064,9 @@ inline int2 *split_seqinfo(void *ws, const AttnPlan &pl, int hkv, int D, int o_b
 // builder publishes as one tagged word.  The other rows inside the tree are
 // stored after it; a larger tree continues with row groups
 // wave + 4, wave + 8, ... from the same buffer (their queries loaded one
-// group ahead).  The partials and chunk records are those of
-// attn_split_bf16.
+// group ahead).  A tree of fixed size (no S(N) stop) fills every row, so
+// there the workgroup computes all row groups at once and never waits.  The
+// partials and chunk records are those of attn_split_bf16.
 // ---------------------------------------------------------------------------
 constexpr int kFusedKeys = Sub<uint16_t>::CH;
 
@@ -1074,6 +1075,7 @@ struct SplitArgs {
     const int64_t *ctx_offsets, *ctx_lengths;
     const uint64_t *ready;  // [batch] tagged tree sizes: (1 << 32) | n
     uint32_t *status;       // kStatusSplit is raised here when the wait gives up
+    int all_rows;           // nonzero: every query row, without waiting (fixed-size trees)
     int batch, nq_max, hq, hkv, group, n_rg, chunk;
     float scale2;
     float *ws;
@@ -1160,6 +1162,21 @@ __device__ __forceinline__ void fused_split(const SplitArgs &a, int64_t item, Fu
     load_q(wave + kAttnWaves, qn);  // the group after it, should the tree be that large
     wait_vm<0>();
     __syncthreads();  // every wave's part of the chunk is in LDS
+    if (a.all_rows) {
+        // A tree of fixed size fills all nq_max rows (unless its candidates
+        // run out; rows past it are never read): every row group now, while
+        // the tree is being built, and no wait for its size.
+        const int rows_all = a.group * a.nq_max;
+        for (int rg = wave; rg < a.n_rg; rg += kAttnWaves) {
+            if (rg > wave) {
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks) qf[0][ks] = qn[0][ks];
+                if (rg + kAttnWaves < a.n_rg) load_q(rg + kAttnWaves, qn);
+            }
+            put(rg, run(qf), 0, rows_all);
+        }
+        return;
+    }
     RowState<D> st0;
     st0.init();
     if (wave < a.n_rg) {

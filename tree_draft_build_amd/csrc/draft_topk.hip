@@ -1176,6 +1176,7 @@ void launch_topk_tree_split(const void *logits, td_dtype dtype, int batch, int b
     sa.ctx_lengths = si.lens;
     sa.ready = to.ready;
     sa.status = static_cast<uint32_t *>(ws);
+    sa.all_rows = tp.use_stop == 0;
     sa.batch = batch;
     sa.nq_max = si.nq_max;
     sa.hq = si.hq;

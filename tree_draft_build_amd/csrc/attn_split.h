@@ -1119,8 +1119,8 @@ __device__ __forceinline__ void fused_split(const SplitArgs &a, int64_t item, Fu
         issue_rows<kFusedKeys, D, true>(valid > 0 ? a.v_ctx + at : a.q, kstride, valid > 0 ? valid : 1,
                                         L.buf + kVOff, wave, lane);
     }
-    // queries of row group rg in the B operand layout (rows past the last
-    // tree row read that row; they are never stored)
+    // queries of row group rg in the B operand layout (rows past the
+    // nq_max query rows read the last one; they are never stored)
     const uint16_t *qb = a.q + static_cast<int64_t>(b) * a.nq_max * a.hq * D;
     auto load_q = [&](int rg, bf16x8 (&qf)[1][D / 32]) __attribute__((always_inline)) {
         const int r = rg * kRowsPerGroup + col;

@@ -340,6 +340,53 @@ def test_attention_five_group_path(td, law):
                    n_nodes[b0:b1])
 
 
+def attn_inputs_with_lengths(cfg, lens):
+    """make_attn_inputs for explicit context lengths."""
+    parts = [wl.attn_inputs_for_seq(cfg, b, int(n)) for b, n in enumerate(lens)]
+    out = {k: np.concatenate([p[k] for p in parts], axis=0) if k in ("k_ctx", "v_ctx")
+           else np.stack([p[k] for p in parts], axis=0) for k in parts[0]}
+    lens = np.asarray(lens, np.int64)
+    out["ctx_offsets"] = wl.ctx_offsets(cfg, lens)
+    out["ctx_len"] = lens
+    return out
+
+
+@pytest.mark.parametrize("case", ["longest_first", "many_sequences"])
+def test_attention_chunk_order(td, case):
+    """Work items take the chunks longest first up to 64 sequences (every
+    full chunk, then the last chunks by decreasing length, ties by sequence)
+    and in sequence order beyond; the partial rows keep the sequence order.
+    longest_first: 24 sequences, 29,941 keys x 8 KV heads (1024-key chunks,
+    40 chunks, 320 work items): exact multiples of the chunk, empty and one-key contexts,
+    last chunks of equal length in different sequences, and more work items
+    than compute units.  many_sequences: 70 sequences (the scan over groups
+    of 64; 2048-key chunks), three of them several chunks long.  Every tree row of the
+    compared sequences against the oracle."""
+    say("attn chunk order", case)
+    if case == "longest_first":
+        lens = [3000, 952, 0, 1024, 2048, 5000, 1, 1023, 1025, 476, 1500, 2047,
+                904, 3000, 64, 700, 1, 1100, 2100, 952, 0, 900, 1024, 1100]
+        cmp = [(0, 12), (12, 24)]
+    else:
+        rng = np.random.default_rng(54)
+        lens = rng.integers(0, 1200, 70)
+        lens[[3, 40, 66]] = [9000, 5000, 7777]
+        lens[[10, 65]] = 0
+        cmp = [(0, 12), (38, 42), (62, 70)]
+    cfg = wl.CONFIGS["qwen3_8b"].replace(name="co", index=54, batch=len(lens), n_max=8,
+                                         use_stop=False, ctx_law="fixed", ctx_p0=0)
+    inp = attn_inputs_with_lengths(cfg, lens)
+    n_nodes = np.resize(np.array([8, 3, 0, 5, 1, 8, 2], np.int32), cfg.batch)
+    par = random_parents(np.random.default_rng(54), n_nodes, cfg.nq_max)
+    got, mask = run_attn(td, cfg, inp, par, n_nodes)
+    for b0, b1 in cmp:
+        want = oracle.tree_attn(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
+                                inp["k_tree"], inp["v_tree"], mask, n_nodes, cfg.hq, cfg.hkv,
+                                cfg.head_dim, wl.attn_scale(cfg), seqs=(b0, b1))
+        attn_close(got[b0:b1], want, "bf16", f"chunk order {case} seqs {b0}..{b1 - 1}",
+                   n_nodes[b0:b1])
+
+
 # ---------------------------------------------------------------------------
 # end to end: the whole path on the GPU vs the whole path in the oracle
 # ---------------------------------------------------------------------------

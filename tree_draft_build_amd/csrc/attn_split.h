@@ -112,15 +112,32 @@ __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
     return v;
 }
 
-// Locate chunk c of the contexts: sequence b, its key range, its first chunk
-// index and its chunk count.  A wave-uniform call: lane j takes sequence
-// s0 + j of each group of 64 (all lanes' loads in flight at once), an
-// inclusive scan of the chunk counts over the lanes finds the sequence whose
-// chunks cover c, and every lane gets the same result.  (A group's chunk
+// A value of lane j of the wave as a 64-bit scalar.
+__device__ __forceinline__ int64_t readlane64(int64_t v, int j) {
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), j));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), j));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Locate the chunk of work item c: sequence b, its key range, its first
+// chunk index and its chunk count; c is replaced by the chunk's index in
+// sequence order (the index of its partial rows).  A wave-uniform call.
+//
+// Up to 64 sequences, the items take the chunks longest first: every full
+// chunk (sequence order), then the sequences' last, shorter chunks by
+// decreasing length (ties: lower sequence first).  Workgroups start in about
+// item order, so the short chunks fill the gaps at the end of the grid
+// instead of a long chunk starting last.  Lane j holds sequence j; inclusive
+// scans of the chunk counts over the lanes place an item, and a tail's rank
+// is counted over the other lanes.
+//
+// More sequences: items in sequence order; lane j takes sequence s0 + j of
+// each group of 64 (all lanes' loads in flight at once) and a scan of the
+// chunk counts finds the sequence whose chunks cover c.  (A group's chunk
 // count fits 32 bits: a chunk holds at least 128 keys of the K buffer.)
 __device__ __forceinline__ bool find_chunk(const int64_t *__restrict__ off,
                                            const int64_t *__restrict__ lens, int batch, int chunk,
-                                           int64_t c, int &b, int64_t &k0, int64_t &k1,
+                                           int64_t &c, int &b, int64_t &k0, int64_t &k1,
                                            int64_t &cbase, int &nch) {
     if (batch == 1) {  // one sequence: uniform loads (scalar cache), no scan
         const int64_t L = seq_len(off, lens, 0);
@@ -134,6 +151,50 @@ __device__ __forceinline__ bool find_chunk(const int64_t *__restrict__ off,
         return true;
     }
     const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+    if (batch <= kWave) {
+        const bool in = lane < batch;
+        const int64_t L = in ? seq_len(off, lens, lane) : 0;
+        const uint32_t n = in ? static_cast<uint32_t>(chunks_of(L, chunk)) : 0u;
+        // the last chunk's length (0 for an empty context), and the full chunks
+        const uint32_t tlen = in ? static_cast<uint32_t>(L - static_cast<int64_t>(n - 1u) * chunk) : 0u;
+        const uint32_t f = in ? (tlen == static_cast<uint32_t>(chunk) ? n : n - 1u) : 0u;
+        const uint32_t tail = n - f;  // 1: the last chunk is short (or has no keys)
+        const uint32_t n_incl = wave_incl_sum(n);
+        const uint32_t f_incl = wave_incl_sum(f);
+        // the grid is sized for an upper bound of the chunk count
+        if (c >= static_cast<int64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(n_incl, kWave - 1))))
+            return false;
+        const int64_t full = static_cast<uint32_t>(__builtin_amdgcn_readlane(f_incl, kWave - 1));
+        int j;
+        int64_t local;  // the chunk's index within its sequence
+        if (c < full) {
+            const uint64_t hit = __ballot(in && c < static_cast<int64_t>(f_incl));
+            j = __ffsll(static_cast<long long>(hit)) - 1;  // uniform
+            local = c - (static_cast<int64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(f_incl, j))) -
+                         static_cast<uint32_t>(__builtin_amdgcn_readlane(f, j)));
+        } else {
+            const int64_t t = c - full;
+            uint32_t rank = 0;
+            for (int s = 0; s < batch; ++s) {
+                const uint32_t ts = static_cast<uint32_t>(__builtin_amdgcn_readlane(tail, s));
+                const uint32_t ls = static_cast<uint32_t>(__builtin_amdgcn_readlane(tlen, s));
+                rank += (ts != 0u && (ls > tlen || (ls == tlen && s < lane))) ? 1u : 0u;
+            }
+            const uint64_t hit = __ballot(in && tail != 0u && static_cast<int64_t>(rank) == t);
+            if (!hit) return false;
+            j = __ffsll(static_cast<long long>(hit)) - 1;
+            local = static_cast<uint32_t>(__builtin_amdgcn_readlane(f, j));
+        }
+        const uint32_t nj = static_cast<uint32_t>(__builtin_amdgcn_readlane(n, j));
+        const int64_t Lj = readlane64(L, j);
+        b = j;
+        cbase = static_cast<int64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(n_incl, j))) - nj;
+        c = cbase + local;
+        k0 = local * chunk;
+        k1 = std::min<int64_t>(Lj, k0 + chunk);
+        nch = static_cast<int>(nj);
+        return true;
+    }
     int64_t acc = 0;
     for (int s0 = 0; s0 < batch; s0 += kWave) {
         const int s = s0 + lane;
@@ -146,9 +207,7 @@ __device__ __forceinline__ bool find_chunk(const int64_t *__restrict__ off,
             const int j = __ffsll(static_cast<long long>(hit)) - 1;  // uniform
             const uint32_t incj = __builtin_amdgcn_readlane(inc, j);
             const uint32_t nj = __builtin_amdgcn_readlane(n, j);
-            const int64_t Lj = static_cast<int64_t>(
-                (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(L >> 32), j))) << 32) |
-                static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(L), j)));
+            const int64_t Lj = readlane64(L, j);
             b = s0 + j;
             cbase = acc + static_cast<int64_t>(incj) - static_cast<int64_t>(nj);
             k0 = (c - cbase) * chunk;
@@ -317,7 +376,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_f32(
     T *sK = reinterpret_cast<T *>(lds);
     T *sV = sK + CH * L::KP;
 
-    const int64_t c = blockIdx.x / hkv;
+    int64_t c = blockIdx.x / hkv;  // the work item, then its chunk
     const int g = static_cast<int>(blockIdx.x % hkv);
     int b, nch;
     int64_t k0, k1, cbase;
@@ -343,7 +402,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_f32(
         const int valid0 = static_cast<int>(std::min<int64_t>(CH, k1 - k0));
         stage.load(kbase + k0 * kstride, vbase + k0 * kstride, kstride, valid0, tid);
     }
-    const int rows_b = group * min(n_nodes[b] + 1, nq_max);
+    const int rows_b = group * min(__builtin_amdgcn_readfirstlane(n_nodes[b]) + 1, nq_max);
     const int n_rg_b = (rows_b + kRowsPerGroup - 1) / kRowsPerGroup;
     const T *qb = q + static_cast<int64_t>(b) * nq_max * hq * D;
 
@@ -806,7 +865,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
     static_assert((kRing - 2) * kLoads < 64, "the loads of the sub-chunks in flight fit the wait counter");
     auto ring = [&](int sc) { return sring + (sc % kRing) * kSubElems; };
 
-    const int64_t c = blockIdx.x / hkv;
+    int64_t c = blockIdx.x / hkv;  // the work item, then its chunk
     const int g = static_cast<int>(blockIdx.x % hkv);
     int b, nch;
     int64_t k0, k1, cbase;
@@ -841,7 +900,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16(
         issue_rows<SUB, D, true>(v_ > 0 ? vbase + s0_ : q, static_cast<int>(kstride),          \
                                       v_ > 0 ? v_ : 1, buf + kVOff, wave, lane);               \
     }
-    const int nn_b = n_nodes[b];  // in flight while the first loads are issued
+    // in flight while the first loads are issued; read as uniform (else the
+    // compiler may run the key loops' control on the vector unit)
+    const int nn_b = __builtin_amdgcn_readfirstlane(n_nodes[b]);
     const uint16_t *qb = q + static_cast<int64_t>(b) * nq_max * hq * D;
     // Row group 0 (tree rows of the root onwards) always has work: its
     // queries load now rather than after the tree size arrives.
@@ -1097,7 +1158,7 @@ constexpr int kNoTree = -0x40000000;  // the wait gave up
 template <int D>
 __device__ __forceinline__ void fused_split(const SplitArgs &a, int64_t item, FusedSplitLds<D> &L) {
     constexpr int kVOff = sub_k_elems<kFusedKeys, D>();
-    const int64_t c = item / a.hkv;
+    int64_t c = item / a.hkv;  // the work item, then its chunk
     const int g = static_cast<int>(item % a.hkv);
     int b, nch;
     int64_t k0, k1, cbase;

@@ -387,6 +387,34 @@ def test_attention_chunk_order(td, case):
                    n_nodes[b0:b1])
 
 
+def test_attention_split_invariance(td):
+    """One sequence (5000 keys, a 16-node tree) alone and as sequence 0 of a
+    batch of 12: alone its context splits into 256-key chunks (20 partials
+    per row), in the batch into 4096-key chunks (2 partials).  Both results
+    meet the oracle bound, and they agree with each other far more tightly
+    (only the summation order of the partials differs)."""
+    say("attn split invariance")
+    cfg = wl.CONFIGS["qwen3_8b"].replace(name="si", index=55, batch=12, n_max=16, use_stop=False,
+                                         ctx_law="fixed", ctx_p0=0)
+    lens = [5000] + [20000 + 997 * i for i in range(11)]
+    n_nodes = np.array([16, 3, 0, 16, 5, 1, 8, 2, 16, 4, 7, 9], np.int32)
+    par = random_parents(np.random.default_rng(55), n_nodes, cfg.nq_max)
+    inp = attn_inputs_with_lengths(cfg, lens)
+    got_b, mask_b = run_attn(td, cfg, inp, par, n_nodes)
+    one = cfg.replace(batch=1)
+    inp1 = attn_inputs_with_lengths(one, lens[:1])
+    got_1, mask_1 = run_attn(td, one, inp1, par[:1], n_nodes[:1])
+    np.testing.assert_array_equal(mask_1[0], mask_b[0])
+    want = oracle.tree_attn(inp1["q"], inp1["k_ctx"], inp1["v_ctx"], inp1["ctx_offsets"],
+                            inp1["k_tree"], inp1["v_tree"], mask_1, n_nodes[:1], cfg.hq, cfg.hkv,
+                            cfg.head_dim, wl.attn_scale(cfg))
+    attn_close(got_1, want, "bf16", "split invariance: alone", n_nodes[:1])
+    attn_close(got_b[:1], want, "bf16", "split invariance: in the batch", n_nodes[:1])
+    rows = int(n_nodes[0]) + 1
+    diff = np.abs(got_1[0, :rows] - got_b[0, :rows]).max()
+    assert diff <= 2e-3, f"alone vs in the batch: {diff:.3g}"
+
+
 # ---------------------------------------------------------------------------
 # end to end: the whole path on the GPU vs the whole path in the oracle
 # ---------------------------------------------------------------------------
